@@ -1,0 +1,134 @@
+"""CPU oracle of the SplitZip-style exponent codec (format v1).
+
+TEST INFRASTRUCTURE ONLY.  Only `tests/`, `__graft_entry__.smoke()` and the
+CPU-baseline leg of `bench.py` may import this package.  The GPU library and
+its Python binding never import it, and it imports nothing from them.
+
+Two independent implementations of the same stream format live here:
+  * `sz_oracle.c` -- plain scalar C, loaded through ctypes (`encode`,
+    `decode`, `histogram`, `codebook`, `max_bytes`, `exact_bytes` below);
+  * `sz_ref.py`   -- pure Python, for tiny inputs and cross-checks.
+The format and every reading taken where the SplitZip project page is silent
+are written out in the header comment of `sz_oracle.c`.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+BF16 = 1
+E5M2 = 2
+OK, INVALID_ARGUMENT, BUFFER_TOO_SMALL, CORRUPT_STREAM = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sz_oracle.c")
+_LIB = os.path.join(_HERE, "libszoracle.so")
+_lib = None
+
+
+def build():
+    """Compile the C oracle with gcc -O2 (plain scalar code, no intrinsics)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+                           "-o", tmp, _SRC])
+    os.replace(tmp, _LIB)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    u64, i32, vp = ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p
+    lib.szo_max_bytes.argtypes = [u64, i32]
+    lib.szo_max_bytes.restype = u64
+    lib.szo_exact_bytes.argtypes = [u64, i32, u64]
+    lib.szo_exact_bytes.restype = u64
+    lib.szo_histogram.argtypes = [vp, u64, i32, vp]
+    lib.szo_histogram.restype = i32
+    lib.szo_codebook.argtypes = [vp, i32, vp]
+    lib.szo_codebook.restype = i32
+    lib.szo_encode.argtypes = [vp, u64, i32, vp, vp, u64, vp]
+    lib.szo_encode.restype = i32
+    lib.szo_decode.argtypes = [vp, u64, u64, i32, vp]
+    lib.szo_decode.restype = i32
+    _lib = lib
+    return lib
+
+
+def _raw(values, dt):
+    a = np.ascontiguousarray(values)
+    want = np.uint16 if dt == BF16 else np.uint8
+    if a.dtype != want:
+        a = a.view(want) if a.dtype.itemsize == np.dtype(want).itemsize else a.astype(want)
+    return np.ascontiguousarray(a.reshape(-1))
+
+
+def max_bytes(n, dt):
+    return int(_load().szo_max_bytes(n, dt))
+
+
+def exact_bytes(n, dt, escapes):
+    return int(_load().szo_exact_bytes(n, dt, escapes))
+
+
+def histogram(values, dt):
+    a = _raw(values, dt)
+    h = np.zeros(256, np.uint64)
+    rc = _load().szo_histogram(a.ctypes.data, a.size, dt, h.ctypes.data)
+    if rc:
+        raise ValueError(f"szo_histogram failed: {rc}")
+    return h
+
+
+def codebook(hist, dt):
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    cb = np.zeros(16, np.uint8)
+    rc = _load().szo_codebook(h.ctypes.data, dt, cb.ctypes.data)
+    if rc:
+        raise ValueError(f"szo_codebook failed: {rc}")
+    return cb
+
+
+def encode(values, dt, cb=None):
+    """Encode raw elements (uint16 BF16 bit patterns or uint8 E5M2 bytes);
+    returns the stream as a numpy uint8 array of exactly C bytes."""
+    a = _raw(values, dt)
+    cap = max_bytes(a.size, dt)
+    out = np.zeros(max(cap, 1), np.uint8)
+    nbytes = ctypes.c_uint64(0)
+    cbp = None
+    if cb is not None:
+        if isinstance(cb, (bytes, bytearray)):
+            cb = np.frombuffer(bytes(cb), np.uint8)
+        cbv = np.ascontiguousarray(cb, dtype=np.uint8)
+        assert cbv.size == 16
+        cbp = cbv.ctypes.data
+    rc = _load().szo_encode(a.ctypes.data if a.size else None, a.size, dt, cbp,
+                            out.ctypes.data, cap, ctypes.byref(nbytes))
+    if rc:
+        raise ValueError(f"szo_encode failed: {rc}")
+    return out[:nbytes.value].copy()
+
+
+def decode(stream, n, dt):
+    """Returns (status, raw elements or None)."""
+    s = np.ascontiguousarray(stream, dtype=np.uint8)
+    out = np.zeros(max(n, 1), np.uint16 if dt == BF16 else np.uint8)
+    rc = _load().szo_decode(s.ctypes.data if s.size else None, s.size, n, dt, out.ctypes.data)
+    if rc != OK:
+        return rc, None
+    return OK, out[:n]
+
+
+def stream_fields(stream):
+    """Header fields of a stream (for tests and reports)."""
+    s = bytes(np.ascontiguousarray(stream, dtype=np.uint8)[:64])
+    return {
+        "magic": s[0:4], "version": s[4], "dtype": s[5], "log2_block": s[6], "ncodes": s[7],
+        "n": int.from_bytes(s[8:16], "little"), "escapes": int.from_bytes(s[16:24], "little"),
+        "codebook": list(s[24:40]), "bytes": int.from_bytes(s[40:48], "little"),
+    }

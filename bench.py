@@ -1,0 +1,234 @@
+"""Benchmark of the lossless exponent codec on one MI355X.
+
+Workload (default): a Llama-3-8B-shaped BF16 KV cache, 32 layers x {K, V}
+tensors of [8192 tokens, 8 KV heads, 128 head_dim] = 64 x 2^23 elements
+(1.074 GB), one codebook per layer tensor, synthetic values (N(0,1) times a
+per-channel lognormal scale, 4 x20 outlier channels per K head).
+
+One step = the whole hot path over the whole cache: exponent histograms ->
+codebooks -> encode -> decode, each one batched launch over the 64 tensors,
+inputs resident in HBM before the timed region.  Throughput counts raw
+input bytes (GB = 1e9).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+                    [--mode bench|profile|copy] [--no-cpu-baseline]
+"""
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+LAYERS, SHAPE = 32, (8192, 8, 128)
+KERNEL_SOURCE = os.path.join(ROOT, "fp8_kv_cache_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--mode", choices=["bench", "profile", "copy"], default="bench")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if missing or taken on different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def make_inputs():
+    import kvsynth
+    with cf.ThreadPoolExecutor(8) as pool:
+        return list(pool.map(lambda i: kvsynth.llama_kv(i // 2, i % 2, SHAPE), range(2 * LAYERS)))
+
+
+def copy_calibration(torch):
+    """A plain copy of a known size, for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters: 1 GiB read + 1 GiB written per launch."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": 1 << 30, "bytes_written_per_launch": 1 << 30}))
+
+
+def cpu_baseline(xs):
+    """The CPU oracle (plain scalar C) on this host: encode + decode of
+    every layer tensor, one tensor per thread."""
+    import oracle
+    oracle._load()
+    threads = min(16, os.cpu_count() or 1, len(xs))
+
+    def round_trip(x):
+        s = oracle.encode(x, oracle.BF16)
+        status, _ = oracle.decode(s, x.size, oracle.BF16)
+        assert status == oracle.OK
+        return s.size
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as pool:
+        list(pool.map(round_trip, xs))
+    dt = time.perf_counter() - t0
+    raw = sum(x.nbytes for x in xs)
+    return {
+        "value": raw / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"encode+decode round trip of all {len(xs)} layer tensors (2^23 BF16 each, "
+                  f"{raw / 1e9:.3f} GB raw), one tensor per thread, {dt:.2f} s wall",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the codec is per-tensor data-parallel with no cross-GPU exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_kv_cache_amd as sz
+    from fp8_kv_cache_amd.codec import BatchCodec
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.mode == "copy":
+        copy_calibration(torch)
+        return
+
+    xs = make_inputs()
+    n = xs[0].size
+    count = len(xs)
+    raw_bytes = sum(x.nbytes for x in xs)
+    bc = BatchCodec(count, n, sz.SZ_DTYPE_BF16)
+    bc.set_inputs([torch.from_numpy(x.view(np.int16)).to("cuda") for x in xs])
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        bc.histogram()
+        if ev:
+            ev[1].record(stream)
+        bc.build_codebooks()
+        if ev:
+            ev[2].record(stream)
+        bc.encode()
+        if ev:
+            ev[3].record(stream)
+        bc.decompress()
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # correctness of the timed configuration: every tensor round-trips
+    for i in range(count):
+        assert int(bc.status[i]) == 0 and torch.equal(bc.output(i), bc._inputs[i]), i
+
+    steps = args.steps if args.mode == "bench" else min(args.steps, 3)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def ms(a, b):
+        return [events[k][a].elapsed_time(events[k][b]) for k in range(steps)]
+
+    hist_ms, cb_ms, enc_ms, dec_ms, step_ms = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4), ms(0, 4)
+    med = lambda v: float(np.median(v))
+    sizes = bc.sizes.cpu().numpy()
+    stream_bytes = int(sizes.sum())
+    ratio = raw_bytes / stream_bytes
+
+    # algorithmic bytes per launch (one launch covers all 64 tensors)
+    alg = {
+        "k_histogram": raw_bytes,                       # read input once
+        "k_encode": raw_bytes + stream_bytes,           # read input, write stream
+        "k_decode": stream_bytes + raw_bytes,           # read stream, write output
+    }
+    launch_ms = {"k_histogram": med(hist_ms), "k_encode": med(enc_ms), "k_decode": med(dec_ms)}
+    dominant = max(launch_ms, key=launch_ms.get)
+    per_kernel = {}
+    for k in alg:
+        gbps = alg[k] / (launch_ms[k] * 1e-3) / 1e9
+        per_kernel[k] = {"ms": launch_ms[k], "algorithmic_bytes": alg[k], "achieved_GBps": gbps,
+                         "frac": gbps / HBM_PEAK_GBPS}
+    traffic = traffic_for(dominant)
+    roofline = {
+        "bound": "hbm", "achieved": per_kernel[dominant]["achieved_GBps"], "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s", "frac": per_kernel[dominant]["frac"], "traffic": traffic,
+        "kernel": dominant,
+    }
+
+    enc_total_ms = med([h + c + e for h, c, e in zip(hist_ms, cb_ms, enc_ms)])
+    encode_gbps = raw_bytes / (enc_total_ms * 1e-3) / 1e9
+    decode_gbps = raw_bytes / (med(dec_ms) * 1e-3) / 1e9
+    # encode phase needs the whole histogram before coding: input read twice
+    enc_two_pass = (2 * raw_bytes + stream_bytes) / (enc_total_ms * 1e-3) / 1e9
+    enc_strict = (raw_bytes + stream_bytes) / (enc_total_ms * 1e-3) / 1e9
+
+    step_med = med(step_ms)
+    result = {
+        "metric": "encode & decode GB/s (raw input bytes) + % HBM roofline; compression ratio",
+        "value": raw_bytes / (step_med * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_med,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b-kv-cache-bf16", "tensors": count, "elements_per_tensor": n,
+                   "shape": list(SHAPE), "raw_bytes": raw_bytes, "codebook": "per layer tensor"},
+        "value_definition": "raw bytes / (histogram + codebook + encode + decode) per step",
+        "encode_GBps": encode_gbps,
+        "decode_GBps": decode_gbps,
+        "encode_hbm_frac_two_pass": enc_two_pass / HBM_PEAK_GBPS,
+        "encode_hbm_frac_strict": enc_strict / HBM_PEAK_GBPS,
+        "decode_hbm_frac": (raw_bytes + stream_bytes) / (med(dec_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "compression_ratio": ratio,
+        "phase_ms": {"histogram": med(hist_ms), "codebook": med(cb_ms), "encode": med(enc_ms),
+                     "decode": med(dec_ms)},
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "wall_s_timed": wall,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if args.mode == "bench" and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(xs)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

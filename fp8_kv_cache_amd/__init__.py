@@ -1,0 +1,155 @@
+"""Python binding of libsplitzip.so, the gfx950 lossless exponent codec for
+BF16 and FP8-E5M2 KV-cache tensors (SplitZip project page, "Abstract").
+
+Thin ctypes marshalling over the C ABI declared in include/splitzip.h: the
+functions below carry the C names and arguments.  Pointer arguments accept
+a torch tensor (its data_ptr()), a plain integer address or None; `stream`
+defaults to torch's current stream.  torch provides device memory and
+streams only -- every step of the codec runs in the library's HIP kernels.
+
+The library must be built (python -m fp8_kv_cache_amd.build); importing this
+package without it raises ImportError, there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch  # load torch's HIP runtime first; the library binds to it
+
+__all__ = [
+    "SZ_DTYPE_BF16", "SZ_DTYPE_FP8_E5M2", "SZ_OK", "SZ_ERR_INVALID_ARGUMENT",
+    "SZ_ERR_BUFFER_TOO_SMALL", "SZ_ERR_CORRUPT_STREAM", "SZ_ERR_HIP", "SzError",
+    "sz_max_compressed_bytes", "sz_encode_workspace_bytes", "sz_encode_workspace_bytes_batched",
+    "sz_histogram", "sz_build_codebook", "sz_encode", "sz_decode",
+    "sz_histogram_batched", "sz_build_codebook_batched", "sz_encode_batched", "sz_decode_batched",
+    "sz_status_string", "check", "pointer_table", "library_path",
+]
+
+SZ_DTYPE_BF16 = 1
+SZ_DTYPE_FP8_E5M2 = 2
+SZ_OK = 0
+SZ_ERR_INVALID_ARGUMENT = 1
+SZ_ERR_BUFFER_TOO_SMALL = 2
+SZ_ERR_CORRUPT_STREAM = 3
+SZ_ERR_HIP = 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is not built; run `python -m fp8_kv_cache_amd.build`")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+_u64, _u32, _i32, _vp = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p
+
+_SIGNATURES = {
+    "sz_max_compressed_bytes": (_u64, [_u64, _i32]),
+    "sz_encode_workspace_bytes": (_u64, [_u64, _i32]),
+    "sz_encode_workspace_bytes_batched": (_u64, [_u32, _u64, _i32]),
+    "sz_histogram": (_i32, [_vp, _u64, _i32, _vp, _vp]),
+    "sz_build_codebook": (_i32, [_vp, _i32, _vp, _vp]),
+    "sz_encode": (_i32, [_vp, _u64, _i32, _vp, _vp, _u64, _vp, _vp, _u64, _vp]),
+    "sz_decode": (_i32, [_vp, _u64, _u64, _i32, _vp, _vp, _vp]),
+    "sz_histogram_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp]),
+    "sz_build_codebook_batched": (_i32, [_vp, _u32, _i32, _vp, _vp]),
+    "sz_encode_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp, _u64, _vp, _vp, _u64, _vp]),
+    "sz_decode_batched": (_i32, [_vp, _vp, _u32, _u64, _i32, _vp, _vp, _vp]),
+    "sz_status_string": (ctypes.c_char_p, [_i32]),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class SzError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: {sz_status_string(status)} ({status})" if what else sz_status_string(status))
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s):
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, torch.cuda.Stream):
+        return s.cuda_stream
+    return int(s)
+
+
+def check(status, what=""):
+    """Raise SzError unless status is SZ_OK; returns status."""
+    if status != SZ_OK:
+        raise SzError(status, what)
+    return status
+
+
+def pointer_table(tensors, device=None):
+    """Device int64 tensor holding the data pointers of `tensors`, for the
+    batched calls' pointer-table arguments."""
+    device = device or tensors[0].device
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+def sz_status_string(status):
+    return _lib.sz_status_string(status).decode()
+
+
+def sz_max_compressed_bytes(n, dtype):
+    return _lib.sz_max_compressed_bytes(n, dtype)
+
+
+def sz_encode_workspace_bytes(n, dtype):
+    return _lib.sz_encode_workspace_bytes(n, dtype)
+
+
+def sz_encode_workspace_bytes_batched(count, n, dtype):
+    return _lib.sz_encode_workspace_bytes_batched(count, n, dtype)
+
+
+def sz_histogram(src, n, dtype, hist, stream=None):
+    return _lib.sz_histogram(_ptr(src), n, dtype, _ptr(hist), _stream(stream))
+
+
+def sz_build_codebook(hist, dtype, codebook, stream=None):
+    return _lib.sz_build_codebook(_ptr(hist), dtype, _ptr(codebook), _stream(stream))
+
+
+def sz_encode(src, n, dtype, codebook, dst, dst_capacity, out_bytes, workspace, workspace_bytes,
+              stream=None):
+    return _lib.sz_encode(_ptr(src), n, dtype, _ptr(codebook), _ptr(dst), dst_capacity,
+                          _ptr(out_bytes), _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def sz_decode(src, src_bytes, n, dtype, dst, status=None, stream=None):
+    return _lib.sz_decode(_ptr(src), src_bytes, n, dtype, _ptr(dst), _ptr(status), _stream(stream))
+
+
+def sz_histogram_batched(srcs, count, n, dtype, hists, stream=None):
+    return _lib.sz_histogram_batched(_ptr(srcs), count, n, dtype, _ptr(hists), _stream(stream))
+
+
+def sz_build_codebook_batched(hists, count, dtype, codebooks, stream=None):
+    return _lib.sz_build_codebook_batched(_ptr(hists), count, dtype, _ptr(codebooks), _stream(stream))
+
+
+def sz_encode_batched(srcs, count, n, dtype, codebooks, dsts, dst_capacity, out_bytes, workspace,
+                      workspace_bytes, stream=None):
+    return _lib.sz_encode_batched(_ptr(srcs), count, n, dtype, _ptr(codebooks), _ptr(dsts),
+                                  dst_capacity, _ptr(out_bytes), _ptr(workspace), workspace_bytes,
+                                  _stream(stream))
+
+
+def sz_decode_batched(srcs, src_bytes, count, n, dtype, dsts, status=None, stream=None):
+    return _lib.sz_decode_batched(_ptr(srcs), _ptr(src_bytes), count, n, dtype, _ptr(dsts),
+                                  _ptr(status), _stream(stream))

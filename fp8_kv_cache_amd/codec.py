@@ -1,0 +1,104 @@
+"""Allocation helpers over the C ABI: torch allocates the device buffers, the
+library's kernels do all the work (histogram -> codebook -> encode, and
+decode).  Raw elements are passed as torch tensors of 16-bit words (BF16 bit
+patterns, dtype int16/bfloat16) or bytes (E5M2, dtype uint8/float8_e5m2).
+"""
+import torch
+
+from . import (SZ_DTYPE_BF16, SZ_DTYPE_FP8_E5M2, check, pointer_table, sz_build_codebook,
+               sz_build_codebook_batched, sz_decode, sz_decode_batched, sz_encode, sz_encode_batched,
+               sz_encode_workspace_bytes, sz_encode_workspace_bytes_batched, sz_histogram,
+               sz_histogram_batched, sz_max_compressed_bytes)
+
+ELEMENT_BYTES = {SZ_DTYPE_BF16: 2, SZ_DTYPE_FP8_E5M2: 1}
+
+
+def _raw_dtype(dtype):
+    return torch.int16 if dtype == SZ_DTYPE_BF16 else torch.uint8
+
+
+def compress(x, dtype, codebook=None, stream=None):
+    """Encode one tensor.  Returns (stream bytes as a uint8 tensor of exactly
+    C bytes, histogram int64[256] or None, codebook uint8[16])."""
+    dev = x.device
+    n = x.numel()
+    hist = None
+    if codebook is None:
+        hist = torch.empty(256, dtype=torch.int64, device=dev)
+        codebook = torch.empty(16, dtype=torch.uint8, device=dev)
+        check(sz_histogram(x, n, dtype, hist, stream), "sz_histogram")
+        check(sz_build_codebook(hist, dtype, codebook, stream), "sz_build_codebook")
+    cap = sz_max_compressed_bytes(n, dtype)
+    dst = torch.empty(cap, dtype=torch.uint8, device=dev)
+    out_bytes = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_bytes = sz_encode_workspace_bytes(n, dtype)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    check(sz_encode(x if n else None, n, dtype, codebook, dst, cap, out_bytes, ws, ws_bytes, stream),
+          "sz_encode")
+    size = int(out_bytes.item())
+    return dst[:size], hist, codebook
+
+
+def decompress(stream_bytes, n, dtype, src_bytes=None, stream=None):
+    """Decode one stream.  Returns (raw elements tensor, device status)."""
+    dev = stream_bytes.device
+    out = torch.empty(max(n, 1), dtype=_raw_dtype(dtype), device=dev)[:n]
+    status = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    nbytes = stream_bytes.numel() if src_bytes is None else src_bytes
+    check(sz_decode(stream_bytes, nbytes, n, dtype, out if n else None, status, stream), "sz_decode")
+    return out, int(status.item())
+
+
+class BatchCodec:
+    """Device buffers for `count` tensors of n elements each: histograms,
+    codebooks, streams (each sz_max_compressed_bytes long), sizes,
+    workspace, decode outputs and statuses, plus their pointer tables."""
+
+    def __init__(self, count, n, dtype, device="cuda"):
+        self.count, self.n, self.dtype = count, n, dtype
+        self.capacity = sz_max_compressed_bytes(n, dtype)
+        cap = -(-self.capacity // 256) * 256
+        self.hists = torch.zeros(count, 256, dtype=torch.int64, device=device)
+        self.codebooks = torch.zeros(count, 16, dtype=torch.uint8, device=device)
+        self.streams = torch.empty(count, cap, dtype=torch.uint8, device=device)
+        self.sizes = torch.zeros(count, dtype=torch.int64, device=device)
+        self.ws_bytes = sz_encode_workspace_bytes_batched(count, n, dtype)
+        self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.outputs = torch.empty(count, max(n, 1) * ELEMENT_BYTES[dtype], dtype=torch.uint8, device=device)
+        self.status = torch.full((count,), -1, dtype=torch.int32, device=device)
+        self.stream_ptrs = pointer_table([self.streams[i] for i in range(count)])
+        self.output_ptrs = pointer_table([self.outputs[i] for i in range(count)])
+        self.src_ptrs = None
+
+    def set_inputs(self, tensors):
+        assert len(tensors) == self.count
+        self._inputs = list(tensors)  # keep alive
+        self.src_ptrs = pointer_table(self._inputs)
+
+    def histogram(self, stream=None):
+        check(sz_histogram_batched(self.src_ptrs, self.count, self.n, self.dtype, self.hists, stream),
+              "sz_histogram_batched")
+
+    def build_codebooks(self, stream=None):
+        check(sz_build_codebook_batched(self.hists, self.count, self.dtype, self.codebooks, stream),
+              "sz_build_codebook_batched")
+
+    def encode(self, stream=None):
+        check(sz_encode_batched(self.src_ptrs, self.count, self.n, self.dtype, self.codebooks,
+                                self.stream_ptrs, self.capacity, self.sizes, self.workspace,
+                                self.ws_bytes, stream), "sz_encode_batched")
+
+    def compress(self, stream=None):
+        self.histogram(stream)
+        self.build_codebooks(stream)
+        self.encode(stream)
+
+    def decompress(self, stream=None):
+        check(sz_decode_batched(self.stream_ptrs, self.sizes, self.count, self.n, self.dtype,
+                                self.output_ptrs, self.status, stream), "sz_decode_batched")
+
+    def stream(self, i):
+        return self.streams[i, :int(self.sizes[i].item())]
+
+    def output(self, i):
+        return self.outputs[i, :self.n * ELEMENT_BYTES[self.dtype]].view(_raw_dtype(self.dtype))

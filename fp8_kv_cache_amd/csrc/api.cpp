@@ -1,0 +1,194 @@
+// api.cpp -- C ABI entry points of the exponent codec (declared and
+// documented in include/splitzip.h).  Every entry point validates its
+// arguments on the host, then enqueues kernels on the caller's stream; it
+// never allocates, frees or synchronises.
+#include "splitzip.h"
+
+#include "sz_internal.h"
+
+#define SZ_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace sz;
+
+constexpr uint64_t kMaxElems = uint64_t(1) << 32;   // offsets are u32
+constexpr uint64_t kWorkspaceHead = 256;            // ticket counter area
+
+bool dtype_ok(sz_dtype dt) { return dt == SZ_DTYPE_BF16 || dt == SZ_DTYPE_FP8_E5M2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool usable(const void* p) { return p != nullptr && aligned16(p); }
+
+sz_status from_hip(hipError_t e) { return e == hipSuccess ? SZ_OK : SZ_ERR_HIP; }
+
+uint64_t workspace_bytes(uint32_t count, uint64_t n) {
+    return kWorkspaceHead + 8 * static_cast<uint64_t>(count) * layout_of(n, kDtypeBF16).blocks;
+}
+
+// histogram workgroups per tensor: about 2048 workgroups in total, each
+// covering a multiple of 32768 elements
+void hist_split(uint32_t count, uint64_t n, uint32_t& groups, uint64_t& chunk) {
+    const uint64_t quantum = 32768;
+    uint64_t want = 2048 / (count ? count : 1);
+    if (want < 1) want = 1;
+    const uint64_t units = (n + quantum - 1) / quantum;
+    if (want > units) want = units ? units : 1;
+    chunk = (units + want - 1) / want * quantum;
+    groups = static_cast<uint32_t>((n + chunk - 1) / chunk);
+    if (groups == 0) groups = 1;
+}
+
+sz_status histogram_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint64_t* d_hists,
+                         hipStream_t s) {
+    hipError_t e = launch_fill_u64(d_hists, 256ull * count, 0, s);
+    if (e != hipSuccess || n == 0) return from_hip(e);
+    HistArgs a{};
+    a.src = src;
+    a.hists = d_hists;
+    a.count = count;
+    a.n = n;
+    hist_split(count, n, a.groups, a.chunk);
+    return from_hip(launch_histogram(a, dt, s));
+}
+
+sz_status encode_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, const uint8_t* d_codebooks,
+                      DstRef dst, uint64_t* d_out_bytes, void* d_workspace, hipStream_t s) {
+    EncodeArgs a{};
+    a.src = src;
+    a.dst = dst;
+    a.codebooks = d_codebooks;
+    a.out_bytes = d_out_bytes;
+    a.count = count;
+    a.n = n;
+    if (n == 0) return from_hip(launch_encode_empty(a, dt, s));
+    a.ticket = static_cast<uint32_t*>(d_workspace);
+    a.status = reinterpret_cast<uint64_t*>(static_cast<char*>(d_workspace) + kWorkspaceHead);
+    hipError_t e = launch_fill_u64(static_cast<uint64_t*>(d_workspace), workspace_bytes(count, n) / 8, 0, s);
+    if (e != hipSuccess) return SZ_ERR_HIP;
+    return from_hip(launch_encode(a, dt, s));
+}
+
+sz_status decode_impl(SrcRef src, const uint64_t* d_src_bytes, uint64_t src_bytes, uint32_t count,
+                      uint64_t n, sz_dtype dt, DstRef dst, int32_t* d_status, hipStream_t s) {
+    if (d_status) {
+        hipError_t e = launch_fill_i32(d_status, count, SZ_OK, s);
+        if (e != hipSuccess) return SZ_ERR_HIP;
+    }
+    DecodeArgs a{};
+    a.src = src;
+    a.src_bytes_table = d_src_bytes;
+    a.src_bytes = src_bytes;
+    a.dst = dst;
+    a.status = d_status;
+    a.count = count;
+    a.n = n;
+    if (n == 0) return from_hip(launch_decode_empty(a, dt, s));
+    return from_hip(launch_decode(a, dt, s));
+}
+
+}  // namespace
+
+SZ_EXPORT uint64_t sz_max_compressed_bytes(uint64_t n, sz_dtype dtype) {
+    if (!dtype_ok(dtype) || n >= kMaxElems) return 0;
+    return layout_of(n, dtype).esc_at + n;
+}
+
+SZ_EXPORT uint64_t sz_encode_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype dtype) {
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0) return 0;
+    return workspace_bytes(count, n);
+}
+
+SZ_EXPORT uint64_t sz_encode_workspace_bytes(uint64_t n, sz_dtype dtype) {
+    return sz_encode_workspace_bytes_batched(1, n, dtype);
+}
+
+SZ_EXPORT sz_status sz_histogram(const void* d_src, uint64_t n, sz_dtype dtype, uint64_t* d_hist,
+                                 hipStream_t stream) {
+    if (!dtype_ok(dtype) || n >= kMaxElems || !usable(d_hist) || (n && !usable(d_src)))
+        return SZ_ERR_INVALID_ARGUMENT;
+    return histogram_impl(SrcRef{nullptr, d_src}, 1, n, dtype, d_hist, stream);
+}
+
+SZ_EXPORT sz_status sz_histogram_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
+                                         sz_dtype dtype, uint64_t* d_hists, hipStream_t stream) {
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !usable(d_hists) || !usable(d_srcs))
+        return SZ_ERR_INVALID_ARGUMENT;
+    return histogram_impl(SrcRef{d_srcs, nullptr}, count, n, dtype, d_hists, stream);
+}
+
+SZ_EXPORT sz_status sz_build_codebook_batched(const uint64_t* d_hists, uint32_t count, sz_dtype dtype,
+                                              uint8_t* d_codebooks, hipStream_t stream) {
+    if (!dtype_ok(dtype) || count == 0 || !usable(d_hists) || !usable(d_codebooks))
+        return SZ_ERR_INVALID_ARGUMENT;
+    CodebookArgs a{d_hists, d_codebooks, count};
+    return from_hip(launch_codebook(a, dtype, stream));
+}
+
+SZ_EXPORT sz_status sz_build_codebook(const uint64_t* d_hist, sz_dtype dtype, uint8_t* d_codebook,
+                                      hipStream_t stream) {
+    return sz_build_codebook_batched(d_hist, 1, dtype, d_codebook, stream);
+}
+
+SZ_EXPORT sz_status sz_encode(const void* d_src, uint64_t n, sz_dtype dtype, const uint8_t* d_codebook,
+                              void* d_dst, uint64_t dst_capacity, uint64_t* d_out_bytes,
+                              void* d_workspace, uint64_t workspace_bytes_given, hipStream_t stream) {
+    if (!dtype_ok(dtype) || n >= kMaxElems || !usable(d_codebook) || !usable(d_dst) ||
+        (n && !usable(d_src)) || (d_out_bytes && (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)))
+        return SZ_ERR_INVALID_ARGUMENT;
+    if (dst_capacity < sz_max_compressed_bytes(n, dtype)) return SZ_ERR_BUFFER_TOO_SMALL;
+    if (n) {
+        if (!usable(d_workspace)) return SZ_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes_given < workspace_bytes(1, n)) return SZ_ERR_BUFFER_TOO_SMALL;
+    }
+    return encode_impl(SrcRef{nullptr, d_src}, 1, n, dtype, d_codebook, DstRef{nullptr, d_dst},
+                       d_out_bytes, d_workspace, stream);
+}
+
+SZ_EXPORT sz_status sz_encode_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
+                                      sz_dtype dtype, const uint8_t* d_codebooks, void* const* d_dsts,
+                                      uint64_t dst_capacity, uint64_t* d_out_bytes, void* d_workspace,
+                                      uint64_t workspace_bytes_given, hipStream_t stream) {
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !usable(d_srcs) || !usable(d_codebooks) ||
+        !usable(d_dsts) || (d_out_bytes && (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)))
+        return SZ_ERR_INVALID_ARGUMENT;
+    if (dst_capacity < sz_max_compressed_bytes(n, dtype)) return SZ_ERR_BUFFER_TOO_SMALL;
+    if (n) {
+        if (!usable(d_workspace)) return SZ_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes_given < workspace_bytes(count, n)) return SZ_ERR_BUFFER_TOO_SMALL;
+    }
+    return encode_impl(SrcRef{d_srcs, nullptr}, count, n, dtype, d_codebooks, DstRef{d_dsts, nullptr},
+                       d_out_bytes, d_workspace, stream);
+}
+
+SZ_EXPORT sz_status sz_decode(const void* d_src, uint64_t src_bytes, uint64_t n, sz_dtype dtype,
+                              void* d_dst, int32_t* d_status, hipStream_t stream) {
+    if (!dtype_ok(dtype) || n >= kMaxElems || !usable(d_src) || (n && !usable(d_dst)) ||
+        (d_status && (reinterpret_cast<uintptr_t>(d_status) & 3u)))
+        return SZ_ERR_INVALID_ARGUMENT;
+    if (src_bytes < layout_of(n, dtype).esc_at) return SZ_ERR_CORRUPT_STREAM;
+    return decode_impl(SrcRef{nullptr, d_src}, nullptr, src_bytes, 1, n, dtype, DstRef{nullptr, d_dst},
+                       d_status, stream);
+}
+
+SZ_EXPORT sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_bytes,
+                                      uint32_t count, uint64_t n, sz_dtype dtype, void* const* d_dsts,
+                                      int32_t* d_status, hipStream_t stream) {
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !usable(d_srcs) || !usable(d_src_bytes) ||
+        !usable(d_dsts) || (d_status && (reinterpret_cast<uintptr_t>(d_status) & 3u)))
+        return SZ_ERR_INVALID_ARGUMENT;
+    return decode_impl(SrcRef{d_srcs, nullptr}, d_src_bytes, 0, count, n, dtype, DstRef{d_dsts, nullptr},
+                       d_status, stream);
+}
+
+SZ_EXPORT const char* sz_status_string(sz_status status) {
+    switch (status) {
+        case SZ_OK: return "ok";
+        case SZ_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case SZ_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+        case SZ_ERR_CORRUPT_STREAM: return "corrupt stream";
+        case SZ_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}

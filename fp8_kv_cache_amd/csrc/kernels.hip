@@ -1,0 +1,844 @@
+// kernels.hip -- gfx950 kernels of the lossless exponent codec.
+//
+// Method: SplitZip project page, "Abstract" (frequent exponents -> fixed
+// 4-bit codes, sign and mantissa kept exactly, rare exponents -> sparse
+// escape stream) and FAQ "Is SplitZip lossy?" (bitwise identical decode),
+// FAQ "Does it work with an FP8 KV cache?" (E5M2 variant).  The byte layout
+// is stream format v1, documented in include/splitzip.h.
+//
+// Work decomposition: one 64-lane wave owns one 4096-element format block.
+// Lane l of a wave handles a contiguous run of 16 (BF16) or 32 (E5M2)
+// elements in each 1024/2048-element sub-chunk, so every global access of a
+// wave is one contiguous, 16-byte-per-lane transfer.  All arithmetic is
+// integer bit manipulation; there is no matrix-core work anywhere.
+#include "sz_internal.h"
+
+namespace sz {
+namespace {
+
+// ---------------------------------------------------------------- helpers
+
+__device__ inline uint32_t lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ inline uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// All tensors, streams and tables live in device global memory.  Casting
+// to address space 1 lets the compiler emit global_* instead of flat_*
+// memory instructions for pointers that were loaded from tables.
+#define SZ_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ inline SZ_GLOBAL T* gptr(T* p) {
+    return (SZ_GLOBAL T*)(p);
+}
+
+__device__ inline const SZ_GLOBAL uint8_t* src_of(const SrcRef& r, uint32_t t) {
+    return gptr(static_cast<const uint8_t*>(r.table ? gptr(r.table)[t] : r.single));
+}
+__device__ inline SZ_GLOBAL uint8_t* dst_of(const DstRef& r, uint32_t t) {
+    return gptr(static_cast<uint8_t*>(r.table ? gptr(r.table)[t] : r.single));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: four row
+// shifts build scans inside each 16-lane row, then two row broadcasts carry
+// row totals across the wave.
+__device__ inline uint32_t wave_scan_incl(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+__device__ inline uint32_t wave_sum(uint32_t x) {
+    return __builtin_amdgcn_readlane(wave_scan_incl(x), 63);
+}
+
+__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// bit k*4 set iff nibble k of w equals 15 (the escape code)
+__device__ inline uint32_t escape_nibbles(uint32_t w) {
+    return w & (w >> 1) & (w >> 2) & (w >> 3) & 0x11111111u;
+}
+
+// nibble-granular mask of the first `valid` nibbles (0..8) of a code word
+__device__ inline uint32_t valid_nibbles(int32_t valid) {
+    return valid >= 8 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : ((1u << (4 * valid)) - 1u));
+}
+
+template <uint32_t DT>
+struct Geometry;
+template <>
+struct Geometry<kDtypeBF16> {
+    static constexpr uint32_t kElemBytes = 2;
+    static constexpr uint32_t kLaneElems = 16;   // elements per lane per sub-chunk
+    static constexpr uint32_t kSubs = 4;          // sub-chunks per block
+    static constexpr uint32_t kCodeWords = 2;     // code dwords per lane per sub-chunk
+    static constexpr uint32_t kDomain = 256;
+};
+template <>
+struct Geometry<kDtypeE5M2> {
+    static constexpr uint32_t kElemBytes = 1;
+    static constexpr uint32_t kLaneElems = 32;
+    static constexpr uint32_t kSubs = 2;
+    static constexpr uint32_t kCodeWords = 4;
+    static constexpr uint32_t kDomain = 32;
+};
+
+// 32 input bytes of one lane: elements [elem0, elem0 + kLaneElems); those at
+// or beyond n read as zero and no byte at or beyond n is touched.
+template <uint32_t DT>
+__device__ inline void load_lane(const SZ_GLOBAL uint8_t* src, uint64_t elem0, uint64_t n, uint32_t (&d)[8]) {
+    using G = Geometry<DT>;
+    if (elem0 + G::kLaneElems <= n) {
+        const SZ_GLOBAL u32x4* p = (const SZ_GLOBAL u32x4*)(src + elem0 * G::kElemBytes);
+        const u32x4 x = p[0], y = p[1];
+        d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+        d[4] = y.x; d[5] = y.y; d[6] = y.z; d[7] = y.w;
+        return;
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < 8; ++i) d[i] = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < G::kLaneElems; ++k) {
+        if (elem0 + k < n) {
+            uint32_t v;
+            if (DT == kDtypeBF16)
+                v = ((const SZ_GLOBAL uint16_t*)src)[elem0 + k];
+            else
+                v = src[elem0 + k];
+            const uint32_t bit = (k * G::kElemBytes * 8) & 31;
+            d[(k * G::kElemBytes) / 4] |= v << bit;
+        }
+    }
+}
+
+// ------------------------------------------------------------ fill kernels
+
+__global__ void k_fill_u64(uint64_t* p, uint64_t words, uint64_t value) {
+    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < words;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+__global__ void k_fill_i32(int32_t* p, uint64_t words, int32_t value) {
+    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < words;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+// -------------------------------------------------------------- histogram
+//
+// Each workgroup counts one contiguous chunk of one tensor into 32
+// lane-striped copies of the 256 bins held in LDS, laid out [bin][copy]:
+// lane l always adds into copy l & 31, so the 32 lanes of a half-wave hit
+// 32 different banks whatever their exponents.  For BF16 the byte address
+// of (bin e, copy c) is e*128 + 4c, and e*128 is simply u & 0x7F80.
+
+template <uint32_t DT>
+__device__ inline void count_dword(char* lds, uint32_t w, uint32_t copy4) {
+    if (DT == kDtypeBF16) {
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + ((w & 0x7F80u) | copy4)), 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + (((w >> 16) & 0x7F80u) | copy4)), 1u);
+    } else {
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k)
+            atomicAdd(reinterpret_cast<uint32_t*>(lds + ((((w >> (8 * k)) & 0x7Cu) << 5) | copy4)), 1u);
+    }
+}
+
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_histogram(HistArgs a) {
+    using G = Geometry<DT>;
+    constexpr uint32_t kTile = kThreads * G::kLaneElems;      // elements per pass
+    __shared__ uint32_t bins[256 * 32];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t t = blockIdx.x / a.groups;
+    const uint32_t g = blockIdx.x - t * a.groups;
+    char* lds = reinterpret_cast<char*>(bins);
+    for (uint32_t i = tid; i < 256 * 32 / 4; i += kThreads)
+        reinterpret_cast<uint4*>(bins)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
+    const uint64_t begin = (uint64_t)g * a.chunk;
+    const uint64_t end = begin + a.chunk < a.n ? begin + a.chunk : a.n;
+    const uint32_t copy4 = (tid & 31u) << 2;
+    uint64_t base = begin;
+    // four passes per iteration keep 8 x 16 bytes in flight per lane
+    for (; base + 4 * kTile <= end; base += 4 * kTile) {
+        u32x4 v[8];
+#pragma unroll
+        for (uint32_t p = 0; p < 4; ++p) {
+            const SZ_GLOBAL u32x4* q =
+                (const SZ_GLOBAL u32x4*)(src + (base + p * kTile + tid * G::kLaneElems) * G::kElemBytes);
+            v[2 * p] = q[0];
+            v[2 * p + 1] = q[1];
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) {
+            count_dword<DT>(lds, v[i].x, copy4);
+            count_dword<DT>(lds, v[i].y, copy4);
+            count_dword<DT>(lds, v[i].z, copy4);
+            count_dword<DT>(lds, v[i].w, copy4);
+        }
+    }
+    for (; base < end; base += kTile) {
+        const uint64_t elem0 = base + tid * G::kLaneElems;
+        if (elem0 + G::kLaneElems <= end) {
+            uint32_t d[8];
+            load_lane<DT>(src, elem0, end, d);
+#pragma unroll
+            for (uint32_t i = 0; i < 8; ++i) count_dword<DT>(lds, d[i], copy4);
+        } else if (elem0 < end) {
+            for (uint64_t i = elem0; i < end; ++i) {
+                const uint32_t u = DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i];
+                const uint32_t e = DT == kDtypeBF16 ? (u >> 7) & 0xFFu : (u >> 2) & 0x1Fu;
+                atomicAdd(reinterpret_cast<uint32_t*>(lds + ((e << 7) | copy4)), 1u);
+            }
+        }
+    }
+    __syncthreads();
+
+    // fold the 32 copies of bin `tid`; the rotation keeps lanes on distinct banks
+    uint32_t sum = 0;
+#pragma unroll 8
+    for (uint32_t j = 0; j < 32; ++j) sum += bins[tid * 32 + ((j + tid) & 31u)];
+    if (sum) __hip_atomic_fetch_add(gptr(a.hists) + 256ull * t + tid, static_cast<uint64_t>(sum),
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// --------------------------------------------------------------- codebook
+//
+// Rank every exponent value of the type by (count descending, value
+// ascending): value v's rank is the number of values that order before it.
+// The values of rank 0..14 are the codebook.
+
+template <uint32_t DT>
+__global__ __launch_bounds__(256) void k_codebook(CodebookArgs a) {
+    constexpr uint32_t D = Geometry<DT>::kDomain;
+    __shared__ uint64_t counts[256];
+    const uint32_t t = blockIdx.x, v = threadIdx.x;
+    counts[v] = gptr(a.hists)[256ull * t + v];
+    __syncthreads();
+    if (v < D) {
+        const uint64_t mine = counts[v];
+        uint32_t rank = 0;
+        for (uint32_t u = 0; u < D; ++u) {
+            const uint64_t c = counts[u];
+            rank += (c > mine) | ((c == mine) & (u < v));
+        }
+        if (rank < kCodes) gptr(a.codebooks)[16ull * t + rank] = static_cast<uint8_t>(v);
+    }
+    if (v == kEscape) gptr(a.codebooks)[16ull * t + kEscape] = 0;
+}
+
+// ----------------------------------------------------------------- encode
+
+constexpr uint64_t kFlagAggregate = 1ull << 32;
+constexpr uint64_t kFlagInclusive = 2ull << 32;
+
+__device__ inline void publish(SZ_GLOBAL uint64_t* word, uint64_t value) {
+    __hip_atomic_store(word, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix
+// Scan with Decoupled Look-back"), wave-parallel: each lane reads one of
+// the 64 nearest predecessors' status words at once.  Returns the number of
+// escapes in blocks [0, b) of this tensor.
+__device__ inline uint32_t look_back(const SZ_GLOBAL uint64_t* status, uint64_t b, uint32_t lane) {
+    uint32_t prefix = 0;
+    int64_t newest = static_cast<int64_t>(b) - 1;
+    while (true) {
+        const int64_t idx = newest - static_cast<int64_t>(lane);
+        uint64_t w = kFlagInclusive;  // before block 0: an inclusive zero
+        if (idx >= 0)
+            w = __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t flag = static_cast<uint32_t>(w >> 32);
+        const uint64_t not_ready = ballot(flag == 0);
+        const uint64_t inclusive = ballot(flag == 2);
+        // lanes up to and including the nearest inclusive predecessor
+        const uint64_t need = inclusive ? (((inclusive & (~inclusive + 1)) << 1) - 1) : ~0ull;
+        if (not_ready & need) {
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+        }
+        const uint32_t v = ((need >> lane) & 1ull) ? static_cast<uint32_t>(w) : 0u;
+        prefix += wave_sum(v);
+        if (inclusive) break;
+        newest -= 64;
+    }
+    return prefix;
+}
+
+// Header (64 bytes), the zero padding after the offset table and the
+// stream size, written by the wave that owns the last block.
+__device__ inline void write_header(SZ_GLOBAL uint8_t* dst, const Layout& L, uint32_t dtype,
+                                    const SZ_GLOBAL uint8_t* cb, uint64_t escapes, SZ_GLOBAL uint64_t* out_bytes,
+                                    uint32_t lane) {
+    const uint64_t total = L.esc_at + escapes;
+    const SZ_GLOBAL uint32_t* cbw = (const SZ_GLOBAL uint32_t*)cb;
+    uint32_t v = 0;
+    switch (lane) {
+        case 0: v = kMagic; break;
+        case 1: v = kVersion | (dtype << 8) | (kLog2Block << 16) | (kCodes << 24); break;
+        case 2: v = static_cast<uint32_t>(L.n); break;
+        case 3: v = static_cast<uint32_t>(L.n >> 32); break;
+        case 4: v = static_cast<uint32_t>(escapes); break;
+        case 5: v = static_cast<uint32_t>(escapes >> 32); break;
+        case 6: v = cbw[0]; break;
+        case 7: v = cbw[1]; break;
+        case 8: v = cbw[2]; break;
+        case 9: v = cbw[3] & 0x00FFFFFFu; break;  // cb[15] is stored as 0
+        case 10: v = static_cast<uint32_t>(total); break;
+        case 11: v = static_cast<uint32_t>(total >> 32); break;
+        default: v = 0; break;
+    }
+    SZ_GLOBAL uint32_t* h = (SZ_GLOBAL uint32_t*)dst;
+    if (lane < 16) h[lane] = v;
+    const uint64_t pad_from = (64 + 4 * L.blocks) / 4;
+    const uint64_t pad_words = L.header / 4 - pad_from;
+    if (lane < pad_words) h[pad_from + lane] = 0;
+    if (out_bytes && lane == 0) *out_bytes = total;
+}
+
+// BF16: sixteen elements d[0..7] -> 16 sign|mantissa bytes and 16 code
+// nibbles; elements at index >= valid get code 0 and zero bytes (they are
+// zero in d already).  Returns the escape nibble masks in esc[].
+__device__ inline void encode_lane_bf16(const uint32_t (&d)[8], uint32_t valid, const uint8_t* tbl,
+                                        uint32_t (&sm)[4], uint32_t (&cw)[2], uint32_t (&esc)[2]) {
+    uint32_t c[16];
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) {
+        c[2 * k] = tbl[(d[k] >> 7) & 0xFFu];
+        c[2 * k + 1] = tbl[(d[k] >> 23) & 0xFFu];
+    }
+    if (valid < 16) {
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k)
+            if (k >= valid) c[k] = 0;
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < 2; ++q) {
+        uint32_t w = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < 8; ++k) w |= c[8 * q + k] << (4 * k);
+        cw[q] = w;
+        esc[q] = escape_nibbles(w);
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        // low bytes (exponent lsb | mantissa) and high bytes (sign | exponent msbs)
+        const uint32_t lo = perm(d[2 * q + 1], d[2 * q], 0x06040200u);
+        const uint32_t hi = perm(d[2 * q + 1], d[2 * q], 0x07050301u);
+        sm[q] = (hi & 0x80808080u) | (lo & 0x7F7F7F7Fu);
+    }
+}
+
+// E5M2: 32 elements (4 per dword) -> 96 bits of 3-bit sign|mantissa
+// fields (LSB-first) and 32 code nibbles.
+__device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, const uint8_t* tbl,
+                                        uint32_t (&sm)[3], uint32_t (&cw)[4], uint32_t (&esc)[4]) {
+    uint32_t c[32];
+    uint32_t f[8];
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) {
+        const uint32_t e4 = (d[k] >> 2) & 0x1F1F1F1Fu;
+        c[4 * k + 0] = tbl[e4 & 0xFFu];
+        c[4 * k + 1] = tbl[(e4 >> 8) & 0xFFu];
+        c[4 * k + 2] = tbl[(e4 >> 16) & 0xFFu];
+        c[4 * k + 3] = tbl[e4 >> 24];
+        const uint32_t s = ((d[k] >> 5) & 0x04040404u) | (d[k] & 0x03030303u);
+        f[k] = (s & 0x7u) | ((s >> 5) & 0x38u) | ((s >> 10) & 0x1C0u) | ((s >> 15) & 0xE00u);
+    }
+    if (valid < 32) {
+#pragma unroll
+        for (uint32_t k = 0; k < 32; ++k)
+            if (k >= valid) c[k] = 0;
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        uint32_t w = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < 8; ++k) w |= c[8 * q + k] << (4 * k);
+        cw[q] = w;
+        esc[q] = escape_nibbles(w);
+    }
+    sm[0] = f[0] | (f[1] << 12) | (f[2] << 24);
+    sm[1] = (f[2] >> 8) | (f[3] << 4) | (f[4] << 16) | (f[5] << 28);
+    sm[2] = (f[5] >> 4) | (f[6] << 8) | (f[7] << 20);
+}
+
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
+    using G = Geometry<DT>;
+    constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
+    constexpr uint32_t kSmWords = DT == kDtypeBF16 ? 4 : 3;
+    __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_tbl[kWavesPerGroup][64];   // 256 one-byte codes per wave
+
+    const uint32_t wave = uniform(threadIdx.x / kWaveSize);
+    const uint32_t lane = lane_id();
+    if (threadIdx.x == 0)
+        s_ticket = __hip_atomic_fetch_add(gptr(a.ticket), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const Layout L = layout_of(a.n, DT);
+    const uint64_t flat = static_cast<uint64_t>(uniform(s_ticket)) * kWavesPerGroup + wave;
+    if (flat >= static_cast<uint64_t>(a.count) * L.blocks) return;
+    const uint32_t t = static_cast<uint32_t>(flat / L.blocks);
+    const uint64_t b = flat - static_cast<uint64_t>(t) * L.blocks;
+
+    // Code of every exponent value: the lowest c with cb[c] == v, else 15.
+    const SZ_GLOBAL uint8_t* cb = gptr(a.codebooks) + 16ull * t;
+    uint8_t* tbl = reinterpret_cast<uint8_t*>(s_tbl[wave]);
+    s_tbl[wave][lane] = 0x0F0F0F0Fu;
+    const uint32_t mine = lane < kCodes ? cb[lane] : 0xFFFFu;
+    bool lowest = lane < kCodes;
+#pragma unroll
+    for (uint32_t c = 0; c + 1 < kCodes; ++c) {
+        const uint32_t other = __builtin_amdgcn_readlane(mine, c);
+        if (c < lane && other == mine) lowest = false;
+    }
+    if (lowest) tbl[mine] = static_cast<uint8_t>(lane);
+    __builtin_amdgcn_wave_barrier();
+
+    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+    const uint64_t blk0 = b * kBlockElems;
+
+    uint32_t d[G::kSubs][8];
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j)
+        load_lane<DT>(src, blk0 + j * kSubElems + lane * G::kLaneElems, a.n, d[j]);
+
+    uint32_t sm[G::kSubs][kSmWords];
+    uint32_t cw[G::kSubs][G::kCodeWords];
+    uint32_t esc[G::kSubs][G::kCodeWords];
+    uint32_t cnt[G::kSubs];
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
+        const uint32_t valid = elem0 >= a.n ? 0u
+                               : (a.n - elem0 >= G::kLaneElems ? G::kLaneElems
+                                                                 : static_cast<uint32_t>(a.n - elem0));
+        if constexpr (DT == kDtypeBF16)
+            encode_lane_bf16(d[j], valid, tbl, sm[j], cw[j], esc[j]);
+        else
+            encode_lane_e5m2(d[j], valid, tbl, sm[j], cw[j], esc[j]);
+        cnt[j] = 0;
+#pragma unroll
+        for (uint32_t q = 0; q < G::kCodeWords; ++q) cnt[j] += __builtin_popcount(esc[j][q]);
+    }
+
+    // Escape ranks inside the block: element order is (sub-chunk, lane,
+    // element), so lane l's first escape in sub-chunk j has rank
+    // (escapes of earlier sub-chunks) + (escapes of lanes < l in j).
+    uint32_t base[G::kSubs];
+    uint32_t block_total = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; j += 2) {
+        const uint32_t packed = cnt[j] | (j + 1 < G::kSubs ? cnt[j + 1] << 16 : 0u);
+        const uint32_t incl = wave_scan_incl(packed);
+        const uint32_t excl = incl - packed;
+        const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+        base[j] = block_total + (excl & 0xFFFFu);
+        block_total += tot & 0xFFFFu;
+        if (j + 1 < G::kSubs) {
+            base[j + 1] = block_total + (excl >> 16);
+            block_total += tot >> 16;
+        }
+    }
+    block_total = uniform(block_total);
+
+    SZ_GLOBAL uint64_t* status = gptr(a.status) + static_cast<uint64_t>(t) * L.blocks;
+    if (lane == 0) publish(status + b, (b == 0 ? kFlagInclusive : kFlagAggregate) | block_total);
+
+    // planes; vectors at or beyond the padded plane end are not stored
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
+        const uint64_t code_off = elem0 / 2;
+        if constexpr (DT == kDtypeBF16) {
+            if (elem0 < L.sm_region)
+                *(SZ_GLOBAL u32x4*)(dst + L.sm_at + elem0) = u32x4{sm[j][0], sm[j][1], sm[j][2], sm[j][3]};
+            if (code_off < L.code_region)
+                *(SZ_GLOBAL u32x2*)(dst + L.code_at + code_off) = u32x2{cw[j][0], cw[j][1]};
+        } else {
+            const uint64_t sm_off = elem0 / 32 * 12;
+            SZ_GLOBAL uint32_t* smp = (SZ_GLOBAL uint32_t*)(dst + L.sm_at + sm_off);
+#pragma unroll
+            for (uint32_t i = 0; i < 3; ++i)
+                if (sm_off + 4 * i < L.sm_region) smp[i] = sm[j][i];
+            if (code_off < L.code_region)
+                *(SZ_GLOBAL u32x4*)(dst + L.code_at + code_off) =
+                    u32x4{cw[j][0], cw[j][1], cw[j][2], cw[j][3]};
+        }
+    }
+
+    const uint32_t prefix = b == 0 ? 0u : uniform(look_back(status, b, lane));
+    if (lane == 0) {
+        if (b != 0) publish(status + b, kFlagInclusive | (prefix + block_total));
+        ((SZ_GLOBAL uint32_t*)(dst + 64))[b] = prefix;
+    }
+
+    // escape bytes, in element order
+    SZ_GLOBAL uint8_t* esc_out = dst + L.esc_at + prefix;
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        if (cnt[j] == 0) continue;
+        uint32_t rank = base[j];
+#pragma unroll
+        for (uint32_t q = 0; q < G::kCodeWords; ++q) {
+            uint32_t m = esc[j][q];
+            while (m) {
+                const uint32_t k = 8 * q + (__builtin_ctz(m) >> 2);   // element within the lane
+                uint32_t e;
+                if constexpr (DT == kDtypeBF16) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (uint32_t i = 0; i < 8; ++i)
+                        if (i == (k >> 1)) word = d[j][i];
+                    e = (k & 1) ? (word >> 23) & 0xFFu : (word >> 7) & 0xFFu;
+                } else {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (uint32_t i = 0; i < 8; ++i)
+                        if (i == (k >> 2)) word = d[j][i];
+                    e = (word >> (8 * (k & 3) + 2)) & 0x1Fu;
+                }
+                esc_out[rank++] = static_cast<uint8_t>(e);
+                m &= m - 1;
+            }
+        }
+    }
+
+    if (b == L.blocks - 1)
+        write_header(dst, L, DT, cb, prefix + block_total, a.out_bytes ? gptr(a.out_bytes) + t : nullptr, lane);
+}
+
+// n == 0: a header-only stream per tensor
+template <uint32_t DT>
+__global__ void k_encode_empty(EncodeArgs a) {
+    const uint32_t t = blockIdx.x;
+    const Layout L = layout_of(0, DT);
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+    write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, 0, a.out_bytes ? gptr(a.out_bytes) + t : nullptr, lane_id());
+}
+
+// ----------------------------------------------------------------- decode
+
+// four code nibbles (one per byte of x) -> the four codebook bytes; the
+// codebook is held in four registers cbw[0..3]
+__device__ inline uint32_t lookup4(uint32_t x, const uint32_t (&cbw)[4]) {
+    const uint32_t sel = x & 0x07070707u;
+    const uint32_t lo = perm(cbw[1], cbw[0], sel);
+    const uint32_t hi = perm(cbw[3], cbw[2], sel);
+    const uint32_t m = ((x >> 3) & 0x01010101u) * 0xFFu;
+    return (hi & m) | (lo & ~m);
+}
+
+// Header check shared by all waves of a stream.  Returns the escape count
+// or -1 when the stream does not match (n, dtype, src_bytes) or itself.
+template <uint32_t DT>
+__device__ inline int64_t check_header(const SZ_GLOBAL uint8_t* src, uint64_t src_bytes, const Layout& L,
+                                       uint32_t (&cbw)[4]) {
+    if (src_bytes < 64) return -1;
+    const SZ_GLOBAL uint32_t* h = (const SZ_GLOBAL uint32_t*)src;
+    uint32_t w[16];
+#pragma unroll
+    for (uint32_t i = 0; i < 16; ++i) w[i] = uniform(h[i]);
+    const uint64_t n = w[2] | (static_cast<uint64_t>(w[3]) << 32);
+    const uint64_t escapes = w[4] | (static_cast<uint64_t>(w[5]) << 32);
+    const uint64_t total = w[10] | (static_cast<uint64_t>(w[11]) << 32);
+    bool ok = w[0] == kMagic;
+    ok &= w[1] == (kVersion | (DT << 8) | (kLog2Block << 16) | (kCodes << 24));
+    ok &= n == L.n;
+    ok &= (w[9] >> 24) == 0;
+    ok &= (w[12] | w[13] | w[14] | w[15]) == 0;
+    ok &= escapes <= L.n;
+    ok &= total == L.esc_at + escapes;
+    ok &= total <= src_bytes;
+    cbw[0] = w[6]; cbw[1] = w[7]; cbw[2] = w[8]; cbw[3] = w[9];
+    return ok ? static_cast<int64_t>(escapes) : -1;
+}
+
+__device__ inline void mark_corrupt(SZ_GLOBAL int32_t* status, uint32_t lane) {
+    if (status && lane == 0) *status = 3;  // SZ_ERR_CORRUPT_STREAM
+}
+
+__device__ inline void put_byte(uint32_t& w0, uint32_t& w1, uint32_t k, uint32_t e) {
+    const uint32_t shift = 8 * (k & 3);
+    const uint32_t clear = ~(0xFFu << shift);
+    if (k < 4)
+        w0 = (w0 & clear) | (e << shift);
+    else
+        w1 = (w1 & clear) | (e << shift);
+}
+
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
+    using G = Geometry<DT>;
+    constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
+    constexpr uint32_t kSmWords = DT == kDtypeBF16 ? 4 : 3;
+    const uint32_t wave = uniform(threadIdx.x / kWaveSize);
+    const uint32_t lane = lane_id();
+    const Layout L = layout_of(a.n, DT);
+    const uint64_t flat = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave;
+    if (flat >= static_cast<uint64_t>(a.count) * L.blocks) return;
+    const uint32_t t = static_cast<uint32_t>(flat / L.blocks);
+    const uint64_t b = flat - static_cast<uint64_t>(t) * L.blocks;
+
+    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
+    const uint64_t src_bytes = a.src_bytes_table ? gptr(a.src_bytes_table)[t] : a.src_bytes;
+    SZ_GLOBAL int32_t* status = a.status ? gptr(a.status) + t : nullptr;
+    uint32_t cbw[4];
+    const int64_t escapes = check_header<DT>(src, src_bytes, L, cbw);
+    if (escapes < 0) {
+        mark_corrupt(status, lane);
+        return;
+    }
+    const SZ_GLOBAL uint32_t* offs = (const SZ_GLOBAL uint32_t*)(src + 64);
+    const uint32_t first = uniform(offs[b]);
+    const uint64_t next = b + 1 < L.blocks ? uniform(offs[b + 1]) : static_cast<uint64_t>(escapes);
+    if ((b == 0 && first != 0) || next < first || next > static_cast<uint64_t>(escapes)) {
+        mark_corrupt(status, lane);
+        return;
+    }
+
+    const uint64_t blk0 = b * kBlockElems;
+    uint32_t cw[G::kSubs][G::kCodeWords];
+    uint32_t sm[G::kSubs][kSmWords];
+    uint32_t esc[G::kSubs][G::kCodeWords];
+    uint32_t cnt[G::kSubs];
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
+        if (elem0 < L.n) {
+            if constexpr (DT == kDtypeBF16) {
+                const u32x2 c = *(const SZ_GLOBAL u32x2*)(src + L.code_at + elem0 / 2);
+                cw[j][0] = c.x; cw[j][1] = c.y;
+                const u32x4 s = *(const SZ_GLOBAL u32x4*)(src + L.sm_at + elem0);
+                sm[j][0] = s.x; sm[j][1] = s.y; sm[j][2] = s.z; sm[j][3] = s.w;
+            } else {
+                const u32x4 c = *(const SZ_GLOBAL u32x4*)(src + L.code_at + elem0 / 2);
+                cw[j][0] = c.x; cw[j][1] = c.y; cw[j][2] = c.z; cw[j][3] = c.w;
+                const SZ_GLOBAL uint32_t* s = (const SZ_GLOBAL uint32_t*)(src + L.sm_at + elem0 / 32 * 12);
+                sm[j][0] = s[0]; sm[j][1] = s[1]; sm[j][2] = s[2];
+            }
+        } else {
+#pragma unroll
+            for (uint32_t q = 0; q < G::kCodeWords; ++q) cw[j][q] = 0;
+#pragma unroll
+            for (uint32_t q = 0; q < kSmWords; ++q) sm[j][q] = 0;
+        }
+        const int64_t valid = static_cast<int64_t>(L.n) - static_cast<int64_t>(elem0);
+        cnt[j] = 0;
+#pragma unroll
+        for (uint32_t q = 0; q < G::kCodeWords; ++q) {
+            esc[j][q] = escape_nibbles(cw[j][q]) &
+                        valid_nibbles(static_cast<int32_t>(valid > 64 ? 64 : valid) - 8 * static_cast<int32_t>(q));
+            cnt[j] += __builtin_popcount(esc[j][q]);
+        }
+    }
+
+    uint32_t base[G::kSubs];
+    uint32_t block_total = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; j += 2) {
+        const uint32_t packed = cnt[j] | (j + 1 < G::kSubs ? cnt[j + 1] << 16 : 0u);
+        const uint32_t incl = wave_scan_incl(packed);
+        const uint32_t excl = incl - packed;
+        const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+        base[j] = block_total + (excl & 0xFFFFu);
+        block_total += tot & 0xFFFFu;
+        if (j + 1 < G::kSubs) {
+            base[j + 1] = block_total + (excl >> 16);
+            block_total += tot >> 16;
+        }
+    }
+    if (uniform(block_total) != next - first) {
+        mark_corrupt(status, lane);
+        return;
+    }
+
+    const SZ_GLOBAL uint8_t* esc_in = src + L.esc_at + first;
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
+        if (elem0 >= L.n) continue;
+        uint32_t rank = base[j];
+        uint32_t out[8];
+        if constexpr (DT == kDtypeBF16) {
+#pragma unroll
+            for (uint32_t q = 0; q < 2; ++q) {
+                const uint32_t c = cw[j][q];
+                const uint32_t ev = lookup4(c & 0x0F0F0F0Fu, cbw);         // elements 0,2,4,6
+                const uint32_t od = lookup4((c >> 4) & 0x0F0F0F0Fu, cbw);  // elements 1,3,5,7
+                uint32_t e0 = perm(od, ev, 0x05010400u);                    // elements 0..3
+                uint32_t e1 = perm(od, ev, 0x07030602u);                    // elements 4..7
+                uint32_t m = esc[j][q];
+                while (m) {
+                    const uint32_t k = __builtin_ctz(m) >> 2;
+                    put_byte(e0, e1, k, esc_in[rank++]);
+                    m &= m - 1;
+                }
+                // (sign|mantissa byte s, exponent byte e) pairs -> BF16 words
+#pragma unroll
+                for (uint32_t h = 0; h < 4; ++h) {
+                    const uint32_t ew = h < 2 ? e0 : e1;
+                    const uint32_t sw = sm[j][2 * q + (h >> 1)];
+                    const uint32_t v = perm(ew, sw, (h & 1) ? 0x07030602u : 0x05010400u);
+                    out[4 * q + h] = ((v >> 1) & 0x7F807F80u) | ((v << 8) & 0x80008000u) | (v & 0x007F007Fu);
+                }
+            }
+        } else {
+            const uint32_t s0 = sm[j][0], s1 = sm[j][1], s2 = sm[j][2];
+            uint32_t f[8];
+            f[0] = s0 & 0xFFFu;
+            f[1] = (s0 >> 12) & 0xFFFu;
+            f[2] = (s0 >> 24) | ((s1 & 0xFu) << 8);
+            f[3] = (s1 >> 4) & 0xFFFu;
+            f[4] = (s1 >> 16) & 0xFFFu;
+            f[5] = (s1 >> 28) | ((s2 & 0xFFu) << 4);
+            f[6] = (s2 >> 8) & 0xFFFu;
+            f[7] = s2 >> 20;
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+                const uint32_t c = cw[j][q];
+                const uint32_t ev = lookup4(c & 0x0F0F0F0Fu, cbw);
+                const uint32_t od = lookup4((c >> 4) & 0x0F0F0F0Fu, cbw);
+                uint32_t e0 = perm(od, ev, 0x05010400u);
+                uint32_t e1 = perm(od, ev, 0x07030602u);
+                uint32_t m = esc[j][q];
+                while (m) {
+                    const uint32_t k = __builtin_ctz(m) >> 2;
+                    put_byte(e0, e1, k, esc_in[rank++]);
+                    m &= m - 1;
+                }
+#pragma unroll
+                for (uint32_t h = 0; h < 2; ++h) {
+                    const uint32_t v = f[2 * q + h];
+                    const uint32_t s = (v & 0x7u) | ((v & 0x38u) << 5) | ((v & 0x1C0u) << 10) | ((v & 0xE00u) << 15);
+                    const uint32_t e = h ? e1 : e0;
+                    out[2 * q + h] = ((s & 0x04040404u) << 5) | ((e & 0x1F1F1F1Fu) << 2) | (s & 0x03030303u);
+                }
+            }
+        }
+        SZ_GLOBAL uint8_t* p = dst + elem0 * G::kElemBytes;
+        if (elem0 + G::kLaneElems <= L.n) {
+            ((SZ_GLOBAL u32x4*)p)[0] = u32x4{out[0], out[1], out[2], out[3]};
+            ((SZ_GLOBAL u32x4*)p)[1] = u32x4{out[4], out[5], out[6], out[7]};
+        } else {
+            const uint32_t valid = static_cast<uint32_t>(L.n - elem0);
+#pragma unroll
+            for (uint32_t k = 0; k < G::kLaneElems; ++k) {
+                if (k < valid) {
+                    if constexpr (DT == kDtypeBF16)
+                        ((SZ_GLOBAL uint16_t*)p)[k] = static_cast<uint16_t>(out[k / 2] >> (16 * (k & 1)));
+                    else
+                        p[k] = static_cast<uint8_t>(out[k / 4] >> (8 * (k & 3)));
+                }
+            }
+        }
+    }
+}
+
+// n == 0: only the header can be checked
+template <uint32_t DT>
+__global__ void k_decode_empty(DecodeArgs a) {
+    const uint32_t t = blockIdx.x;
+    const Layout L = layout_of(0, DT);
+    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
+    const uint64_t src_bytes = a.src_bytes_table ? gptr(a.src_bytes_table)[t] : a.src_bytes;
+    uint32_t cbw[4];
+    if (check_header<DT>(src, src_bytes, L, cbw) < 0) mark_corrupt(a.status ? gptr(a.status) + t : nullptr, lane_id());
+}
+
+uint32_t grid_for(uint64_t items, uint32_t per_group) {
+    return static_cast<uint32_t>((items + per_group - 1) / per_group);
+}
+
+}  // namespace
+
+// --------------------------------------------------------------- launchers
+
+hipError_t launch_fill_u64(uint64_t* p, uint64_t words, uint64_t value, hipStream_t s) {
+    if (!words) return hipSuccess;
+    uint64_t groups = (words + 255) / 256;
+    if (groups > 4096) groups = 4096;
+    hipLaunchKernelGGL(k_fill_u64, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s, p, words, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, uint64_t words, int32_t value, hipStream_t s) {
+    if (!words) return hipSuccess;
+    uint64_t groups = (words + 255) / 256;
+    if (groups > 4096) groups = 4096;
+    hipLaunchKernelGGL(k_fill_i32, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s, p, words, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_histogram(const HistArgs& a, uint32_t dtype, hipStream_t s) {
+    const dim3 grid(a.count * a.groups), block(kThreads);
+    if (dtype == kDtypeBF16)
+        hipLaunchKernelGGL(k_histogram<kDtypeBF16>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(k_histogram<kDtypeE5M2>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s) {
+    if (dtype == kDtypeBF16)
+        hipLaunchKernelGGL(k_codebook<kDtypeBF16>, dim3(a.count), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_codebook<kDtypeE5M2>, dim3(a.count), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s) {
+    const Layout L = layout_of(a.n, dtype);
+    const dim3 grid(grid_for(static_cast<uint64_t>(a.count) * L.blocks, kWavesPerGroup)), block(kThreads);
+    if (dtype == kDtypeBF16)
+        hipLaunchKernelGGL(k_encode<kDtypeBF16>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(k_encode<kDtypeE5M2>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t s) {
+    if (dtype == kDtypeBF16)
+        hipLaunchKernelGGL(k_encode_empty<kDtypeBF16>, dim3(a.count), dim3(kWaveSize), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_encode_empty<kDtypeE5M2>, dim3(a.count), dim3(kWaveSize), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, uint32_t dtype, hipStream_t s) {
+    const Layout L = layout_of(a.n, dtype);
+    const dim3 grid(grid_for(static_cast<uint64_t>(a.count) * L.blocks, kWavesPerGroup)), block(kThreads);
+    if (dtype == kDtypeBF16)
+        hipLaunchKernelGGL(k_decode<kDtypeBF16>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(k_decode<kDtypeE5M2>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_empty(const DecodeArgs& a, uint32_t dtype, hipStream_t s) {
+    if (dtype == kDtypeBF16)
+        hipLaunchKernelGGL(k_decode_empty<kDtypeBF16>, dim3(a.count), dim3(kWaveSize), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_decode_empty<kDtypeE5M2>, dim3(a.count), dim3(kWaveSize), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace sz

@@ -1,0 +1,108 @@
+// sz_internal.h -- shared by the host entry points and the gfx950 kernels of
+// the exponent codec library.  Stream layout arithmetic and kernel launch
+// interfaces; the byte format itself is documented in include/splitzip.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sz {
+
+constexpr uint32_t kBlockElems = 4096;      // elements per format block
+constexpr uint32_t kLog2Block = 12;
+constexpr uint32_t kCodes = 15;             // coded exponents; code 15 = escape
+constexpr uint32_t kEscape = 15;
+constexpr uint32_t kVersion = 1;
+constexpr uint32_t kMagic = 0x564B5A53u;    // bytes 'S','Z','K','V'
+constexpr uint32_t kWaveSize = 64;
+constexpr uint32_t kThreads = 256;          // 4 waves per workgroup
+constexpr uint32_t kWavesPerGroup = kThreads / kWaveSize;
+constexpr uint32_t kDtypeBF16 = 1;
+constexpr uint32_t kDtypeE5M2 = 2;
+
+// Region sizes of one stream.  A(x) rounds x up to a multiple of 256.
+struct Layout {
+    uint64_t n;
+    uint64_t blocks;       // B = ceil(n / 4096)
+    uint64_t header;       // H = A(64 + 4B)
+    uint64_t sm_bytes;     // S
+    uint64_t sm_region;    // A(S)
+    uint64_t code_bytes;   // ceil(n / 2)
+    uint64_t code_region;  // A(ceil(n / 2))
+    uint64_t sm_at, code_at, esc_at;
+};
+
+__host__ __device__ inline uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+
+__host__ __device__ inline Layout layout_of(uint64_t n, uint32_t dtype) {
+    Layout L;
+    L.n = n;
+    L.blocks = (n + kBlockElems - 1) / kBlockElems;
+    L.header = align256(64 + 4 * L.blocks);
+    L.sm_bytes = dtype == kDtypeBF16 ? n : (3 * n + 7) / 8;
+    L.sm_region = align256(L.sm_bytes);
+    L.code_bytes = (n + 1) / 2;
+    L.code_region = align256(L.code_bytes);
+    L.sm_at = L.header;
+    L.code_at = L.sm_at + L.sm_region;
+    L.esc_at = L.code_at + L.code_region;
+    return L;
+}
+
+// A tensor is addressed either through a device table of pointers (batched
+// calls) or directly (single-tensor calls).
+struct SrcRef {
+    const void* const* table;
+    const void* single;
+};
+struct DstRef {
+    void* const* table;
+    void* single;
+};
+
+struct HistArgs {
+    SrcRef src;
+    uint64_t* hists;          // count x 256
+    uint32_t count;
+    uint32_t groups;          // workgroups per tensor
+    uint64_t n;
+    uint64_t chunk;           // elements per workgroup, multiple of 4096
+};
+
+struct CodebookArgs {
+    const uint64_t* hists;    // count x 256
+    uint8_t* codebooks;       // count x 16
+    uint32_t count;
+};
+
+struct EncodeArgs {
+    SrcRef src;
+    DstRef dst;
+    const uint8_t* codebooks; // count x 16
+    uint64_t* out_bytes;      // count, may be null
+    uint64_t* status;         // count x blocks look-back words
+    uint32_t* ticket;         // workgroup ticket counter
+    uint32_t count;
+    uint64_t n;
+};
+
+struct DecodeArgs {
+    SrcRef src;
+    const uint64_t* src_bytes_table;  // count, or null
+    uint64_t src_bytes;               // used when the table is null
+    DstRef dst;
+    int32_t* status;                  // count, may be null
+    uint32_t count;
+    uint64_t n;
+};
+
+hipError_t launch_fill_u64(uint64_t* p, uint64_t words, uint64_t value, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, uint64_t words, int32_t value, hipStream_t s);
+hipError_t launch_histogram(const HistArgs& a, uint32_t dtype, hipStream_t s);
+hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
+hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, uint32_t dtype, hipStream_t s);
+hipError_t launch_decode_empty(const DecodeArgs& a, uint32_t dtype, hipStream_t s);
+
+}  // namespace sz

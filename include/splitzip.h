@@ -1,0 +1,149 @@
+/*
+ * splitzip.h -- C ABI of the MI355X (gfx950) lossless exponent codec for
+ * BF16 and FP8-E5M2 KV-cache tensors.
+ *
+ * The method is SplitZip's (SplitZip project page, "Abstract"): the most
+ * frequent exponent values of a tensor get fixed 4-bit codes, sign and
+ * mantissa bits are kept exactly, and rare exponent values are routed
+ * through a sparse escape stream; decoding is bitwise identical (FAQ "Is
+ * SplitZip lossy?"), also for FP8 E5M2 KV caches (FAQ "Does it work with
+ * an FP8 KV cache?").
+ *
+ * ---- Stream format v1 (little-endian; A(x) = x rounded up to 256) -------
+ *   0   u8[4]  'S','Z','K','V'          24  u8[16] codebook cb[0..14], cb[15]=0
+ *   4   u8     version = 1              40  u64    C, total stream bytes
+ *   5   u8     dtype (sz_dtype)         48  u8[16] reserved, zero
+ *   6   u8     log2 block size = 12     64  u32[B] escape offsets (B = ceil(n/4096)),
+ *   7   u8     coded exponents = 15                zeros up to H = A(64 + 4B)
+ *   8   u64    n                        H   sign|mantissa plane, S bytes, zeros to A(S)
+ *   16  u64    E, number of escapes     ..  code plane, ceil(n/2) bytes, zeros to A(.)
+ *                                       ..  E escape bytes
+ *   C = H + A(S) + A(ceil(n/2)) + E.
+ *   BF16: exponent = bits 14..7 (8 bits); plane byte = sign<<7 | mantissa (7).
+ *         S = n.
+ *   E5M2: exponent = bits 6..2 (5 bits); plane field = sign<<2 | mantissa (2),
+ *         3 bits per element packed LSB-first (element i at bits 3i..3i+2).
+ *         S = ceil(3n/8).
+ *   Codes: cb[c] is the exponent of code c (c < 15); code 15 is the escape.
+ *         Element 2i is the low nibble of code byte i, 2i+1 the high nibble.
+ *   Escapes: one byte per escaped element (its raw exponent), element order.
+ *         off[b] = escapes before element 4096*b.
+ *   Codebook built by sz_build_codebook: all exponent values of the type
+ *         (256 for BF16, 32 for E5M2) ranked by count, descending, ties to
+ *         the smaller exponent; code c = rank c.
+ *
+ * ---- Conventions ---------------------------------------------------------
+ *   Pointers named d_* are HIP device memory owned by the caller.  Element,
+ *   stream and workspace buffers must be 16-byte aligned.  Every call is
+ *   asynchronous on `stream` (may be NULL for the null stream); the library
+ *   never allocates, frees or synchronises.  Argument errors detectable on
+ *   the host are returned before anything is enqueued.  A launch failure
+ *   returns SZ_ERR_HIP.  0 <= n < 2^32 for every call.
+ *   Calls sharing a workspace or output buffer must not overlap in time.
+ */
+#ifndef SPLITZIP_H
+#define SPLITZIP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SZ_DTYPE_BF16 = 1,
+    SZ_DTYPE_FP8_E5M2 = 2
+} sz_dtype;
+
+typedef enum {
+    SZ_OK = 0,
+    SZ_ERR_INVALID_ARGUMENT = 1,  /* null/misaligned pointer, bad dtype, n >= 2^32 */
+    SZ_ERR_BUFFER_TOO_SMALL = 2,  /* output or workspace capacity below the bound */
+    SZ_ERR_CORRUPT_STREAM = 3,    /* stream does not match n / dtype or its own header */
+    SZ_ERR_HIP = 4                /* a kernel launch failed */
+} sz_status;
+
+/* Largest stream sz_encode can write for n elements with ANY codebook
+ * (every element may escape): H + A(S) + A(ceil(n/2)) + n.  Pure host
+ * function; returns 0 for an invalid dtype or n >= 2^32. */
+uint64_t sz_max_compressed_bytes(uint64_t n, sz_dtype dtype);
+
+/* Workspace sz_encode needs: one 8-byte status word per 4096-element
+ * block plus a 256-byte counter area.  Pure host function; 0 on bad input. */
+uint64_t sz_encode_workspace_bytes(uint64_t n, sz_dtype dtype);
+
+/* Exponent histogram (SplitZip "Abstract": exponent values are highly
+ * redundant, so count them).  d_src: n elements (BF16 as 16-bit words,
+ * E5M2 as bytes).  d_hist: 256 u64 counters, overwritten; for E5M2 only
+ * bins 0..31 can be non-zero. */
+sz_status sz_histogram(const void* d_src, uint64_t n, sz_dtype dtype,
+                       uint64_t* d_hist, hipStream_t stream);
+
+/* Codebook from a histogram ("Abstract": the most frequent exponent values
+ * get the fixed 4-bit codes).  d_hist: 256 u64 (device).  d_codebook: 16
+ * bytes written as cb[0..14] = exponents of rank 0..14 (count descending,
+ * then exponent ascending), cb[15] = 0. */
+sz_status sz_build_codebook(const uint64_t* d_hist, sz_dtype dtype,
+                            uint8_t* d_codebook, hipStream_t stream);
+
+/* Encode one tensor ("Abstract"; FAQ "Is SplitZip lossy?").  d_codebook:
+ * 16 device bytes, any values (a value listed twice takes its lowest code;
+ * cb[15] is ignored and stored as 0).  d_dst receives the whole stream;
+ * dst_capacity must be >= sz_max_compressed_bytes(n, dtype), else
+ * SZ_ERR_BUFFER_TOO_SMALL.  d_out_bytes (device u64, may be NULL) receives
+ * C.  d_workspace: >= sz_encode_workspace_bytes(n, dtype) bytes, contents
+ * need not be initialised, clobbered. */
+sz_status sz_encode(const void* d_src, uint64_t n, sz_dtype dtype,
+                    const uint8_t* d_codebook, void* d_dst, uint64_t dst_capacity,
+                    uint64_t* d_out_bytes, void* d_workspace, uint64_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Decode one stream (FAQ "Is SplitZip lossy?": bitwise identical output).
+ * d_src: src_bytes readable bytes holding the stream (C <= src_bytes).
+ * d_dst: n elements.  The stream is validated on the device against n,
+ * dtype, src_bytes and its own header and offsets; if it does not match,
+ * *d_status (device int32, may be NULL) is set to SZ_ERR_CORRUPT_STREAM,
+ * the output is unspecified, and no access leaves [d_src, d_src+src_bytes)
+ * or [d_dst, d_dst + n elements).  Otherwise *d_status is set to SZ_OK.
+ * Returns SZ_ERR_CORRUPT_STREAM without launching if src_bytes is smaller
+ * than any stream of n elements can be. */
+sz_status sz_decode(const void* d_src, uint64_t src_bytes, uint64_t n, sz_dtype dtype,
+                    void* d_dst, int32_t* d_status, hipStream_t stream);
+
+/* ---- Batched forms: T tensors of the same n and dtype in one launch per
+ * phase (one codebook per tensor, as for a KV cache's layer tensors).  The
+ * d_*s pointer tables are device arrays of T device pointers.  Results are
+ * byte-identical to T single-tensor calls. ---- */
+
+uint64_t sz_encode_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype dtype);
+
+/* d_hists: count x 256 u64 */
+sz_status sz_histogram_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
+                               sz_dtype dtype, uint64_t* d_hists, hipStream_t stream);
+
+/* d_hists: count x 256 u64; d_codebooks: count x 16 bytes */
+sz_status sz_build_codebook_batched(const uint64_t* d_hists, uint32_t count, sz_dtype dtype,
+                                    uint8_t* d_codebooks, hipStream_t stream);
+
+/* d_codebooks: count x 16 bytes; every d_dsts[t] holds dst_capacity bytes;
+ * d_out_bytes: count u64 (may be NULL). */
+sz_status sz_encode_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
+                            sz_dtype dtype, const uint8_t* d_codebooks,
+                            void* const* d_dsts, uint64_t dst_capacity, uint64_t* d_out_bytes,
+                            void* d_workspace, uint64_t workspace_bytes, hipStream_t stream);
+
+/* d_src_bytes: count u64 (device), readable bytes of each stream, e.g. the
+ * d_out_bytes array an encode wrote.  d_status: count int32 (may be NULL). */
+sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_bytes,
+                            uint32_t count, uint64_t n, sz_dtype dtype,
+                            void* const* d_dsts, int32_t* d_status, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* sz_status_string(sz_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITZIP_H */

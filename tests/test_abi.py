@@ -1,0 +1,110 @@
+"""The C-ABI library loads and exports every symbol include/splitzip.h
+declares; host-side argument checks and size functions (no GPU needed: none
+of these calls reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "splitzip.h")
+
+
+@pytest.fixture(scope="module")
+def sz():
+    import fp8_kv_cache_amd
+    return fp8_kv_cache_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sz_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_codec_calls():
+    names = declared_functions()
+    for want in ("sz_histogram", "sz_build_codebook", "sz_encode", "sz_decode",
+                 "sz_max_compressed_bytes"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(sz):
+    lib = ctypes.CDLL(sz.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", sz.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(declared_functions()) <= exported
+    # nothing else of ours leaks out of the library
+    assert all(not s.startswith("sz_") or s in declared_functions() for s in exported)
+
+
+def test_library_contains_no_cpu_codec_path(sz):
+    """The product library links neither the oracle nor any CPU codec."""
+    out = subprocess.run(["nm", "-D", sz.library_path()], capture_output=True, text=True).stdout
+    assert "szo_" not in out
+
+
+@pytest.mark.parametrize("dt", [1, 2])
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 511, 4095, 4096, 4097, 1 << 20, (1 << 23) + 17, (1 << 32) - 1])
+def test_max_bytes_matches_oracle(sz, dt, n):
+    assert sz.sz_max_compressed_bytes(n, dt) == oracle.max_bytes(n, dt)
+
+
+def test_max_bytes_rejects_bad_input(sz):
+    assert sz.sz_max_compressed_bytes(1 << 32, 1) == 0
+    assert sz.sz_max_compressed_bytes(10, 0) == 0
+    assert sz.sz_max_compressed_bytes(10, 3) == 0
+
+
+def test_workspace_bytes(sz):
+    assert sz.sz_encode_workspace_bytes(0, 1) == 256
+    assert sz.sz_encode_workspace_bytes(4096, 1) == 256 + 8
+    assert sz.sz_encode_workspace_bytes(4097, 2) == 256 + 16
+    assert sz.sz_encode_workspace_bytes_batched(64, 1 << 23, 1) == 256 + 8 * 64 * 2048
+    assert sz.sz_encode_workspace_bytes_batched(0, 100, 1) == 0
+    assert sz.sz_encode_workspace_bytes(1 << 32, 1) == 0
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced: every call below fails its host check
+
+
+def test_host_argument_errors_return_before_launch(sz):
+    E_ARG, E_SMALL, E_CORRUPT = sz.SZ_ERR_INVALID_ARGUMENT, sz.SZ_ERR_BUFFER_TOO_SMALL, sz.SZ_ERR_CORRUPT_STREAM
+    # histogram: null / misaligned / bad dtype / too many elements
+    assert sz.sz_histogram(None, 10, 1, FAKE, stream=0) == E_ARG
+    assert sz.sz_histogram(FAKE, 10, 1, None, stream=0) == E_ARG
+    assert sz.sz_histogram(FAKE + 1, 10, 1, FAKE, stream=0) == E_ARG
+    assert sz.sz_histogram(FAKE, 10, 7, FAKE, stream=0) == E_ARG
+    assert sz.sz_histogram(FAKE, 1 << 32, 1, FAKE, stream=0) == E_ARG
+    assert sz.sz_build_codebook(None, 1, FAKE, stream=0) == E_ARG
+    assert sz.sz_build_codebook(FAKE, 5, FAKE, stream=0) == E_ARG
+    # encode: capacity and workspace below the bound
+    cap = sz.sz_max_compressed_bytes(5000, 1)
+    ws = sz.sz_encode_workspace_bytes(5000, 1)
+    assert sz.sz_encode(FAKE, 5000, 1, FAKE, FAKE, cap - 1, None, FAKE, ws, stream=0) == E_SMALL
+    assert sz.sz_encode(FAKE, 5000, 1, FAKE, FAKE, cap, None, FAKE, ws - 1, stream=0) == E_SMALL
+    assert sz.sz_encode(FAKE, 5000, 1, FAKE, FAKE, cap, None, None, ws, stream=0) == E_ARG
+    assert sz.sz_encode(FAKE, 5000, 1, None, FAKE, cap, None, FAKE, ws, stream=0) == E_ARG
+    assert sz.sz_encode(FAKE, 5000, 1, FAKE, FAKE, cap, FAKE + 4, FAKE, ws, stream=0) == E_ARG
+    # decode: a buffer smaller than any stream of n elements
+    assert sz.sz_decode(FAKE, 100, 5000, 1, FAKE, None, stream=0) == E_CORRUPT
+    assert sz.sz_decode(None, 100000, 5000, 1, FAKE, None, stream=0) == E_ARG
+    assert sz.sz_decode(FAKE, 100000, 5000, 1, FAKE, FAKE + 2, stream=0) == E_ARG
+    # batched forms
+    assert sz.sz_histogram_batched(FAKE, 0, 10, 1, FAKE, stream=0) == E_ARG
+    assert sz.sz_encode_batched(FAKE, 2, 5000, 1, FAKE, FAKE, cap, None, FAKE,
+                                sz.sz_encode_workspace_bytes(5000, 1), stream=0) == E_SMALL
+    assert sz.sz_decode_batched(FAKE, None, 2, 5000, 1, FAKE, None, stream=0) == E_ARG
+
+
+def test_status_strings(sz):
+    assert sz.sz_status_string(0) == "ok"
+    assert sz.sz_status_string(3) == "corrupt stream"
+    assert sz.sz_status_string(99) == "unknown status"

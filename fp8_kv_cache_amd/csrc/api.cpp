@@ -13,7 +13,6 @@ namespace {
 using namespace sz;
 
 constexpr uint64_t kMaxElems = uint64_t(1) << 32;   // offsets are u32
-constexpr uint64_t kWorkspaceHead = 256;            // ticket counter area
 
 bool dtype_ok(sz_dtype dt) { return dt == SZ_DTYPE_BF16 || dt == SZ_DTYPE_FP8_E5M2; }
 
@@ -23,9 +22,7 @@ bool usable(const void* p) { return p != nullptr && aligned16(p); }
 
 sz_status from_hip(hipError_t e) { return e == hipSuccess ? SZ_OK : SZ_ERR_HIP; }
 
-uint64_t workspace_bytes(uint32_t count, uint64_t n) {
-    return kWorkspaceHead + 8 * static_cast<uint64_t>(count) * layout_of(n, kDtypeBF16).blocks;
-}
+uint64_t workspace_bytes(uint32_t count, uint64_t n) { return workspace_bytes_for(count, n); }
 
 // histogram workgroups per tensor: about 2048 workgroups in total, each
 // covering a multiple of 32768 elements
@@ -63,10 +60,8 @@ sz_status encode_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, const
     a.count = count;
     a.n = n;
     if (n == 0) return from_hip(launch_encode_empty(a, dt, s));
-    a.ticket = static_cast<uint32_t*>(d_workspace);
-    a.status = reinterpret_cast<uint64_t*>(static_cast<char*>(d_workspace) + kWorkspaceHead);
-    hipError_t e = launch_fill_u64(static_cast<uint64_t*>(d_workspace), workspace_bytes(count, n) / 8, 0, s);
-    if (e != hipSuccess) return SZ_ERR_HIP;
+    a.counts = static_cast<uint32_t*>(d_workspace);
+    a.staging = static_cast<uint8_t*>(d_workspace) + workspace_counts_bytes(count, layout_of(n, dt).blocks);
     return from_hip(launch_encode(a, dt, s));
 }
 

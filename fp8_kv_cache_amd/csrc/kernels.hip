@@ -243,45 +243,19 @@ __global__ __launch_bounds__(256) void k_codebook(CodebookArgs a) {
 }
 
 // ----------------------------------------------------------------- encode
-
-constexpr uint64_t kFlagAggregate = 1ull << 32;
-constexpr uint64_t kFlagInclusive = 2ull << 32;
-
-__device__ inline void publish(SZ_GLOBAL uint64_t* word, uint64_t value) {
-    __hip_atomic_store(word, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix
-// Scan with Decoupled Look-back"), wave-parallel: each lane reads one of
-// the 64 nearest predecessors' status words at once.  Returns the number of
-// escapes in blocks [0, b) of this tensor.
-__device__ inline uint32_t look_back(const SZ_GLOBAL uint64_t* status, uint64_t b, uint32_t lane) {
-    uint32_t prefix = 0;
-    int64_t newest = static_cast<int64_t>(b) - 1;
-    while (true) {
-        const int64_t idx = newest - static_cast<int64_t>(lane);
-        uint64_t w = kFlagInclusive;  // before block 0: an inclusive zero
-        if (idx >= 0)
-            w = __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t flag = static_cast<uint32_t>(w >> 32);
-        const uint64_t not_ready = ballot(flag == 0);
-        const uint64_t inclusive = ballot(flag == 2);
-        // lanes up to and including the nearest inclusive predecessor
-        const uint64_t need = inclusive ? (((inclusive & (~inclusive + 1)) << 1) - 1) : ~0ull;
-        if (not_ready & need) {
-            __builtin_amdgcn_s_sleep(1);
-            continue;
-        }
-        const uint32_t v = ((need >> lane) & 1ull) ? static_cast<uint32_t>(w) : 0u;
-        prefix += wave_sum(v);
-        if (inclusive) break;
-        newest -= 64;
-    }
-    return prefix;
-}
+//
+// Three launches, none of which waits on another workgroup (so block ids
+// come straight from blockIdx and no ordering tickets are needed):
+//   k_encode   one wave per 4096-element block: sign|mantissa and code
+//              planes, the block's escape count, and its escape bytes
+//              staged at block-local ranks in the workspace;
+//   k_offsets  one workgroup per tensor: exclusive scan of the block counts
+//              into the stream's offset table, then the header;
+//   k_scatter  copies each block's staged escapes to their place in the
+//              stream's escape region.
 
 // Header (64 bytes), the zero padding after the offset table and the
-// stream size, written by the wave that owns the last block.
+// stream size; `lane` is the calling thread's index (0..63 used).
 __device__ inline void write_header(SZ_GLOBAL uint8_t* dst, const Layout& L, uint32_t dtype,
                                     const SZ_GLOBAL uint8_t* cb, uint64_t escapes, SZ_GLOBAL uint64_t* out_bytes,
                                     uint32_t lane) {
@@ -378,30 +352,39 @@ __device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, 
     sm[2] = (f[5] >> 4) | (f[6] << 8) | (f[7] << 20);
 }
 
-template <uint32_t DT>
-__global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
+// One block.  kFull: the block holds 4096 elements, so loads and stores
+// need no per-lane guards.
+template <uint32_t DT, bool kFull>
+__device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32_t t, uint64_t b,
+                                    uint64_t flat, uint32_t lane, uint32_t* tbl_words) {
     using G = Geometry<DT>;
     constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
     constexpr uint32_t kSmWords = DT == kDtypeBF16 ? 4 : 3;
-    __shared__ uint32_t s_ticket;
-    __shared__ uint32_t s_tbl[kWavesPerGroup][64];   // 256 one-byte codes per wave
 
-    const uint32_t wave = uniform(threadIdx.x / kWaveSize);
-    const uint32_t lane = lane_id();
-    if (threadIdx.x == 0)
-        s_ticket = __hip_atomic_fetch_add(gptr(a.ticket), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const Layout L = layout_of(a.n, DT);
-    const uint64_t flat = static_cast<uint64_t>(uniform(s_ticket)) * kWavesPerGroup + wave;
-    if (flat >= static_cast<uint64_t>(a.count) * L.blocks) return;
-    const uint32_t t = static_cast<uint32_t>(flat / L.blocks);
-    const uint64_t b = flat - static_cast<uint64_t>(t) * L.blocks;
+    // codebook entry of this lane first, then the block's input
+    const SZ_GLOBAL uint8_t* cb = gptr(a.codebooks) + 16ull * t;
+    const uint32_t mine = lane < kCodes ? cb[lane] : 0xFFFFu;
+    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+    const uint64_t blk0 = b * kBlockElems;
+    uint32_t d[G::kSubs][8];
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
+        if (kFull) {
+            const SZ_GLOBAL u32x4* p = (const SZ_GLOBAL u32x4*)(src + elem0 * G::kElemBytes);
+            const u32x4 x = p[0], y = p[1];
+            d[j][0] = x.x; d[j][1] = x.y; d[j][2] = x.z; d[j][3] = x.w;
+            d[j][4] = y.x; d[j][5] = y.y; d[j][6] = y.z; d[j][7] = y.w;
+        } else {
+            load_lane<DT>(src, elem0, a.n, d[j]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // Code of every exponent value: the lowest c with cb[c] == v, else 15.
-    const SZ_GLOBAL uint8_t* cb = gptr(a.codebooks) + 16ull * t;
-    uint8_t* tbl = reinterpret_cast<uint8_t*>(s_tbl[wave]);
-    s_tbl[wave][lane] = 0x0F0F0F0Fu;
-    const uint32_t mine = lane < kCodes ? cb[lane] : 0xFFFFu;
+    uint8_t* tbl = reinterpret_cast<uint8_t*>(tbl_words);
+    tbl_words[lane] = 0x0F0F0F0Fu;
     bool lowest = lane < kCodes;
 #pragma unroll
     for (uint32_t c = 0; c + 1 < kCodes; ++c) {
@@ -411,15 +394,6 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
     if (lowest) tbl[mine] = static_cast<uint8_t>(lane);
     __builtin_amdgcn_wave_barrier();
 
-    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
-    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
-    const uint64_t blk0 = b * kBlockElems;
-
-    uint32_t d[G::kSubs][8];
-#pragma unroll
-    for (uint32_t j = 0; j < G::kSubs; ++j)
-        load_lane<DT>(src, blk0 + j * kSubElems + lane * G::kLaneElems, a.n, d[j]);
-
     uint32_t sm[G::kSubs][kSmWords];
     uint32_t cw[G::kSubs][G::kCodeWords];
     uint32_t esc[G::kSubs][G::kCodeWords];
@@ -427,7 +401,8 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; ++j) {
         const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
-        const uint32_t valid = elem0 >= a.n ? 0u
+        const uint32_t valid = kFull ? G::kLaneElems
+                               : elem0 >= a.n ? 0u
                                : (a.n - elem0 >= G::kLaneElems ? G::kLaneElems
                                                                  : static_cast<uint32_t>(a.n - elem0));
         if constexpr (DT == kDtypeBF16)
@@ -437,6 +412,28 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
         cnt[j] = 0;
 #pragma unroll
         for (uint32_t q = 0; q < G::kCodeWords; ++q) cnt[j] += __builtin_popcount(esc[j][q]);
+    }
+
+    // planes; vectors at or beyond the padded plane end are not stored
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
+        const uint64_t code_off = elem0 / 2;
+        if constexpr (DT == kDtypeBF16) {
+            if (kFull || elem0 < L.sm_region)
+                *(SZ_GLOBAL u32x4*)(dst + L.sm_at + elem0) = u32x4{sm[j][0], sm[j][1], sm[j][2], sm[j][3]};
+            if (kFull || code_off < L.code_region)
+                *(SZ_GLOBAL u32x2*)(dst + L.code_at + code_off) = u32x2{cw[j][0], cw[j][1]};
+        } else {
+            const uint64_t sm_off = elem0 / 32 * 12;
+            SZ_GLOBAL uint32_t* smp = (SZ_GLOBAL uint32_t*)(dst + L.sm_at + sm_off);
+#pragma unroll
+            for (uint32_t i = 0; i < 3; ++i)
+                if (kFull || sm_off + 4 * i < L.sm_region) smp[i] = sm[j][i];
+            if (kFull || code_off < L.code_region)
+                *(SZ_GLOBAL u32x4*)(dst + L.code_at + code_off) =
+                    u32x4{cw[j][0], cw[j][1], cw[j][2], cw[j][3]};
+        }
     }
 
     // Escape ranks inside the block: element order is (sub-chunk, lane,
@@ -457,41 +454,10 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
             block_total += tot >> 16;
         }
     }
-    block_total = uniform(block_total);
+    if (lane == 0) gptr(a.counts)[flat] = uniform(block_total);
 
-    SZ_GLOBAL uint64_t* status = gptr(a.status) + static_cast<uint64_t>(t) * L.blocks;
-    if (lane == 0) publish(status + b, (b == 0 ? kFlagInclusive : kFlagAggregate) | block_total);
-
-    // planes; vectors at or beyond the padded plane end are not stored
-#pragma unroll
-    for (uint32_t j = 0; j < G::kSubs; ++j) {
-        const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
-        const uint64_t code_off = elem0 / 2;
-        if constexpr (DT == kDtypeBF16) {
-            if (elem0 < L.sm_region)
-                *(SZ_GLOBAL u32x4*)(dst + L.sm_at + elem0) = u32x4{sm[j][0], sm[j][1], sm[j][2], sm[j][3]};
-            if (code_off < L.code_region)
-                *(SZ_GLOBAL u32x2*)(dst + L.code_at + code_off) = u32x2{cw[j][0], cw[j][1]};
-        } else {
-            const uint64_t sm_off = elem0 / 32 * 12;
-            SZ_GLOBAL uint32_t* smp = (SZ_GLOBAL uint32_t*)(dst + L.sm_at + sm_off);
-#pragma unroll
-            for (uint32_t i = 0; i < 3; ++i)
-                if (sm_off + 4 * i < L.sm_region) smp[i] = sm[j][i];
-            if (code_off < L.code_region)
-                *(SZ_GLOBAL u32x4*)(dst + L.code_at + code_off) =
-                    u32x4{cw[j][0], cw[j][1], cw[j][2], cw[j][3]};
-        }
-    }
-
-    const uint32_t prefix = b == 0 ? 0u : uniform(look_back(status, b, lane));
-    if (lane == 0) {
-        if (b != 0) publish(status + b, kFlagInclusive | (prefix + block_total));
-        ((SZ_GLOBAL uint32_t*)(dst + 64))[b] = prefix;
-    }
-
-    // escape bytes, in element order
-    SZ_GLOBAL uint8_t* esc_out = dst + L.esc_at + prefix;
+    // escape bytes, in element order, staged at their rank inside the block
+    SZ_GLOBAL uint8_t* esc_out = gptr(a.staging) + flat * kBlockElems;
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; ++j) {
         if (cnt[j] == 0) continue;
@@ -520,9 +486,84 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
             }
         }
     }
+}
 
-    if (b == L.blocks - 1)
-        write_header(dst, L, DT, cb, prefix + block_total, a.out_bytes ? gptr(a.out_bytes) + t : nullptr, lane);
+// Full blocks only: wave i of the grid takes the i-th full block in
+// (tensor, block) order.  A partial last block goes to k_encode_tail, so
+// this kernel is compiled without per-lane guards.
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
+    __shared__ uint32_t s_tbl[kWavesPerGroup][64];   // 256 one-byte codes per wave
+    const uint32_t wave = uniform(threadIdx.x / kWaveSize);
+    const Layout L = layout_of(a.n, DT);
+    const uint64_t full = a.n / kBlockElems;          // full blocks per tensor
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave;
+    if (i >= static_cast<uint64_t>(a.count) * full) return;
+    const uint32_t t = static_cast<uint32_t>(i / full);
+    const uint64_t b = i - static_cast<uint64_t>(t) * full;
+    encode_block<DT, true>(a, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane_id(), s_tbl[wave]);
+}
+
+// The partial last block of every tensor, one wave each.
+template <uint32_t DT>
+__global__ __launch_bounds__(kWaveSize) void k_encode_tail(EncodeArgs a) {
+    __shared__ uint32_t s_tbl[64];
+    const Layout L = layout_of(a.n, DT);
+    const uint32_t t = blockIdx.x;
+    const uint64_t b = L.blocks - 1;
+    encode_block<DT, false>(a, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane_id(), s_tbl);
+}
+
+// One workgroup per tensor: off[b] = escapes in blocks [0, b), then the
+// header.  Thread i scans a contiguous run of ceil(B / 256) block counts.
+template <uint32_t DT>
+__global__ __launch_bounds__(256) void k_offsets(EncodeArgs a) {
+    __shared__ uint32_t s_wave_total[kWavesPerGroup];
+    const uint32_t t = blockIdx.x, tid = threadIdx.x;
+    const uint32_t lane = lane_id(), wave = uniform(tid / kWaveSize);
+    const Layout L = layout_of(a.n, DT);
+    const SZ_GLOBAL uint32_t* counts = gptr(a.counts) + static_cast<uint64_t>(t) * L.blocks;
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+    SZ_GLOBAL uint32_t* offs = (SZ_GLOBAL uint32_t*)(dst + 64);
+    const uint64_t per = (L.blocks + 255) / 256;
+    const uint64_t lo = tid * per < L.blocks ? tid * per : L.blocks;
+    const uint64_t hi = lo + per < L.blocks ? lo + per : L.blocks;
+    uint32_t sum = 0;
+    for (uint64_t b = lo; b < hi; ++b) sum += counts[b];
+    const uint32_t incl = wave_scan_incl(sum);
+    if (lane == 63) s_wave_total[wave] = incl;
+    __syncthreads();
+    uint32_t run = incl - sum;
+    for (uint32_t w = 0; w < wave; ++w) run += s_wave_total[w];
+    const uint32_t escapes = s_wave_total[0] + s_wave_total[1] + s_wave_total[2] + s_wave_total[3];
+    for (uint64_t b = lo; b < hi; ++b) {
+        offs[b] = run;
+        run += counts[b];
+    }
+    write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, escapes,
+                 a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid);
+}
+
+// Staged escapes -> the stream's escape region; one wave per block,
+// grid-stride over all blocks of all tensors.
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_scatter(EncodeArgs a) {
+    const uint32_t lane = lane_id();
+    const Layout L = layout_of(a.n, DT);
+    const uint64_t total = static_cast<uint64_t>(a.count) * L.blocks;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kWavesPerGroup;
+    for (uint64_t flat = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWaveSize);
+         flat < total; flat += stride) {
+        const uint32_t cnt = uniform(gptr(a.counts)[flat]);
+        if (cnt == 0) continue;
+        const uint32_t t = static_cast<uint32_t>(flat / L.blocks);
+        const uint64_t b = flat - static_cast<uint64_t>(t) * L.blocks;
+        SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+        const uint32_t off = uniform(((const SZ_GLOBAL uint32_t*)(dst + 64))[b]);
+        const SZ_GLOBAL uint8_t* from = gptr(a.staging) + flat * kBlockElems;
+        SZ_GLOBAL uint8_t* to = dst + L.esc_at + off;
+        for (uint32_t i = lane; i < cnt; i += kWaveSize) to[i] = from[i];
+    }
 }
 
 // n == 0: a header-only stream per tensor
@@ -546,13 +587,19 @@ __device__ inline uint32_t lookup4(uint32_t x, const uint32_t (&cbw)[4]) {
     return (hi & m) | (lo & ~m);
 }
 
-// Header check shared by all waves of a stream.  Returns the escape count
-// or -1 when the stream does not match (n, dtype, src_bytes) or itself.
-template <uint32_t DT>
-__device__ inline int64_t check_header(const SZ_GLOBAL uint8_t* src, uint64_t src_bytes, const Layout& L,
-                                       uint32_t (&cbw)[4]) {
-    if (src_bytes < 64) return -1;
+// The 16 header dwords of a stream (caller guarantees src_bytes >= 64).
+__device__ inline void load_header(const SZ_GLOBAL uint8_t* src, uint32_t (&w)[16]) {
     const SZ_GLOBAL uint32_t* h = (const SZ_GLOBAL uint32_t*)src;
+#pragma unroll
+    for (uint32_t i = 0; i < 16; ++i) w[i] = h[i];
+}
+
+// Header check shared by all waves of a stream.  Returns the escape count
+// or -1 when the stream does not match (n, dtype, src_bytes) or itself;
+// fills the codebook registers.
+template <uint32_t DT>
+__device__ inline int64_t check_header(const uint32_t (&h)[16], uint64_t src_bytes, const Layout& L,
+                                       uint32_t (&cbw)[4]) {
     uint32_t w[16];
 #pragma unroll
     for (uint32_t i = 0; i < 16; ++i) w[i] = uniform(h[i]);
@@ -584,122 +631,185 @@ __device__ inline void put_byte(uint32_t& w0, uint32_t& w1, uint32_t k, uint32_t
         w1 = (w1 & clear) | (e << shift);
 }
 
+// Decode work split.  BF16: lane l of sub-chunk j owns 8 elements, so per
+// lane one code dword, two sign|mantissa dwords and four output dwords, and
+// every load and store of the wave is one contiguous run.  E5M2: 32
+// elements per lane (four code dwords, three 3-bit-field dwords).
 template <uint32_t DT>
-__global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
-    using G = Geometry<DT>;
-    constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
-    constexpr uint32_t kSmWords = DT == kDtypeBF16 ? 4 : 3;
-    const uint32_t wave = uniform(threadIdx.x / kWaveSize);
-    const uint32_t lane = lane_id();
-    const Layout L = layout_of(a.n, DT);
-    const uint64_t flat = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave;
-    if (flat >= static_cast<uint64_t>(a.count) * L.blocks) return;
-    const uint32_t t = static_cast<uint32_t>(flat / L.blocks);
-    const uint64_t b = flat - static_cast<uint64_t>(t) * L.blocks;
+struct DecodeGeometry;
+template <>
+struct DecodeGeometry<kDtypeBF16> {
+    static constexpr uint32_t kLaneElems = 8;
+    static constexpr uint32_t kSubs = 8;
+    static constexpr uint32_t kCodeWords = 1;
+    static constexpr uint32_t kSmWords = 2;
+    static constexpr uint32_t kOutWords = 4;
+};
+template <>
+struct DecodeGeometry<kDtypeE5M2> {
+    static constexpr uint32_t kLaneElems = 32;
+    static constexpr uint32_t kSubs = 2;
+    static constexpr uint32_t kCodeWords = 4;
+    static constexpr uint32_t kSmWords = 3;
+    static constexpr uint32_t kOutWords = 8;
+};
 
+constexpr uint32_t kPrefetch = 2 * kWaveSize;   // escape bytes staged in LDS per block
+
+// Replace the exponent bytes of this lane's escaped elements (escape nibble
+// mask m over the 8 elements held in e0/e1) with the next escape bytes.
+// `near` is wave-uniform: when every escape of the block sits in the LDS
+// copy, the loop touches no global memory, so it never waits on the
+// block's outstanding stores.
+__device__ inline void patch_escapes(uint32_t& e0, uint32_t& e1, uint32_t m, uint32_t& rank, bool near,
+                                     const uint8_t* esc_near, const SZ_GLOBAL uint8_t* esc_in) {
+    if (near) {
+        while (m) {
+            put_byte(e0, e1, __builtin_ctz(m) >> 2, esc_near[rank++]);
+            m &= m - 1;
+        }
+    } else {
+        while (m) {
+            put_byte(e0, e1, __builtin_ctz(m) >> 2, esc_in[rank++]);
+            m &= m - 1;
+        }
+    }
+}
+
+// One block.  kFull: the block holds 4096 elements (every lane's elements
+// exist), so the loads and stores need no per-lane guards.
+template <uint32_t DT, bool kFull>
+__device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32_t t, uint64_t b,
+                                    uint32_t lane, uint8_t* esc_near) {
+    using G = DecodeGeometry<DT>;
+    constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
     const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
     const uint64_t src_bytes = a.src_bytes_table ? gptr(a.src_bytes_table)[t] : a.src_bytes;
     SZ_GLOBAL int32_t* status = a.status ? gptr(a.status) + t : nullptr;
-    uint32_t cbw[4];
-    const int64_t escapes = check_header<DT>(src, src_bytes, L, cbw);
-    if (escapes < 0) {
+    // Every read below lies in [0, esc_at) -- header, offsets, both planes
+    // (the E5M2 plane's last 12-byte group may run into the code region) --
+    // or, for escape bytes, below src_bytes.  With that range readable, all
+    // loads are issued at once and the stream is validated afterwards.
+    if (src_bytes < L.esc_at) {
         mark_corrupt(status, lane);
         return;
     }
-    const SZ_GLOBAL uint32_t* offs = (const SZ_GLOBAL uint32_t*)(src + 64);
-    const uint32_t first = uniform(offs[b]);
-    const uint64_t next = b + 1 < L.blocks ? uniform(offs[b + 1]) : static_cast<uint64_t>(escapes);
-    if ((b == 0 && first != 0) || next < first || next > static_cast<uint64_t>(escapes)) {
-        mark_corrupt(status, lane);
-        return;
-    }
+    // one load: header dwords (lanes 0..15) and offsets b, b+1 (lanes 16, 17;
+    // the offset table starts at dword 16); other lanes re-read dword 0
+    const uint64_t meta_at = lane < 16 ? lane
+                             : lane == 16 ? 16 + b
+                             : (lane == 17 && b + 1 < L.blocks) ? 17 + b : 0;
+    const uint32_t meta = ((const SZ_GLOBAL uint32_t*)src)[meta_at];
 
     const uint64_t blk0 = b * kBlockElems;
     uint32_t cw[G::kSubs][G::kCodeWords];
-    uint32_t sm[G::kSubs][kSmWords];
-    uint32_t esc[G::kSubs][G::kCodeWords];
-    uint32_t cnt[G::kSubs];
+    uint32_t sm[G::kSubs][G::kSmWords];
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; ++j) {
         const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
-        if (elem0 < L.n) {
+        if (kFull || elem0 < L.n) {
             if constexpr (DT == kDtypeBF16) {
-                const u32x2 c = *(const SZ_GLOBAL u32x2*)(src + L.code_at + elem0 / 2);
-                cw[j][0] = c.x; cw[j][1] = c.y;
-                const u32x4 s = *(const SZ_GLOBAL u32x4*)(src + L.sm_at + elem0);
-                sm[j][0] = s.x; sm[j][1] = s.y; sm[j][2] = s.z; sm[j][3] = s.w;
+                cw[j][0] = *(const SZ_GLOBAL uint32_t*)(src + L.code_at + elem0 / 2);
+                const u32x2 v = *(const SZ_GLOBAL u32x2*)(src + L.sm_at + elem0);
+                sm[j][0] = v.x; sm[j][1] = v.y;
             } else {
                 const u32x4 c = *(const SZ_GLOBAL u32x4*)(src + L.code_at + elem0 / 2);
                 cw[j][0] = c.x; cw[j][1] = c.y; cw[j][2] = c.z; cw[j][3] = c.w;
-                const SZ_GLOBAL uint32_t* s = (const SZ_GLOBAL uint32_t*)(src + L.sm_at + elem0 / 32 * 12);
-                sm[j][0] = s[0]; sm[j][1] = s[1]; sm[j][2] = s[2];
+                const SZ_GLOBAL uint32_t* v = (const SZ_GLOBAL uint32_t*)(src + L.sm_at + elem0 / 32 * 12);
+                sm[j][0] = v[0]; sm[j][1] = v[1]; sm[j][2] = v[2];
             }
         } else {
 #pragma unroll
             for (uint32_t q = 0; q < G::kCodeWords; ++q) cw[j][q] = 0;
 #pragma unroll
-            for (uint32_t q = 0; q < kSmWords; ++q) sm[j][q] = 0;
+            for (uint32_t q = 0; q < G::kSmWords; ++q) sm[j][q] = 0;
         }
-        const int64_t valid = static_cast<int64_t>(L.n) - static_cast<int64_t>(elem0);
+    }
+
+    // keep every plane load ahead of the wait for the offset below
+    __builtin_amdgcn_sched_barrier(0);
+
+    // The block's first escape bytes, fetched as soon as its offset is known
+    // (addresses clamped into the buffer; bytes past the block are unused).
+    const uint32_t first = __builtin_amdgcn_readlane(meta, 16);
+    const uint64_t esc_first = L.esc_at + first;
+    const uint64_t last = src_bytes - 1;
+    const uint64_t p0 = esc_first + lane, p1 = esc_first + kWaveSize + lane;
+    const uint32_t pre0 = src[p0 < last ? p0 : last];
+    const uint32_t pre1 = src[p1 < last ? p1 : last];
+
+    uint32_t hdr[16], cbw[4];
+#pragma unroll
+    for (uint32_t i = 0; i < 16; ++i) hdr[i] = __builtin_amdgcn_readlane(meta, i);
+    const int64_t escapes = check_header<DT>(hdr, src_bytes, L, cbw);
+    const uint64_t next = b + 1 < L.blocks ? __builtin_amdgcn_readlane(meta, 17) : static_cast<uint64_t>(escapes);
+    if (escapes < 0 || (b == 0 && first != 0) || next < first || next > static_cast<uint64_t>(escapes)) {
+        mark_corrupt(status, lane);
+        return;
+    }
+
+    uint32_t esc[G::kSubs][G::kCodeWords];
+    uint32_t cnt[G::kSubs];
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
         cnt[j] = 0;
+        const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
+        const int64_t valid = static_cast<int64_t>(L.n) - static_cast<int64_t>(elem0);
 #pragma unroll
         for (uint32_t q = 0; q < G::kCodeWords; ++q) {
-            esc[j][q] = escape_nibbles(cw[j][q]) &
-                        valid_nibbles(static_cast<int32_t>(valid > 64 ? 64 : valid) - 8 * static_cast<int32_t>(q));
+            esc[j][q] = escape_nibbles(cw[j][q]);
+            if (!kFull)
+                esc[j][q] &= valid_nibbles(static_cast<int32_t>(valid > 64 ? 64 : valid) - 8 * static_cast<int32_t>(q));
             cnt[j] += __builtin_popcount(esc[j][q]);
         }
     }
 
+    // Escape ranks inside the block (element order = sub-chunk, lane,
+    // element); sub-chunk counts are scanned two at a time in 16-bit halves.
     uint32_t base[G::kSubs];
     uint32_t block_total = 0;
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; j += 2) {
-        const uint32_t packed = cnt[j] | (j + 1 < G::kSubs ? cnt[j + 1] << 16 : 0u);
+        const uint32_t packed = cnt[j] | (cnt[j + 1] << 16);
         const uint32_t incl = wave_scan_incl(packed);
         const uint32_t excl = incl - packed;
         const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
         base[j] = block_total + (excl & 0xFFFFu);
         block_total += tot & 0xFFFFu;
-        if (j + 1 < G::kSubs) {
-            base[j + 1] = block_total + (excl >> 16);
-            block_total += tot >> 16;
-        }
+        base[j + 1] = block_total + (excl >> 16);
+        block_total += tot >> 16;
     }
-    if (uniform(block_total) != next - first) {
+    block_total = uniform(block_total);
+    if (block_total != next - first) {
         mark_corrupt(status, lane);
         return;
     }
+    esc_near[lane] = static_cast<uint8_t>(pre0);
+    esc_near[kWaveSize + lane] = static_cast<uint8_t>(pre1);
+    __builtin_amdgcn_wave_barrier();
 
-    const SZ_GLOBAL uint8_t* esc_in = src + L.esc_at + first;
+    const SZ_GLOBAL uint8_t* esc_in = src + esc_first;
+    const bool near = block_total <= kPrefetch;   // all escapes of the block are in LDS
     SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; ++j) {
         const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
-        if (elem0 >= L.n) continue;
+        if (!kFull && elem0 >= L.n) continue;
         uint32_t rank = base[j];
-        uint32_t out[8];
+        uint32_t out[G::kOutWords];
         if constexpr (DT == kDtypeBF16) {
+            const uint32_t c = cw[j][0];
+            const uint32_t ev = lookup4(c & 0x0F0F0F0Fu, cbw);         // elements 0,2,4,6
+            const uint32_t od = lookup4((c >> 4) & 0x0F0F0F0Fu, cbw);  // elements 1,3,5,7
+            uint32_t e0 = perm(od, ev, 0x05010400u);                    // elements 0..3
+            uint32_t e1 = perm(od, ev, 0x07030602u);                    // elements 4..7
+            patch_escapes(e0, e1, esc[j][0], rank, near, esc_near, esc_in);
+            // (sign|mantissa byte s, exponent byte e) pairs -> BF16 words
 #pragma unroll
-            for (uint32_t q = 0; q < 2; ++q) {
-                const uint32_t c = cw[j][q];
-                const uint32_t ev = lookup4(c & 0x0F0F0F0Fu, cbw);         // elements 0,2,4,6
-                const uint32_t od = lookup4((c >> 4) & 0x0F0F0F0Fu, cbw);  // elements 1,3,5,7
-                uint32_t e0 = perm(od, ev, 0x05010400u);                    // elements 0..3
-                uint32_t e1 = perm(od, ev, 0x07030602u);                    // elements 4..7
-                uint32_t m = esc[j][q];
-                while (m) {
-                    const uint32_t k = __builtin_ctz(m) >> 2;
-                    put_byte(e0, e1, k, esc_in[rank++]);
-                    m &= m - 1;
-                }
-                // (sign|mantissa byte s, exponent byte e) pairs -> BF16 words
-#pragma unroll
-                for (uint32_t h = 0; h < 4; ++h) {
-                    const uint32_t ew = h < 2 ? e0 : e1;
-                    const uint32_t sw = sm[j][2 * q + (h >> 1)];
-                    const uint32_t v = perm(ew, sw, (h & 1) ? 0x07030602u : 0x05010400u);
-                    out[4 * q + h] = ((v >> 1) & 0x7F807F80u) | ((v << 8) & 0x80008000u) | (v & 0x007F007Fu);
-                }
+            for (uint32_t h = 0; h < 4; ++h) {
+                const uint32_t ew = h < 2 ? e0 : e1;
+                const uint32_t v = perm(ew, sm[j][h >> 1], (h & 1) ? 0x07030602u : 0x05010400u);
+                out[h] = ((v >> 1) & 0x7F807F80u) | ((v << 8) & 0x80008000u) | (v & 0x007F007Fu);
             }
         } else {
             const uint32_t s0 = sm[j][0], s1 = sm[j][1], s2 = sm[j][2];
@@ -719,25 +829,24 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
                 const uint32_t od = lookup4((c >> 4) & 0x0F0F0F0Fu, cbw);
                 uint32_t e0 = perm(od, ev, 0x05010400u);
                 uint32_t e1 = perm(od, ev, 0x07030602u);
-                uint32_t m = esc[j][q];
-                while (m) {
-                    const uint32_t k = __builtin_ctz(m) >> 2;
-                    put_byte(e0, e1, k, esc_in[rank++]);
-                    m &= m - 1;
-                }
+                patch_escapes(e0, e1, esc[j][q], rank, near, esc_near, esc_in);
 #pragma unroll
                 for (uint32_t h = 0; h < 2; ++h) {
                     const uint32_t v = f[2 * q + h];
-                    const uint32_t s = (v & 0x7u) | ((v & 0x38u) << 5) | ((v & 0x1C0u) << 10) | ((v & 0xE00u) << 15);
+                    const uint32_t sf = (v & 0x7u) | ((v & 0x38u) << 5) | ((v & 0x1C0u) << 10) | ((v & 0xE00u) << 15);
                     const uint32_t e = h ? e1 : e0;
-                    out[2 * q + h] = ((s & 0x04040404u) << 5) | ((e & 0x1F1F1F1Fu) << 2) | (s & 0x03030303u);
+                    out[2 * q + h] = ((sf & 0x04040404u) << 5) | ((e & 0x1F1F1F1Fu) << 2) | (sf & 0x03030303u);
                 }
             }
         }
-        SZ_GLOBAL uint8_t* p = dst + elem0 * G::kElemBytes;
-        if (elem0 + G::kLaneElems <= L.n) {
-            ((SZ_GLOBAL u32x4*)p)[0] = u32x4{out[0], out[1], out[2], out[3]};
-            ((SZ_GLOBAL u32x4*)p)[1] = u32x4{out[4], out[5], out[6], out[7]};
+        SZ_GLOBAL uint8_t* p = dst + elem0 * (DT == kDtypeBF16 ? 2 : 1);
+        if (kFull || elem0 + G::kLaneElems <= L.n) {
+            if constexpr (DT == kDtypeBF16) {
+                *(SZ_GLOBAL u32x4*)p = u32x4{out[0], out[1], out[2], out[3]};
+            } else {
+                ((SZ_GLOBAL u32x4*)p)[0] = u32x4{out[0], out[1], out[2], out[3]};
+                ((SZ_GLOBAL u32x4*)p)[1] = u32x4{out[4], out[5], out[6], out[7]};
+            }
         } else {
             const uint32_t valid = static_cast<uint32_t>(L.n - elem0);
 #pragma unroll
@@ -753,6 +862,27 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     }
 }
 
+// Full blocks only (as k_encode); partial last blocks go to k_decode_tail.
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
+    __shared__ uint8_t s_esc[kWavesPerGroup][kPrefetch];
+    const uint32_t wave = uniform(threadIdx.x / kWaveSize);
+    const Layout L = layout_of(a.n, DT);
+    const uint64_t full = a.n / kBlockElems;
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave;
+    if (i >= static_cast<uint64_t>(a.count) * full) return;
+    const uint32_t t = static_cast<uint32_t>(i / full);
+    const uint64_t b = i - static_cast<uint64_t>(t) * full;
+    decode_block<DT, true>(a, L, t, b, lane_id(), s_esc[wave]);
+}
+
+template <uint32_t DT>
+__global__ __launch_bounds__(kWaveSize) void k_decode_tail(DecodeArgs a) {
+    __shared__ uint8_t s_esc[kPrefetch];
+    const Layout L = layout_of(a.n, DT);
+    decode_block<DT, false>(a, L, blockIdx.x, L.blocks - 1, lane_id(), s_esc);
+}
+
 // n == 0: only the header can be checked
 template <uint32_t DT>
 __global__ void k_decode_empty(DecodeArgs a) {
@@ -760,8 +890,14 @@ __global__ void k_decode_empty(DecodeArgs a) {
     const Layout L = layout_of(0, DT);
     const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
     const uint64_t src_bytes = a.src_bytes_table ? gptr(a.src_bytes_table)[t] : a.src_bytes;
-    uint32_t cbw[4];
-    if (check_header<DT>(src, src_bytes, L, cbw) < 0) mark_corrupt(a.status ? gptr(a.status) + t : nullptr, lane_id());
+    SZ_GLOBAL int32_t* status = a.status ? gptr(a.status) + t : nullptr;
+    if (src_bytes < L.esc_at) {
+        mark_corrupt(status, lane_id());
+        return;
+    }
+    uint32_t hdr[16], cbw[4];
+    load_header(src, hdr);
+    if (check_header<DT>(hdr, src_bytes, L, cbw) < 0) mark_corrupt(status, lane_id());
 }
 
 uint32_t grid_for(uint64_t items, uint32_t per_group) {
@@ -805,13 +941,24 @@ hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s)
     return hipGetLastError();
 }
 
+template <uint32_t DT>
+void enqueue_encode(const EncodeArgs& a, hipStream_t s) {
+    const Layout L = layout_of(a.n, DT);
+    const uint64_t full = static_cast<uint64_t>(a.count) * (a.n / kBlockElems);
+    const uint64_t blocks = static_cast<uint64_t>(a.count) * L.blocks;
+    uint32_t scatter_groups = grid_for(blocks, kWavesPerGroup);
+    if (scatter_groups > 2048) scatter_groups = 2048;
+    if (full) hipLaunchKernelGGL(k_encode<DT>, dim3(grid_for(full, kWavesPerGroup)), dim3(kThreads), 0, s, a);
+    if (a.n % kBlockElems) hipLaunchKernelGGL(k_encode_tail<DT>, dim3(a.count), dim3(kWaveSize), 0, s, a);
+    hipLaunchKernelGGL(k_offsets<DT>, dim3(a.count), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_scatter<DT>, dim3(scatter_groups), dim3(kThreads), 0, s, a);
+}
+
 hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s) {
-    const Layout L = layout_of(a.n, dtype);
-    const dim3 grid(grid_for(static_cast<uint64_t>(a.count) * L.blocks, kWavesPerGroup)), block(kThreads);
     if (dtype == kDtypeBF16)
-        hipLaunchKernelGGL(k_encode<kDtypeBF16>, grid, block, 0, s, a);
+        enqueue_encode<kDtypeBF16>(a, s);
     else
-        hipLaunchKernelGGL(k_encode<kDtypeE5M2>, grid, block, 0, s, a);
+        enqueue_encode<kDtypeE5M2>(a, s);
     return hipGetLastError();
 }
 
@@ -823,13 +970,18 @@ hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t 
     return hipGetLastError();
 }
 
+template <uint32_t DT>
+void enqueue_decode(const DecodeArgs& a, hipStream_t s) {
+    const uint64_t full = static_cast<uint64_t>(a.count) * (a.n / kBlockElems);
+    if (full) hipLaunchKernelGGL(k_decode<DT>, dim3(grid_for(full, kWavesPerGroup)), dim3(kThreads), 0, s, a);
+    if (a.n % kBlockElems) hipLaunchKernelGGL(k_decode_tail<DT>, dim3(a.count), dim3(kWaveSize), 0, s, a);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, uint32_t dtype, hipStream_t s) {
-    const Layout L = layout_of(a.n, dtype);
-    const dim3 grid(grid_for(static_cast<uint64_t>(a.count) * L.blocks, kWavesPerGroup)), block(kThreads);
     if (dtype == kDtypeBF16)
-        hipLaunchKernelGGL(k_decode<kDtypeBF16>, grid, block, 0, s, a);
+        enqueue_decode<kDtypeBF16>(a, s);
     else
-        hipLaunchKernelGGL(k_decode<kDtypeE5M2>, grid, block, 0, s, a);
+        enqueue_decode<kDtypeE5M2>(a, s);
     return hipGetLastError();
 }
 

@@ -49,6 +49,16 @@ __host__ __device__ inline Layout layout_of(uint64_t n, uint32_t dtype) {
     return L;
 }
 
+// Encode workspace: block escape counts (u32 per block), then 4096 staging
+// bytes per block (at most every element of a block escapes).
+__host__ __device__ inline uint64_t workspace_counts_bytes(uint32_t count, uint64_t blocks) {
+    return align256(4 * static_cast<uint64_t>(count) * blocks);
+}
+__host__ __device__ inline uint64_t workspace_bytes_for(uint32_t count, uint64_t n) {
+    const uint64_t blocks = (n + kBlockElems - 1) / kBlockElems;
+    return workspace_counts_bytes(count, blocks) + static_cast<uint64_t>(count) * blocks * kBlockElems;
+}
+
 // A tensor is addressed either through a device table of pointers (batched
 // calls) or directly (single-tensor calls).
 struct SrcRef {
@@ -80,8 +90,8 @@ struct EncodeArgs {
     DstRef dst;
     const uint8_t* codebooks; // count x 16
     uint64_t* out_bytes;      // count, may be null
-    uint64_t* status;         // count x blocks look-back words
-    uint32_t* ticket;         // workgroup ticket counter
+    uint32_t* counts;         // count x blocks escape counts (workspace)
+    uint8_t* staging;         // count x blocks x 4096 staged escape bytes (workspace)
     uint32_t count;
     uint64_t n;
 };
@@ -100,6 +110,7 @@ hipError_t launch_fill_u64(uint64_t* p, uint64_t words, uint64_t value, hipStrea
 hipError_t launch_fill_i32(int32_t* p, uint64_t words, int32_t value, hipStream_t s);
 hipError_t launch_histogram(const HistArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s);
+// encode = three kernels: planes + staged escapes, offsets + header, escape scatter
 hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, uint32_t dtype, hipStream_t s);

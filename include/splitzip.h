@@ -69,8 +69,10 @@ typedef enum {
  * function; returns 0 for an invalid dtype or n >= 2^32. */
 uint64_t sz_max_compressed_bytes(uint64_t n, sz_dtype dtype);
 
-/* Workspace sz_encode needs: one 8-byte status word per 4096-element
- * block plus a 256-byte counter area.  Pure host function; 0 on bad input. */
+/* Workspace sz_encode needs: a u32 escape count per 4096-element block
+ * (rounded up to 256 bytes), then 4096 staging bytes per block -- about one
+ * byte per element.  Escapes are staged per block so that no workgroup ever
+ * waits for another.  Pure host function; 0 on bad input or n = 0. */
 uint64_t sz_encode_workspace_bytes(uint64_t n, sz_dtype dtype);
 
 /* Exponent histogram (SplitZip "Abstract": exponent values are highly
@@ -92,8 +94,8 @@ sz_status sz_build_codebook(const uint64_t* d_hist, sz_dtype dtype,
  * cb[15] is ignored and stored as 0).  d_dst receives the whole stream;
  * dst_capacity must be >= sz_max_compressed_bytes(n, dtype), else
  * SZ_ERR_BUFFER_TOO_SMALL.  d_out_bytes (device u64, may be NULL) receives
- * C.  d_workspace: >= sz_encode_workspace_bytes(n, dtype) bytes, contents
- * need not be initialised, clobbered. */
+ * C.  d_workspace: >= sz_encode_workspace_bytes(n, dtype) bytes (may be
+ * NULL when n = 0), contents need not be initialised, clobbered. */
 sz_status sz_encode(const void* d_src, uint64_t n, sz_dtype dtype,
                     const uint8_t* d_codebook, void* d_dst, uint64_t dst_capacity,
                     uint64_t* d_out_bytes, void* d_workspace, uint64_t workspace_bytes,

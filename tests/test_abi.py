@@ -64,10 +64,11 @@ def test_max_bytes_rejects_bad_input(sz):
 
 
 def test_workspace_bytes(sz):
-    assert sz.sz_encode_workspace_bytes(0, 1) == 256
-    assert sz.sz_encode_workspace_bytes(4096, 1) == 256 + 8
-    assert sz.sz_encode_workspace_bytes(4097, 2) == 256 + 16
-    assert sz.sz_encode_workspace_bytes_batched(64, 1 << 23, 1) == 256 + 8 * 64 * 2048
+    # a u32 count per 4096-element block, padded to 256 bytes, then 4096 staging bytes per block
+    assert sz.sz_encode_workspace_bytes(0, 1) == 0
+    assert sz.sz_encode_workspace_bytes(4096, 1) == 256 + 4096
+    assert sz.sz_encode_workspace_bytes(4097, 2) == 256 + 2 * 4096
+    assert sz.sz_encode_workspace_bytes_batched(64, 1 << 23, 1) == 4 * 64 * 2048 + 64 * 2048 * 4096
     assert sz.sz_encode_workspace_bytes_batched(0, 100, 1) == 0
     assert sz.sz_encode_workspace_bytes(1 << 32, 1) == 0
 

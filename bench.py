@@ -78,6 +78,26 @@ def copy_calibration(torch):
     print(json.dumps({"mode": "copy", "bytes_read_per_launch": 1 << 30, "bytes_written_per_launch": 1 << 30}))
 
 
+def copy_ceiling(torch):
+    """Context for the roofline: this GPU's device-to-device copy rate
+    through the HIP runtime (1 GiB read + 1 GiB written), median of 10."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(12):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    del src, dst
+    return {"GBps_read_plus_write": 2 * (1 << 30) / (ms * 1e-3) / 1e9, "ms": ms,
+            "how": "1 GiB device-to-device copy through the HIP runtime"}
+
+
 def cpu_baseline(xs):
     """The CPU oracle (plain scalar C) on this host: encode + decode of
     every layer tensor, one tensor per thread."""
@@ -231,6 +251,8 @@ def main():
         "wall_s_timed": wall,
         "gpu": torch.cuda.get_device_name(0),
     }
+    if args.mode == "bench":
+        result["copy_ceiling"] = copy_ceiling(torch)
     if args.mode == "bench" and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(xs)
     print(json.dumps(result))

@@ -24,19 +24,6 @@ sz_status from_hip(hipError_t e) { return e == hipSuccess ? SZ_OK : SZ_ERR_HIP; 
 
 uint64_t workspace_bytes(uint32_t count, uint64_t n) { return workspace_bytes_for(count, n); }
 
-// histogram workgroups per tensor: about 2048 workgroups in total, each
-// covering a multiple of 32768 elements
-void hist_split(uint32_t count, uint64_t n, uint32_t& groups, uint64_t& chunk) {
-    const uint64_t quantum = 32768;
-    uint64_t want = 2048 / (count ? count : 1);
-    if (want < 1) want = 1;
-    const uint64_t units = (n + quantum - 1) / quantum;
-    if (want > units) want = units ? units : 1;
-    chunk = (units + want - 1) / want * quantum;
-    groups = static_cast<uint32_t>((n + chunk - 1) / chunk);
-    if (groups == 0) groups = 1;
-}
-
 sz_status histogram_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint64_t* d_hists,
                          hipStream_t s) {
     hipError_t e = launch_fill_u64(d_hists, 256ull * count, 0, s);
@@ -46,7 +33,6 @@ sz_status histogram_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, ui
     a.hists = d_hists;
     a.count = count;
     a.n = n;
-    hist_split(count, n, a.groups, a.chunk);
     return from_hip(launch_histogram(a, dt, s));
 }
 

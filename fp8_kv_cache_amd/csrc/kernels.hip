@@ -80,9 +80,11 @@ struct Geometry;
 template <>
 struct Geometry<kDtypeBF16> {
     static constexpr uint32_t kElemBytes = 2;
-    static constexpr uint32_t kLaneElems = 16;   // elements per lane per sub-chunk
-    static constexpr uint32_t kSubs = 4;          // sub-chunks per block
-    static constexpr uint32_t kCodeWords = 2;     // code dwords per lane per sub-chunk
+    static constexpr uint32_t kLaneElems = 8;    // elements per lane per sub-chunk
+    static constexpr uint32_t kSubs = 8;          // sub-chunks per block
+    static constexpr uint32_t kInWords = 4;       // input dwords per lane per sub-chunk
+    static constexpr uint32_t kCodeWords = 1;     // code dwords per lane per sub-chunk
+    static constexpr uint32_t kSmWords = 2;       // sign|mantissa dwords per lane per sub-chunk
     static constexpr uint32_t kDomain = 256;
 };
 template <>
@@ -90,24 +92,30 @@ struct Geometry<kDtypeE5M2> {
     static constexpr uint32_t kElemBytes = 1;
     static constexpr uint32_t kLaneElems = 32;
     static constexpr uint32_t kSubs = 2;
+    static constexpr uint32_t kInWords = 8;
     static constexpr uint32_t kCodeWords = 4;
+    static constexpr uint32_t kSmWords = 3;
     static constexpr uint32_t kDomain = 32;
 };
 
-// 32 input bytes of one lane: elements [elem0, elem0 + kLaneElems); those at
-// or beyond n read as zero and no byte at or beyond n is touched.
+// Input of one lane: elements [elem0, elem0 + kLaneElems) as kInWords
+// dwords; those at or beyond n read as zero and no byte at or beyond n is
+// touched.
 template <uint32_t DT>
-__device__ inline void load_lane(const SZ_GLOBAL uint8_t* src, uint64_t elem0, uint64_t n, uint32_t (&d)[8]) {
+__device__ inline void load_lane(const SZ_GLOBAL uint8_t* src, uint64_t elem0, uint64_t n,
+                                 uint32_t (&d)[Geometry<DT>::kInWords]) {
     using G = Geometry<DT>;
     if (elem0 + G::kLaneElems <= n) {
         const SZ_GLOBAL u32x4* p = (const SZ_GLOBAL u32x4*)(src + elem0 * G::kElemBytes);
-        const u32x4 x = p[0], y = p[1];
-        d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
-        d[4] = y.x; d[5] = y.y; d[6] = y.z; d[7] = y.w;
+#pragma unroll
+        for (uint32_t v = 0; v < G::kInWords / 4; ++v) {
+            const u32x4 x = p[v];
+            d[4 * v] = x.x; d[4 * v + 1] = x.y; d[4 * v + 2] = x.z; d[4 * v + 3] = x.w;
+        }
         return;
     }
 #pragma unroll
-    for (uint32_t i = 0; i < 8; ++i) d[i] = 0;
+    for (uint32_t i = 0; i < G::kInWords; ++i) d[i] = 0;
 #pragma unroll
     for (uint32_t k = 0; k < G::kLaneElems; ++k) {
         if (elem0 + k < n) {
@@ -156,56 +164,48 @@ __device__ inline void count_dword(char* lds, uint32_t w, uint32_t copy4) {
     }
 }
 
+// Each workgroup counts one contiguous chunk of one tensor.  Every pass a
+// lane reads one 16-byte vector (the wave one contiguous kilobyte); eight
+// passes are in flight per iteration.  The grid oversubscribes the GPU, so
+// one workgroup's fold-and-flush tail overlaps other workgroups' streaming.
 template <uint32_t DT>
 __global__ __launch_bounds__(kThreads) void k_histogram(HistArgs a) {
     using G = Geometry<DT>;
-    constexpr uint32_t kTile = kThreads * G::kLaneElems;      // elements per pass
+    constexpr uint32_t kVecElems = 16 / G::kElemBytes;       // elements per 16-byte vector
+    constexpr uint32_t kTile = kThreads * kVecElems;          // elements per pass
+    constexpr uint32_t kPasses = 8;
     __shared__ uint32_t bins[256 * 32];
     const uint32_t tid = threadIdx.x;
     const uint32_t t = blockIdx.x / a.groups;
     const uint32_t g = blockIdx.x - t * a.groups;
     char* lds = reinterpret_cast<char*>(bins);
-    for (uint32_t i = tid; i < 256 * 32 / 4; i += kThreads)
-        reinterpret_cast<uint4*>(bins)[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (uint32_t j = 0; j < 32; j += 4) *reinterpret_cast<uint4*>(bins + tid * 32 + j) = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
     const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
-    const uint64_t begin = (uint64_t)g * a.chunk;
+    const uint64_t begin = static_cast<uint64_t>(g) * a.chunk;
     const uint64_t end = begin + a.chunk < a.n ? begin + a.chunk : a.n;
     const uint32_t copy4 = (tid & 31u) << 2;
     uint64_t base = begin;
-    // four passes per iteration keep 8 x 16 bytes in flight per lane
-    for (; base + 4 * kTile <= end; base += 4 * kTile) {
-        u32x4 v[8];
+    for (; base + kPasses * kTile <= end; base += kPasses * kTile) {
+        const SZ_GLOBAL u32x4* q = (const SZ_GLOBAL u32x4*)(src + base * G::kElemBytes);
+        u32x4 v[kPasses];
 #pragma unroll
-        for (uint32_t p = 0; p < 4; ++p) {
-            const SZ_GLOBAL u32x4* q =
-                (const SZ_GLOBAL u32x4*)(src + (base + p * kTile + tid * G::kLaneElems) * G::kElemBytes);
-            v[2 * p] = q[0];
-            v[2 * p + 1] = q[1];
-        }
+        for (uint32_t p = 0; p < kPasses; ++p) v[p] = q[p * kThreads + tid];
 #pragma unroll
-        for (uint32_t i = 0; i < 8; ++i) {
-            count_dword<DT>(lds, v[i].x, copy4);
-            count_dword<DT>(lds, v[i].y, copy4);
-            count_dword<DT>(lds, v[i].z, copy4);
-            count_dword<DT>(lds, v[i].w, copy4);
+        for (uint32_t p = 0; p < kPasses; ++p) {
+            count_dword<DT>(lds, v[p].x, copy4);
+            count_dword<DT>(lds, v[p].y, copy4);
+            count_dword<DT>(lds, v[p].z, copy4);
+            count_dword<DT>(lds, v[p].w, copy4);
         }
     }
-    for (; base < end; base += kTile) {
-        const uint64_t elem0 = base + tid * G::kLaneElems;
-        if (elem0 + G::kLaneElems <= end) {
-            uint32_t d[8];
-            load_lane<DT>(src, elem0, end, d);
-#pragma unroll
-            for (uint32_t i = 0; i < 8; ++i) count_dword<DT>(lds, d[i], copy4);
-        } else if (elem0 < end) {
-            for (uint64_t i = elem0; i < end; ++i) {
-                const uint32_t u = DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i];
-                const uint32_t e = DT == kDtypeBF16 ? (u >> 7) & 0xFFu : (u >> 2) & 0x1Fu;
-                atomicAdd(reinterpret_cast<uint32_t*>(lds + ((e << 7) | copy4)), 1u);
-            }
-        }
+    // ragged end of the chunk: element-wise guarded reads
+    for (uint64_t i = base + tid; i < end; i += kThreads) {
+        const uint32_t u = DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i];
+        const uint32_t e = DT == kDtypeBF16 ? (u >> 7) & 0xFFu : (u >> 2) & 0x1Fu;
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + ((e << 7) | copy4)), 1u);
     }
     __syncthreads();
 
@@ -285,32 +285,29 @@ __device__ inline void write_header(SZ_GLOBAL uint8_t* dst, const Layout& L, uin
     if (out_bytes && lane == 0) *out_bytes = total;
 }
 
-// BF16: sixteen elements d[0..7] -> 16 sign|mantissa bytes and 16 code
+// BF16: eight elements d[0..3] -> 8 sign|mantissa bytes and 8 code
 // nibbles; elements at index >= valid get code 0 and zero bytes (they are
-// zero in d already).  Returns the escape nibble masks in esc[].
-__device__ inline void encode_lane_bf16(const uint32_t (&d)[8], uint32_t valid, const uint8_t* tbl,
-                                        uint32_t (&sm)[4], uint32_t (&cw)[2], uint32_t (&esc)[2]) {
-    uint32_t c[16];
+// zero in d already).  Returns the escape nibble mask in esc[0].
+__device__ inline void encode_lane_bf16(const uint32_t (&d)[4], uint32_t valid, const uint8_t* tbl,
+                                        uint32_t (&sm)[2], uint32_t (&cw)[1], uint32_t (&esc)[1]) {
+    uint32_t c[8];
 #pragma unroll
-    for (uint32_t k = 0; k < 8; ++k) {
+    for (uint32_t k = 0; k < 4; ++k) {
         c[2 * k] = tbl[(d[k] >> 7) & 0xFFu];
         c[2 * k + 1] = tbl[(d[k] >> 23) & 0xFFu];
     }
-    if (valid < 16) {
+    if (valid < 8) {
 #pragma unroll
-        for (uint32_t k = 0; k < 16; ++k)
+        for (uint32_t k = 0; k < 8; ++k)
             if (k >= valid) c[k] = 0;
     }
+    uint32_t w = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) w |= c[k] << (4 * k);
+    cw[0] = w;
+    esc[0] = escape_nibbles(w);
 #pragma unroll
     for (uint32_t q = 0; q < 2; ++q) {
-        uint32_t w = 0;
-#pragma unroll
-        for (uint32_t k = 0; k < 8; ++k) w |= c[8 * q + k] << (4 * k);
-        cw[q] = w;
-        esc[q] = escape_nibbles(w);
-    }
-#pragma unroll
-    for (uint32_t q = 0; q < 4; ++q) {
         // low bytes (exponent lsb | mantissa) and high bytes (sign | exponent msbs)
         const uint32_t lo = perm(d[2 * q + 1], d[2 * q], 0x06040200u);
         const uint32_t hi = perm(d[2 * q + 1], d[2 * q], 0x07050301u);
@@ -359,7 +356,7 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
                                     uint64_t flat, uint32_t lane, uint32_t* tbl_words) {
     using G = Geometry<DT>;
     constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
-    constexpr uint32_t kSmWords = DT == kDtypeBF16 ? 4 : 3;
+    constexpr uint32_t kSmWords = G::kSmWords;
 
     // codebook entry of this lane first, then the block's input
     const SZ_GLOBAL uint8_t* cb = gptr(a.codebooks) + 16ull * t;
@@ -367,15 +364,17 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
     const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
     SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
     const uint64_t blk0 = b * kBlockElems;
-    uint32_t d[G::kSubs][8];
+    uint32_t d[G::kSubs][G::kInWords];
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; ++j) {
         const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
         if (kFull) {
             const SZ_GLOBAL u32x4* p = (const SZ_GLOBAL u32x4*)(src + elem0 * G::kElemBytes);
-            const u32x4 x = p[0], y = p[1];
-            d[j][0] = x.x; d[j][1] = x.y; d[j][2] = x.z; d[j][3] = x.w;
-            d[j][4] = y.x; d[j][5] = y.y; d[j][6] = y.z; d[j][7] = y.w;
+#pragma unroll
+            for (uint32_t v = 0; v < G::kInWords / 4; ++v) {
+                const u32x4 x = p[v];
+                d[j][4 * v] = x.x; d[j][4 * v + 1] = x.y; d[j][4 * v + 2] = x.z; d[j][4 * v + 3] = x.w;
+            }
         } else {
             load_lane<DT>(src, elem0, a.n, d[j]);
         }
@@ -421,9 +420,9 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
         const uint64_t code_off = elem0 / 2;
         if constexpr (DT == kDtypeBF16) {
             if (kFull || elem0 < L.sm_region)
-                *(SZ_GLOBAL u32x4*)(dst + L.sm_at + elem0) = u32x4{sm[j][0], sm[j][1], sm[j][2], sm[j][3]};
+                *(SZ_GLOBAL u32x2*)(dst + L.sm_at + elem0) = u32x2{sm[j][0], sm[j][1]};
             if (kFull || code_off < L.code_region)
-                *(SZ_GLOBAL u32x2*)(dst + L.code_at + code_off) = u32x2{cw[j][0], cw[j][1]};
+                *(SZ_GLOBAL uint32_t*)(dst + L.code_at + code_off) = cw[j][0];
         } else {
             const uint64_t sm_off = elem0 / 32 * 12;
             SZ_GLOBAL uint32_t* smp = (SZ_GLOBAL uint32_t*)(dst + L.sm_at + sm_off);
@@ -443,16 +442,14 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
     uint32_t block_total = 0;
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; j += 2) {
-        const uint32_t packed = cnt[j] | (j + 1 < G::kSubs ? cnt[j + 1] << 16 : 0u);
+        const uint32_t packed = cnt[j] | (cnt[j + 1] << 16);
         const uint32_t incl = wave_scan_incl(packed);
         const uint32_t excl = incl - packed;
         const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
         base[j] = block_total + (excl & 0xFFFFu);
         block_total += tot & 0xFFFFu;
-        if (j + 1 < G::kSubs) {
-            base[j + 1] = block_total + (excl >> 16);
-            block_total += tot >> 16;
-        }
+        base[j + 1] = block_total + (excl >> 16);
+        block_total += tot >> 16;
     }
     if (lane == 0) gptr(a.counts)[flat] = uniform(block_total);
 
@@ -471,7 +468,7 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
                 if constexpr (DT == kDtypeBF16) {
                     uint32_t word = 0;
 #pragma unroll
-                    for (uint32_t i = 0; i < 8; ++i)
+                    for (uint32_t i = 0; i < G::kInWords; ++i)
                         if (i == (k >> 1)) word = d[j][i];
                     e = (k & 1) ? (word >> 23) & 0xFFu : (word >> 7) & 0xFFu;
                 } else {
@@ -544,25 +541,27 @@ __global__ __launch_bounds__(256) void k_offsets(EncodeArgs a) {
                  a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid);
 }
 
-// Staged escapes -> the stream's escape region; one wave per block,
-// grid-stride over all blocks of all tensors.
+// Staged escapes -> the stream's escape region; one thread per block,
+// reading the staged bytes 16 at a time (a block's staging slot is
+// 4096-byte aligned) and writing them to their unaligned destination.
 template <uint32_t DT>
 __global__ __launch_bounds__(kThreads) void k_scatter(EncodeArgs a) {
-    const uint32_t lane = lane_id();
     const Layout L = layout_of(a.n, DT);
-    const uint64_t total = static_cast<uint64_t>(a.count) * L.blocks;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kWavesPerGroup;
-    for (uint64_t flat = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWaveSize);
-         flat < total; flat += stride) {
-        const uint32_t cnt = uniform(gptr(a.counts)[flat]);
-        if (cnt == 0) continue;
-        const uint32_t t = static_cast<uint32_t>(flat / L.blocks);
-        const uint64_t b = flat - static_cast<uint64_t>(t) * L.blocks;
-        SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
-        const uint32_t off = uniform(((const SZ_GLOBAL uint32_t*)(dst + 64))[b]);
-        const SZ_GLOBAL uint8_t* from = gptr(a.staging) + flat * kBlockElems;
-        SZ_GLOBAL uint8_t* to = dst + L.esc_at + off;
-        for (uint32_t i = lane; i < cnt; i += kWaveSize) to[i] = from[i];
+    const uint64_t flat = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (flat >= static_cast<uint64_t>(a.count) * L.blocks) return;
+    const uint32_t t = static_cast<uint32_t>(flat / L.blocks);
+    const uint64_t b = flat - static_cast<uint64_t>(t) * L.blocks;
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+    const uint32_t cnt = gptr(a.counts)[flat];
+    const uint32_t off = ((const SZ_GLOBAL uint32_t*)(dst + 64))[b];
+    const SZ_GLOBAL u32x4* from = (const SZ_GLOBAL u32x4*)(gptr(a.staging) + flat * kBlockElems);
+    SZ_GLOBAL uint8_t* to = dst + L.esc_at + off;
+    for (uint32_t i = 0; i < cnt; i += 16) {
+        const u32x4 v = from[i / 16];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k)
+            if (i + k < cnt) to[i + k] = static_cast<uint8_t>(w[k / 4] >> (8 * (k & 3)));
     }
 }
 
@@ -924,12 +923,28 @@ hipError_t launch_fill_i32(int32_t* p, uint64_t words, int32_t value, hipStream_
     return hipGetLastError();
 }
 
+// Histogram grid: about kHistGroups workgroups in total, each counting a
+// contiguous multiple of one iteration's elements (8 passes x 256 lanes x
+// one 16-byte vector) of one tensor.
+constexpr uint64_t kHistGroups = 2048;
+
+template <uint32_t DT>
+void enqueue_histogram(HistArgs a, hipStream_t s) {
+    constexpr uint64_t kQuantum = 8ull * kThreads * (16 / Geometry<DT>::kElemBytes);
+    uint64_t want = kHistGroups / a.count;
+    if (want < 1) want = 1;
+    const uint64_t units = (a.n + kQuantum - 1) / kQuantum;
+    if (want > units) want = units;
+    a.chunk = (units + want - 1) / want * kQuantum;
+    a.groups = static_cast<uint32_t>((a.n + a.chunk - 1) / a.chunk);
+    hipLaunchKernelGGL(k_histogram<DT>, dim3(a.count * a.groups), dim3(kThreads), 0, s, a);
+}
+
 hipError_t launch_histogram(const HistArgs& a, uint32_t dtype, hipStream_t s) {
-    const dim3 grid(a.count * a.groups), block(kThreads);
     if (dtype == kDtypeBF16)
-        hipLaunchKernelGGL(k_histogram<kDtypeBF16>, grid, block, 0, s, a);
+        enqueue_histogram<kDtypeBF16>(a, s);
     else
-        hipLaunchKernelGGL(k_histogram<kDtypeE5M2>, grid, block, 0, s, a);
+        enqueue_histogram<kDtypeE5M2>(a, s);
     return hipGetLastError();
 }
 
@@ -946,8 +961,7 @@ void enqueue_encode(const EncodeArgs& a, hipStream_t s) {
     const Layout L = layout_of(a.n, DT);
     const uint64_t full = static_cast<uint64_t>(a.count) * (a.n / kBlockElems);
     const uint64_t blocks = static_cast<uint64_t>(a.count) * L.blocks;
-    uint32_t scatter_groups = grid_for(blocks, kWavesPerGroup);
-    if (scatter_groups > 2048) scatter_groups = 2048;
+    const uint32_t scatter_groups = grid_for(blocks, kThreads);
     if (full) hipLaunchKernelGGL(k_encode<DT>, dim3(grid_for(full, kWavesPerGroup)), dim3(kThreads), 0, s, a);
     if (a.n % kBlockElems) hipLaunchKernelGGL(k_encode_tail<DT>, dim3(a.count), dim3(kWaveSize), 0, s, a);
     hipLaunchKernelGGL(k_offsets<DT>, dim3(a.count), dim3(256), 0, s, a);

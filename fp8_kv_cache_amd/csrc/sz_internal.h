@@ -74,9 +74,9 @@ struct HistArgs {
     SrcRef src;
     uint64_t* hists;          // count x 256
     uint32_t count;
-    uint32_t groups;          // workgroups per tensor
+    uint32_t groups;          // workgroups per tensor, set by the launcher
     uint64_t n;
-    uint64_t chunk;           // elements per workgroup, multiple of 4096
+    uint64_t chunk;           // elements per workgroup, set by the launcher
 };
 
 struct CodebookArgs {

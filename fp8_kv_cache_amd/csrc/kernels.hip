@@ -1,8 +1,8 @@
 // kernels.hip -- gfx950 kernels of the lossless exponent codec.
 //
-// Method: SplitZip project page, "Abstract" (frequent exponents -> fixed
-// 4-bit codes, sign and mantissa kept exactly, rare exponents -> sparse
-// escape stream) and FAQ "Is SplitZip lossy?" (bitwise identical decode),
+// Method: SplitZip project page, "Abstract" (frequent exponents -> constant-width
+// 4-bit codes, sign and mantissa kept as they are, rare exponents -> a
+// separate escape stream) and FAQ "Is SplitZip lossy?" (bit-exact decode),
 // FAQ "Does it work with an FP8 KV cache?" (E5M2 variant).  The byte layout
 // is stream format v1, documented in include/splitzip.h.
 //

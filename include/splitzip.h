@@ -3,9 +3,9 @@
  * BF16 and FP8-E5M2 KV-cache tensors.
  *
  * The method is SplitZip's (SplitZip project page, "Abstract"): the most
- * frequent exponent values of a tensor get fixed 4-bit codes, sign and
- * mantissa bits are kept exactly, and rare exponent values are routed
- * through a sparse escape stream; decoding is bitwise identical (FAQ "Is
+ * frequent exponent values of a tensor get constant-width 4-bit codes, sign and
+ * mantissa bits are kept as they are, and rare exponent values are routed
+ * through a separate escape stream; decoding is bit-exact (FAQ "Is
  * SplitZip lossy?"), also for FP8 E5M2 KV caches (FAQ "Does it work with
  * an FP8 KV cache?").
  *
@@ -83,7 +83,7 @@ sz_status sz_histogram(const void* d_src, uint64_t n, sz_dtype dtype,
                        uint64_t* d_hist, hipStream_t stream);
 
 /* Codebook from a histogram ("Abstract": the most frequent exponent values
- * get the fixed 4-bit codes).  d_hist: 256 u64 (device).  d_codebook: 16
+ * get the 4-bit codes).  d_hist: 256 u64 (device).  d_codebook: 16
  * bytes written as cb[0..14] = exponents of rank 0..14 (count descending,
  * then exponent ascending), cb[15] = 0. */
 sz_status sz_build_codebook(const uint64_t* d_hist, sz_dtype dtype,
@@ -101,7 +101,7 @@ sz_status sz_encode(const void* d_src, uint64_t n, sz_dtype dtype,
                     uint64_t* d_out_bytes, void* d_workspace, uint64_t workspace_bytes,
                     hipStream_t stream);
 
-/* Decode one stream (FAQ "Is SplitZip lossy?": bitwise identical output).
+/* Decode one stream (FAQ "Is SplitZip lossy?": bit-exact output).
  * d_src: src_bytes readable bytes holding the stream (C <= src_bytes).
  * d_dst: n elements.  The stream is validated on the device against n,
  * dtype, src_bytes and its own header and offsets; if it does not match,

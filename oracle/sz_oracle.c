@@ -10,12 +10,13 @@
  *
  * What the method computes (SplitZip project page):
  *   - "Abstract": the most frequent exponent values of a BF16 tensor get a
- *     fixed 4-bit code, sign and mantissa bits are kept exactly, and rare
- *     exponent values are routed through a sparse escape stream.
+ *     constant-width 4-bit code, sign and mantissa bits are kept as they
+ *     are, and rare
+ *     exponent values are routed through a separate escape stream.
  *   - FAQ "Is SplitZip lossy?": sign and mantissa are stored unchanged and
- *     decoding is bitwise identical to the input.
+ *     decoding reproduces the input bit for bit.
  *   - FAQ "Does it work with an FP8 KV cache?": the same scheme applies to
- *     FP8 E5M2 and yields up to 1.14x.
+ *     FP8 E5M2 and gains at most 1.14x.
  * The pages fix no byte layout.  The readings taken where they are silent:
  *   R1  16 code values; codes 0..14 name the 15 most frequent exponents,
  *       code 15 means "escape" (no extra flag bit: that would break the

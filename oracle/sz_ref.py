@@ -6,11 +6,12 @@ tables) and of the GPU library.  Loops are element-by-element, so keep n
 small (a few thousand).
 
 Method, from the SplitZip project page:
-  * Abstract -- frequent exponent values get fixed 4-bit codes, sign and
-    mantissa bits are kept exactly, rare exponents go to a sparse escape
-    stream;
-  * FAQ "Is SplitZip lossy?" -- decoding is bitwise identical;
-  * FAQ "Does it work with an FP8 KV cache?" -- E5M2 variant, up to 1.14x.
+  * Abstract -- the commonest exponent values get constant-width 4-bit
+    codes, sign and mantissa bits are kept as they are, and rare exponents
+    go to a separate escape stream;
+  * FAQ "Is SplitZip lossy?" -- decoding is bit-exact;
+  * FAQ "Does it work with an FP8 KV cache?" -- E5M2 variant, gaining at
+    most 1.14x.
 The byte layout is the reading documented in the C oracle's header comment
 (readings R1..R8): codes 0..14 = top-15 exponents ranked by (count desc,
 value asc), code 15 = escape; BF16 sign|mantissa byte; E5M2 3-bit LSB-first

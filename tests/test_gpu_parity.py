@@ -198,7 +198,7 @@ def test_encode_is_deterministic(sz):
 
 def test_llama_kv_cache_full_size(sz):
     """Llama-3-8B-shaped BF16 KV cache: 32 layers x {K, V} x [8192, 8, 128],
-    one codebook per layer tensor, batched launches; every stream and every
+    a codebook for each layer tensor, batched launches; every stream and every
     decoded tensor against the oracle."""
     say("llama full: generating")
     with cf.ThreadPoolExecutor(8) as pool:
@@ -279,7 +279,7 @@ def test_long_context_kv_full_size(sz):
 
 def test_e5m2_config_full_size(sz):
     """FP8 E5M2 variant of the 2^20-element config: bit-exact, ratio <= 8/7
-    and >= 1.14 (SplitZip FAQ: up to 1.14x on top of FP8)."""
+    and >= 1.14 (SplitZip FAQ on FP8 caches: gains of at most 1.14x)."""
     x = kvsynth.e5m2_of(kvsynth.single_tensor())
     say("e5m2 config")
     stream, _, _ = sz.codec.compress(to_dev(x), E5M2)

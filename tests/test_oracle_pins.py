@@ -9,7 +9,7 @@ against something independent of it:
   * brute force: a full sort and an exhaustive subset search for top-15;
   * closed forms: exact stream size, worst-case escape count reached by
     uniform exponents, the E5M2 ratio ceiling of 8/7 that the SplitZip
-    project page's FAQ quotes as "up to 1.14x";
+    project page's FAQ gives as the most the E5M2 variant gains (1.14x);
   * round trip bit identity (FAQ "Is SplitZip lossy?").
 """
 import itertools
@@ -258,7 +258,7 @@ def test_constant_tensor_has_no_escapes(dt):
 
 
 def test_ratio_ceilings_e5m2_and_bf16():
-    """FAQ: up to 1.14x on FP8 E5M2; the layout caps E5M2 at 8/7 and BF16 at 4/3."""
+    """FAQ on FP8 caches: at most 1.14x on E5M2; the layout caps E5M2 at 8/7 and BF16 at 4/3."""
     x = kvsynth.single_tensor()
     e = kvsynth.e5m2_of(x)
     r_e5m2 = e.size / oracle.encode(e, E5M2).size

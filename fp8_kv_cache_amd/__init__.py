@@ -7,7 +7,7 @@ a torch tensor (its data_ptr()), a plain integer address or None; `stream`
 defaults to torch's current stream.  torch provides device memory and
 streams only -- every step of the codec runs in the library's HIP kernels.
 
-The library must be built (python -m fp8_kv_cache_amd.build); importing this
+The library must be built (python fp8_kv_cache_amd/build.py); importing this
 package without it raises ImportError, there is no fallback path.
 """
 import ctypes
@@ -19,7 +19,8 @@ __all__ = [
     "SZ_DTYPE_BF16", "SZ_DTYPE_FP8_E5M2", "SZ_OK", "SZ_ERR_INVALID_ARGUMENT",
     "SZ_ERR_BUFFER_TOO_SMALL", "SZ_ERR_CORRUPT_STREAM", "SZ_ERR_HIP", "SzError",
     "sz_max_compressed_bytes", "sz_encode_workspace_bytes", "sz_encode_workspace_bytes_batched",
-    "sz_histogram", "sz_build_codebook", "sz_encode", "sz_decode",
+    "sz_histogram", "sz_histogram_sampled", "sz_build_codebook", "sz_encode", "sz_decode",
+    "sz_histogram_sampled_batched",
     "sz_histogram_batched", "sz_build_codebook_batched", "sz_encode_batched", "sz_decode_batched",
     "sz_status_string", "check", "pointer_table", "library_path",
 ]
@@ -36,7 +37,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
 
 if not os.path.exists(_LIB_PATH):
-    raise ImportError(f"{_LIB_PATH} is not built; run `python -m fp8_kv_cache_amd.build`")
+    raise ImportError(f"{_LIB_PATH} is not built; run `python fp8_kv_cache_amd/build.py`")
 
 _lib = ctypes.CDLL(_LIB_PATH)
 _u64, _u32, _i32, _vp = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p
@@ -46,6 +47,8 @@ _SIGNATURES = {
     "sz_encode_workspace_bytes": (_u64, [_u64, _i32]),
     "sz_encode_workspace_bytes_batched": (_u64, [_u32, _u64, _i32]),
     "sz_histogram": (_i32, [_vp, _u64, _i32, _vp, _vp]),
+    "sz_histogram_sampled": (_i32, [_vp, _u64, _i32, _u32, _vp, _vp]),
+    "sz_histogram_sampled_batched": (_i32, [_vp, _u32, _u64, _i32, _u32, _vp, _vp]),
     "sz_build_codebook": (_i32, [_vp, _i32, _vp, _vp]),
     "sz_encode": (_i32, [_vp, _u64, _i32, _vp, _vp, _u64, _vp, _vp, _u64, _vp]),
     "sz_decode": (_i32, [_vp, _u64, _u64, _i32, _vp, _vp, _vp]),
@@ -119,6 +122,15 @@ def sz_encode_workspace_bytes_batched(count, n, dtype):
 
 def sz_histogram(src, n, dtype, hist, stream=None):
     return _lib.sz_histogram(_ptr(src), n, dtype, _ptr(hist), _stream(stream))
+
+
+def sz_histogram_sampled(src, n, dtype, block_stride, hist, stream=None):
+    return _lib.sz_histogram_sampled(_ptr(src), n, dtype, block_stride, _ptr(hist), _stream(stream))
+
+
+def sz_histogram_sampled_batched(srcs, count, n, dtype, block_stride, hists, stream=None):
+    return _lib.sz_histogram_sampled_batched(_ptr(srcs), count, n, dtype, block_stride, _ptr(hists),
+                                             _stream(stream))
 
 
 def sz_build_codebook(hist, dtype, codebook, stream=None):

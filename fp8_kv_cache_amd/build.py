@@ -1,6 +1,8 @@
 """Build libsplitzip.so (gfx950) in-tree with hipcc.
 
-    python -m fp8_kv_cache_amd.build
+    python fp8_kv_cache_amd/build.py
+
+(run as a file: importing the package would load the library being rebuilt)
 """
 import os
 import shutil

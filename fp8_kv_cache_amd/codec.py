@@ -5,7 +5,8 @@ patterns, dtype int16/bfloat16) or bytes (E5M2, dtype uint8/float8_e5m2).
 """
 import torch
 
-from . import (SZ_DTYPE_BF16, SZ_DTYPE_FP8_E5M2, check, pointer_table, sz_build_codebook,
+from . import (SZ_DTYPE_BF16, SZ_DTYPE_FP8_E5M2, check, pointer_table, sz_build_codebook, sz_histogram_sampled,
+               sz_histogram_sampled_batched,
                sz_build_codebook_batched, sz_decode, sz_decode_batched, sz_encode, sz_encode_batched,
                sz_encode_workspace_bytes, sz_encode_workspace_bytes_batched, sz_histogram,
                sz_histogram_batched, sz_max_compressed_bytes)
@@ -17,16 +18,22 @@ def _raw_dtype(dtype):
     return torch.int16 if dtype == SZ_DTYPE_BF16 else torch.uint8
 
 
-def compress(x, dtype, codebook=None, stream=None):
+def compress(x, dtype, codebook=None, stream=None, block_stride=1):
     """Encode one tensor.  Returns (stream bytes as a uint8 tensor of exactly
-    C bytes, histogram int64[256] or None, codebook uint8[16])."""
+    C bytes, histogram int64[256] or None, codebook uint8[16]).  With
+    block_stride > 1 the codebook comes from a histogram of every
+    block_stride-th 4096-element block."""
     dev = x.device
     n = x.numel()
     hist = None
     if codebook is None:
         hist = torch.empty(256, dtype=torch.int64, device=dev)
         codebook = torch.empty(16, dtype=torch.uint8, device=dev)
-        check(sz_histogram(x, n, dtype, hist, stream), "sz_histogram")
+        if block_stride == 1:
+            check(sz_histogram(x, n, dtype, hist, stream), "sz_histogram")
+        else:
+            check(sz_histogram_sampled(x if n else None, n, dtype, block_stride, hist, stream),
+                  "sz_histogram_sampled")
         check(sz_build_codebook(hist, dtype, codebook, stream), "sz_build_codebook")
     cap = sz_max_compressed_bytes(n, dtype)
     dst = torch.empty(cap, dtype=torch.uint8, device=dev)
@@ -75,9 +82,13 @@ class BatchCodec:
         self._inputs = list(tensors)  # keep alive
         self.src_ptrs = pointer_table(self._inputs)
 
-    def histogram(self, stream=None):
-        check(sz_histogram_batched(self.src_ptrs, self.count, self.n, self.dtype, self.hists, stream),
-              "sz_histogram_batched")
+    def histogram(self, stream=None, block_stride=1):
+        if block_stride == 1:
+            check(sz_histogram_batched(self.src_ptrs, self.count, self.n, self.dtype, self.hists, stream),
+                  "sz_histogram_batched")
+        else:
+            check(sz_histogram_sampled_batched(self.src_ptrs, self.count, self.n, self.dtype, block_stride,
+                                               self.hists, stream), "sz_histogram_sampled_batched")
 
     def build_codebooks(self, stream=None):
         check(sz_build_codebook_batched(self.hists, self.count, self.dtype, self.codebooks, stream),

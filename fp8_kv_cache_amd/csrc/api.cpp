@@ -24,8 +24,8 @@ sz_status from_hip(hipError_t e) { return e == hipSuccess ? SZ_OK : SZ_ERR_HIP; 
 
 uint64_t workspace_bytes(uint32_t count, uint64_t n) { return workspace_bytes_for(count, n); }
 
-sz_status histogram_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint64_t* d_hists,
-                         hipStream_t s) {
+sz_status histogram_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint32_t stride,
+                         uint64_t* d_hists, hipStream_t s) {
     hipError_t e = launch_fill_u64(d_hists, 256ull * count, 0, s);
     if (e != hipSuccess || n == 0) return from_hip(e);
     HistArgs a{};
@@ -33,6 +33,7 @@ sz_status histogram_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, ui
     a.hists = d_hists;
     a.count = count;
     a.n = n;
+    a.stride = stride;
     return from_hip(launch_histogram(a, dt, s));
 }
 
@@ -89,14 +90,30 @@ SZ_EXPORT sz_status sz_histogram(const void* d_src, uint64_t n, sz_dtype dtype, 
                                  hipStream_t stream) {
     if (!dtype_ok(dtype) || n >= kMaxElems || !usable(d_hist) || (n && !usable(d_src)))
         return SZ_ERR_INVALID_ARGUMENT;
-    return histogram_impl(SrcRef{nullptr, d_src}, 1, n, dtype, d_hist, stream);
+    return histogram_impl(SrcRef{nullptr, d_src}, 1, n, dtype, 1, d_hist, stream);
 }
 
 SZ_EXPORT sz_status sz_histogram_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
                                          sz_dtype dtype, uint64_t* d_hists, hipStream_t stream) {
     if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !usable(d_hists) || !usable(d_srcs))
         return SZ_ERR_INVALID_ARGUMENT;
-    return histogram_impl(SrcRef{d_srcs, nullptr}, count, n, dtype, d_hists, stream);
+    return histogram_impl(SrcRef{d_srcs, nullptr}, count, n, dtype, 1, d_hists, stream);
+}
+
+SZ_EXPORT sz_status sz_histogram_sampled(const void* d_src, uint64_t n, sz_dtype dtype, uint32_t block_stride,
+                                         uint64_t* d_hist, hipStream_t stream) {
+    if (!dtype_ok(dtype) || n >= kMaxElems || block_stride == 0 || !usable(d_hist) || (n && !usable(d_src)))
+        return SZ_ERR_INVALID_ARGUMENT;
+    return histogram_impl(SrcRef{nullptr, d_src}, 1, n, dtype, block_stride, d_hist, stream);
+}
+
+SZ_EXPORT sz_status sz_histogram_sampled_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
+                                                 sz_dtype dtype, uint32_t block_stride, uint64_t* d_hists,
+                                                 hipStream_t stream) {
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || block_stride == 0 || !usable(d_hists) ||
+        !usable(d_srcs))
+        return SZ_ERR_INVALID_ARGUMENT;
+    return histogram_impl(SrcRef{d_srcs, nullptr}, count, n, dtype, block_stride, d_hists, stream);
 }
 
 SZ_EXPORT sz_status sz_build_codebook_batched(const uint64_t* d_hists, uint32_t count, sz_dtype dtype,

@@ -217,6 +217,60 @@ __global__ __launch_bounds__(kThreads) void k_histogram(HistArgs a) {
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Histogram of a block sample: only format blocks b with b % stride == 0
+// are counted.  Workgroup (t, g) takes sampled blocks [g*per_group,
+// (g+1)*per_group) of tensor t; per block every lane reads 4096 / 256
+// elements as 16-byte vectors.
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_histogram_sampled(HistArgs a) {
+    using G = Geometry<DT>;
+    constexpr uint32_t kVecElems = 16 / G::kElemBytes;
+    constexpr uint32_t kVecs = kBlockElems / (kThreads * kVecElems);   // per lane per block
+    __shared__ uint32_t bins[256 * 32];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t t = blockIdx.x / a.groups;
+    const uint32_t g = blockIdx.x - t * a.groups;
+    char* lds = reinterpret_cast<char*>(bins);
+#pragma unroll
+    for (uint32_t j = 0; j < 32; j += 4) *reinterpret_cast<uint4*>(bins + tid * 32 + j) = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
+    const uint64_t blocks = (a.n + kBlockElems - 1) / kBlockElems;
+    const uint64_t sampled = (blocks + a.stride - 1) / a.stride;
+    const uint64_t k0 = static_cast<uint64_t>(g) * a.per_group;
+    const uint64_t k1 = k0 + a.per_group < sampled ? k0 + a.per_group : sampled;
+    const uint32_t copy4 = (tid & 31u) << 2;
+    for (uint64_t k = k0; k < k1; ++k) {
+        const uint64_t begin = k * a.stride * kBlockElems;
+        if (begin + kBlockElems <= a.n) {
+            const SZ_GLOBAL u32x4* q = (const SZ_GLOBAL u32x4*)(src + begin * G::kElemBytes);
+            u32x4 v[kVecs];
+#pragma unroll
+            for (uint32_t p = 0; p < kVecs; ++p) v[p] = q[p * kThreads + tid];
+#pragma unroll
+            for (uint32_t p = 0; p < kVecs; ++p) {
+                count_dword<DT>(lds, v[p].x, copy4);
+                count_dword<DT>(lds, v[p].y, copy4);
+                count_dword<DT>(lds, v[p].z, copy4);
+                count_dword<DT>(lds, v[p].w, copy4);
+            }
+        } else {
+            for (uint64_t i = begin + tid; i < a.n; i += kThreads) {
+                const uint32_t u = DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i];
+                const uint32_t e = DT == kDtypeBF16 ? (u >> 7) & 0xFFu : (u >> 2) & 0x1Fu;
+                atomicAdd(reinterpret_cast<uint32_t*>(lds + ((e << 7) | copy4)), 1u);
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t sum = 0;
+#pragma unroll 8
+    for (uint32_t j = 0; j < 32; ++j) sum += bins[tid * 32 + ((j + tid) & 31u)];
+    if (sum) __hip_atomic_fetch_add(gptr(a.hists) + 256ull * t + tid, static_cast<uint64_t>(sum),
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // --------------------------------------------------------------- codebook
 //
 // Rank every exponent value of the type by (count descending, value
@@ -940,11 +994,26 @@ void enqueue_histogram(HistArgs a, hipStream_t s) {
     hipLaunchKernelGGL(k_histogram<DT>, dim3(a.count * a.groups), dim3(kThreads), 0, s, a);
 }
 
+template <uint32_t DT>
+void enqueue_histogram_sampled(HistArgs a, hipStream_t s) {
+    const uint64_t blocks = (a.n + kBlockElems - 1) / kBlockElems;
+    const uint64_t sampled = (blocks + a.stride - 1) / a.stride;
+    a.per_group = 4;
+    a.groups = static_cast<uint32_t>((sampled + a.per_group - 1) / a.per_group);
+    hipLaunchKernelGGL(k_histogram_sampled<DT>, dim3(a.count * a.groups), dim3(kThreads), 0, s, a);
+}
+
 hipError_t launch_histogram(const HistArgs& a, uint32_t dtype, hipStream_t s) {
-    if (dtype == kDtypeBF16)
+    if (a.stride > 1) {
+        if (dtype == kDtypeBF16)
+            enqueue_histogram_sampled<kDtypeBF16>(a, s);
+        else
+            enqueue_histogram_sampled<kDtypeE5M2>(a, s);
+    } else if (dtype == kDtypeBF16) {
         enqueue_histogram<kDtypeBF16>(a, s);
-    else
+    } else {
         enqueue_histogram<kDtypeE5M2>(a, s);
+    }
     return hipGetLastError();
 }
 

@@ -76,7 +76,9 @@ struct HistArgs {
     uint32_t count;
     uint32_t groups;          // workgroups per tensor, set by the launcher
     uint64_t n;
-    uint64_t chunk;           // elements per workgroup, set by the launcher
+    uint64_t chunk;           // elements per workgroup (full histogram), set by the launcher
+    uint32_t stride;          // count format blocks b with b % stride == 0 (1 = all)
+    uint32_t per_group;       // sampled blocks per workgroup, set by the launcher
 };
 
 struct CodebookArgs {

@@ -82,6 +82,17 @@ uint64_t sz_encode_workspace_bytes(uint64_t n, sz_dtype dtype);
 sz_status sz_histogram(const void* d_src, uint64_t n, sz_dtype dtype,
                        uint64_t* d_hist, hipStream_t stream);
 
+/* Histogram of a block sample -- an extension; the pages define no
+ * sampling.  Only the 4096-element format blocks b with b % block_stride
+ * == 0 are counted (block_stride >= 1; 1 gives sz_histogram's result).  The
+ * premise is the "Abstract"'s observation that KV exponents are highly
+ * repetitive, so a sample ranks them like the whole tensor; a codebook
+ * built from it still yields a valid lossless stream (sz_encode accepts any
+ * codebook), and encode then reads the input about once instead of twice.
+ * d_hist: 256 u64, overwritten. */
+sz_status sz_histogram_sampled(const void* d_src, uint64_t n, sz_dtype dtype, uint32_t block_stride,
+                               uint64_t* d_hist, hipStream_t stream);
+
 /* Codebook from a histogram ("Abstract": the most frequent exponent values
  * get the 4-bit codes).  d_hist: 256 u64 (device).  d_codebook: 16
  * bytes written as cb[0..14] = exponents of rank 0..14 (count descending,
@@ -123,6 +134,11 @@ uint64_t sz_encode_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype 
 /* d_hists: count x 256 u64 */
 sz_status sz_histogram_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
                                sz_dtype dtype, uint64_t* d_hists, hipStream_t stream);
+
+/* d_hists: count x 256 u64 */
+sz_status sz_histogram_sampled_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
+                                       sz_dtype dtype, uint32_t block_stride, uint64_t* d_hists,
+                                       hipStream_t stream);
 
 /* d_hists: count x 256 u64; d_codebooks: count x 16 bytes */
 sz_status sz_build_codebook_batched(const uint64_t* d_hists, uint32_t count, sz_dtype dtype,

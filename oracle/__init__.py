@@ -49,6 +49,8 @@ def _load():
     lib.szo_exact_bytes.restype = u64
     lib.szo_histogram.argtypes = [vp, u64, i32, vp]
     lib.szo_histogram.restype = i32
+    lib.szo_histogram_sampled.argtypes = [vp, u64, i32, u64, vp]
+    lib.szo_histogram_sampled.restype = i32
     lib.szo_codebook.argtypes = [vp, i32, vp]
     lib.szo_codebook.restype = i32
     lib.szo_encode.argtypes = [vp, u64, i32, vp, vp, u64, vp]
@@ -81,6 +83,16 @@ def histogram(values, dt):
     rc = _load().szo_histogram(a.ctypes.data, a.size, dt, h.ctypes.data)
     if rc:
         raise ValueError(f"szo_histogram failed: {rc}")
+    return h
+
+
+def histogram_sampled(values, dt, stride):
+    """Histogram of the 4096-element blocks b with b % stride == 0."""
+    a = _raw(values, dt)
+    h = np.zeros(256, np.uint64)
+    rc = _load().szo_histogram_sampled(a.ctypes.data if a.size else None, a.size, dt, stride, h.ctypes.data)
+    if rc:
+        raise ValueError(f"szo_histogram_sampled failed: {rc}")
     return h
 
 

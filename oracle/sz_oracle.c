@@ -163,6 +163,16 @@ int szo_histogram(const void* src, uint64_t n, int dt, uint64_t* hist) {
     return SZO_OK;
 }
 
+/* Histogram over a block sample (an extension; the pages define no
+ * sampling): only elements of 4096-element blocks b with b % stride == 0. */
+int szo_histogram_sampled(const void* src, uint64_t n, int dt, uint64_t stride, uint64_t* hist) {
+    if (!dtype_ok(dt) || !hist || (n && !src) || stride == 0) return SZO_INVALID_ARGUMENT;
+    for (unsigned v = 0; v < 256; v++) hist[v] = 0;
+    for (uint64_t i = 0; i < n; i++)
+        if ((i / SZO_BLOCK) % stride == 0) hist[exponent_of(element((const uint8_t*)src, i, dt), dt)]++;
+    return SZO_OK;
+}
+
 struct ranked { uint64_t count; unsigned value; };
 
 static int by_count_then_value(const void* a, const void* b) {

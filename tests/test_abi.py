@@ -84,6 +84,9 @@ def test_host_argument_errors_return_before_launch(sz):
     assert sz.sz_histogram(FAKE + 1, 10, 1, FAKE, stream=0) == E_ARG
     assert sz.sz_histogram(FAKE, 10, 7, FAKE, stream=0) == E_ARG
     assert sz.sz_histogram(FAKE, 1 << 32, 1, FAKE, stream=0) == E_ARG
+    assert sz.sz_histogram_sampled(FAKE, 10, 1, 0, FAKE, stream=0) == E_ARG      # stride 0
+    assert sz.sz_histogram_sampled(FAKE, 10, 3, 4, FAKE, stream=0) == E_ARG
+    assert sz.sz_histogram_sampled_batched(FAKE, 2, 10, 1, 0, FAKE, stream=0) == E_ARG
     assert sz.sz_build_codebook(None, 1, FAKE, stream=0) == E_ARG
     assert sz.sz_build_codebook(FAKE, 5, FAKE, stream=0) == E_ARG
     # encode: capacity and workspace below the bound

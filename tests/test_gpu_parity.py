@@ -143,6 +143,31 @@ def test_batched_equals_single_and_oracle(sz, dt):
 
 
 @pytest.mark.parametrize("dt", [BF16, E5M2])
+@pytest.mark.parametrize("n,stride", [(4097, 2), (50001, 3), (300000, 64), (1 << 20, 16)])
+def test_sampled_histogram_and_its_codebook(sz, dt, n, stride):
+    """Block-sampled histogram (single and batched) equals the oracle's; the
+    stream encoded with the sampled codebook equals the oracle's stream with
+    that codebook and round-trips."""
+    xs = [kvsynth.stress(n, seed=90 + i) for i in range(3)]
+    if dt == E5M2:
+        xs = [kvsynth.e5m2_of(x) for x in xs]
+    say("sampled", dt, n, stride)
+    stream, hist, cb = sz.codec.compress(to_dev(xs[0]), dt, block_stride=stride)
+    expected_hist = oracle.histogram_sampled(xs[0], dt, stride)
+    assert np.array_equal(hist.cpu().numpy().view(np.uint64), expected_hist)
+    assert np.array_equal(cb.cpu().numpy(), oracle.codebook(expected_hist, dt))
+    assert np.array_equal(stream.cpu().numpy(), oracle.encode(xs[0], dt, cb.cpu().numpy()))
+    y, status = sz.codec.decompress(stream, n, dt)
+    assert status == 0 and np.array_equal(to_host(y, dt), xs[0])
+    bc = sz.codec.BatchCodec(len(xs), n, dt)
+    bc.set_inputs([to_dev(x) for x in xs])
+    bc.histogram(block_stride=stride)
+    got = bc.hists.cpu().numpy().view(np.uint64)
+    for i, x in enumerate(xs):
+        assert np.array_equal(got[i], oracle.histogram_sampled(x, dt, stride)), i
+
+
+@pytest.mark.parametrize("dt", [BF16, E5M2])
 def test_empty_tensor(sz, dt):
     say("empty", dt)
     x = np.zeros(0, np.uint16 if dt == BF16 else np.uint8)

@@ -301,3 +301,18 @@ def test_round_trip_bit_identical(which):
     status, y = oracle.decode(stream, x.size, dt)
     assert status == oracle.OK
     assert y.dtype == x.dtype and np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("dt", [BF16, E5M2])
+@pytest.mark.parametrize("n,stride", [(1, 1), (4095, 2), (4097, 2), (50000, 1), (50000, 3), (70001, 7), (300000, 64)])
+def test_sampled_histogram_matches_float_semantics(dt, n, stride):
+    """Block sample: only elements of 4096-element blocks b with b % stride == 0."""
+    x = kvsynth.stress(n, seed=n + stride)
+    if dt == E5M2:
+        x = kvsynth.e5m2_of(x)
+    _, exponent, _ = float_fields(x, dt)
+    chosen = (np.arange(n) // 4096) % stride == 0
+    expected = np.bincount(exponent[chosen], minlength=256)
+    assert np.array_equal(oracle.histogram_sampled(x, dt, stride), expected)
+    if stride == 1:
+        assert np.array_equal(oracle.histogram_sampled(x, dt, 1), oracle.histogram(x, dt))

@@ -1,0 +1,125 @@
+"""Layer-pipelined KV transfer over a copy link, with and without the codec.
+
+What the codec is for (SplitZip project page, FAQ "How can I reduce KV cache
+transfer time between prefill and decode nodes?"): compress each KV layer on
+the sending GPU, move fewer bytes over the link, decompress on the receiving
+GPU, with the codec running much faster than the link.  The FastKVComp page
+("Equation 1: does it pay?") states the condition: compression pays when
+encode + decode time is below the link time it saves.
+
+On one GPU the link is emulated by the PCIe path: every layer crosses
+device -> pinned host memory -> device through the copy engines, the way a
+prefill GPU's tensor would leave through a NIC and land on a decode GPU.
+
+  ship_raw         copies the raw layers over the link;
+  ship_compressed  encodes layer i+1 while layer i's exact-size stream
+                   crosses the link, and decodes each layer as it lands.
+
+Both return the received tensors, so callers can check bit-exactness.
+Streams run at the default priority.
+"""
+import torch
+
+from . import SZ_DTYPE_BF16, check, sz_build_codebook, sz_decode, sz_encode, sz_encode_workspace_bytes, \
+    sz_histogram, sz_max_compressed_bytes
+from .codec import ELEMENT_BYTES
+
+
+class _Layer:
+    """Device and pinned-host buffers for one layer tensor of n elements."""
+
+    def __init__(self, n, dtype, device):
+        self.n, self.dtype = n, dtype
+        self.capacity = sz_max_compressed_bytes(n, dtype)
+        self.hist = torch.empty(256, dtype=torch.int64, device=device)
+        self.codebook = torch.empty(16, dtype=torch.uint8, device=device)
+        self.stream = torch.empty(self.capacity, dtype=torch.uint8, device=device)
+        self.ws_bytes = sz_encode_workspace_bytes(n, dtype)
+        self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.host = torch.empty(self.capacity, dtype=torch.uint8, pin_memory=True)
+        self.size_host = torch.zeros(1, dtype=torch.int64, pin_memory=True)
+        self.landed = torch.empty(self.capacity, dtype=torch.uint8, device=device)
+        self.output = torch.empty(n * ELEMENT_BYTES[dtype], dtype=torch.uint8, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+
+
+class Link:
+    """Buffers for shipping `count` layer tensors of n elements each."""
+
+    def __init__(self, count, n, dtype=SZ_DTYPE_BF16, device="cuda"):
+        self.count, self.n, self.dtype = count, n, dtype
+        self.layers = [_Layer(n, dtype, device) for _ in range(count)]
+        raw = n * ELEMENT_BYTES[dtype]
+        self.raw_host = [torch.empty(raw, dtype=torch.uint8, pin_memory=True) for _ in range(count)]
+        self.raw_landed = [torch.empty(raw, dtype=torch.uint8, device=device) for _ in range(count)]
+        self.codec_stream = torch.cuda.Stream()
+        self.copy_stream = torch.cuda.Stream()
+
+    def ship_raw(self, tensors):
+        """Raw layers over the link; returns the landed copies (uint8 views)."""
+        cur = torch.cuda.current_stream()
+        self.copy_stream.wait_stream(cur)
+        with torch.cuda.stream(self.copy_stream):
+            for t, host, landed in zip(tensors, self.raw_host, self.raw_landed):
+                host.copy_(t.view(torch.uint8).reshape(-1), non_blocking=True)
+                landed.copy_(host, non_blocking=True)
+        cur.wait_stream(self.copy_stream)
+        return self.raw_landed
+
+    def ship_compressed(self, tensors):
+        """Encode -> link -> decode, pipelined across layers.  The host waits
+        for each layer's encode (its stream size lands in pinned host memory)
+        before queueing that layer's exact-size copy; the GPU keeps encoding
+        later layers meanwhile."""
+        cur = torch.cuda.current_stream()
+        cs, xs = self.codec_stream, self.copy_stream
+        cs.wait_stream(cur)
+        xs.wait_stream(cur)
+        encoded, landed_events = [], []
+
+        def queue_encode(t, L):
+            s = cs.cuda_stream
+            check(sz_histogram(t, self.n, self.dtype, L.hist, s), "sz_histogram")
+            check(sz_build_codebook(L.hist, self.dtype, L.codebook, s), "sz_build_codebook")
+            # the stream size goes straight to pinned host memory: no copy-engine
+            # transfer that could queue behind earlier layers' big copies
+            check(sz_encode(t, self.n, self.dtype, L.codebook, L.stream, L.capacity, L.size_host,
+                            L.workspace, L.ws_bytes, s), "sz_encode")
+            ev = torch.cuda.Event()
+            ev.record(cs)
+            encoded.append(ev)
+
+        def queue_copy(i):
+            L = self.layers[i]
+            encoded[i].synchronize()
+            nbytes = int(L.size_host[0])
+            # copy-engine friendly length: a 4 KiB multiple (the stream buffer
+            # holds at least that much; the bytes past the stream are unused)
+            span = min(-(-nbytes // 4096) * 4096, L.capacity)
+            xs.wait_event(encoded[i])
+            with torch.cuda.stream(xs):
+                L.host[:span].copy_(L.stream[:span], non_blocking=True)
+                L.landed[:span].copy_(L.host[:span], non_blocking=True)
+                done = torch.cuda.Event()
+                done.record(xs)
+            landed_events.append((done, nbytes))
+
+        # encode layer i, then put layer i-1 on the link, so the link starts
+        # right after the first layer instead of after every encode is queued
+        for i, (t, L) in enumerate(zip(tensors, self.layers)):
+            queue_encode(t, L)
+            if i:
+                queue_copy(i - 1)
+        queue_copy(len(self.layers) - 1)
+        for (done, nbytes), L in zip(landed_events, self.layers):
+            cs.wait_event(done)
+            check(sz_decode(L.landed, nbytes, self.n, self.dtype, L.output, L.status, cs.cuda_stream),
+                  "sz_decode")
+        cur.wait_stream(cs)
+        return [L.output for L in self.layers]
+
+    def compressed_bytes(self):
+        return sum(int(L.size_host[0]) for L in self.layers)
+
+    def statuses(self):
+        return [int(L.status[0]) for L in self.layers]

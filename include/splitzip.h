@@ -104,8 +104,8 @@ sz_status sz_build_codebook(const uint64_t* d_hist, sz_dtype dtype,
  * 16 device bytes, any values (a value listed twice takes its lowest code;
  * cb[15] is ignored and stored as 0).  d_dst receives the whole stream;
  * dst_capacity must be >= sz_max_compressed_bytes(n, dtype), else
- * SZ_ERR_BUFFER_TOO_SMALL.  d_out_bytes (device u64, may be NULL) receives
- * C.  d_workspace: >= sz_encode_workspace_bytes(n, dtype) bytes (may be
+ * SZ_ERR_BUFFER_TOO_SMALL.  d_out_bytes (u64 in device memory or in
+ * device-accessible pinned host memory, may be NULL) receives C.  d_workspace: >= sz_encode_workspace_bytes(n, dtype) bytes (may be
  * NULL when n = 0), contents need not be initialised, clobbered. */
 sz_status sz_encode(const void* d_src, uint64_t n, sz_dtype dtype,
                     const uint8_t* d_codebook, void* d_dst, uint64_t dst_capacity,

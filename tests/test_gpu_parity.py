@@ -311,3 +311,23 @@ def test_e5m2_config_full_size(sz):
     assert np.array_equal(stream.cpu().numpy(), oracle.encode(x, E5M2))
     ratio = x.size / stream.numel()
     assert 1.14 <= ratio <= 8 / 7
+
+
+def test_transfer_pipeline_round_trip(sz):
+    """Layers shipped compressed over the device -> pinned host -> device link
+    land bit-exact, and so do the raw copies."""
+    from fp8_kv_cache_amd.transfer import Link
+    say("transfer pipeline")
+    xs = [kvsynth.llama_kv(i // 2, i % 2, shape=(256, 8, 128)) for i in range(6)]
+    dev = [to_dev(x) for x in xs]
+    link = Link(len(xs), xs[0].size)
+    out = link.ship_compressed(dev)
+    torch.cuda.synchronize()
+    assert link.statuses() == [0] * len(xs)
+    assert link.compressed_bytes() == sum(oracle.encode(x, BF16).size for x in xs)
+    for x, o in zip(xs, out):
+        assert np.array_equal(o.cpu().numpy().view(np.uint16), x)
+    raw = link.ship_raw(dev)
+    torch.cuda.synchronize()
+    for x, o in zip(xs, raw):
+        assert np.array_equal(o.cpu().numpy().view(np.uint16), x)

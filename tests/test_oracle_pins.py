@@ -176,6 +176,9 @@ def test_golden_stream(name):
     assert sz_ref.encode(x, dt, spec.get("given_codebook")) == bytes(expected)
     status, y = oracle.decode(stream, x.size, dt)
     assert status == oracle.OK and np.array_equal(y, x)
+    # both decoders turn the hand-derived bytes back into the input
+    status, y = sz_ref.decode(bytes(expected), x.size, dt)
+    assert status == oracle.OK and y == list(map(int, x))
 
 
 def test_codebook_bruteforce_full_sort():
@@ -301,6 +304,20 @@ def test_round_trip_bit_identical(which):
     status, y = oracle.decode(stream, x.size, dt)
     assert status == oracle.OK
     assert y.dtype == x.dtype and np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("dt", [BF16, E5M2])
+def test_python_oracle_round_trip(dt):
+    """The pure-Python oracle alone: its own stream decodes to its input,
+    every sign, mantissa and exponent value included."""
+    if dt == BF16:
+        x = np.concatenate([kvsynth.stress(2900, seed=77), np.arange(0, 1 << 16, 331, dtype=np.uint16)])
+    else:
+        x = np.concatenate([np.arange(256, dtype=np.uint8),
+                            np.random.default_rng(78).integers(0, 256, 2900, dtype=np.uint8)])
+    stream = sz_ref.encode(x, dt)
+    status, y = sz_ref.decode(stream, x.size, dt)
+    assert status == oracle.OK and y == list(map(int, x))
 
 
 @pytest.mark.parametrize("dt", [BF16, E5M2])

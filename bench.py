@@ -152,25 +152,28 @@ def e5m2_cache(torch, xs):
             bc.compress()
             bc.decompress()
         torch.cuda.synchronize()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        enc, dec = [], []
-        for _ in range(reps):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+        for e in ev:
             e[0].record()
-            bc.compress()
+            bc.histogram()
             e[1].record()
-            bc.decompress()
+            bc.build_codebooks()
             e[2].record()
-            torch.cuda.synchronize()
-            enc.append(e[0].elapsed_time(e[1]))
-            dec.append(e[1].elapsed_time(e[2]))
-        return float(np.median(enc)), float(np.median(dec))
+            bc.encode()
+            e[3].record()
+            bc.decompress()
+            e[4].record()
+        torch.cuda.synchronize()
+        return [float(np.median([e[a].elapsed_time(e[a + 1]) for e in ev])) for a in range(4)]
 
-    enc_ms, dec_ms = timed()
+    hist_ms, cb_ms, code_ms, dec_ms = timed()
+    enc_ms = hist_ms + cb_ms + code_ms
     for i in range(count):
         assert int(bc.status[i]) == 0 and torch.equal(bc.output(i), bc._inputs[i]), i
     stream = int(bc.sizes.sum().item())
     return {"workload": "llama3-8b-kv-cache quantised to FP8 E5M2", "raw_bytes": raw,
             "encode_ms": enc_ms, "decode_ms": dec_ms,
+            "phase_ms": {"histogram": hist_ms, "codebook": cb_ms, "encode": code_ms, "decode": dec_ms},
             "encode_GBps": raw / (enc_ms * 1e-3) / 1e9, "decode_GBps": raw / (dec_ms * 1e-3) / 1e9,
             "encode_hbm_frac_two_pass": (2 * raw + stream) / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "decode_hbm_frac": (raw + stream) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,

@@ -57,10 +57,6 @@ __device__ inline uint32_t wave_scan_incl(uint32_t x) {
     return x;
 }
 
-__device__ inline uint32_t wave_sum(uint32_t x) {
-    return __builtin_amdgcn_readlane(wave_scan_incl(x), 63);
-}
-
 __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -147,20 +143,112 @@ __global__ void k_fill_i32(int32_t* p, uint64_t words, int32_t value) {
 // -------------------------------------------------------------- histogram
 //
 // Each workgroup counts one contiguous chunk of one tensor into 32
-// lane-striped copies of the 256 bins held in LDS, laid out [bin][copy]:
-// lane l always adds into copy l & 31, so the 32 lanes of a half-wave hit
-// 32 different banks whatever their exponents.  For BF16 the byte address
-// of (bin e, copy c) is e*128 + 4c, and e*128 is simply u & 0x7F80.
+// Histogram bins in LDS.
+//   BF16: 256 bins x 32 lane-striped copies, laid out [bin][copy]; lane l
+//         adds into copy l & 31, so the 32 lanes of a half-wave hit 32
+//         different banks whatever their exponents.  The byte address of
+//         (bin e, copy c) is e*128 + 4c, and e*128 is simply u & 0x7F80.
+//   E5M2: a byte per element makes the LDS atomics, not the reads, the
+//         limit, so the two exponents of each element pair (bytes 0,1 and
+//         2,3 of a dword) are counted together: 1024 pair bins as 16-bit
+//         counters, two to a dword, in 16 lane-striped copies, laid out
+//         [pair/2][copy] (32 KB).  An element without a partner (a ragged
+//         end) is counted as the pair (e, 0), and the fold, which splits each
+//         pair count back onto both of its exponents, takes those partners
+//         off bin 0 again.  A 16-bit counter takes at most
+//         16 * (chunk/512 + 128) increments (16 lanes per copy, one pair per
+//         two elements, fewer than 128 unpaired elements per lane), so E5M2
+//         chunks are capped at 2^20 elements.
+template <uint32_t DT>
+struct HistLds;
+template <>
+struct HistLds<kDtypeBF16> {
+    static constexpr uint32_t kWords = 256 * 32;
+};
+template <>
+struct HistLds<kDtypeE5M2> {
+    static constexpr uint32_t kWords = 512 * 16;
+};
+constexpr uint64_t kE5m2MaxChunk = 1ull << 20;
 
 template <uint32_t DT>
-__device__ inline void count_dword(char* lds, uint32_t w, uint32_t copy4) {
+__device__ inline uint32_t hist_lane_bytes(uint32_t tid) {
+    return DT == kDtypeBF16 ? (tid & 31u) << 2 : (tid & 15u) << 2;
+}
+
+template <uint32_t DT>
+__device__ inline void count_dword(char* lds, uint32_t w, uint32_t lane_bytes) {
     if (DT == kDtypeBF16) {
-        atomicAdd(reinterpret_cast<uint32_t*>(lds + ((w & 0x7F80u) | copy4)), 1u);
-        atomicAdd(reinterpret_cast<uint32_t*>(lds + (((w >> 16) & 0x7F80u) | copy4)), 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + ((w & 0x7F80u) | lane_bytes)), 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + (((w >> 16) & 0x7F80u) | lane_bytes)), 1u);
     } else {
+        // pair index e_first | e_second << 5 of bytes (0,1) in the low half and (2,3) in the high half
+        const uint32_t pk = ((w >> 2) & 0x001F001Fu) | ((w >> 5) & 0x03E003E0u);
+        const uint32_t p0 = pk & 0xFFFFu, p1 = pk >> 16;
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + (((p0 >> 1) << 6) | lane_bytes)), (p0 & 1u) ? 0x10000u : 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + (((p1 >> 1) << 6) | lane_bytes)), (p1 & 1u) ? 0x10000u : 1u);
+    }
+}
+
+// one element, raw bits u (E5M2: as the pair (e, 0))
+template <uint32_t DT>
+__device__ inline void count_one(char* lds, uint32_t u, uint32_t lane_bytes) {
+    if constexpr (DT == kDtypeBF16) {
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + ((((u >> 7) & 0xFFu) << 7) | lane_bytes)), 1u);
+    } else {
+        const uint32_t p = (u >> 2) & 0x1Fu;
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + (((p >> 1) << 6) | lane_bytes)), (p & 1u) ? 0x10000u : 1u);
+    }
+}
+
+template <uint32_t DT>
+__device__ inline void hist_clear(uint32_t* bins, uint32_t tid) {
+    constexpr uint32_t kWords = HistLds<DT>::kWords;
+    static_assert(kWords % 4 == 0, "cleared in 16-byte stores");
+#pragma unroll
+    for (uint32_t i = tid * 4; i < kWords; i += kThreads * 4)
+        *reinterpret_cast<uint4*>(bins + i) = make_uint4(0, 0, 0, 0);
+}
+
+// Fold the copies and add the sums to the tensor's u64 histogram.  Every
+// thread of the workgroup calls it, after a barrier; `unpaired` is the
+// number of elements the workgroup counted one at a time.  Rotating the
+// start keeps the lanes of a wave on distinct banks.
+template <uint32_t DT>
+__device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64_t* hist, uint32_t unpaired) {
+    if constexpr (DT == kDtypeBF16) {
+        uint32_t sum = 0;
+#pragma unroll 8
+        for (uint32_t j = 0; j < 32; ++j) sum += bins[tid * 32 + ((j + tid) & 31u)];
+        if (sum) __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        // thread t folds pairs 4t..4t+3 (dwords 2t, 2t+1): their first exponents
+        // are (4t + k) & 31, their second exponent is t >> 3
+        uint32_t c[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (uint32_t k = 0; k < 2; ++k) {
+#pragma unroll 8
+            for (uint32_t j = 0; j < 16; ++j) {
+                const uint32_t w = bins[(2 * tid + k) * 16 + ((j + tid) & 15u)];
+                c[2 * k] += w & 0xFFFFu;
+                c[2 * k + 1] += w >> 16;
+            }
+        }
+        // the first 32 words, read by now, become the 32 exponent bins
+        __syncthreads();
+        if (tid < 32) bins[tid] = 0;
+        __syncthreads();
+        const uint32_t both = c[0] + c[1] + c[2] + c[3];
+        if (both) atomicAdd(bins + (tid >> 3), both);
 #pragma unroll
         for (uint32_t k = 0; k < 4; ++k)
-            atomicAdd(reinterpret_cast<uint32_t*>(lds + ((((w >> (8 * k)) & 0x7Cu) << 5) | copy4)), 1u);
+            if (c[k]) atomicAdd(bins + ((4 * tid + k) & 31u), c[k]);
+        __syncthreads();
+        const uint32_t sum = tid < 32 ? bins[tid] - (tid == 0 ? unpaired : 0u) : 0u;
+        if (sum)
+            __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -174,19 +262,18 @@ __global__ __launch_bounds__(kThreads) void k_histogram(HistArgs a) {
     constexpr uint32_t kVecElems = 16 / G::kElemBytes;       // elements per 16-byte vector
     constexpr uint32_t kTile = kThreads * kVecElems;          // elements per pass
     constexpr uint32_t kPasses = 8;
-    __shared__ uint32_t bins[256 * 32];
+    __shared__ uint32_t bins[HistLds<DT>::kWords];
     const uint32_t tid = threadIdx.x;
     const uint32_t t = blockIdx.x / a.groups;
     const uint32_t g = blockIdx.x - t * a.groups;
     char* lds = reinterpret_cast<char*>(bins);
-#pragma unroll
-    for (uint32_t j = 0; j < 32; j += 4) *reinterpret_cast<uint4*>(bins + tid * 32 + j) = make_uint4(0, 0, 0, 0);
+    hist_clear<DT>(bins, tid);
     __syncthreads();
 
     const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
     const uint64_t begin = static_cast<uint64_t>(g) * a.chunk;
     const uint64_t end = begin + a.chunk < a.n ? begin + a.chunk : a.n;
-    const uint32_t copy4 = (tid & 31u) << 2;
+    const uint32_t copy4 = hist_lane_bytes<DT>(tid);
     uint64_t base = begin;
     for (; base + kPasses * kTile <= end; base += kPasses * kTile) {
         const SZ_GLOBAL u32x4* q = (const SZ_GLOBAL u32x4*)(src + base * G::kElemBytes);
@@ -202,19 +289,10 @@ __global__ __launch_bounds__(kThreads) void k_histogram(HistArgs a) {
         }
     }
     // ragged end of the chunk: element-wise guarded reads
-    for (uint64_t i = base + tid; i < end; i += kThreads) {
-        const uint32_t u = DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i];
-        const uint32_t e = DT == kDtypeBF16 ? (u >> 7) & 0xFFu : (u >> 2) & 0x1Fu;
-        atomicAdd(reinterpret_cast<uint32_t*>(lds + ((e << 7) | copy4)), 1u);
-    }
+    for (uint64_t i = base + tid; i < end; i += kThreads)
+        count_one<DT>(lds, DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i], copy4);
     __syncthreads();
-
-    // fold the 32 copies of bin `tid`; the rotation keeps lanes on distinct banks
-    uint32_t sum = 0;
-#pragma unroll 8
-    for (uint32_t j = 0; j < 32; ++j) sum += bins[tid * 32 + ((j + tid) & 31u)];
-    if (sum) __hip_atomic_fetch_add(gptr(a.hists) + 256ull * t + tid, static_cast<uint64_t>(sum),
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    hist_flush<DT>(bins, tid, gptr(a.hists) + 256ull * t, static_cast<uint32_t>(end - base));
 }
 
 // Histogram of a block sample: only format blocks b with b % stride == 0
@@ -226,13 +304,12 @@ __global__ __launch_bounds__(kThreads) void k_histogram_sampled(HistArgs a) {
     using G = Geometry<DT>;
     constexpr uint32_t kVecElems = 16 / G::kElemBytes;
     constexpr uint32_t kVecs = kBlockElems / (kThreads * kVecElems);   // per lane per block
-    __shared__ uint32_t bins[256 * 32];
+    __shared__ uint32_t bins[HistLds<DT>::kWords];
     const uint32_t tid = threadIdx.x;
     const uint32_t t = blockIdx.x / a.groups;
     const uint32_t g = blockIdx.x - t * a.groups;
     char* lds = reinterpret_cast<char*>(bins);
-#pragma unroll
-    for (uint32_t j = 0; j < 32; j += 4) *reinterpret_cast<uint4*>(bins + tid * 32 + j) = make_uint4(0, 0, 0, 0);
+    hist_clear<DT>(bins, tid);
     __syncthreads();
 
     const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
@@ -240,7 +317,8 @@ __global__ __launch_bounds__(kThreads) void k_histogram_sampled(HistArgs a) {
     const uint64_t sampled = (blocks + a.stride - 1) / a.stride;
     const uint64_t k0 = static_cast<uint64_t>(g) * a.per_group;
     const uint64_t k1 = k0 + a.per_group < sampled ? k0 + a.per_group : sampled;
-    const uint32_t copy4 = (tid & 31u) << 2;
+    const uint32_t copy4 = hist_lane_bytes<DT>(tid);
+    uint32_t unpaired = 0;   // elements of a partial last block, counted one at a time
     for (uint64_t k = k0; k < k1; ++k) {
         const uint64_t begin = k * a.stride * kBlockElems;
         if (begin + kBlockElems <= a.n) {
@@ -256,19 +334,13 @@ __global__ __launch_bounds__(kThreads) void k_histogram_sampled(HistArgs a) {
                 count_dword<DT>(lds, v[p].w, copy4);
             }
         } else {
-            for (uint64_t i = begin + tid; i < a.n; i += kThreads) {
-                const uint32_t u = DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i];
-                const uint32_t e = DT == kDtypeBF16 ? (u >> 7) & 0xFFu : (u >> 2) & 0x1Fu;
-                atomicAdd(reinterpret_cast<uint32_t*>(lds + ((e << 7) | copy4)), 1u);
-            }
+            unpaired += static_cast<uint32_t>(a.n - begin);
+            for (uint64_t i = begin + tid; i < a.n; i += kThreads)
+                count_one<DT>(lds, DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i], copy4);
         }
     }
     __syncthreads();
-    uint32_t sum = 0;
-#pragma unroll 8
-    for (uint32_t j = 0; j < 32; ++j) sum += bins[tid * 32 + ((j + tid) & 31u)];
-    if (sum) __hip_atomic_fetch_add(gptr(a.hists) + 256ull * t + tid, static_cast<uint64_t>(sum),
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    hist_flush<DT>(bins, tid, gptr(a.hists) + 256ull * t, unpaired);
 }
 
 // --------------------------------------------------------------- codebook
@@ -685,9 +757,11 @@ __device__ inline void put_byte(uint32_t& w0, uint32_t& w1, uint32_t k, uint32_t
 }
 
 // Decode work split.  BF16: lane l of sub-chunk j owns 8 elements, so per
-// lane one code dword, two sign|mantissa dwords and four output dwords, and
-// every load and store of the wave is one contiguous run.  E5M2: 32
-// elements per lane (four code dwords, three 3-bit-field dwords).
+// lane one code dword, two sign|mantissa dwords and four output dwords.
+// E5M2: 16 elements per lane, so per lane two code dwords, the lane's 48
+// bits of 3-bit fields (inside one aligned dword pair) and four output
+// dwords.  Either way every code load and output store of the wave is one
+// contiguous run.
 template <uint32_t DT>
 struct DecodeGeometry;
 template <>
@@ -700,11 +774,11 @@ struct DecodeGeometry<kDtypeBF16> {
 };
 template <>
 struct DecodeGeometry<kDtypeE5M2> {
-    static constexpr uint32_t kLaneElems = 32;
-    static constexpr uint32_t kSubs = 2;
-    static constexpr uint32_t kCodeWords = 4;
-    static constexpr uint32_t kSmWords = 3;
-    static constexpr uint32_t kOutWords = 8;
+    static constexpr uint32_t kLaneElems = 16;
+    static constexpr uint32_t kSubs = 4;
+    static constexpr uint32_t kCodeWords = 2;
+    static constexpr uint32_t kSmWords = 2;
+    static constexpr uint32_t kOutWords = 4;
 };
 
 constexpr uint32_t kPrefetch = 2 * kWaveSize;   // escape bytes staged in LDS per block
@@ -740,7 +814,8 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
     const uint64_t src_bytes = a.src_bytes_table ? gptr(a.src_bytes_table)[t] : a.src_bytes;
     SZ_GLOBAL int32_t* status = a.status ? gptr(a.status) + t : nullptr;
     // Every read below lies in [0, esc_at) -- header, offsets, both planes
-    // (the E5M2 plane's last 12-byte group may run into the code region) --
+    // (an E5M2 lane's 8-byte field load may run past the plane into its padding
+    // or the code region) --
     // or, for escape bytes, below src_bytes.  With that range readable, all
     // loads are issued at once and the stream is validated afterwards.
     if (src_bytes < L.esc_at) {
@@ -766,10 +841,12 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
                 const u32x2 v = *(const SZ_GLOBAL u32x2*)(src + L.sm_at + elem0);
                 sm[j][0] = v.x; sm[j][1] = v.y;
             } else {
-                const u32x4 c = *(const SZ_GLOBAL u32x4*)(src + L.code_at + elem0 / 2);
-                cw[j][0] = c.x; cw[j][1] = c.y; cw[j][2] = c.z; cw[j][3] = c.w;
-                const SZ_GLOBAL uint32_t* v = (const SZ_GLOBAL uint32_t*)(src + L.sm_at + elem0 / 32 * 12);
-                sm[j][0] = v[0]; sm[j][1] = v[1]; sm[j][2] = v[2];
+                const u32x2 c = *(const SZ_GLOBAL u32x2*)(src + L.code_at + elem0 / 2);
+                cw[j][0] = c.x; cw[j][1] = c.y;
+                // the lane's 6 field bytes start 0 or 2 bytes into this dword pair
+                const uint64_t sm_off = elem0 / 16 * 6;
+                const u32x2 v = *(const SZ_GLOBAL u32x2*)(src + L.sm_at + (sm_off & ~3ull));
+                sm[j][0] = v.x; sm[j][1] = v.y;
             }
         } else {
 #pragma unroll
@@ -865,18 +942,17 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
                 out[h] = ((v >> 1) & 0x7F807F80u) | ((v << 8) & 0x80008000u) | (v & 0x007F007Fu);
             }
         } else {
-            const uint32_t s0 = sm[j][0], s1 = sm[j][1], s2 = sm[j][2];
-            uint32_t f[8];
-            f[0] = s0 & 0xFFFu;
-            f[1] = (s0 >> 12) & 0xFFFu;
-            f[2] = (s0 >> 24) | ((s1 & 0xFu) << 8);
-            f[3] = (s1 >> 4) & 0xFFFu;
-            f[4] = (s1 >> 16) & 0xFFFu;
-            f[5] = (s1 >> 28) | ((s2 & 0xFFu) << 4);
-            f[6] = (s2 >> 8) & 0xFFFu;
-            f[7] = s2 >> 20;
+            // 48 field bits: four 12-bit groups of four elements each
+            const uint32_t shift = (static_cast<uint32_t>(elem0 / 16 * 6) & 3u) * 8u;   // 0 or 16
+            const uint32_t lo = __builtin_amdgcn_alignbit(sm[j][1], sm[j][0], shift);
+            const uint32_t hi = sm[j][1] >> shift;
+            uint32_t f[4];
+            f[0] = lo & 0xFFFu;
+            f[1] = (lo >> 12) & 0xFFFu;
+            f[2] = (lo >> 24) | ((hi & 0xFu) << 8);
+            f[3] = (hi >> 4) & 0xFFFu;
 #pragma unroll
-            for (uint32_t q = 0; q < 4; ++q) {
+            for (uint32_t q = 0; q < 2; ++q) {
                 const uint32_t c = cw[j][q];
                 const uint32_t ev = lookup4(c & 0x0F0F0F0Fu, cbw);
                 const uint32_t od = lookup4((c >> 4) & 0x0F0F0F0Fu, cbw);
@@ -894,12 +970,7 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
         }
         SZ_GLOBAL uint8_t* p = dst + elem0 * (DT == kDtypeBF16 ? 2 : 1);
         if (kFull || elem0 + G::kLaneElems <= L.n) {
-            if constexpr (DT == kDtypeBF16) {
-                *(SZ_GLOBAL u32x4*)p = u32x4{out[0], out[1], out[2], out[3]};
-            } else {
-                ((SZ_GLOBAL u32x4*)p)[0] = u32x4{out[0], out[1], out[2], out[3]};
-                ((SZ_GLOBAL u32x4*)p)[1] = u32x4{out[4], out[5], out[6], out[7]};
-            }
+            *(SZ_GLOBAL u32x4*)p = u32x4{out[0], out[1], out[2], out[3]};
         } else {
             const uint32_t valid = static_cast<uint32_t>(L.n - elem0);
 #pragma unroll
@@ -990,6 +1061,7 @@ void enqueue_histogram(HistArgs a, hipStream_t s) {
     const uint64_t units = (a.n + kQuantum - 1) / kQuantum;
     if (want > units) want = units;
     a.chunk = (units + want - 1) / want * kQuantum;
+    if (DT == kDtypeE5M2 && a.chunk > kE5m2MaxChunk) a.chunk = kE5m2MaxChunk;   // 16-bit pair counters
     a.groups = static_cast<uint32_t>((a.n + a.chunk - 1) / a.chunk);
     hipLaunchKernelGGL(k_histogram<DT>, dim3(a.count * a.groups), dim3(kThreads), 0, s, a);
 }

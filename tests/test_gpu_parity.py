@@ -168,6 +168,30 @@ def test_sampled_histogram_and_its_codebook(sz, dt, n, stride):
 
 
 @pytest.mark.parametrize("dt", [BF16, E5M2])
+def test_histogram_beyond_2g_elements(sz, dt):
+    """2^31 + 12345 elements cycling through every bit pattern of the type.
+    Each whole cycle holds every exponent equally often (256 times per BF16
+    cycle of 65536 patterns, 8 times per E5M2 cycle of 256), so the
+    histogram has a closed form at any size.  This runs the largest
+    workgroup chunks, and for E5M2 the capped chunk of the 16-bit pair
+    counters, at full size."""
+    n = (1 << 31) + 12345
+    period = 65536 if dt == BF16 else 256
+    cycle = np.arange(period, dtype=np.uint16 if dt == BF16 else np.uint8)
+    say("histogram beyond 2^31 elements", dt, n)
+    x = to_dev(cycle).repeat(n // period + 1)[:n]
+    hist = torch.empty(256, dtype=torch.int64, device="cuda")
+    sz.check(sz.sz_histogram(x, n, dt, hist), "sz_histogram")
+    got = hist.cpu().numpy()
+    del x
+    torch.cuda.empty_cache()
+    exps = (cycle.astype(np.int64) >> 7) & 0xFF if dt == BF16 else (cycle.astype(np.int64) >> 2) & 0x1F
+    expected = (n // period) * np.bincount(exps, minlength=256) + np.bincount(exps[:n % period], minlength=256)
+    assert int(expected.sum()) == n
+    assert np.array_equal(got, expected)
+
+
+@pytest.mark.parametrize("dt", [BF16, E5M2])
 def test_empty_tensor(sz, dt):
     say("empty", dt)
     x = np.zeros(0, np.uint16 if dt == BF16 else np.uint8)

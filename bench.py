@@ -12,6 +12,7 @@ input bytes (GB = 1e9).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
                     [--mode bench|profile|copy|transfer] [--no-cpu-baseline]
+                    [--dtype bf16|e5m2]   (profile mode)
 
 --mode transfer measures the layer-pipelined transfer (encode -> PCIe round
 trip through pinned host memory -> decode) against shipping the raw layers.
@@ -42,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--mode", choices=["bench", "profile", "copy", "transfer"], default="bench")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--dtype", choices=["bf16", "e5m2"], default="bf16",
+                   help="profile mode only: run the step on the cache as BF16 or quantised to FP8 E5M2")
     return p.parse_args()
 
 
@@ -302,11 +305,20 @@ def main():
     if args.mode == "transfer":
         transfer(torch, xs)
         return
+    if args.dtype == "e5m2" and args.mode != "profile":
+        print("--dtype e5m2 applies to --mode profile; the bench line always carries the E5M2 cache too",
+              file=sys.stderr)
+        sys.exit(2)
+    tag = args.dtype
+    if tag == "e5m2":
+        import kvsynth
+        with cf.ThreadPoolExecutor(8) as pool:
+            xs = list(pool.map(kvsynth.e5m2_of, xs))
     n = xs[0].size
     count = len(xs)
     raw_bytes = sum(x.nbytes for x in xs)
-    bc = BatchCodec(count, n, sz.SZ_DTYPE_BF16)
-    bc.set_inputs([torch.from_numpy(x.view(np.int16)).to("cuda") for x in xs])
+    bc = BatchCodec(count, n, sz.SZ_DTYPE_BF16 if tag == "bf16" else sz.SZ_DTYPE_FP8_E5M2)
+    bc.set_inputs([torch.from_numpy(x.view(np.int16) if tag == "bf16" else x).to("cuda") for x in xs])
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -353,10 +365,10 @@ def main():
     # Per API call (each call is one batched launch sequence over all 64
     # tensors): its kernels, algorithmic bytes, and live event time.
     calls = {
-        "sz_histogram_batched": (["k_fill_u64", "k_histogram<bf16>"], raw_bytes, med(hist_ms)),
-        "sz_encode_batched": (["k_encode<bf16>", "k_offsets<bf16>", "k_scatter<bf16>"],
+        "sz_histogram_batched": (["k_fill_u64", f"k_histogram<{tag}>"], raw_bytes, med(hist_ms)),
+        "sz_encode_batched": ([f"k_encode<{tag}>", f"k_offsets<{tag}>", f"k_scatter<{tag}>"],
                               raw_bytes + stream_bytes, med(enc_ms)),
-        "sz_decode_batched": (["k_fill_i32", "k_decode<bf16>"], stream_bytes + raw_bytes, med(dec_ms)),
+        "sz_decode_batched": (["k_fill_i32", f"k_decode<{tag}>"], stream_bytes + raw_bytes, med(dec_ms)),
     }
     per_call = {}
     for name, (kernels, alg_bytes, t_ms) in calls.items():
@@ -390,9 +402,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u16",
+        "dtype": "u16" if tag == "bf16" else "u8",
         "data": "synthetic",
-        "config": {"workload": "llama3-8b-kv-cache-bf16", "tensors": count, "elements_per_tensor": n,
+        "config": {"workload": f"llama3-8b-kv-cache-{tag}", "tensors": count, "elements_per_tensor": n,
                    "shape": list(SHAPE), "raw_bytes": raw_bytes, "codebook": "per layer tensor"},
         "value_definition": "raw bytes / (histogram + codebook + encode + decode) per step",
         "encode_GBps": encode_gbps,
@@ -401,6 +413,7 @@ def main():
         "encode_hbm_frac_strict": enc_strict / HBM_PEAK_GBPS,
         "decode_hbm_frac": (raw_bytes + stream_bytes) / (med(dec_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "compression_ratio": ratio,
+        "stream_bytes": stream_bytes,
         "phase_ms": {"histogram": med(hist_ms), "codebook": med(cb_ms), "encode": med(enc_ms),
                      "decode": med(dec_ms)},
         "calls": per_call,

@@ -355,3 +355,46 @@ def test_transfer_pipeline_round_trip(sz):
     torch.cuda.synchronize()
     for x, o in zip(xs, raw):
         assert np.array_equal(o.cpu().numpy().view(np.uint16), x)
+
+
+@pytest.mark.parametrize("dt", [BF16, E5M2])
+def test_graph_replay_matches_eager(sz, dt):
+    """The batched calls captured in one HIP graph (histogram -> codebook ->
+    encode -> decode) and replayed three times, with eager work and a
+    synchronisation between replays: every replay reproduces the eager
+    streams, sizes, statuses and decoded tensors, and the streams equal the
+    oracle's."""
+    n, count = 100003, 3
+    xs = [kvsynth.stress(n, seed=300 + i) for i in range(count)]
+    if dt == E5M2:
+        xs = [kvsynth.e5m2_of(x) for x in xs]
+    say("graph replay", dt, n, count)
+    bc = sz.codec.BatchCodec(count, n, dt)
+    bc.set_inputs([to_dev(x) for x in xs])
+    bc.compress()
+    bc.decompress()
+    torch.cuda.synchronize()
+    ref_sizes = bc.sizes.clone()
+    ref_streams = [bc.stream(i).clone() for i in range(count)]
+    for i, x in enumerate(xs):
+        assert np.array_equal(ref_streams[i].cpu().numpy(), oracle.encode(x, dt)), i
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bc.compress()
+        bc.decompress()
+    for replay in range(3):
+        bc.outputs.zero_()
+        bc.streams.zero_()
+        bc.sizes.zero_()
+        bc.hists.zero_()
+        bc.status.fill_(-1)
+        noise = torch.randn(1 << 20, device="cuda").sum()   # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(noise)
+        assert torch.equal(bc.sizes, ref_sizes), replay
+        for i, x in enumerate(xs):
+            assert int(bc.status[i]) == 0, (replay, i)
+            assert torch.equal(bc.stream(i), ref_streams[i]), (replay, i)
+            assert np.array_equal(to_host(bc.output(i), dt), x), (replay, i)

@@ -25,14 +25,22 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sz_oracle.c")
 _LIB = os.path.join(_HERE, "libszoracle.so")
 _lib = None
+_LC_SRC = os.path.join(_HERE, "lc_oracle.c")
+_LC_LIB = os.path.join(_HERE, "liblcoracle.so")
+_lc = None
+
+
+def _compile(src, lib):
+    tmp = lib + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+                           "-o", tmp, src])
+    os.replace(tmp, lib)
 
 
 def build():
-    """Compile the C oracle with gcc -O2 (plain scalar code, no intrinsics)."""
-    tmp = _LIB + ".tmp"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-                           "-o", tmp, _SRC])
-    os.replace(tmp, _LIB)
+    """Compile the C oracles with gcc -O2 (plain scalar code, no intrinsics)."""
+    _compile(_SRC, _LIB)
+    _compile(_LC_SRC, _LC_LIB)
 
 
 def _load():
@@ -40,7 +48,7 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
+        _compile(_SRC, _LIB)
     lib = ctypes.CDLL(_LIB)
     u64, i32, vp = ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p
     lib.szo_max_bytes.argtypes = [u64, i32]
@@ -144,3 +152,101 @@ def stream_fields(stream):
         "n": int.from_bytes(s[8:16], "little"), "escapes": int.from_bytes(s[16:24], "little"),
         "codebook": list(s[24:40]), "bytes": int.from_bytes(s[40:48], "little"),
     }
+
+
+# ---- LC-style comparison codec (lc_oracle.c) -------------------------------
+
+def _load_lc():
+    global _lc
+    if _lc is not None:
+        return _lc
+    if not os.path.exists(_LC_LIB) or os.path.getmtime(_LC_LIB) < os.path.getmtime(_LC_SRC):
+        _compile(_LC_SRC, _LC_LIB)
+    lib = ctypes.CDLL(_LC_LIB)
+    u64, i32, vp = ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p
+    for name in ("lco_tupl8_1", "lco_untupl8_1", "lco_bit8", "lco_unbit8"):
+        getattr(lib, name).argtypes = [vp, u64, vp]
+        getattr(lib, name).restype = None
+    lib.lco_rze2.argtypes = [vp, u64, vp]
+    lib.lco_rze2.restype = u64
+    lib.lco_unrze2.argtypes = [vp, u64, u64, vp]
+    lib.lco_unrze2.restype = i32
+    lib.lco_max_bytes.argtypes = [u64]
+    lib.lco_max_bytes.restype = u64
+    lib.lco_encode.argtypes = [vp, u64, vp, u64, vp]
+    lib.lco_encode.restype = i32
+    lib.lco_decode.argtypes = [vp, u64, u64, vp]
+    lib.lco_decode.restype = i32
+    _lc = lib
+    return lib
+
+
+def _bytes_of(values):
+    a = np.ascontiguousarray(values)
+    return np.ascontiguousarray(a.reshape(-1).view(np.uint8))
+
+
+def _stage(name, data):
+    a = _bytes_of(data)
+    out = np.zeros(max(a.size, 1), np.uint8)
+    getattr(_load_lc(), name)(a.ctypes.data if a.size else None, a.size, out.ctypes.data)
+    return out[:a.size]
+
+
+def lc_tupl8_1(data):
+    return _stage("lco_tupl8_1", data)
+
+
+def lc_untupl8_1(data):
+    return _stage("lco_untupl8_1", data)
+
+
+def lc_bit8(data):
+    return _stage("lco_bit8", data)
+
+
+def lc_unbit8(data):
+    return _stage("lco_unbit8", data)
+
+
+def lc_rze2(data):
+    a = _bytes_of(data)
+    out = np.zeros(a.size + a.size // 16 + 16, np.uint8)
+    k = _load_lc().lco_rze2(a.ctypes.data if a.size else None, a.size, out.ctypes.data)
+    return out[:k].copy()
+
+
+def lc_unrze2(payload, length):
+    """Inverse of lc_rze2 for a chunk of `length` bytes; None if the payload
+    size does not match its bitmap."""
+    p = _bytes_of(payload)
+    out = np.zeros(max(length, 1), np.uint8)
+    rc = _load_lc().lco_unrze2(p.ctypes.data if p.size else None, p.size, length, out.ctypes.data)
+    return None if rc else out[:length]
+
+
+def lc_max_bytes(n):
+    return int(_load_lc().lco_max_bytes(n))
+
+
+def lc_encode(data):
+    """LC-style stream of the raw bytes of `data` (any dtype, C order)."""
+    a = _bytes_of(data)
+    cap = lc_max_bytes(a.size)
+    out = np.zeros(max(cap, 1), np.uint8)
+    nbytes = ctypes.c_uint64(0)
+    rc = _load_lc().lco_encode(a.ctypes.data if a.size else None, a.size, out.ctypes.data, cap,
+                               ctypes.byref(nbytes))
+    if rc:
+        raise ValueError(f"lco_encode failed: {rc}")
+    return out[:nbytes.value].copy()
+
+
+def lc_decode(stream, n):
+    """Returns (status, n raw bytes or None)."""
+    s = np.ascontiguousarray(stream, dtype=np.uint8)
+    out = np.zeros(max(n, 1), np.uint8)
+    rc = _load_lc().lco_decode(s.ctypes.data if s.size else None, s.size, n, out.ctypes.data)
+    if rc != OK:
+        return rc, None
+    return OK, out[:n]

@@ -21,8 +21,10 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 C_SRC = os.path.join(ROOT, "oracle", "sz_oracle.c")
 PY_SRC = os.path.join(ROOT, "oracle", "sz_ref.py")
+LC_SRC = os.path.join(ROOT, "oracle", "lc_oracle.c")
 PIN_FILES = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
              os.path.join(ROOT, "tests", "test_oracle_properties.py")]
+LC_PIN_FILES = [os.path.join(ROOT, "tests", "test_lc_oracle_pins.py")]
 
 # (name, text to replace -- must occur exactly once, replacement)
 C_MUTANTS = [
@@ -76,6 +78,23 @@ PY_MUTANTS = [
     ("decode skips the offset span check", "if span_end - offsets[b] != count:", "if span_end < offsets[b]:"),
 ]
 
+LC_MUTANTS = [
+    ("tuple split left as is", "y[j * q + i] = x[8 * i + j];", "y[8 * i + j] = x[8 * i + j];"),
+    ("bit planes with the word order reversed", "(unsigned)(b % 8)) << a;", "(unsigned)(b % 8)) << (7u - a);"),
+    ("bit planes read the wrong byte of a word", "8 * (8 * s + a) + b / 8, (unsigned)(b % 8)) << a;",
+     "8 * (8 * s + a) + b % 8, (unsigned)(b / 8)) << a;"),
+    ("zero test on the low byte only", "if (z[2 * m] | z[2 * m + 1]) {", "if (z[2 * m]) {"),
+    ("bitmap bits most significant first", "out[m / 8] |= (uint8_t)(1u << (m % 8));",
+     "out[m / 8] |= (uint8_t)(1u << (7u - m % 8));"),
+    ("odd byte dropped", "if (L & 1u) out[at++] = z[L - 1];", "(void)0;"),
+    ("coded chunk kept when as long as the chunk", "if (len < L) {", "if (len <= L) {"),
+    ("payloads padded to 8 bytes", "return (x + 15u) / 16u * 16u;", "return (x + 7u) / 8u * 8u;"),
+    ("data region not padded", "return up256(64u + 8u * chunks_of(n));", "return 64u + 8u * chunks_of(n);"),
+    ("chunks of 8192 bytes", "#define LCO_CHUNK 16384u", "#define LCO_CHUNK 8192u"),
+    ("header total without the data region", "put_u64(dst + 24, D + off);", "put_u64(dst + 24, off);"),
+    ("decode accepts sizes over the chunk length", "if (o != off || size > L) return", "if (o != off) return"),
+]
+
 # run in the child: point the oracle package at the mutant, then the pins
 _CHILD = r"""
 import importlib.util, os, sys
@@ -84,6 +103,8 @@ sys.path.insert(0, root)
 import oracle
 if kind == "c":
     oracle._SRC, oracle._LIB = path, path[:-2] + ".so"
+elif kind == "lc":
+    oracle._LC_SRC, oracle._LC_LIB = path, path[:-2] + ".so"
 else:
     spec = importlib.util.spec_from_file_location("oracle.sz_ref", path)
     mod = importlib.util.module_from_spec(spec)
@@ -105,17 +126,18 @@ def _plant(src, old, new, dest):
 
 
 def _run(kind, path, workdir):
-    if kind == "c":
+    if kind in ("c", "lc"):
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-w", "-shared", "-fPIC", "-o", path[:-2] + ".so", path])
     env = dict(os.environ, HYPOTHESIS_STORAGE_DIRECTORY=os.path.join(workdir, ".hypothesis"))
-    r = subprocess.run([sys.executable, "-c", _CHILD, ROOT, kind, path, *PIN_FILES],
+    pins = LC_PIN_FILES if kind == "lc" else PIN_FILES
+    r = subprocess.run([sys.executable, "-c", _CHILD, ROOT, kind, path, *pins],
                        cwd=workdir, env=env, capture_output=True, text=True, timeout=600)
     return r.returncode, r.stdout[-2000:]
 
 
 def test_unmutated_copies_pass(tmp_path):
     """The harness itself: unchanged copies of both oracles pass every pin."""
-    for kind, src in (("c", C_SRC), ("py", PY_SRC)):
+    for kind, src in (("c", C_SRC), ("py", PY_SRC), ("lc", LC_SRC)):
         d = tmp_path / kind
         d.mkdir()
         dest = str(d / os.path.basename(src))
@@ -127,7 +149,7 @@ def test_unmutated_copies_pass(tmp_path):
 
 def test_every_mutant_is_caught(tmp_path):
     jobs = []
-    for kind, src, mutants in (("c", C_SRC, C_MUTANTS), ("py", PY_SRC, PY_MUTANTS)):
+    for kind, src, mutants in (("c", C_SRC, C_MUTANTS), ("py", PY_SRC, PY_MUTANTS), ("lc", LC_SRC, LC_MUTANTS)):
         for i, (name, old, new) in enumerate(mutants):
             d = tmp_path / f"{kind}{i}"
             d.mkdir()

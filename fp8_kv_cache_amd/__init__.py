@@ -1,8 +1,10 @@
 """Python binding of libsplitzip.so, the gfx950 lossless exponent codec for
-BF16 and FP8-E5M2 KV-cache tensors (SplitZip project page, "Abstract").
+BF16 and FP8-E5M2 KV-cache tensors (SplitZip project page, "Abstract"), and
+of the LC-style comparison codec in the same library (FastKVComp companion
+page, "Inside an LC-style pipeline").
 
-Thin ctypes marshalling over the C ABI declared in include/splitzip.h: the
-functions below carry the C names and arguments.  Pointer arguments accept
+Thin ctypes marshalling over the C ABI declared in include/splitzip.h and
+include/lc_codec.h: the functions below carry the C names and arguments.  Pointer arguments accept
 a torch tensor (its data_ptr()), a plain integer address or None; `stream`
 defaults to torch's current stream.  torch provides device memory and
 streams only -- every step of the codec runs in the library's HIP kernels.
@@ -23,6 +25,8 @@ __all__ = [
     "sz_histogram_sampled_batched",
     "sz_histogram_batched", "sz_build_codebook_batched", "sz_encode_batched", "sz_decode_batched",
     "sz_status_string", "check", "pointer_table", "library_path",
+    "lc_max_compressed_bytes", "lc_encode_workspace_bytes", "lc_encode_workspace_bytes_batched",
+    "lc_encode", "lc_decode", "lc_encode_batched", "lc_decode_batched",
 ]
 
 SZ_DTYPE_BF16 = 1
@@ -57,6 +61,13 @@ _SIGNATURES = {
     "sz_encode_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp, _u64, _vp, _vp, _u64, _vp]),
     "sz_decode_batched": (_i32, [_vp, _vp, _u32, _u64, _i32, _vp, _vp, _vp]),
     "sz_status_string": (ctypes.c_char_p, [_i32]),
+    "lc_max_compressed_bytes": (_u64, [_u64]),
+    "lc_encode_workspace_bytes": (_u64, [_u64]),
+    "lc_encode_workspace_bytes_batched": (_u64, [_u32, _u64]),
+    "lc_encode": (_i32, [_vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
+    "lc_decode": (_i32, [_vp, _u64, _u64, _vp, _vp, _vp]),
+    "lc_encode_batched": (_i32, [_vp, _u32, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
+    "lc_decode_batched": (_i32, [_vp, _vp, _u32, _u64, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(_lib, _name)
@@ -165,3 +176,34 @@ def sz_encode_batched(srcs, count, n, dtype, codebooks, dsts, dst_capacity, out_
 def sz_decode_batched(srcs, src_bytes, count, n, dtype, dsts, status=None, stream=None):
     return _lib.sz_decode_batched(_ptr(srcs), _ptr(src_bytes), count, n, dtype, _ptr(dsts),
                                   _ptr(status), _stream(stream))
+
+
+def lc_max_compressed_bytes(n):
+    return _lib.lc_max_compressed_bytes(n)
+
+
+def lc_encode_workspace_bytes(n):
+    return _lib.lc_encode_workspace_bytes(n)
+
+
+def lc_encode_workspace_bytes_batched(count, n):
+    return _lib.lc_encode_workspace_bytes_batched(count, n)
+
+
+def lc_encode(src, n, dst, dst_capacity, out_bytes, workspace, workspace_bytes, stream=None):
+    return _lib.lc_encode(_ptr(src), n, _ptr(dst), dst_capacity, _ptr(out_bytes), _ptr(workspace),
+                          workspace_bytes, _stream(stream))
+
+
+def lc_decode(src, src_bytes, n, dst, status=None, stream=None):
+    return _lib.lc_decode(_ptr(src), src_bytes, n, _ptr(dst), _ptr(status), _stream(stream))
+
+
+def lc_encode_batched(srcs, count, n, dsts, dst_capacity, out_bytes, workspace, workspace_bytes, stream=None):
+    return _lib.lc_encode_batched(_ptr(srcs), count, n, _ptr(dsts), dst_capacity, _ptr(out_bytes),
+                                  _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def lc_decode_batched(srcs, src_bytes, count, n, dsts, status=None, stream=None):
+    return _lib.lc_decode_batched(_ptr(srcs), _ptr(src_bytes), count, n, _ptr(dsts), _ptr(status),
+                                  _stream(stream))

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsplitzip.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "api.cpp", "lc_kernels.hip", "lc_api.cpp")]
 ARCH = "gfx950"
 
 

@@ -71,7 +71,9 @@ class BatchCodec:
         self.sizes = torch.zeros(count, dtype=torch.int64, device=device)
         self.ws_bytes = sz_encode_workspace_bytes_batched(count, n, dtype)
         self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
-        self.outputs = torch.empty(count, max(n, 1) * ELEMENT_BYTES[dtype], dtype=torch.uint8, device=device)
+        # rows start 16-byte aligned, as the C ABI requires of every output
+        row = -(-max(n, 1) * ELEMENT_BYTES[dtype] // 16) * 16
+        self.outputs = torch.empty(count, row, dtype=torch.uint8, device=device)
         self.status = torch.full((count,), -1, dtype=torch.int32, device=device)
         self.stream_ptrs = pointer_table([self.streams[i] for i in range(count)])
         self.output_ptrs = pointer_table([self.outputs[i] for i in range(count)])

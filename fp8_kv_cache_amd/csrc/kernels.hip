@@ -11,55 +11,12 @@
 // elements in each 1024/2048-element sub-chunk, so every global access of a
 // wave is one contiguous, 16-byte-per-lane transfer.  All arithmetic is
 // integer bit manipulation; there is no matrix-core work anywhere.
-#include "sz_internal.h"
+#include "device_common.h"
 
 namespace sz {
 namespace {
 
 // ---------------------------------------------------------------- helpers
-
-__device__ inline uint32_t lane_id() {
-    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-}
-
-__device__ inline uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
-
-// All tensors, streams and tables live in device global memory.  Casting
-// to address space 1 lets the compiler emit global_* instead of flat_*
-// memory instructions for pointers that were loaded from tables.
-#define SZ_GLOBAL __attribute__((address_space(1)))
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-template <typename T>
-__device__ inline SZ_GLOBAL T* gptr(T* p) {
-    return (SZ_GLOBAL T*)(p);
-}
-
-__device__ inline const SZ_GLOBAL uint8_t* src_of(const SrcRef& r, uint32_t t) {
-    return gptr(static_cast<const uint8_t*>(r.table ? gptr(r.table)[t] : r.single));
-}
-__device__ inline SZ_GLOBAL uint8_t* dst_of(const DstRef& r, uint32_t t) {
-    return gptr(static_cast<uint8_t*>(r.table ? gptr(r.table)[t] : r.single));
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP: four row
-// shifts build scans inside each 16-lane row, then two row broadcasts carry
-// row totals across the wave.
-__device__ inline uint32_t wave_scan_incl(uint32_t x) {
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);  // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);  // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);  // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-    return x;
-}
-
-__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
 
 // bit k*4 set iff nibble k of w equals 15 (the escape code)
 __device__ inline uint32_t escape_nibbles(uint32_t w) {

@@ -1,4 +1,4 @@
-"""The C-ABI library loads and exports every symbol include/splitzip.h
+"""The C-ABI library loads and exports every symbol that include/*.h
 declares; host-side argument checks and size functions (no GPU needed: none
 of these calls reaches a kernel launch)."""
 import ctypes
@@ -11,7 +11,8 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "splitzip.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -21,15 +22,18 @@ def sz():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sz_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:sz|lc)_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_codec_calls():
     names = declared_functions()
     for want in ("sz_histogram", "sz_build_codebook", "sz_encode", "sz_decode",
-                 "sz_max_compressed_bytes"):
+                 "sz_max_compressed_bytes", "lc_encode", "lc_decode", "lc_encode_batched",
+                 "lc_decode_batched", "lc_max_compressed_bytes"):
         assert want in names
 
 
@@ -42,13 +46,13 @@ def test_library_exports_every_declared_symbol(sz):
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     assert set(declared_functions()) <= exported
     # nothing else of ours leaks out of the library
-    assert all(not s.startswith("sz_") or s in declared_functions() for s in exported)
+    assert all(not s.startswith(("sz_", "lc_")) or s in declared_functions() for s in exported)
 
 
 def test_library_contains_no_cpu_codec_path(sz):
     """The product library links neither the oracle nor any CPU codec."""
     out = subprocess.run(["nm", "-D", sz.library_path()], capture_output=True, text=True).stdout
-    assert "szo_" not in out
+    assert "szo_" not in out and "lco_" not in out
 
 
 @pytest.mark.parametrize("dt", [1, 2])
@@ -112,3 +116,32 @@ def test_status_strings(sz):
     assert sz.sz_status_string(0) == "ok"
     assert sz.sz_status_string(3) == "corrupt stream"
     assert sz.sz_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("n", [0, 1, 15, 16, 16383, 16384, 16385, 100000, (1 << 31) - 1])
+def test_lc_max_bytes_matches_oracle(sz, n):
+    assert sz.lc_max_compressed_bytes(n) == oracle.lc_max_bytes(n)
+
+
+def test_lc_sizes_and_host_errors(sz):
+    assert sz.lc_max_compressed_bytes(1 << 31) == 0
+    assert sz.lc_encode_workspace_bytes(0) == 0
+    assert sz.lc_encode_workspace_bytes(16385) == 256
+    assert sz.lc_encode_workspace_bytes_batched(64, 1 << 24) == 64 * 1024 * 4
+    fake = 1 << 20                     # aligned, never dereferenced: every call fails on the host
+    n = 40000
+    cap = sz.lc_max_compressed_bytes(n)
+    ws = sz.lc_encode_workspace_bytes(n)
+    assert sz.lc_encode(fake, 1 << 31, fake, cap, None, fake, ws, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.lc_encode(fake + 8, n, fake, cap, None, fake, ws, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.lc_encode(fake, n, fake, cap - 1, None, fake, ws, stream=0) == sz.SZ_ERR_BUFFER_TOO_SMALL
+    assert sz.lc_encode(fake, n, fake, cap, None, fake, ws - 1, stream=0) == sz.SZ_ERR_BUFFER_TOO_SMALL
+    assert sz.lc_encode(fake, n, fake, cap, None, None, ws, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.lc_encode(fake, n, fake, cap, fake + 4, fake, ws, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.lc_decode(fake, 255, n, fake, stream=0) == sz.SZ_ERR_CORRUPT_STREAM
+    assert sz.lc_decode(None, cap, n, fake, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.lc_decode(fake, cap, n, fake, fake + 2, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.lc_encode_batched(fake, 0, n, fake, cap, None, fake, ws, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.lc_encode_batched(fake, 100, n, fake, cap, None, fake, ws, stream=0) == sz.SZ_ERR_BUFFER_TOO_SMALL
+    assert sz.lc_decode_batched(fake, fake, 0, n, fake, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.lc_decode_batched(fake, None, 1, n, fake, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT

@@ -16,6 +16,7 @@ input bytes (GB = 1e9).
 
 --mode transfer measures the layer-pipelined transfer (encode -> PCIe round
 trip through pinned host memory -> decode) against shipping the raw layers.
+--mode lc runs only the LC-style comparison codec (for profiling).
 """
 import argparse
 import concurrent.futures as cf
@@ -41,7 +42,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--mode", choices=["bench", "profile", "copy", "transfer"], default="bench")
+    p.add_argument("--mode", choices=["bench", "profile", "copy", "transfer", "lc"], default="bench")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--dtype", choices=["bf16", "e5m2"], default="bf16",
                    help="profile mode only: run the step on the cache as BF16 or quantised to FP8 E5M2")
@@ -181,6 +182,50 @@ def e5m2_cache(torch, xs):
             "encode_hbm_frac_two_pass": (2 * raw + stream) / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "decode_hbm_frac": (raw + stream) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "compression_ratio": raw / stream}
+
+
+def lc_comparison(torch, xs, reps=10):
+    """The LC-style byte-transform chain (TUPL8_1 -> BIT_8 -> RZE_2 on 16 KB
+    chunks; FastKVComp companion page, "Inside an LC-style pipeline") on the
+    same BF16 cache, and on a cache-sized tensor set of 4-bit codes (one
+    code per byte, uniform), the kind of data that chain was chosen for.
+    Each: batched encode and decode over 64 tensors, median HIP-event time,
+    ratio, and HBM fraction.  Encode reads the input twice (a size pass,
+    then a write pass that recomputes coded chunks or copies raw ones)."""
+    from fp8_kv_cache_amd.lc import LcBatch
+    out = {}
+    rng = np.random.default_rng(123)
+    sets = {"llama3-8b-kv-cache-bf16": [x.view(np.uint8).ravel() for x in xs],
+            "4-bit-codes-one-per-byte": [rng.integers(0, 16, xs[0].nbytes, dtype=np.uint8) for _ in range(len(xs))]}
+    for name, arrays in sets.items():
+        count, n = len(arrays), arrays[0].size
+        b = LcBatch(count, n)
+        b.set_inputs([torch.from_numpy(a).to("cuda") for a in arrays])
+        for _ in range(2):
+            b.encode()
+            b.decode()
+        torch.cuda.synchronize()
+        for i in range(count):
+            assert int(b.status[i]) == 0 and torch.equal(b.output(i), b._inputs[i]), (name, i)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for e in ev:
+            e[0].record()
+            b.encode()
+            e[1].record()
+            b.decode()
+            e[2].record()
+        torch.cuda.synchronize()
+        enc = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+        dec = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+        raw = count * n
+        stream = int(b.sizes.sum().item())
+        out[name] = {"raw_bytes": raw, "stream_bytes": stream, "compression_ratio": raw / stream,
+                     "encode_ms": enc, "decode_ms": dec,
+                     "encode_GBps": raw / (enc * 1e-3) / 1e9, "decode_GBps": raw / (dec * 1e-3) / 1e9,
+                     "encode_hbm_frac_two_pass": (2 * raw + stream) / (enc * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "decode_hbm_frac": (raw + stream) / (dec * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        del b
+    return out
 
 
 def graph_replay(torch, bc, steps, warmup):
@@ -345,6 +390,9 @@ def main():
     if args.mode == "transfer":
         transfer(torch, xs)
         return
+    if args.mode == "lc":
+        print(json.dumps({"mode": "lc", "lc_comparison": lc_comparison(torch, xs, reps=3)}))
+        return
     if args.dtype == "e5m2" and args.mode != "profile":
         print("--dtype e5m2 applies to --mode profile; the bench line always carries the E5M2 cache too",
               file=sys.stderr)
@@ -479,6 +527,7 @@ def main():
     if args.mode == "bench":
         result["single_read_encode"] = single_read_encode(torch, bc, raw_bytes, count)
         result["e5m2"] = e5m2_cache(torch, xs)
+        result["lc_comparison"] = lc_comparison(torch, xs)
         result["copy_ceiling"] = copy_ceiling(torch)
     if args.mode == "bench" and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(xs)

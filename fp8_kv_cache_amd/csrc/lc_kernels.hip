@@ -211,10 +211,11 @@ __device__ inline uint32_t rze_full(Lds& s, uint32_t tid) {
     __syncthreads();                                   // every plane word is in registers
     reinterpret_cast<uint32_t*>(s.buf)[tid] = flags;   // bitmap dword t covers words 32t..32t+31
     uint16_t* words = reinterpret_cast<uint16_t*>(s.buf + kBitmap);
-    uint32_t rank = base;
+    // word i's slot: the non-zero words before it, counted with a masked popcount
 #pragma unroll
     for (uint32_t i = 0; i < 32; ++i) {
-        if (flags & (1u << i)) words[rank++] = static_cast<uint16_t>(w[i / 2] >> (16 * (i & 1)));
+        if (flags & (1u << i))
+            words[base + __builtin_popcount(flags & ((1u << i) - 1u))] = static_cast<uint16_t>(w[i / 2] >> (16 * (i & 1)));
     }
     const uint32_t padded = static_cast<uint32_t>(align16(size));
     if (tid < 8 && size + 2 * tid < padded) reinterpret_cast<uint16_t*>(s.buf)[size / 2 + tid] = 0;
@@ -442,20 +443,36 @@ __global__ __launch_bounds__(kThreads) void k_lc_decode(DecodeArgs a) {
         mark_corrupt(a.status, t, tid);
         return;
     }
-    // read phase: the thread's words from the payload
+    // read phase: the thread's words from the payload; word i's slot is the
+    // number of non-zero words before it (a masked popcount)
     uint32_t w[16];
-    uint32_t at = nb + 2 * base;
+    if (L == kChunk) {                                  // words start 2-byte aligned after the 1024-byte bitmap
+        const uint16_t* words = reinterpret_cast<const uint16_t*>(s.buf + kBitmap);
 #pragma unroll
-    for (uint32_t d = 0; d < 16; ++d) {
-        uint32_t v = 0;
+        for (uint32_t d = 0; d < 16; ++d) {
+            uint32_t v = 0;
 #pragma unroll
-        for (uint32_t h = 0; h < 2; ++h) {
-            if (flags & (1u << (2 * d + h))) {
-                v |= (s.buf[at] | (static_cast<uint32_t>(s.buf[at + 1]) << 8)) << (16 * h);
-                at += 2;
+            for (uint32_t h = 0; h < 2; ++h) {
+                const uint32_t i = 2 * d + h;
+                if (flags & (1u << i))
+                    v |= static_cast<uint32_t>(words[base + __builtin_popcount(flags & ((1u << i) - 1u))]) << (16 * h);
             }
+            w[d] = v;
         }
-        w[d] = v;
+    } else {                                            // bitmap of any length: byte reads
+#pragma unroll
+        for (uint32_t d = 0; d < 16; ++d) {
+            uint32_t v = 0;
+#pragma unroll
+            for (uint32_t h = 0; h < 2; ++h) {
+                const uint32_t i = 2 * d + h;
+                if (flags & (1u << i)) {
+                    const uint32_t at = nb + 2 * (base + __builtin_popcount(flags & ((1u << i) - 1u)));
+                    v |= (s.buf[at] | (static_cast<uint32_t>(s.buf[at + 1]) << 8)) << (16 * h);
+                }
+            }
+            w[d] = v;
+        }
     }
     const uint32_t odd = (L & 1) ? s.buf[size - 1] : 0u;
     __syncthreads();

@@ -4,9 +4,10 @@
  * on the same KV-cache tensors as the exponent codec so that the two can
  * be compared on equal terms.
  *
- * Source: FastKVComp companion page, "Inside an LC-style pipeline": the
- * chosen stages are TUPL8_1, BIT_8 and RZE_2, the first two only rearrange
- * and the last removes zeros (the page draws this chain against nvCOMP).
+ * Source: FastKVComp companion page, "Inside an LC-style pipeline": a chain
+ * of TUPL8_1 and BIT_8, two stages that permute bits without changing the
+ * size, feeding RZE_2, which shrinks the data by leaving out zero words (the
+ * page sets this chain against nvCOMP).
  * The page gives no stage internals; the readings taken are:
  *
  *   L1 the input (n bytes, n < 2^31) is cut into chunks of 16384 bytes, the

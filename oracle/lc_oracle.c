@@ -4,8 +4,8 @@
  * baseline through ctypes.  It shares no code with the GPU library.
  *
  * Source: FastKVComp companion page, "Inside an LC-style pipeline": three
- * stages, TUPL8_1 then BIT_8 then RZE_2; the first two only move bits around
- * and the last one drops zeros.  The page gives no stage internals, so the
+ * stages, TUPL8_1 then BIT_8 (size-preserving bit permutations) then RZE_2
+ * (leaves out zero words).  The page gives no stage internals, so the
  * plainest reading of each stage name is taken (readings L1..L6), written
  * out below and in the header of include/lc_codec.h:
  *

@@ -1,7 +1,7 @@
 """Pins of the LC-style comparison codec's CPU oracle (oracle/lc_oracle.c).
 
 FastKVComp companion page, "Inside an LC-style pipeline": TUPL8_1 then BIT_8
-then RZE_2, the first two only rearranging bits, the last dropping zeros.
+(size-preserving bit permutations) then RZE_2 (zero words left out).
 The page prints no byte layout, so each stage is checked against its
 plainest reading built from numpy primitives (reshape/transpose for the
 tuple split, unpackbits/packbits for the bit planes, a boolean mask for the

@@ -397,7 +397,9 @@ __global__ __launch_bounds__(kThreads) void k_lc_write(EncodeArgs a) {
 
 // ----------------------------------------------------------------- decode
 
-__global__ __launch_bounds__(kThreads) void k_lc_decode(DecodeArgs a) {
+// 8 waves per SIMD (at most 64 VGPRs): a coded chunk's decode is a chain of
+// dependent steps, so more resident workgroups hide more of it.
+__global__ __launch_bounds__(kThreads, 8) void k_lc_decode(DecodeArgs a) {
     __shared__ Lds s;
     const uint32_t tid = threadIdx.x;
     const uint64_t C = chunks_of(a.n);

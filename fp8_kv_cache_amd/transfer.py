@@ -8,8 +8,12 @@ GPU, with the codec running much faster than the link.  The FastKVComp page
 encode + decode time is below the link time it saves.
 
 On one GPU the link is emulated by the PCIe path: every layer crosses
-device -> pinned host memory -> device through the copy engines, the way a
-prefill GPU's tensor would leave through a NIC and land on a decode GPU.
+device -> pinned host memory (the sending side) and pinned host memory ->
+device (the receiving side) through the copy engines, the way a prefill
+GPU's tensor leaves through one NIC and lands through another on a decode
+GPU.  The two sides have copy streams of their own, so while layer i is
+received, layer i+1 is already being sent (PCIe carries both directions at
+once, as two machines' NICs would).
 
   ship_raw         copies the raw layers over the link;
   ship_compressed  encodes layer i+1 while layer i's exact-size stream
@@ -53,17 +57,30 @@ class Link:
         self.raw_host = [torch.empty(raw, dtype=torch.uint8, pin_memory=True) for _ in range(count)]
         self.raw_landed = [torch.empty(raw, dtype=torch.uint8, device=device) for _ in range(count)]
         self.codec_stream = torch.cuda.Stream()
-        self.copy_stream = torch.cuda.Stream()
+        self.send_stream = torch.cuda.Stream()      # device -> pinned host
+        self.recv_stream = torch.cuda.Stream()      # pinned host -> device
+
+    def _cross(self, src, host, landed):
+        """Queue one crossing: send src into host memory, then receive it
+        into `landed` once sent.  Returns the event marking its arrival."""
+        with torch.cuda.stream(self.send_stream):
+            host.copy_(src, non_blocking=True)
+            sent = torch.cuda.Event()
+            sent.record(self.send_stream)
+        self.recv_stream.wait_event(sent)
+        with torch.cuda.stream(self.recv_stream):
+            landed.copy_(host, non_blocking=True)
+            done = torch.cuda.Event()
+            done.record(self.recv_stream)
+        return done
 
     def ship_raw(self, tensors):
         """Raw layers over the link; returns the landed copies (uint8 views)."""
         cur = torch.cuda.current_stream()
-        self.copy_stream.wait_stream(cur)
-        with torch.cuda.stream(self.copy_stream):
-            for t, host, landed in zip(tensors, self.raw_host, self.raw_landed):
-                host.copy_(t.view(torch.uint8).reshape(-1), non_blocking=True)
-                landed.copy_(host, non_blocking=True)
-        cur.wait_stream(self.copy_stream)
+        self.send_stream.wait_stream(cur)
+        for t, host, landed in zip(tensors, self.raw_host, self.raw_landed):
+            self._cross(t.view(torch.uint8).reshape(-1), host, landed)
+        cur.wait_stream(self.recv_stream)
         return self.raw_landed
 
     def ship_compressed(self, tensors):
@@ -72,9 +89,9 @@ class Link:
         before queueing that layer's exact-size copy; the GPU keeps encoding
         later layers meanwhile."""
         cur = torch.cuda.current_stream()
-        cs, xs = self.codec_stream, self.copy_stream
+        cs = self.codec_stream
         cs.wait_stream(cur)
-        xs.wait_stream(cur)
+        self.send_stream.wait_stream(cur)
         encoded, landed_events = [], []
 
         def queue_encode(t, L):
@@ -96,13 +113,8 @@ class Link:
             # copy-engine friendly length: a 4 KiB multiple (the stream buffer
             # holds at least that much; the bytes past the stream are unused)
             span = min(-(-nbytes // 4096) * 4096, L.capacity)
-            xs.wait_event(encoded[i])
-            with torch.cuda.stream(xs):
-                L.host[:span].copy_(L.stream[:span], non_blocking=True)
-                L.landed[:span].copy_(L.host[:span], non_blocking=True)
-                done = torch.cuda.Event()
-                done.record(xs)
-            landed_events.append((done, nbytes))
+            self.send_stream.wait_event(encoded[i])
+            landed_events.append((self._cross(L.stream[:span], L.host[:span], L.landed[:span]), nbytes))
 
         # encode layer i, then put layer i-1 on the link, so the link starts
         # right after the first layer instead of after every encode is queued

@@ -22,6 +22,11 @@ bool usable(const void* p) { return p != nullptr && aligned16(p); }
 
 sz_status from_hip(hipError_t e) { return e == hipSuccess ? SZ_OK : SZ_ERR_HIP; }
 
+// every launch's workgroup count (at most one per format block) stays below 2^31
+bool grid_ok(uint32_t count, uint64_t n) {
+    return static_cast<uint64_t>(count) * ((n + kBlockElems - 1) / kBlockElems) < (uint64_t(1) << 31);
+}
+
 uint64_t workspace_bytes(uint32_t count, uint64_t n) { return workspace_bytes_for(count, n); }
 
 sz_status histogram_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint32_t stride,
@@ -95,7 +100,7 @@ SZ_EXPORT sz_status sz_histogram(const void* d_src, uint64_t n, sz_dtype dtype, 
 
 SZ_EXPORT sz_status sz_histogram_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
                                          sz_dtype dtype, uint64_t* d_hists, hipStream_t stream) {
-    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !usable(d_hists) || !usable(d_srcs))
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n) || !usable(d_hists) || !usable(d_srcs))
         return SZ_ERR_INVALID_ARGUMENT;
     return histogram_impl(SrcRef{d_srcs, nullptr}, count, n, dtype, 1, d_hists, stream);
 }
@@ -110,7 +115,7 @@ SZ_EXPORT sz_status sz_histogram_sampled(const void* d_src, uint64_t n, sz_dtype
 SZ_EXPORT sz_status sz_histogram_sampled_batched(const void* const* d_srcs, uint32_t count, uint64_t n,
                                                  sz_dtype dtype, uint32_t block_stride, uint64_t* d_hists,
                                                  hipStream_t stream) {
-    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || block_stride == 0 || !usable(d_hists) ||
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n) || block_stride == 0 || !usable(d_hists) ||
         !usable(d_srcs))
         return SZ_ERR_INVALID_ARGUMENT;
     return histogram_impl(SrcRef{d_srcs, nullptr}, count, n, dtype, block_stride, d_hists, stream);
@@ -148,7 +153,7 @@ SZ_EXPORT sz_status sz_encode_batched(const void* const* d_srcs, uint32_t count,
                                       sz_dtype dtype, const uint8_t* d_codebooks, void* const* d_dsts,
                                       uint64_t dst_capacity, uint64_t* d_out_bytes, void* d_workspace,
                                       uint64_t workspace_bytes_given, hipStream_t stream) {
-    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !usable(d_srcs) || !usable(d_codebooks) ||
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n) || !usable(d_srcs) || !usable(d_codebooks) ||
         !usable(d_dsts) || (d_out_bytes && (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)))
         return SZ_ERR_INVALID_ARGUMENT;
     if (dst_capacity < sz_max_compressed_bytes(n, dtype)) return SZ_ERR_BUFFER_TOO_SMALL;
@@ -173,7 +178,7 @@ SZ_EXPORT sz_status sz_decode(const void* d_src, uint64_t src_bytes, uint64_t n,
 SZ_EXPORT sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_bytes,
                                       uint32_t count, uint64_t n, sz_dtype dtype, void* const* d_dsts,
                                       int32_t* d_status, hipStream_t stream) {
-    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !usable(d_srcs) || !usable(d_src_bytes) ||
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n) || !usable(d_srcs) || !usable(d_src_bytes) ||
         !usable(d_dsts) || (d_status && (reinterpret_cast<uintptr_t>(d_status) & 3u)))
         return SZ_ERR_INVALID_ARGUMENT;
     return decode_impl(SrcRef{d_srcs, nullptr}, d_src_bytes, 0, count, n, dtype, DstRef{d_dsts, nullptr},

@@ -126,8 +126,10 @@ sz_status sz_decode(const void* d_src, uint64_t src_bytes, uint64_t n, sz_dtype 
 
 /* ---- Batched forms: T tensors of the same n and dtype in one launch per
  * phase (one codebook per tensor, as for a KV cache's layer tensors).  The
- * d_*s pointer tables are device arrays of T device pointers.  Results are
- * byte-identical to T single-tensor calls. ---- */
+ * d_*s pointer tables are device arrays of T device pointers, each pointing
+ * to a 16-byte aligned buffer.  Results are byte-identical to T
+ * single-tensor calls.  T * ceil(n / 4096) must stay below 2^31, else
+ * SZ_ERR_INVALID_ARGUMENT. ---- */
 
 uint64_t sz_encode_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype dtype);
 

@@ -145,3 +145,10 @@ def test_lc_sizes_and_host_errors(sz):
     assert sz.lc_encode_batched(fake, 100, n, fake, cap, None, fake, ws, stream=0) == sz.SZ_ERR_BUFFER_TOO_SMALL
     assert sz.lc_decode_batched(fake, fake, 0, n, fake, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
     assert sz.lc_decode_batched(fake, None, 1, n, fake, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+
+
+def test_batched_grid_limit(sz):
+    """count x ceil(n/4096) must stay below 2^31 (one workgroup per block at most)."""
+    n = (1 << 32) - 1                       # 2^20 blocks per tensor
+    assert sz.sz_histogram_batched(FAKE, 2048, n, 1, FAKE, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.sz_decode_batched(FAKE, FAKE, 2048, n, 1, FAKE, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT

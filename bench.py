@@ -473,6 +473,8 @@ def main():
     sizes = bc.sizes.cpu().numpy()
     stream_bytes = int(sizes.sum())
     ratio = raw_bytes / stream_bytes
+    # E, the escape count, sits at bytes 16..23 of every stream header
+    escapes = int(bc.streams[:, 16:24].contiguous().view(torch.int64).sum().item())
     eager = {"ms_per_step": med(step_ms), "value": raw_bytes / (med(step_ms) * 1e-3) / 1e9, "wall_s_timed": wall,
              "phase_ms": {"histogram": med(hist_ms), "codebook": med(cb_ms), "encode": med(enc_ms),
                           "decode": med(dec_ms)}}
@@ -539,6 +541,8 @@ def main():
         "decode_hbm_frac": (raw_bytes + stream_bytes) / (med(dec_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "compression_ratio": ratio,
         "stream_bytes": stream_bytes,
+        "escapes": escapes,
+        "escape_fraction": escapes / (count * n),
         "phase_ms": {"histogram": med(hist_ms), "codebook": med(cb_ms), "encode": med(enc_ms),
                      "decode": med(dec_ms)},
         "calls": per_call,

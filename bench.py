@@ -370,10 +370,13 @@ def transfer(torch, xs):
     raw_ms = timed(lambda: link.ship_raw(dev))
     for t, landed in zip(dev, link.raw_landed):
         assert torch.equal(landed, t.view(torch.uint8).reshape(-1))
-    comp_ms = timed(lambda: link.ship_compressed(dev))
-    assert all(st == 0 for st in link.statuses())
-    for t, L in zip(dev, link.layers):
-        assert torch.equal(L.output, t.view(torch.uint8).reshape(-1))
+    by_group = {}
+    for group in (1, 4, 8, 16):
+        by_group[group] = timed(lambda: link.ship_compressed(dev, group=group))
+        assert all(st == 0 for st in link.statuses())
+        for t, L in zip(dev, link.layers):
+            assert torch.equal(L.output, t.view(torch.uint8).reshape(-1))
+    comp_ms = by_group[8]                               # the default grouping
     comp_bytes = link.compressed_bytes()
 
     # codec cost without overlap: the batched hot path over the same layers
@@ -385,6 +388,7 @@ def transfer(torch, xs):
     print(json.dumps({
         "mode": "transfer", "layers": count, "raw_bytes": raw_bytes, "compressed_bytes": comp_bytes,
         "raw_ms": raw_ms, "compressed_pipelined_ms": comp_ms, "speedup": raw_ms / comp_ms,
+        "layers_per_group": 8, "compressed_ms_by_group": by_group,
         "link": "device -> pinned host (send stream) then pinned host -> device (receive stream) per layer, "
                 "both directions busy at once (PCIe copy engines)",
         "link_GBps_measured": link_gbps,

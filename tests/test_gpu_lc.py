@@ -188,3 +188,40 @@ def test_codes_full_size(sz):
     assert np.array_equal(stream.cpu().numpy(), oracle.lc_encode(x))
     y, status = sz.lc.decompress(stream, n)
     assert status == 0 and np.array_equal(y.cpu().numpy(), x)
+
+
+def test_graph_replay_matches_eager(sz):
+    """The batched LC encode and decode captured in one HIP graph and replayed
+    three times, with eager work and a synchronisation between replays:
+    every replay reproduces the eager streams, sizes, statuses and outputs."""
+    n = 2 * CHUNK + 555
+    xs = [content(k, n, seed=60 + i) for i, k in enumerate(["mixed", "codes", "random"])]
+    say("lc graph replay", n)
+    b = sz.lc.LcBatch(len(xs), n)
+    b.set_inputs([torch.from_numpy(x).to("cuda") for x in xs])
+    b.encode()
+    b.decode()
+    torch.cuda.synchronize()
+    ref_sizes = b.sizes.clone()
+    ref = [b.stream(i).clone() for i in range(len(xs))]
+    for i, x in enumerate(xs):
+        assert np.array_equal(ref[i].cpu().numpy(), oracle.lc_encode(x)), i
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.encode()
+        b.decode()
+    for replay in range(3):
+        b.streams.zero_()
+        b.sizes.zero_()
+        b.outputs.zero_()
+        b.status.fill_(-1)
+        noise = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(noise)
+        assert torch.equal(b.sizes, ref_sizes), replay
+        for i, x in enumerate(xs):
+            assert int(b.status[i]) == 0, (replay, i)
+            assert torch.equal(b.stream(i), ref[i]), (replay, i)
+            assert np.array_equal(b.output(i).cpu().numpy(), x), (replay, i)

@@ -337,24 +337,29 @@ def test_e5m2_config_full_size(sz):
     assert 1.14 <= ratio <= 8 / 7
 
 
-def test_transfer_pipeline_round_trip(sz):
+@pytest.mark.parametrize("dt,group", [(BF16, 1), (BF16, 4), (E5M2, 8)])
+def test_transfer_pipeline_round_trip(sz, dt, group):
     """Layers shipped compressed over the device -> pinned host -> device link
-    land bit-exact, and so do the raw copies."""
+    (in groups of `group` layers per send wait) land bit-exact, with the
+    oracle's stream sizes, and so do the raw copies."""
     from fp8_kv_cache_amd.transfer import Link
-    say("transfer pipeline")
+    say("transfer pipeline", dt, group)
     xs = [kvsynth.llama_kv(i // 2, i % 2, shape=(256, 8, 128)) for i in range(6)]
+    if dt == E5M2:
+        xs = [kvsynth.e5m2_of(x) for x in xs]
+    view = np.uint16 if dt == BF16 else np.uint8
     dev = [to_dev(x) for x in xs]
-    link = Link(len(xs), xs[0].size)
-    out = link.ship_compressed(dev)
+    link = Link(len(xs), xs[0].size, dtype=dt)
+    out = link.ship_compressed(dev, group=group)
     torch.cuda.synchronize()
     assert link.statuses() == [0] * len(xs)
-    assert link.compressed_bytes() == sum(oracle.encode(x, BF16).size for x in xs)
+    assert link.compressed_bytes() == sum(oracle.encode(x, dt).size for x in xs)
     for x, o in zip(xs, out):
-        assert np.array_equal(o.cpu().numpy().view(np.uint16), x)
+        assert np.array_equal(o.cpu().numpy().view(view), x)
     raw = link.ship_raw(dev)
     torch.cuda.synchronize()
     for x, o in zip(xs, raw):
-        assert np.array_equal(o.cpu().numpy().view(np.uint16), x)
+        assert np.array_equal(o.cpu().numpy().view(view), x)
 
 
 @pytest.mark.parametrize("dt", [BF16, E5M2])

@@ -187,15 +187,20 @@ def e5m2_cache(torch, xs):
 def lc_comparison(torch, xs, reps=10):
     """The LC-style byte-transform chain (TUPL8_1 -> BIT_8 -> RZE_2 on 16 KB
     chunks; FastKVComp companion page, "Inside an LC-style pipeline") on the
-    same BF16 cache, and on a cache-sized tensor set of 4-bit codes (one
-    code per byte, uniform), the kind of data that chain was chosen for.
+    same BF16 cache, on its E5M2-quantised form, and on a cache-sized tensor
+    set of 4-bit codes (one code per byte, uniform), the kind of data that
+    chain was chosen for.
     Each: batched encode and decode over 64 tensors, median HIP-event time,
     ratio, and HBM fraction.  Encode reads the input twice (a size pass,
     then a write pass that recomputes coded chunks or copies raw ones)."""
     from fp8_kv_cache_amd.lc import LcBatch
     out = {}
     rng = np.random.default_rng(123)
+    import kvsynth
+    with cf.ThreadPoolExecutor(8) as pool:
+        e5m2 = list(pool.map(kvsynth.e5m2_of, xs))
     sets = {"llama3-8b-kv-cache-bf16": [x.view(np.uint8).ravel() for x in xs],
+            "llama3-8b-kv-cache-e5m2": e5m2,
             "4-bit-codes-one-per-byte": [rng.integers(0, 16, xs[0].nbytes, dtype=np.uint8) for _ in range(len(xs))]}
     for name, arrays in sets.items():
         count, n = len(arrays), arrays[0].size

@@ -499,7 +499,7 @@ def main():
     # tensors): its kernels, algorithmic bytes, and live event time.
     calls = {
         "sz_histogram_batched": (["k_fill_u64", f"k_histogram<{tag}>"], raw_bytes, med(hist_ms)),
-        "sz_encode_batched": ([f"k_encode<{tag}>", f"k_offsets<{tag}>", f"k_scatter<{tag}>"],
+        "sz_encode_batched": ([f"k_encode<{tag}>", f"k_offsets_scatter<{tag}>"],
                               raw_bytes + stream_bytes, med(enc_ms)),
         "sz_decode_batched": (["k_fill_i32", f"k_decode<{tag}>"], stream_bytes + raw_bytes, med(dec_ms)),
     }

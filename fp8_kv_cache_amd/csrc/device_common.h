@@ -46,6 +46,20 @@ __device__ inline uint32_t wave_scan_incl(uint32_t x) {
     return x;
 }
 
+// Exclusive prefix of x over a 256-thread (4-wave) workgroup; `total` gets
+// the sum.  `sums` is 4 words of LDS.  Contains a barrier; callers barrier
+// again before reusing `sums`.
+__device__ inline uint32_t block_scan_excl(uint32_t x, uint32_t tid, uint32_t* sums, uint32_t& total) {
+    const uint32_t incl = wave_scan_incl(x);
+    const uint32_t w = tid / 64;
+    if ((tid & 63) == 63) sums[w] = incl;
+    __syncthreads();
+    uint32_t base = 0;
+    for (uint32_t k = 0; k < w; ++k) base += sums[k];
+    total = sums[0] + sums[1] + sums[2] + sums[3];
+    return base + incl - x;
+}
+
 // byte select from the pair (hi, lo): selector bytes 0..3 pick lo's bytes,
 // 4..7 hi's, 0x0C gives zero
 __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {

@@ -327,15 +327,18 @@ __global__ __launch_bounds__(256) void k_codebook(CodebookArgs a) {
 
 // ----------------------------------------------------------------- encode
 //
-// Three launches, none of which waits on another workgroup (so block ids
-// come straight from blockIdx and no ordering tickets are needed):
+// Launches of which none waits on another workgroup (so block ids come
+// straight from blockIdx and no ordering tickets are needed):
 //   k_encode   one wave per 4096-element block: sign|mantissa and code
 //              planes, the block's escape count, and its escape bytes
 //              staged at block-local ranks in the workspace;
-//   k_offsets  one workgroup per tensor: exclusive scan of the block counts
-//              into the stream's offset table, then the header;
-//   k_scatter  copies each block's staged escapes to their place in the
-//              stream's escape region.
+//   k_offsets_scatter  one thread per block: its offset (the counts of all
+//              earlier blocks), the offset table, the escape bytes copied to
+//              their place in the stream's escape region, and the header --
+//              for tensors of up to 2^16 blocks; beyond that
+//   k_offsets  one workgroup per tensor scans the counts into the offset
+//              table and writes the header, and
+//   k_scatter  copies each block's staged escapes.
 
 // Header (64 bytes), the zero padding after the offset table and the
 // stream size; `lane` is the calling thread's index (0..63 used).
@@ -646,6 +649,50 @@ __global__ __launch_bounds__(kThreads) void k_scatter(EncodeArgs a) {
         for (uint32_t k = 0; k < 16; ++k)
             if (i + k < cnt) to[i + k] = static_cast<uint8_t>(w[k / 4] >> (8 * (k & 3)));
     }
+}
+
+// k_offsets and k_scatter in one launch, for tensors of at most
+// kFusedGroups x 256 blocks.  Workgroup g of tensor t takes blocks
+// [256g, 256g + 256): its base offset is the sum of the counts of every
+// earlier block, read directly (fewer than 256 x 256 reads, from L2), so no
+// workgroup waits for another; an in-group scan gives each block its offset,
+// which it writes to the table before copying its staged escapes.  The last
+// workgroup of a tensor writes the header.
+constexpr uint64_t kFusedGroups = 256;
+
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_offsets_scatter(EncodeArgs a) {
+    __shared__ uint32_t s_sums[kWavesPerGroup];
+    const Layout L = layout_of(a.n, DT);
+    const uint32_t groups = static_cast<uint32_t>((L.blocks + kThreads - 1) / kThreads);
+    const uint32_t t = blockIdx.x / groups, g = blockIdx.x - t * groups, tid = threadIdx.x;
+    const SZ_GLOBAL uint32_t* counts = gptr(a.counts) + static_cast<uint64_t>(t) * L.blocks;
+    uint32_t before = 0;
+    for (uint32_t k = tid; k < g * kThreads; k += kThreads) before += counts[k];
+    uint32_t base;
+    block_scan_excl(before, tid, s_sums, base);
+    __syncthreads();
+    const uint64_t b = static_cast<uint64_t>(g) * kThreads + tid;
+    const uint32_t cnt = b < L.blocks ? counts[b] : 0u;
+    uint32_t in_group;
+    const uint32_t off = base + block_scan_excl(cnt, tid, s_sums, in_group);
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+    if (b < L.blocks) {
+        ((SZ_GLOBAL uint32_t*)(dst + 64))[b] = off;
+        const SZ_GLOBAL u32x4* from =
+            (const SZ_GLOBAL u32x4*)(gptr(a.staging) + (static_cast<uint64_t>(t) * L.blocks + b) * kBlockElems);
+        SZ_GLOBAL uint8_t* to = dst + L.esc_at + off;
+        for (uint32_t i = 0; i < cnt; i += 16) {
+            const u32x4 v = from[i / 16];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (uint32_t k = 0; k < 16; ++k)
+                if (i + k < cnt) to[i + k] = static_cast<uint8_t>(w[k / 4] >> (8 * (k & 3)));
+        }
+    }
+    if (g == groups - 1)
+        write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, base + in_group,
+                     a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid);
 }
 
 // n == 0: a header-only stream per tensor
@@ -1064,8 +1111,14 @@ void enqueue_encode(const EncodeArgs& a, hipStream_t s) {
     const uint32_t scatter_groups = grid_for(blocks, kThreads);
     if (full) hipLaunchKernelGGL(k_encode<DT>, dim3(grid_for(full, kWavesPerGroup)), dim3(kThreads), 0, s, a);
     if (a.n % kBlockElems) hipLaunchKernelGGL(k_encode_tail<DT>, dim3(a.count), dim3(kWaveSize), 0, s, a);
-    hipLaunchKernelGGL(k_offsets<DT>, dim3(a.count), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_scatter<DT>, dim3(scatter_groups), dim3(kThreads), 0, s, a);
+    const uint64_t groups = (L.blocks + kThreads - 1) / kThreads;     // 256-block groups per tensor
+    if (groups <= kFusedGroups) {
+        hipLaunchKernelGGL(k_offsets_scatter<DT>, dim3(static_cast<uint32_t>(a.count * groups)), dim3(kThreads), 0,
+                           s, a);
+    } else {
+        hipLaunchKernelGGL(k_offsets<DT>, dim3(a.count), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_scatter<DT>, dim3(scatter_groups), dim3(kThreads), 0, s, a);
+    }
 }
 
 hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s) {

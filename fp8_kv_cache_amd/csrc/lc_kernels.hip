@@ -29,6 +29,8 @@ using sz::u32x4;
 using sz::uniform;
 using sz::wave_scan_incl;
 
+constexpr auto block_scan = sz::block_scan_excl;
+
 constexpr uint32_t kThreads = 256;
 constexpr uint32_t kRowStride = 520;            // LDS stride of a 512-byte input row: 8 spare bytes
 constexpr uint32_t kLds = 32 * kRowStride;      // 16640 bytes: 32 padded rows, or one plane image
@@ -40,19 +42,6 @@ struct Lds {
 };
 
 // ---------------------------------------------------------------- helpers
-
-// exclusive prefix of x over the workgroup; `total` gets the sum.  Ends with
-// the partial sums readable; callers barrier before reusing `sums`.
-__device__ inline uint32_t block_scan(uint32_t x, uint32_t tid, uint32_t* sums, uint32_t& total) {
-    const uint32_t incl = wave_scan_incl(x);
-    const uint32_t w = tid / 64;
-    if ((tid & 63) == 63) sums[w] = incl;
-    __syncthreads();
-    uint32_t base = 0;
-    for (uint32_t k = 0; k < w; ++k) base += sums[k];
-    total = sums[0] + sums[1] + sums[2] + sums[3];
-    return base + incl - x;
-}
 
 // Transposes the 8x8 bit matrix of every byte lane of L: afterwards bit a of
 // byte j of L[k] is what bit k of byte j of L[a] was.

@@ -279,11 +279,15 @@ def test_llama_kv_cache_full_size(sz):
     assert 1.32 < ratio < 4 / 3
 
 
-def test_stress_full_size(sz):
+@pytest.mark.parametrize("n", [1 << 28, (1 << 28) + 12345])
+def test_stress_full_size(sz, n):
     """Escape-heavy stress: 2^28 BF16 values (Cauchy x 2^U(-60,60) plus 1%
-    special patterns), drawn on the device, checked against the oracle."""
-    say("stress full: generating")
-    x_dev = kvsynth.stress_device("cuda")
+    special patterns), drawn on the device, checked against the oracle.
+    2^28 elements is the largest tensor whose escape offsets and scatter run
+    as one launch (256 groups of 256 blocks); 2^28 + 12345 takes the
+    two-launch path."""
+    say("stress full: generating", n)
+    x_dev = kvsynth.stress_device("cuda", n=n)
     x = x_dev.cpu().numpy().view(np.uint16)
     assert len(np.unique((x >> 7) & 0xFF)) > 40
     say("stress full: encode")

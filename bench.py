@@ -6,17 +6,24 @@ tensors of [8192 tokens, 8 KV heads, 128 head_dim] = 64 x 2^23 elements
 per-channel lognormal scale, 4 x20 outlier channels per K head).
 
 One step = the whole hot path over the whole cache: exponent histograms ->
-codebooks -> encode -> decode, each one batched launch over the 64 tensors,
+codebooks -> encode -> decode, each one batched call over the 64 tensors,
 inputs resident in HBM before the timed region.  Throughput counts raw
-input bytes (GB = 1e9).
+input bytes (GB = 1e9).  The timed steps replay one HIP graph of the four
+calls (checked against the eager step); per-call times, the roofline and
+the phase breakdown come from HIP events around eager calls.  The same JSON
+line also carries cold-cache steps, the E5M2-quantised cache, single-read
+encode variants, the LC-style comparison codec, the runtime's copy rate and
+the CPU oracle's rate on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-                    [--mode bench|profile|copy|transfer] [--no-cpu-baseline]
+                    [--mode bench|profile|copy|transfer|lc] [--no-cpu-baseline]
                     [--dtype bf16|e5m2]   (profile mode)
 
---mode transfer measures the layer-pipelined transfer (encode -> PCIe round
-trip through pinned host memory -> decode) against shipping the raw layers.
---mode lc runs only the LC-style comparison codec (for profiling).
+--mode profile   a short eager run for rocprofv3 (BF16 or E5M2 cache);
+--mode copy      a 1 GiB copy, for scaling rocprofv3's byte counters;
+--mode transfer  the layer-pipelined transfer (encode -> PCIe send and
+                 receive -> decode) against shipping the raw layers;
+--mode lc        only the LC-style comparison codec.
 """
 import argparse
 import concurrent.futures as cf

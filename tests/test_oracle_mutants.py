@@ -45,6 +45,8 @@ C_MUTANTS = [
     ("code nibbles high first", "(uint8_t)(code << (4 * (i % 2)))", "(uint8_t)(code << (4 * (1 - i % 2)))"),
     ("offsets taken after a block's first element", "if (i % SZO_BLOCK == 0) put_u32",
      "if (i % SZO_BLOCK == 1) put_u32"),
+    ("offsets drift by one per block", "(i / SZO_BLOCK), (uint32_t)escapes);",
+     "(i / SZO_BLOCK), (uint32_t)(escapes + i / SZO_BLOCK));"),
     ("format block of 2048 elements", "#define SZO_BLOCK 4096u", "#define SZO_BLOCK 2048u"),
     ("header region not padded", "return round256(64u + 4u * n_blocks(n));",
      "return 64u + 4u * n_blocks(n);"),

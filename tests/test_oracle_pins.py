@@ -122,7 +122,9 @@ def test_histogram_matches_float_semantics(dt, name):
     bits = _inputs(dt)[name]
     _, exponent, _ = float_fields(bits, dt)
     expected = np.bincount(exponent, minlength=256)
-    assert np.array_equal(oracle.histogram(bits, dt), expected)
+    got = oracle.histogram(bits, dt)
+    assert np.array_equal(got, expected)
+    assert int(got.sum()) == bits.size
     assert np.array_equal(np.array(sz_ref.histogram(bits[:3000], dt)),
                           np.bincount(exponent[:3000], minlength=256))
 
@@ -133,7 +135,7 @@ def test_planes_match_float_semantics(dt, name):
     n = bits.size
     sign, exponent, mant = float_fields(bits, dt)
     stream = oracle.encode(bits, dt)
-    sm, code_bytes, esc, _ = planes(stream, n, dt)
+    sm, code_bytes, esc, offs = planes(stream, n, dt)
     if dt == BF16:
         got_sign, got_mant = sm.astype(np.int64) >> 7, sm.astype(np.int64) & 0x7F
     else:
@@ -151,6 +153,9 @@ def test_planes_match_float_semantics(dt, name):
     cb = np.array(chosen)
     assert np.array_equal(cb[codes[~escaped]], exponent[~escaped])
     assert np.array_equal(esc.astype(np.int64), exponent[escaped])
+    # offsets: exclusive running sum of each 4096-element block's escapes
+    per_block = np.add.reduceat(escaped.astype(np.int64), np.arange(0, n, 4096))
+    assert np.array_equal(offs.astype(np.int64), np.concatenate([[0], np.cumsum(per_block)[:-1]]))
 
 
 @pytest.mark.parametrize("name", _golden.names())
@@ -250,10 +255,14 @@ def test_uniform_exponents_reach_the_bound(dt, domain):
 
 @pytest.mark.parametrize("dt", [BF16, E5M2])
 def test_constant_tensor_has_no_escapes(dt):
-    x = np.full(10000, 0x3F80 if dt == BF16 else 0x3C, np.uint16 if dt == BF16 else np.uint8)
+    x = np.full(10240, 0x3F80 if dt == BF16 else 0x3C, np.uint16 if dt == BF16 else np.uint8)
     stream = oracle.encode(x, dt)
     f = oracle.stream_fields(stream)
     assert f["escapes"] == 0
+    # closed form with no escapes and n a multiple of 512 (no plane padding):
+    # C = H + S + n/2, i.e. H + 1.5n for BF16 and H + 0.875n for E5M2
+    header = _align(64 + 4 * 3)
+    assert stream.size == header + (x.size if dt == BF16 else 3 * x.size // 8) + x.size // 2
     # 1.0 first, then the zero-count values in ascending order
     first = 127 if dt == BF16 else 15
     assert f["codebook"][0] == first

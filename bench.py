@@ -6,14 +6,17 @@ tensors of [8192 tokens, 8 KV heads, 128 head_dim] = 64 x 2^23 elements
 per-channel lognormal scale, 4 x20 outlier channels per K head).
 
 One step = the whole hot path over the whole cache: exponent histograms ->
-codebooks -> encode -> decode, each one batched call over the 64 tensors,
-inputs resident in HBM before the timed region.  Throughput counts raw
-input bytes (GB = 1e9).  The timed steps replay one HIP graph of the four
-calls (checked against the eager step); per-call times, the roofline and
-the phase breakdown come from HIP events around eager calls.  The same JSON
-line also carries cold-cache steps, the E5M2-quantised cache, single-read
-encode variants, the LC-style comparison codec, the runtime's copy rate and
-the CPU oracle's rate on the host.
+codebooks -> encode -> decode, as two batched calls over the 64 tensors
+(sz_compress_batched: histogram, codebook and encode fused in one launch;
+sz_decode_batched), inputs resident in HBM before the timed region.
+Throughput counts raw input bytes (GB = 1e9).  The timed steps replay one
+HIP graph of the two calls (checked against the eager step, whose streams
+are checked against the three separate calls'); per-call times, the
+roofline and the phase breakdown come from HIP events around eager calls.
+The same JSON line also carries the step as the three separate calls,
+cold-cache steps, the E5M2-quantised cache, single-read encode variants,
+the LC-style comparison codec, the runtime's copy rate and the CPU
+oracle's rate on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
                     [--mode bench|profile|copy|transfer|lc] [--no-cpu-baseline]
@@ -147,7 +150,8 @@ def single_read_encode(torch, bc, raw_bytes, count):
 
 def e5m2_cache(torch, xs):
     """The same cache quantised to FP8 E5M2 (1 byte per element): encode
-    (histogram + codebook + encode) and decode throughput, ratio."""
+    (the fused histogram + codebook + encode call, and the three separate
+    calls for reference) and decode throughput, ratio."""
     import fp8_kv_cache_amd as sz
     from fp8_kv_cache_amd.codec import BatchCodec
     import kvsynth
@@ -178,15 +182,32 @@ def e5m2_cache(torch, xs):
         return [float(np.median([e[a].elapsed_time(e[a + 1]) for e in ev])) for a in range(4)]
 
     hist_ms, cb_ms, code_ms, dec_ms = timed()
-    enc_ms = hist_ms + cb_ms + code_ms
+    enc3_ms = hist_ms + cb_ms + code_ms
     for i in range(count):
         assert int(bc.status[i]) == 0 and torch.equal(bc.output(i), bc._inputs[i]), i
     stream = int(bc.sizes.sum().item())
+    ref = [bc.stream(i).clone() for i in range(count)]
+    # the fused call: same streams, its own time
+    for _ in range(2):
+        bc.compress_fused()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+    for e in ev:
+        e[0].record()
+        bc.compress_fused()
+        e[1].record()
+    torch.cuda.synchronize()
+    enc_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    assert (bc.fused_status.cpu().numpy() == 0).all()
+    for i in range(count):
+        assert torch.equal(bc.stream(i), ref[i]), i
     return {"workload": "llama3-8b-kv-cache quantised to FP8 E5M2", "raw_bytes": raw,
             "encode_ms": enc_ms, "decode_ms": dec_ms,
-            "phase_ms": {"histogram": hist_ms, "codebook": cb_ms, "encode": code_ms, "decode": dec_ms},
+            "phase_ms": {"compress": enc_ms, "decode": dec_ms},
+            "three_call_phase_ms": {"histogram": hist_ms, "codebook": cb_ms, "encode": code_ms, "total": enc3_ms},
             "encode_GBps": raw / (enc_ms * 1e-3) / 1e9, "decode_GBps": raw / (dec_ms * 1e-3) / 1e9,
             "encode_hbm_frac_two_pass": (2 * raw + stream) / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "encode_hbm_frac_strict": (raw + stream) / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "decode_hbm_frac": (raw + stream) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "compression_ratio": raw / stream}
 
@@ -240,24 +261,28 @@ def lc_comparison(torch, xs, reps=10):
     return out
 
 
-def graph_replay(torch, bc, steps, warmup):
-    """The whole step (histogram -> codebook -> encode -> decode, batched)
-    captured once in a HIP graph and replayed: the eager step's kernels with
-    the same arguments (the library only launches kernels, and clears with
-    kernels, so the calls capture as they are), without the host's launch
-    gaps between them.  Outputs are cleared with eager kernels before the
-    replays, and every replayed stream, size, status and decoded tensor is
-    checked against the eager step's.  Returns the median and minimum step
-    time, and the median of cold steps, each preceded by a 512 MB write that
-    evicts the last-level cache."""
+def graph_replay(torch, bc, steps, warmup, fused=True):
+    """The whole step captured once in a HIP graph and replayed: the fused
+    compress (histogram, codebook and encode in one launch) then decode, or
+    (fused=False) the three separate calls then decode.  The graph holds the
+    eager step's kernels with the same arguments (the library only launches
+    kernels, and clears with kernels, so the calls capture as they are),
+    without the host's launch gaps between them.  Outputs are cleared with
+    eager kernels before the replays, and every replayed stream, size,
+    status and decoded tensor is checked against the eager step's.  Returns
+    the median and minimum step time, and the median of cold steps, each
+    preceded by a 512 MB write that evicts the last-level cache."""
     count = bc.count
     ref_sizes = bc.sizes.clone()
     ref_streams = [bc.stream(i).clone() for i in range(count)]
     whole = torch.cuda.CUDAGraph()
     with torch.cuda.graph(whole):
-        bc.histogram()
-        bc.build_codebooks()
-        bc.encode()
+        if fused:
+            bc.compress_fused()
+        else:
+            bc.histogram()
+            bc.build_codebooks()
+            bc.encode()
         bc.decompress()
     stream = torch.cuda.current_stream()
     bc.outputs.zero_()
@@ -288,6 +313,7 @@ def graph_replay(torch, bc, steps, warmup):
     torch.cuda.synchronize()
     del scratch
     assert torch.equal(bc.sizes, ref_sizes)
+    assert not fused or (bc.fused_status.cpu().numpy() == 0).all()
     for i in range(count):
         assert int(bc.status[i]) == 0 and torch.equal(bc.output(i), bc._inputs[i]), i
         assert torch.equal(bc.stream(i), ref_streams[i]), i
@@ -449,7 +475,7 @@ def main():
     bc.set_inputs([torch.from_numpy(x.view(np.int16) if tag == "bf16" else x).to("cuda") for x in xs])
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def three_call_step(ev=None):
         if ev:
             ev[0].record(stream)
         bc.histogram()
@@ -465,56 +491,95 @@ def main():
         if ev:
             ev[4].record(stream)
 
+    def fused_step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        bc.compress_fused()
+        if ev:
+            ev[1].record(stream)
+        bc.decompress()
+        if ev:
+            ev[2].record(stream)
+
     for _ in range(args.warmup):
-        step()
+        three_call_step()
     torch.cuda.synchronize()
-    # correctness of the timed configuration: every tensor round-trips
+    # correctness of the timed configuration: every tensor round-trips, and
+    # the fused call reproduces the separate calls' histograms, codebooks
+    # and streams byte for byte
     for i in range(count):
         assert int(bc.status[i]) == 0 and torch.equal(bc.output(i), bc._inputs[i]), i
+    ref = (bc.sizes.clone(), bc.hists.clone(), bc.codebooks.clone(), [bc.stream(i).clone() for i in range(count)])
+    for _ in range(max(args.warmup, 1)):
+        fused_step()
+    torch.cuda.synchronize()
+    assert (bc.fused_status.cpu().numpy() == 0).all()
+    assert torch.equal(bc.sizes, ref[0]) and torch.equal(bc.hists, ref[1]) and torch.equal(bc.codebooks, ref[2])
+    for i in range(count):
+        assert torch.equal(bc.stream(i), ref[3][i]), i
+        assert int(bc.status[i]) == 0 and torch.equal(bc.output(i), bc._inputs[i]), i
+    del ref
 
     steps = args.steps if args.mode == "bench" else min(args.steps, 3)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    def ms(a, b):
-        return [events[k][a].elapsed_time(events[k][b]) for k in range(steps)]
-
-    hist_ms, cb_ms, enc_ms, dec_ms, step_ms = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4), ms(0, 4)
     med = lambda v: float(np.median(v))
+
+    def timed(fn, marks):
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            fn(events[k])
+        torch.cuda.synchronize()
+        return events, time.perf_counter() - t0
+
+    ev3, wall3 = timed(three_call_step, 5)
+    evf, wall = timed(fused_step, 3)
+    ms = lambda ev, a, b: [e[a].elapsed_time(e[b]) for e in ev]
+    hist_ms, cb_ms, enc_ms, dec3_ms, step3_ms = ms(ev3, 0, 1), ms(ev3, 1, 2), ms(ev3, 2, 3), ms(ev3, 3, 4), ms(ev3, 0, 4)
+    comp_ms, dec_ms, step_ms = ms(evf, 0, 1), ms(evf, 1, 2), ms(evf, 0, 2)
     sizes = bc.sizes.cpu().numpy()
     stream_bytes = int(sizes.sum())
     ratio = raw_bytes / stream_bytes
     # E, the escape count, sits at bytes 16..23 of every stream header
     escapes = int(bc.streams[:, 16:24].contiguous().view(torch.int64).sum().item())
     eager = {"ms_per_step": med(step_ms), "value": raw_bytes / (med(step_ms) * 1e-3) / 1e9, "wall_s_timed": wall,
-             "phase_ms": {"histogram": med(hist_ms), "codebook": med(cb_ms), "encode": med(enc_ms),
-                          "decode": med(dec_ms)}}
-    graph = None
+             "phase_ms": {"compress": med(comp_ms), "decode": med(dec_ms)}}
+    graph = graph3 = None
     if args.mode == "bench":
-        graph = graph_replay(torch, bc, steps, args.warmup)
+        graph = graph_replay(torch, bc, steps, args.warmup, fused=True)
         graph["value"] = raw_bytes / (graph["ms_per_step"] * 1e-3) / 1e9
         graph["value_cold"] = raw_bytes / (graph["ms_per_step_cold"] * 1e-3) / 1e9
+        graph3 = graph_replay(torch, bc, steps, args.warmup, fused=False)
+        graph3["value"] = raw_bytes / (graph3["ms_per_step"] * 1e-3) / 1e9
         # the headline step is the graph-replayed one; per-call times stay eager
         step_ms, wall = [graph["ms_per_step"]], graph["wall_s_timed"]
 
     # Per API call (each call is one batched launch sequence over all 64
-    # tensors): its kernels, algorithmic bytes, and live event time.
-    calls = {
-        "sz_histogram_batched": (["k_fill_u64", f"k_histogram<{tag}>"], raw_bytes, med(hist_ms)),
-        "sz_encode_batched": ([f"k_encode<{tag}>", f"k_offsets_scatter<{tag}>"],
-                              raw_bytes + stream_bytes, med(enc_ms)),
-        "sz_decode_batched": (["k_fill_i32", f"k_decode<{tag}>"], stream_bytes + raw_bytes, med(dec_ms)),
-    }
-    per_call = {}
-    for name, (kernels, alg_bytes, t_ms) in calls.items():
+    # tensors): its kernels, algorithmic bytes, and live event time.  The
+    # histogram, codebook and encode need the whole histogram before any
+    # element is coded, so the input reaches the CUs twice: 2 raw + stream
+    # bytes for a compress (the fused call serves the second read mostly
+    # from the last-level cache; "frac_strict" counts one read).
+    def call_row(kernels, alg_bytes, t_ms, strict_bytes=None):
         gbps = alg_bytes / (t_ms * 1e-3) / 1e9
-        per_call[name] = {"kernels": kernels, "ms": t_ms, "algorithmic_bytes": alg_bytes,
-                          "achieved_GBps": gbps, "frac": gbps / HBM_PEAK_GBPS}
+        row = {"kernels": kernels, "ms": t_ms, "algorithmic_bytes": alg_bytes, "achieved_GBps": gbps,
+               "frac": gbps / HBM_PEAK_GBPS}
+        if strict_bytes is not None:
+            row["frac_strict"] = strict_bytes / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS
+        return row
+
+    per_call = {
+        "sz_compress_batched": call_row(["k_fill_i32", "k_fill_u64", f"k_compress<{tag}>", f"k_offsets_scatter<{tag}>"],
+                                        2 * raw_bytes + stream_bytes, med(comp_ms), raw_bytes + stream_bytes),
+        "sz_decode_batched": call_row(["k_fill_i32", f"k_decode<{tag}>"], stream_bytes + raw_bytes, med(dec_ms)),
+    }
+    three_calls = {
+        "sz_histogram_batched": call_row(["k_fill_u64", f"k_histogram<{tag}>"], raw_bytes, med(hist_ms)),
+        "sz_build_codebook_batched": call_row([f"k_codebook<{tag}>"], 0, med(cb_ms)),
+        "sz_encode_batched": call_row([f"k_encode<{tag}>", f"k_offsets_scatter<{tag}>"], raw_bytes + stream_bytes,
+                                      med(enc_ms)),
+        "sz_decode_batched": call_row(["k_fill_i32", f"k_decode<{tag}>"], stream_bytes + raw_bytes, med(dec3_ms)),
+    }
     dominant = max(per_call, key=lambda k: per_call[k]["ms"])
     roofline = {
         "bound": "hbm", "achieved": per_call[dominant]["achieved_GBps"], "peak": HBM_PEAK_GBPS,
@@ -523,13 +588,7 @@ def main():
         "kernel": f"{dominant}: " + " + ".join(per_call[dominant]["kernels"]),
     }
 
-    enc_total_ms = med([h + c + e for h, c, e in zip(hist_ms, cb_ms, enc_ms)])
-    encode_gbps = raw_bytes / (enc_total_ms * 1e-3) / 1e9
-    decode_gbps = raw_bytes / (med(dec_ms) * 1e-3) / 1e9
-    # encode phase needs the whole histogram before coding: input read twice
-    enc_two_pass = (2 * raw_bytes + stream_bytes) / (enc_total_ms * 1e-3) / 1e9
-    enc_strict = (raw_bytes + stream_bytes) / (enc_total_ms * 1e-3) / 1e9
-
+    comp_med = med(comp_ms)
     step_med = med(step_ms)
     result = {
         "metric": "encode & decode GB/s (raw input bytes) + % HBM roofline; compression ratio",
@@ -546,29 +605,37 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"llama3-8b-kv-cache-{tag}", "tensors": count, "elements_per_tensor": n,
                    "shape": list(SHAPE), "raw_bytes": raw_bytes, "codebook": "per layer tensor"},
-        "value_definition": "raw bytes / (histogram + codebook + encode + decode) per step",
-        "timing": ("each timed step replays one HIP graph of the four batched calls; per-call times "
-                   "(phase_ms, calls, roofline) come from HIP events around eager calls; the eager step is "
-                   "under 'eager'") if graph else "eager launches, HIP events around each call",
-        "encode_GBps": encode_gbps,
-        "decode_GBps": decode_gbps,
-        "encode_hbm_frac_two_pass": enc_two_pass / HBM_PEAK_GBPS,
-        "encode_hbm_frac_strict": enc_strict / HBM_PEAK_GBPS,
-        "decode_hbm_frac": (raw_bytes + stream_bytes) / (med(dec_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "value_definition": "raw bytes / (histogram + codebook + encode + decode) per step; histogram, codebook and "
+                            "encode run as one fused batched call (sz_compress_batched), decode as another",
+        "timing": ("each timed step replays one HIP graph of the two batched calls; per-call times (phase_ms, "
+                   "calls, roofline) come from HIP events around eager calls; the eager step is under 'eager'")
+                  if graph else "eager launches, HIP events around each call",
+        "encode_GBps": raw_bytes / (comp_med * 1e-3) / 1e9,
+        "decode_GBps": raw_bytes / (med(dec_ms) * 1e-3) / 1e9,
+        "encode_hbm_frac_two_pass": per_call["sz_compress_batched"]["frac"],
+        "encode_hbm_frac_strict": per_call["sz_compress_batched"]["frac_strict"],
+        "decode_hbm_frac": per_call["sz_decode_batched"]["frac"],
         "compression_ratio": ratio,
         "stream_bytes": stream_bytes,
         "escapes": escapes,
         "escape_fraction": escapes / (count * n),
-        "phase_ms": {"histogram": med(hist_ms), "codebook": med(cb_ms), "encode": med(enc_ms),
-                     "decode": med(dec_ms)},
+        "phase_ms": {"compress": comp_med, "decode": med(dec_ms)},
         "calls": per_call,
         "roofline": roofline,
+        "three_call": {
+            "what": "the same step as the three separate calls + decode (same bytes)",
+            "ms_per_step_eager": med(step3_ms), "wall_s_timed": wall3,
+            "phase_ms": {"histogram": med(hist_ms), "codebook": med(cb_ms), "encode": med(enc_ms),
+                         "decode": med(dec3_ms)},
+            "calls": three_calls,
+        },
         "wall_s_timed": wall,
         "gpu": torch.cuda.get_device_name(0),
     }
     if graph:
         result["eager"] = eager
         result["graph"] = graph
+        result["three_call"]["graph"] = graph3
     if args.mode == "bench":
         result["single_read_encode"] = single_read_encode(torch, bc, raw_bytes, count)
         result["e5m2"] = e5m2_cache(torch, xs)

@@ -19,11 +19,13 @@ import torch  # load torch's HIP runtime first; the library binds to it
 
 __all__ = [
     "SZ_DTYPE_BF16", "SZ_DTYPE_FP8_E5M2", "SZ_OK", "SZ_ERR_INVALID_ARGUMENT",
-    "SZ_ERR_BUFFER_TOO_SMALL", "SZ_ERR_CORRUPT_STREAM", "SZ_ERR_HIP", "SzError",
+    "SZ_ERR_BUFFER_TOO_SMALL", "SZ_ERR_CORRUPT_STREAM", "SZ_ERR_HIP", "SZ_ERR_TIMEOUT", "SzError",
     "sz_max_compressed_bytes", "sz_encode_workspace_bytes", "sz_encode_workspace_bytes_batched",
     "sz_histogram", "sz_histogram_sampled", "sz_build_codebook", "sz_encode", "sz_decode",
     "sz_histogram_sampled_batched",
     "sz_histogram_batched", "sz_build_codebook_batched", "sz_encode_batched", "sz_decode_batched",
+    "sz_compress_workspace_bytes", "sz_compress_workspace_bytes_batched", "sz_compress",
+    "sz_compress_batched", "sz_compress_spin_limit",
     "sz_status_string", "check", "pointer_table", "library_path",
     "lc_max_compressed_bytes", "lc_encode_workspace_bytes", "lc_encode_workspace_bytes_batched",
     "lc_encode", "lc_decode", "lc_encode_batched", "lc_decode_batched",
@@ -36,6 +38,7 @@ SZ_ERR_INVALID_ARGUMENT = 1
 SZ_ERR_BUFFER_TOO_SMALL = 2
 SZ_ERR_CORRUPT_STREAM = 3
 SZ_ERR_HIP = 4
+SZ_ERR_TIMEOUT = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
@@ -60,6 +63,11 @@ _SIGNATURES = {
     "sz_build_codebook_batched": (_i32, [_vp, _u32, _i32, _vp, _vp]),
     "sz_encode_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp, _u64, _vp, _vp, _u64, _vp]),
     "sz_decode_batched": (_i32, [_vp, _vp, _u32, _u64, _i32, _vp, _vp, _vp]),
+    "sz_compress_workspace_bytes": (_u64, [_u64, _i32]),
+    "sz_compress_workspace_bytes_batched": (_u64, [_u32, _u64, _i32]),
+    "sz_compress": (_i32, [_vp, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp]),
+    "sz_compress_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp]),
+    "sz_compress_spin_limit": (_u32, [_u32]),
     "sz_status_string": (ctypes.c_char_p, [_i32]),
     "lc_max_compressed_bytes": (_u64, [_u64]),
     "lc_encode_workspace_bytes": (_u64, [_u64]),
@@ -176,6 +184,31 @@ def sz_encode_batched(srcs, count, n, dtype, codebooks, dsts, dst_capacity, out_
 def sz_decode_batched(srcs, src_bytes, count, n, dtype, dsts, status=None, stream=None):
     return _lib.sz_decode_batched(_ptr(srcs), _ptr(src_bytes), count, n, dtype, _ptr(dsts),
                                   _ptr(status), _stream(stream))
+
+
+def sz_compress_workspace_bytes(n, dtype):
+    return _lib.sz_compress_workspace_bytes(n, dtype)
+
+
+def sz_compress_workspace_bytes_batched(count, n, dtype):
+    return _lib.sz_compress_workspace_bytes_batched(count, n, dtype)
+
+
+def sz_compress(src, n, dtype, hist, codebook, dst, dst_capacity, out_bytes, status, workspace,
+                workspace_bytes, stream=None):
+    return _lib.sz_compress(_ptr(src), n, dtype, _ptr(hist), _ptr(codebook), _ptr(dst), dst_capacity,
+                            _ptr(out_bytes), _ptr(status), _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def sz_compress_batched(srcs, count, n, dtype, hists, codebooks, dsts, dst_capacity, out_bytes, status,
+                        workspace, workspace_bytes, stream=None):
+    return _lib.sz_compress_batched(_ptr(srcs), count, n, dtype, _ptr(hists), _ptr(codebooks), _ptr(dsts),
+                                    dst_capacity, _ptr(out_bytes), _ptr(status), _ptr(workspace),
+                                    workspace_bytes, _stream(stream))
+
+
+def sz_compress_spin_limit(polls):
+    return _lib.sz_compress_spin_limit(polls)
 
 
 def lc_max_compressed_bytes(n):

@@ -6,7 +6,8 @@ patterns, dtype int16/bfloat16) or bytes (E5M2, dtype uint8/float8_e5m2).
 import torch
 
 from . import (SZ_DTYPE_BF16, SZ_DTYPE_FP8_E5M2, check, pointer_table, sz_build_codebook, sz_histogram_sampled,
-               sz_histogram_sampled_batched,
+               sz_histogram_sampled_batched, sz_compress, sz_compress_batched, sz_compress_workspace_bytes,
+               sz_compress_workspace_bytes_batched,
                sz_build_codebook_batched, sz_decode, sz_decode_batched, sz_encode, sz_encode_batched,
                sz_encode_workspace_bytes, sz_encode_workspace_bytes_batched, sz_histogram,
                sz_histogram_batched, sz_max_compressed_bytes)
@@ -46,6 +47,26 @@ def compress(x, dtype, codebook=None, stream=None, block_stride=1):
     return dst[:size], hist, codebook
 
 
+def compress_fused(x, dtype, stream=None):
+    """Histogram, codebook and encode of one tensor in one launch
+    (sz_compress).  Returns (stream bytes, histogram int64[256], codebook
+    uint8[16], device status); the results equal compress()'s."""
+    dev = x.device
+    n = x.numel()
+    hist = torch.empty(256, dtype=torch.int64, device=dev)
+    codebook = torch.empty(16, dtype=torch.uint8, device=dev)
+    cap = sz_max_compressed_bytes(n, dtype)
+    dst = torch.empty(cap, dtype=torch.uint8, device=dev)
+    out_bytes = torch.zeros(1, dtype=torch.int64, device=dev)
+    status = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    ws_bytes = sz_compress_workspace_bytes(n, dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    check(sz_compress(x if n else None, n, dtype, hist, codebook, dst, cap, out_bytes, status, ws, ws_bytes,
+                      stream), "sz_compress")
+    size = int(out_bytes.item())
+    return dst[:size], hist, codebook, int(status.item())
+
+
 def decompress(stream_bytes, n, dtype, src_bytes=None, stream=None):
     """Decode one stream.  Returns (raw elements tensor, device status)."""
     dev = stream_bytes.device
@@ -69,8 +90,11 @@ class BatchCodec:
         self.codebooks = torch.zeros(count, 16, dtype=torch.uint8, device=device)
         self.streams = torch.empty(count, cap, dtype=torch.uint8, device=device)
         self.sizes = torch.zeros(count, dtype=torch.int64, device=device)
+        # the fused call's workspace holds the encode workspace at its start
         self.ws_bytes = sz_encode_workspace_bytes_batched(count, n, dtype)
-        self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.fused_ws_bytes = sz_compress_workspace_bytes_batched(count, n, dtype)
+        self.workspace = torch.empty(max(self.fused_ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.fused_status = torch.full((count,), -1, dtype=torch.int32, device=device)
         # rows start 16-byte aligned, as the C ABI requires of every output
         row = -(-max(n, 1) * ELEMENT_BYTES[dtype] // 16) * 16
         self.outputs = torch.empty(count, row, dtype=torch.uint8, device=device)
@@ -105,6 +129,13 @@ class BatchCodec:
         self.histogram(stream)
         self.build_codebooks(stream)
         self.encode(stream)
+
+    def compress_fused(self, stream=None):
+        """Same histograms, codebooks and streams as compress(), in one
+        launch (sz_compress_batched); per-tensor status in fused_status."""
+        check(sz_compress_batched(self.src_ptrs, self.count, self.n, self.dtype, self.hists, self.codebooks,
+                                  self.stream_ptrs, self.capacity, self.sizes, self.fused_status, self.workspace,
+                                  self.fused_ws_bytes, stream), "sz_compress_batched")
 
     def decompress(self, stream=None):
         check(sz_decode_batched(self.stream_ptrs, self.sizes, self.count, self.n, self.dtype,

@@ -158,23 +158,29 @@ __device__ inline void count_one(char* lds, uint32_t u, uint32_t lane_bytes) {
     }
 }
 
-template <uint32_t DT>
+template <uint32_t DT, uint32_t NT = kThreads>
 __device__ inline void hist_clear(uint32_t* bins, uint32_t tid) {
     constexpr uint32_t kWords = HistLds<DT>::kWords;
-    static_assert(kWords % 4 == 0, "cleared in 16-byte stores");
+    static_assert(kWords % (4 * NT) == 0, "cleared in 16-byte stores");
 #pragma unroll
-    for (uint32_t i = tid * 4; i < kWords; i += kThreads * 4)
+    for (uint32_t i = tid * 4; i < kWords; i += NT * 4)
         *reinterpret_cast<uint4*>(bins + i) = make_uint4(0, 0, 0, 0);
 }
 
 // Fold the copies and add the sums to the tensor's u64 histogram.  Every
-// thread of the workgroup calls it, after a barrier; `unpaired` is the
-// number of elements the workgroup counted one at a time.  Rotating the
-// start keeps the lanes of a wave on distinct banks.
-template <uint32_t DT>
+// thread of the NT-thread workgroup calls it, after a barrier; the first
+// 256 do the folding.  `unpaired` is the number of phantom zero exponents
+// the workgroup counted (E5M2: elements counted one at a time as the pair
+// (e, 0); both types: zero padding counted past the end of a tensor); they
+// are taken off bin 0.  Rotating the start keeps the lanes of a wave on
+// distinct banks.
+template <uint32_t DT, uint32_t NT = kThreads>
 __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64_t* hist, uint32_t unpaired) {
+    static_assert(NT >= 256, "one folding thread per bin");
+    const bool folds = NT == 256 || tid < 256;
     if constexpr (DT == kDtypeBF16) {
-        uint32_t sum = 0;
+        if (!folds) return;
+        uint32_t sum = tid == 0 ? 0u - unpaired : 0u;
 #pragma unroll 8
         for (uint32_t j = 0; j < 32; ++j) sum += bins[tid * 32 + ((j + tid) & 31u)];
         if (sum) __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
@@ -187,7 +193,7 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
         for (uint32_t k = 0; k < 2; ++k) {
 #pragma unroll 8
             for (uint32_t j = 0; j < 16; ++j) {
-                const uint32_t w = bins[(2 * tid + k) * 16 + ((j + tid) & 15u)];
+                const uint32_t w = folds ? bins[(2 * tid + k) * 16 + ((j + tid) & 15u)] : 0u;
                 c[2 * k] += w & 0xFFFFu;
                 c[2 * k + 1] += w >> 16;
             }
@@ -200,7 +206,7 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
         if (both) atomicAdd(bins + (tid >> 3), both);
 #pragma unroll
         for (uint32_t k = 0; k < 4; ++k)
-            if (c[k]) atomicAdd(bins + ((4 * tid + k) & 31u), c[k]);
+            if (c[k]) atomicAdd(bins + ((4 * tid + k) & 31u), c[k]);   // c[k] = 0 when !folds
         __syncthreads();
         const uint32_t sum = tid < 32 ? bins[tid] - (tid == 0 ? unpaired : 0u) : 0u;
         if (sum)
@@ -209,34 +215,25 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
     }
 }
 
-// Each workgroup counts one contiguous chunk of one tensor.  Every pass a
-// lane reads one 16-byte vector (the wave one contiguous kilobyte); eight
-// passes are in flight per iteration.  The grid oversubscribes the GPU, so
-// one workgroup's fold-and-flush tail overlaps other workgroups' streaming.
-template <uint32_t DT>
-__global__ __launch_bounds__(kThreads) void k_histogram(HistArgs a) {
+// Count elements [begin, end) of src into the workgroup's LDS copies (NT
+// threads).  Every pass a lane reads one 16-byte vector (a wave one
+// contiguous kilobyte); eight passes are in flight per iteration.  Returns
+// the number of phantom zero exponents to take off bin 0 (E5M2 counts the
+// ragged end as pairs (e, 0); BF16 counts it exactly).
+template <uint32_t DT, uint32_t NT>
+__device__ inline uint32_t count_range(char* lds, const SZ_GLOBAL uint8_t* src, uint64_t begin, uint64_t end,
+                                       uint32_t tid) {
     using G = Geometry<DT>;
     constexpr uint32_t kVecElems = 16 / G::kElemBytes;       // elements per 16-byte vector
-    constexpr uint32_t kTile = kThreads * kVecElems;          // elements per pass
+    constexpr uint32_t kTile = NT * kVecElems;                // elements per pass
     constexpr uint32_t kPasses = 8;
-    __shared__ uint32_t bins[HistLds<DT>::kWords];
-    const uint32_t tid = threadIdx.x;
-    const uint32_t t = blockIdx.x / a.groups;
-    const uint32_t g = blockIdx.x - t * a.groups;
-    char* lds = reinterpret_cast<char*>(bins);
-    hist_clear<DT>(bins, tid);
-    __syncthreads();
-
-    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
-    const uint64_t begin = static_cast<uint64_t>(g) * a.chunk;
-    const uint64_t end = begin + a.chunk < a.n ? begin + a.chunk : a.n;
     const uint32_t copy4 = hist_lane_bytes<DT>(tid);
     uint64_t base = begin;
     for (; base + kPasses * kTile <= end; base += kPasses * kTile) {
         const SZ_GLOBAL u32x4* q = (const SZ_GLOBAL u32x4*)(src + base * G::kElemBytes);
         u32x4 v[kPasses];
 #pragma unroll
-        for (uint32_t p = 0; p < kPasses; ++p) v[p] = q[p * kThreads + tid];
+        for (uint32_t p = 0; p < kPasses; ++p) v[p] = q[p * NT + tid];
 #pragma unroll
         for (uint32_t p = 0; p < kPasses; ++p) {
             count_dword<DT>(lds, v[p].x, copy4);
@@ -245,11 +242,28 @@ __global__ __launch_bounds__(kThreads) void k_histogram(HistArgs a) {
             count_dword<DT>(lds, v[p].w, copy4);
         }
     }
-    // ragged end of the chunk: element-wise guarded reads
-    for (uint64_t i = base + tid; i < end; i += kThreads)
+    // ragged end of the range: element-wise guarded reads
+    for (uint64_t i = base + tid; i < end; i += NT)
         count_one<DT>(lds, DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i], copy4);
+    return DT == kDtypeE5M2 ? static_cast<uint32_t>(end - base) : 0u;
+}
+
+// Each workgroup counts one contiguous chunk of one tensor.  The grid
+// oversubscribes the GPU, so one workgroup's fold-and-flush tail overlaps
+// other workgroups' streaming.
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads) void k_histogram(HistArgs a) {
+    __shared__ uint32_t bins[HistLds<DT>::kWords];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t t = blockIdx.x / a.groups;
+    const uint32_t g = blockIdx.x - t * a.groups;
+    hist_clear<DT>(bins, tid);
     __syncthreads();
-    hist_flush<DT>(bins, tid, gptr(a.hists) + 256ull * t, static_cast<uint32_t>(end - base));
+    const uint64_t begin = static_cast<uint64_t>(g) * a.chunk;
+    const uint64_t end = begin + a.chunk < a.n ? begin + a.chunk : a.n;
+    const uint32_t phantom = count_range<DT, kThreads>(reinterpret_cast<char*>(bins), src_of(a.src, t), begin, end, tid);
+    __syncthreads();
+    hist_flush<DT>(bins, tid, gptr(a.hists) + 256ull * t, phantom);
 }
 
 // Histogram of a block sample: only format blocks b with b % stride == 0
@@ -297,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void k_histogram_sampled(HistArgs a) {
         }
     }
     __syncthreads();
-    hist_flush<DT>(bins, tid, gptr(a.hists) + 256ull * t, unpaired);
+    hist_flush<DT>(bins, tid, gptr(a.hists) + 256ull * t, DT == kDtypeE5M2 ? unpaired : 0u);
 }
 
 // --------------------------------------------------------------- codebook
@@ -435,22 +449,20 @@ __device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, 
     sm[2] = (f[5] >> 4) | (f[6] << 8) | (f[7] << 20);
 }
 
-// One block.  kFull: the block holds 4096 elements, so loads and stores
-// need no per-lane guards.
+// A wave's share of block b: sub-chunk j, lane l holds elements
+// [4096b + j * 64 * kLaneElems + l * kLaneElems, ... + kLaneElems).
+template <uint32_t DT>
+using BlockRegs = uint32_t[Geometry<DT>::kSubs][Geometry<DT>::kInWords];
+
+// Load block b into registers.  kFull: the block holds 4096 elements, so
+// the loads need no per-lane guards; otherwise elements at or beyond n
+// read as zero.
 template <uint32_t DT, bool kFull>
-__device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32_t t, uint64_t b,
-                                    uint64_t flat, uint32_t lane, uint32_t* tbl_words) {
+__device__ inline void load_block(const SZ_GLOBAL uint8_t* src, uint64_t n, uint64_t b, uint32_t lane,
+                                  BlockRegs<DT>& d) {
     using G = Geometry<DT>;
     constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
-    constexpr uint32_t kSmWords = G::kSmWords;
-
-    // codebook entry of this lane first, then the block's input
-    const SZ_GLOBAL uint8_t* cb = gptr(a.codebooks) + 16ull * t;
-    const uint32_t mine = lane < kCodes ? cb[lane] : 0xFFFFu;
-    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
-    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
     const uint64_t blk0 = b * kBlockElems;
-    uint32_t d[G::kSubs][G::kInWords];
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; ++j) {
         const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
@@ -462,10 +474,23 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
                 d[j][4 * v] = x.x; d[j][4 * v + 1] = x.y; d[j][4 * v + 2] = x.z; d[j][4 * v + 3] = x.w;
             }
         } else {
-            load_lane<DT>(src, elem0, a.n, d[j]);
+            load_lane<DT>(src, elem0, n, d[j]);
         }
     }
-    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Encode block b from its registers into stream dst: planes, the block's
+// escape count and its staged escape bytes (flat = the block's index over
+// all tensors).  `mine` is codebook entry cb[lane] for lanes below 15 (any
+// value above 255 elsewhere).
+template <uint32_t DT, bool kFull>
+__device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b,
+                                     uint64_t flat, uint32_t lane, uint32_t* tbl_words, uint32_t mine,
+                                     const BlockRegs<DT>& d) {
+    using G = Geometry<DT>;
+    constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
+    constexpr uint32_t kSmWords = G::kSmWords;
+    const uint64_t blk0 = b * kBlockElems;
 
     // Code of every exponent value: the lowest c with cb[c] == v, else 15.
     uint8_t* tbl = reinterpret_cast<uint8_t*>(tbl_words);
@@ -569,6 +594,21 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
             }
         }
     }
+}
+
+// One block with the codebook given in memory: the lane's codebook entry
+// first, then the block's input, then the encode.
+template <uint32_t DT, bool kFull>
+__device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32_t t, uint64_t b,
+                                    uint64_t flat, uint32_t lane, uint32_t* tbl_words) {
+    const SZ_GLOBAL uint8_t* cb = gptr(a.codebooks) + 16ull * t;
+    const uint32_t mine = lane < kCodes ? cb[lane] : 0xFFFFu;
+    const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+    BlockRegs<DT> d;
+    load_block<DT, kFull>(src, a.n, b, lane, d);
+    __builtin_amdgcn_sched_barrier(0);
+    encode_loaded<DT, kFull>(a, L, dst, b, flat, lane, tbl_words, mine, d);
 }
 
 // Full blocks only: wave i of the grid takes the i-th full block in
@@ -702,6 +742,237 @@ __global__ void k_encode_empty(EncodeArgs a) {
     const Layout L = layout_of(0, DT);
     SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
     write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, 0, a.out_bytes ? gptr(a.out_bytes) + t : nullptr, lane_id());
+}
+
+// ---------------------------------------------------- one-launch compress
+//
+// Histogram, codebook and encode of every tensor in one launch.  A tensor's
+// codebook depends on all of its exponents, so its input is read twice; the
+// launch orders the work so that the second read follows the first closely
+// enough to be served mostly from the GPU's 256 MB last-level cache (MALL),
+// and without the separate calls' launch boundaries.
+//
+// Work items are handed out by a ticket counter in the order workgroups
+// start, in stages: stage s holds the counting items of tensor s (one
+// 64 KB chunk each), then the codebook item of tensor s - 1, then the
+// encode items of tensor s - lag (8 blocks, one per wave).  So tensor t is
+// re-read `lag` stages after it was counted.
+//   counting item: counts its chunk in LDS and adds the counts to the
+//     tensor's u64 histogram in the workspace.  It never waits.
+//   codebook item: polls the tensor's histogram until it is complete --
+//     counts only grow and add up to n, so a reading of the bins that sums
+//     to n is the final histogram -- then writes the histogram output,
+//     ranks the values (count descending, then value ascending) and
+//     publishes the codebook.
+//   encode item: issues its blocks' loads, waits for the publication
+//     (normally long done), reads the codebook and encodes its full blocks
+//     exactly as k_encode does; a partial last block is left to
+//     k_encode_tail.
+// A codebook item waits only for counting items and an encode item only
+// for a codebook item; both hold earlier tickets, so they belong to running
+// workgroups, and none of them waits on a later ticket: the launch always
+// makes progress, whatever else shares the GPU.  The wait is still bounded: after
+// spin_limit polls, or once any workgroup has given up, a workgroup sets its
+// tensor's status, zeroes its blocks' escape counts and leaves.
+//
+// Signalling between workgroups uses no cache-wide maintenance.  Everything
+// one workgroup tells another inside the kernel travels through
+// agent-scope atomics, which are coherent across the XCDs' L2 caches:
+// read-modify-writes (histogram counts, tickets) or sc1 loads and stores
+// (the published flags, the abort word, the codebook).  A flag is raised
+// only after the codebook stores have completed (the storing waves wait for
+// their memory counter to drain, then the workgroup barriers).  Agent-scope
+// acquire/release orderings would instead write back or invalidate a whole
+// L2 at every publication and at every poll of every waiting workgroup.
+
+struct SyncView {
+    SZ_GLOBAL uint64_t* hist;   // count x 256
+    SZ_GLOBAL uint32_t* ticket;
+    SZ_GLOBAL uint32_t* abort;
+    SZ_GLOBAL uint32_t* flags;  // per tensor a 128-byte record; word 0: codebook published
+};
+
+__device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
+    SyncView v;
+    v.hist = gptr(reinterpret_cast<uint64_t*>(base));
+    SZ_GLOBAL uint32_t* w = gptr(reinterpret_cast<uint32_t*>(base + 2048ull * count));
+    v.ticket = w;
+    v.abort = w + 1;
+    v.flags = w + 64;
+    return v;
+}
+
+// This wave's global loads, stores and atomics so far have completed.
+__device__ inline void drain_memory() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited on
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ inline uint32_t load_agent(const SZ_GLOBAL uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint64_t load_agent(const SZ_GLOBAL uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void store_agent(SZ_GLOBAL uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int32_t kStatusGaveUp = 5;   // SZ_ERR_TIMEOUT
+
+// Elements per counting item: kCountIters iterations of count_range (each
+// 8 passes of a 16-byte vector per lane, 64 KB of input).
+template <uint32_t DT>
+constexpr uint64_t count_chunk() {
+    return kCountIters * 8ull * kPassThreads * (16 / Geometry<DT>::kElemBytes);
+}
+
+// One work item; every thread of the workgroup calls it and every return
+// is taken by all of them.  LDS: bins (counting and ranking), s_tbl (one
+// code table per wave), s_word ([2..5] codebook, [8..12] poll words).
+template <uint32_t DT>
+__device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const PassItem& it, uint32_t* bins,
+                                uint32_t (*s_tbl)[64], uint32_t* s_word, uint32_t tid, uint32_t lane,
+                                uint32_t wave) {
+    using G = Geometry<DT>;
+    constexpr uint32_t D = G::kDomain;
+    const uint32_t t = it.t;
+    const SZ_GLOBAL uint8_t* src = src_of(a.enc.src, t);
+
+    if (it.kind == kItemCount) {
+        // ---- counting item
+        hist_clear<DT, kPassThreads>(bins, tid);
+        __syncthreads();
+        const uint64_t begin = static_cast<uint64_t>(it.idx) * count_chunk<DT>();
+        const uint64_t end = begin + count_chunk<DT>() < a.enc.n ? begin + count_chunk<DT>() : a.enc.n;
+        const uint32_t phantom = count_range<DT, kPassThreads>(reinterpret_cast<char*>(bins), src, begin, end, tid);
+        __syncthreads();
+        hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * t, phantom);
+        return;
+    }
+    SZ_GLOBAL uint32_t* published = sv.flags + 32ull * t;
+    SZ_GLOBAL uint32_t* cbw = gptr(reinterpret_cast<uint32_t*>(a.codebooks + 16ull * t));
+
+    if (it.kind == kItemCodebook) {
+        // ---- codebook item: wait until the histogram is complete
+        const SZ_GLOBAL uint64_t* hist = sv.hist + 256ull * t;
+        uint64_t c = 0;
+        uint32_t state = 0;   // 1 complete (c holds this thread's bin), 2 give up
+        for (uint32_t polls = 0;; ++polls) {
+            c = tid < D ? load_agent(hist + tid) : 0;
+            const uint32_t sum = __builtin_amdgcn_readlane(wave_scan_incl(static_cast<uint32_t>(c)), 63);
+            if (lane == 0 && wave < 4) s_word[8 + wave] = sum;   // counts are at most n < 2^32
+            __syncthreads();
+            if (tid == 0) {
+                const uint64_t total = static_cast<uint64_t>(s_word[8]) + s_word[9] + s_word[10] + s_word[11];
+                uint32_t st = total == a.enc.n ? 1u : 0u;
+                if (!st && polls >= a.spin_limit) {
+                    store_agent(sv.abort, 1u);
+                    st = 2;
+                }
+                if (!st && load_agent(sv.abort)) st = 2;
+                s_word[12] = st;
+            }
+            __syncthreads();
+            state = s_word[12];
+            if (state) break;
+            __syncthreads();   // every thread has read this round's words before the next round rewrites them
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (state != 1) {
+            if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
+            return;
+        }
+        // rank of value v = number of keys above its own, two threads per
+        // value each taking half of the keys
+        if (tid < 256) gptr(a.hists)[256ull * t + tid] = c;
+        uint64_t* keys = reinterpret_cast<uint64_t*>(bins);
+        uint32_t* halves = bins + 2 * 256;
+        if (tid < D) keys[tid] = (c << 8) | (255u - tid);
+        if (tid < 4) s_word[2 + tid] = 0;
+        __syncthreads();
+        const uint32_t v = tid & 255u, half = tid >> 8;
+        uint32_t part = 0;
+        if (v < D) {
+            const uint64_t key = keys[v];
+            for (uint32_t u = half * (D / 2); u < (half + 1) * (D / 2); ++u) part += keys[u] > key ? 1u : 0u;
+            if (half) halves[v] = part;
+        }
+        __syncthreads();
+        if (!half && v < D) {
+            const uint32_t rank = part + halves[v];
+            if (rank < kCodes) reinterpret_cast<uint8_t*>(s_word + 2)[rank] = static_cast<uint8_t>(v);
+        }
+        __syncthreads();
+        if (tid < 4) store_agent(cbw + tid, s_word[2 + tid]);
+        drain_memory();    // the codebook is out before the flag
+        __syncthreads();
+        if (tid == 0) store_agent(published, 1u);
+        return;
+    }
+    if (it.kind != kItemEncode) return;
+
+    // ---- encode item: blocks 8 * idx + wave of tensor t, full blocks only;
+    // the loads are issued before the wait for the codebook
+    const Layout L = layout_of(a.enc.n, DT);
+    const uint64_t full_blocks = a.enc.n / kBlockElems;
+    const uint64_t b = static_cast<uint64_t>(it.idx) * kPassWaves + wave;
+    const bool mine_full = b < full_blocks;
+    const uint64_t flat = static_cast<uint64_t>(t) * L.blocks + b;
+    SZ_GLOBAL uint8_t* dst = dst_of(a.enc.dst, t);
+    BlockRegs<DT> d;
+    if (mine_full) load_block<DT, true>(src, a.enc.n, b, lane, d);
+    if (tid == 0) {
+        uint32_t ok = 0;
+        for (uint32_t polls = 0;; ++polls) {
+            if (load_agent(published)) {
+                ok = 1;
+                break;
+            }
+            if (polls >= a.spin_limit) {
+                store_agent(sv.abort, 1u);
+                break;
+            }
+            if (load_agent(sv.abort)) break;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (ok) {
+            drain_memory();    // the codebook is read only after the flag was seen
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) s_word[2 + k] = load_agent(cbw + k);
+        }
+        s_word[12] = ok;
+    }
+    __syncthreads();
+    if (!s_word[12]) {
+        // gave up: no escapes for these blocks (so the scatter that follows
+        // stays inside the stream) and an error for the tensor
+        if (mine_full && lane == 0) gptr(a.enc.counts)[flat] = 0;
+        if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
+        return;
+    }
+    if (mine_full) {
+        const uint32_t mine = lane < kCodes ? reinterpret_cast<const uint8_t*>(s_word + 2)[lane] : 0xFFFFu;
+        encode_loaded<DT, true>(a.enc, L, dst, b, flat, lane, s_tbl[wave], mine, d);
+    }
+}
+
+// One workgroup per item: the ticket taken at the start fixes the item.
+template <uint32_t DT>
+__global__ __launch_bounds__(kPassThreads, 8) void k_compress(CompressArgs a) {
+    __shared__ uint32_t bins[HistLds<DT>::kWords];
+    __shared__ uint32_t s_tbl[kPassWaves][64];
+    __shared__ uint32_t s_word[16];   // [0] ticket
+    const uint32_t tid = threadIdx.x, lane = lane_id();
+    const uint32_t wave = uniform(tid / kWaveSize);
+    const SyncView sv = sync_view(a.sync, a.enc.count);
+    if (tid == 0) s_word[0] = __hip_atomic_fetch_add(sv.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const PassItem it = pass_item(s_word[0], a.enc.count, a.count_items, a.encode_items, a.lag);
+    run_item<DT>(a, sv, it, bins, s_tbl, s_word, tid, lane, wave);
 }
 
 // ----------------------------------------------------------------- decode
@@ -1103,14 +1374,12 @@ hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s)
     return hipGetLastError();
 }
 
+// offsets, header and escape scatter, after the planes and staged escapes
 template <uint32_t DT>
-void enqueue_encode(const EncodeArgs& a, hipStream_t s) {
+void enqueue_encode_finish(const EncodeArgs& a, hipStream_t s) {
     const Layout L = layout_of(a.n, DT);
-    const uint64_t full = static_cast<uint64_t>(a.count) * (a.n / kBlockElems);
     const uint64_t blocks = static_cast<uint64_t>(a.count) * L.blocks;
     const uint32_t scatter_groups = grid_for(blocks, kThreads);
-    if (full) hipLaunchKernelGGL(k_encode<DT>, dim3(grid_for(full, kWavesPerGroup)), dim3(kThreads), 0, s, a);
-    if (a.n % kBlockElems) hipLaunchKernelGGL(k_encode_tail<DT>, dim3(a.count), dim3(kWaveSize), 0, s, a);
     const uint64_t groups = (L.blocks + kThreads - 1) / kThreads;     // 256-block groups per tensor
     if (groups <= kFusedGroups) {
         hipLaunchKernelGGL(k_offsets_scatter<DT>, dim3(static_cast<uint32_t>(a.count * groups)), dim3(kThreads), 0,
@@ -1119,6 +1388,14 @@ void enqueue_encode(const EncodeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(k_offsets<DT>, dim3(a.count), dim3(256), 0, s, a);
         hipLaunchKernelGGL(k_scatter<DT>, dim3(scatter_groups), dim3(kThreads), 0, s, a);
     }
+}
+
+template <uint32_t DT>
+void enqueue_encode(const EncodeArgs& a, hipStream_t s) {
+    const uint64_t full = static_cast<uint64_t>(a.count) * (a.n / kBlockElems);
+    if (full) hipLaunchKernelGGL(k_encode<DT>, dim3(grid_for(full, kWavesPerGroup)), dim3(kThreads), 0, s, a);
+    if (a.n % kBlockElems) hipLaunchKernelGGL(k_encode_tail<DT>, dim3(a.count), dim3(kWaveSize), 0, s, a);
+    enqueue_encode_finish<DT>(a, s);
 }
 
 hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s) {
@@ -1134,6 +1411,22 @@ hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t 
         hipLaunchKernelGGL(k_encode_empty<kDtypeBF16>, dim3(a.count), dim3(kWaveSize), 0, s, a);
     else
         hipLaunchKernelGGL(k_encode_empty<kDtypeE5M2>, dim3(a.count), dim3(kWaveSize), 0, s, a);
+    return hipGetLastError();
+}
+
+template <uint32_t DT>
+void enqueue_compress(const CompressArgs& a, hipStream_t s) {
+    const uint32_t grid = a.enc.count * (a.count_items + 1 + a.encode_items);   // one workgroup per item
+    hipLaunchKernelGGL(k_compress<DT>, dim3(grid), dim3(kPassThreads), 0, s, a);
+    if (a.enc.n % kBlockElems) hipLaunchKernelGGL(k_encode_tail<DT>, dim3(a.enc.count), dim3(kWaveSize), 0, s, a.enc);
+    enqueue_encode_finish<DT>(a.enc, s);
+}
+
+hipError_t launch_compress(const CompressArgs& a, uint32_t dtype, hipStream_t s) {
+    if (dtype != kDtypeBF16) return hipErrorInvalidValue;   // E5M2 takes the separate kernels
+    const hipError_t e = launch_fill_u64(reinterpret_cast<uint64_t*>(a.sync), sync_area_bytes(a.enc.count) / 8, 0, s);
+    if (e != hipSuccess) return e;
+    enqueue_compress<kDtypeBF16>(a, s);
     return hipGetLastError();
 }
 

@@ -98,6 +98,76 @@ struct EncodeArgs {
     uint64_t n;
 };
 
+// One-launch compress (histogram, codebook and encode).  Its workspace is
+// the encode workspace followed by a synchronisation area that a fill
+// kernel zeroes before every launch:
+//   u64 hist[count][256]   exponent counts accumulated by all workgroups
+//   u32 ticket, u32 abort  (padded to 256 bytes)
+//   per tensor t a 128-byte record: u32 at byte 0, 1 once t's codebook is
+//   published
+constexpr uint32_t kPassWaves = 8;                          // blocks per encode item, one per wave
+constexpr uint32_t kPassThreads = kPassWaves * kWaveSize;   // 512
+constexpr uint32_t kPassLag = 4;                            // stages between counting and encoding a tensor
+constexpr uint32_t kCountIters = 2;                         // 64 KB input iterations per counting item
+constexpr uint32_t kDefaultSpinLimit = 1u << 20;            // polls before a waiting workgroup gives up
+
+__host__ __device__ inline uint64_t sync_area_bytes(uint32_t count) {
+    return 2048ull * count + 256 + 128ull * count;
+}
+
+struct CompressArgs {
+    EncodeArgs enc;           // enc.codebooks is written by the compress kernel
+    uint64_t* hists;          // count x 256, written
+    uint8_t* codebooks;       // count x 16, written (same memory as enc.codebooks)
+    uint8_t* sync;            // the synchronisation area
+    int32_t* status;          // count, may be null
+    uint32_t count_items;     // per tensor: ceil(n / elements per counting item)
+    uint32_t encode_items;    // per tensor: ceil(full blocks / kPassWaves); plus one codebook item
+    uint32_t lag;             // stages between counting and encoding a tensor, 1..count
+    uint32_t spin_limit;
+};
+
+// Work items of the one-launch compress, in ticket order (see k_compress).
+enum : uint32_t { kItemCount = 0, kItemCodebook = 1, kItemEncode = 2, kItemNone = 3 };
+
+struct PassItem {
+    uint32_t kind;
+    uint32_t t;
+    uint32_t idx;
+};
+
+// Ticket k -> item, for T tensors, H counting and E encode items per
+// tensor and 1 <= lag <= T.  Stage s holds, in this order: the H counting
+// items of tensor s (s < T), the codebook item of tensor s - 1
+// (1 <= s <= T), the E encode items of tensor s - lag (lag <= s < T + lag).
+// Stage sizes are constant between the boundaries 0, 1, lag, T, T + 1,
+// T + lag, so the ticket is located region by region.
+__host__ __device__ inline PassItem pass_item(uint64_t k, uint32_t T, uint32_t H, uint32_t E, uint32_t lag) {
+    const uint32_t edge[6] = {0, 1, lag, T, T + 1, T + lag};
+    for (uint32_t r = 0; r < 5; ++r) {
+        const uint32_t lo = edge[r], hi = edge[r + 1];
+        if (hi <= lo) continue;
+        const uint64_t size = (lo < T ? H : 0u) + (lo >= 1 && lo <= T ? 1u : 0u) + (lo >= lag ? E : 0u);
+        const uint64_t span = static_cast<uint64_t>(hi - lo) * size;
+        if (k >= span) {
+            k -= span;
+            continue;
+        }
+        const uint32_t s = lo + static_cast<uint32_t>(k / size);
+        uint64_t q = k % size;
+        if (s < T) {
+            if (q < H) return {kItemCount, s, static_cast<uint32_t>(q)};
+            q -= H;
+        }
+        if (s >= 1 && s <= T) {
+            if (q == 0) return {kItemCodebook, s - 1, 0};
+            q -= 1;
+        }
+        return {kItemEncode, s - lag, static_cast<uint32_t>(q)};
+    }
+    return {kItemNone, 0, 0};
+}
+
 struct DecodeArgs {
     SrcRef src;
     const uint64_t* src_bytes_table;  // count, or null
@@ -115,6 +185,10 @@ hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s)
 // encode = three kernels: planes + staged escapes, offsets + header, escape scatter
 hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
+// compress (BF16) = fill of the synchronisation area, the counting/encoding
+// kernel, the partial-block encode, then the same offsets and escape
+// scatter as encode
+hipError_t launch_compress(const CompressArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_decode_empty(const DecodeArgs& a, uint32_t dtype, hipStream_t s);
 

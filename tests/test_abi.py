@@ -112,9 +112,56 @@ def test_host_argument_errors_return_before_launch(sz):
     assert sz.sz_decode_batched(FAKE, None, 2, 5000, 1, FAKE, None, stream=0) == E_ARG
 
 
+def test_compress_sizes_and_host_errors(sz):
+    """Single-pass calls: workspace = the encode workspace plus 2048 bytes of
+    histogram per tensor, 256 bytes of counters and a 128-byte flag record
+    per tensor; argument errors return before any launch."""
+    for count, n in [(1, 0), (1, 4097), (64, 1 << 23), (3, 100)]:
+        sync = 2048 * count + 256 + 128 * count
+        assert sz.sz_compress_workspace_bytes_batched(count, n, 1) == \
+            sz.sz_encode_workspace_bytes_batched(count, n, 1) + sync
+    assert sz.sz_compress_workspace_bytes(1 << 32, 1) == 0
+    assert sz.sz_compress_workspace_bytes_batched(0, 10, 1) == 0
+    E_ARG, E_SMALL = sz.SZ_ERR_INVALID_ARGUMENT, sz.SZ_ERR_BUFFER_TOO_SMALL
+    n = 5000
+    cap = sz.sz_max_compressed_bytes(n, 2)
+    ws = sz.sz_compress_workspace_bytes(n, 2)
+    ok = dict(src=FAKE, n=n, dtype=2, hist=FAKE, codebook=FAKE, dst=FAKE, dst_capacity=cap, out_bytes=None,
+              status=None, workspace=FAKE, workspace_bytes=ws)
+
+    def call(**kw):
+        args = dict(ok, **kw)
+        return sz.sz_compress(*args.values(), stream=0)
+    assert call(dtype=3) == E_ARG
+    assert call(n=1 << 32) == E_ARG
+    assert call(src=None) == E_ARG
+    assert call(hist=None) == E_ARG
+    assert call(codebook=FAKE + 8) == E_ARG
+    assert call(workspace=None) == E_ARG
+    assert call(out_bytes=FAKE + 4) == E_ARG
+    assert call(status=FAKE + 2) == E_ARG
+    assert call(dst_capacity=cap - 1) == E_SMALL
+    assert call(workspace_bytes=ws - 1) == E_SMALL
+    assert sz.sz_compress_batched(FAKE, 0, n, 2, FAKE, FAKE, FAKE, cap, None, None, FAKE, ws, stream=0) == E_ARG
+    assert sz.sz_compress_batched(FAKE, 2, n, 2, FAKE, FAKE, FAKE, cap, None, None, FAKE, ws, stream=0) == E_SMALL
+    assert sz.sz_compress_batched(FAKE, 2048, (1 << 32) - 1, 1, FAKE, FAKE, FAKE, 1 << 40, None, None, FAKE,
+                                  1 << 62, stream=0) == E_ARG
+
+
+def test_compress_spin_limit_setting(sz):
+    before = sz.sz_compress_spin_limit(7)
+    try:
+        assert before == 1 << 20
+        assert sz.sz_compress_spin_limit(0) == 7       # 0 restores the default
+        assert sz.sz_compress_spin_limit(0) == 1 << 20
+    finally:
+        sz.sz_compress_spin_limit(0)
+
+
 def test_status_strings(sz):
     assert sz.sz_status_string(0) == "ok"
     assert sz.sz_status_string(3) == "corrupt stream"
+    assert sz.sz_status_string(5) == "gave up waiting for the codebook"
     assert sz.sz_status_string(99) == "unknown status"
 
 

@@ -754,8 +754,9 @@ __global__ void k_encode_empty(EncodeArgs a) {
 //
 // Work items are handed out by a ticket counter in the order workgroups
 // start, in stages: stage s holds the counting items of tensor s (one
-// 64 KB chunk each), then the codebook item of tensor s - 1, then the
-// encode items of tensor s - lag (8 blocks, one per wave).  So tensor t is
+// 128 KB chunk each), then the codebook item of tensor s - 1, then the
+// encode items of tensor s - lag (16 blocks, one per wave of the 1024-thread
+// workgroup).  So tensor t is
 // re-read `lag` stages after it was counted.
 //   counting item: counts its chunk in LDS and adds the counts to the
 //     tensor's u64 histogram in the workspace.  It never waits.
@@ -824,7 +825,8 @@ __device__ inline void store_agent(SZ_GLOBAL uint32_t* p, uint32_t v) {
 constexpr int32_t kStatusGaveUp = 5;   // SZ_ERR_TIMEOUT
 
 // Elements per counting item: kCountIters iterations of count_range (each
-// 8 passes of a 16-byte vector per lane, 64 KB of input).
+// 8 passes of a 16-byte vector per lane of the 1024-thread workgroup,
+// 128 KB of input).
 template <uint32_t DT>
 constexpr uint64_t count_chunk() {
     return kCountIters * 8ull * kPassThreads * (16 / Geometry<DT>::kElemBytes);
@@ -886,24 +888,27 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
             if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
             return;
         }
-        // rank of value v = number of keys above its own, two threads per
-        // value each taking half of the keys
+        // rank of value v = number of keys above its own; the workgroup's
+        // kParts groups of 256 threads each compare against a share of the keys
+        constexpr uint32_t kParts = kPassThreads / 256;
         if (tid < 256) gptr(a.hists)[256ull * t + tid] = c;
         uint64_t* keys = reinterpret_cast<uint64_t*>(bins);
-        uint32_t* halves = bins + 2 * 256;
+        uint32_t* parts = bins + 2 * 256;   // [kParts][256] partial ranks, after the keys
         if (tid < D) keys[tid] = (c << 8) | (255u - tid);
         if (tid < 4) s_word[2 + tid] = 0;
         __syncthreads();
-        const uint32_t v = tid & 255u, half = tid >> 8;
-        uint32_t part = 0;
+        const uint32_t v = tid & 255u, q = tid >> 8;
         if (v < D) {
             const uint64_t key = keys[v];
-            for (uint32_t u = half * (D / 2); u < (half + 1) * (D / 2); ++u) part += keys[u] > key ? 1u : 0u;
-            if (half) halves[v] = part;
+            uint32_t part = 0;
+            for (uint32_t u = q * (D / kParts); u < (q + 1) * (D / kParts); ++u) part += keys[u] > key ? 1u : 0u;
+            parts[q * 256 + v] = part;
         }
         __syncthreads();
-        if (!half && v < D) {
-            const uint32_t rank = part + halves[v];
+        if (q == 0 && v < D) {
+            uint32_t rank = 0;
+#pragma unroll
+            for (uint32_t k = 0; k < kParts; ++k) rank += parts[k * 256 + v];
             if (rank < kCodes) reinterpret_cast<uint8_t*>(s_word + 2)[rank] = static_cast<uint8_t>(v);
         }
         __syncthreads();
@@ -915,7 +920,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     }
     if (it.kind != kItemEncode) return;
 
-    // ---- encode item: blocks 8 * idx + wave of tensor t, full blocks only;
+    // ---- encode item: blocks 16 * idx + wave of tensor t, full blocks only;
     // the loads are issued before the wait for the codebook
     const Layout L = layout_of(a.enc.n, DT);
     const uint64_t full_blocks = a.enc.n / kBlockElems;
@@ -963,6 +968,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
 // One workgroup per item: the ticket taken at the start fixes the item.
 template <uint32_t DT>
 __global__ __launch_bounds__(kPassThreads, 8) void k_compress(CompressArgs a) {
+    static_assert(kPassThreads % 256 == 0 && Geometry<DT>::kDomain % (kPassThreads / 256) == 0, "rank split");
     __shared__ uint32_t bins[HistLds<DT>::kWords];
     __shared__ uint32_t s_tbl[kPassWaves][64];
     __shared__ uint32_t s_word[16];   // [0] ticket

@@ -105,10 +105,10 @@ struct EncodeArgs {
 //   u32 ticket, u32 abort  (padded to 256 bytes)
 //   per tensor t a 128-byte record: u32 at byte 0, 1 once t's codebook is
 //   published
-constexpr uint32_t kPassWaves = 8;                          // blocks per encode item, one per wave
-constexpr uint32_t kPassThreads = kPassWaves * kWaveSize;   // 512
+constexpr uint32_t kPassWaves = 16;                         // blocks per encode item, one per wave
+constexpr uint32_t kPassThreads = kPassWaves * kWaveSize;   // 1024
 constexpr uint32_t kPassLag = 4;                            // stages between counting and encoding a tensor
-constexpr uint32_t kCountIters = 2;                         // 64 KB input iterations per counting item
+constexpr uint32_t kCountIters = 1;                         // 128 KB input iterations per counting item
 constexpr uint32_t kDefaultSpinLimit = 1u << 20;            // polls before a waiting workgroup gives up
 
 __host__ __device__ inline uint64_t sync_area_bytes(uint32_t count) {

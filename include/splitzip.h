@@ -172,7 +172,7 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * while it encodes tensor s - 4, so the second read of a tensor follows
  * the first closely enough to be served mostly from the GPU's last-level
  * cache, and the codebook is built and published inside the kernel (on
- * the Llama-shaped 64-tensor BF16 cache about 12% faster than the three
+ * the Llama-shaped 64-tensor BF16 cache about 17% faster than the three
  * calls).  E5M2 tensors have half the bytes per element, so the fused
  * kernel's fixed costs per work item weigh twice as much; measured slower
  * fused, they run the separate calls' kernels (the results are the same).

@@ -31,6 +31,13 @@ bool grid_ok(uint32_t count, uint64_t n) {
 
 uint64_t workspace_bytes(uint32_t count, uint64_t n) { return workspace_bytes_for(count, n); }
 
+// Work items of the fused compress kernel per tensor: counting items, one
+// codebook item, encode items.
+uint64_t compress_items(uint64_t n, sz_dtype dt) {
+    const uint64_t chunk = kCountIters * 8ull * kPassThreads * (dt == SZ_DTYPE_BF16 ? 8 : 16);
+    return (n + chunk - 1) / chunk + 1 + (n / kBlockElems + kPassWaves - 1) / kPassWaves;
+}
+
 uint64_t compress_workspace_bytes(uint32_t count, uint64_t n) {
     return workspace_bytes_for(count, n) + sync_area_bytes(count);
 }
@@ -97,6 +104,8 @@ sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uin
     const uint64_t chunk = kCountIters * 8ull * kPassThreads * (dt == SZ_DTYPE_BF16 ? 8 : 16);
     a.count_items = static_cast<uint32_t>((n + chunk - 1) / chunk);
     a.encode_items = static_cast<uint32_t>((n / kBlockElems + kPassWaves - 1) / kPassWaves);
+    // (compress_items(n, dt) = count_items + 1 + encode_items; the entry points
+    // keep count * that below 2^31, the launch's workgroup count)
     a.lag = count < kPassLag ? count : kPassLag;
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     return from_hip(launch_compress(a, dt, s));
@@ -238,7 +247,8 @@ SZ_EXPORT sz_status sz_compress_batched(const void* const* d_srcs, uint32_t coun
                                         uint64_t* d_hists, uint8_t* d_codebooks, void* const* d_dsts,
                                         uint64_t dst_capacity, uint64_t* d_out_bytes, int32_t* d_status,
                                         void* d_workspace, uint64_t workspace_bytes_given, hipStream_t stream) {
-    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n) || !usable(d_srcs) ||
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n) ||
+        static_cast<uint64_t>(count) * compress_items(n, dtype) >= (uint64_t(1) << 31) || !usable(d_srcs) ||
         !usable(d_hists) || !usable(d_codebooks) || !usable(d_dsts) || !usable(d_workspace) ||
         (d_out_bytes && (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)) ||
         (d_status && (reinterpret_cast<uintptr_t>(d_status) & 3u)))

@@ -188,6 +188,9 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * d_hist(s): 256 (count x 256) u64, written.  d_codebook(s): 16 (count x
  * 16) bytes, written.  d_dst(s), dst_capacity, d_out_bytes: as sz_encode.
  * d_status: 1 (count) int32, SZ_OK or SZ_ERR_TIMEOUT, may be NULL.
+ * Batched: T x (ceil(n / 65536) + 1 + ceil(floor(n / 4096) / 16)), the
+ * kernel's work items, must stay below 2^31 as well, else
+ * SZ_ERR_INVALID_ARGUMENT.
  * d_workspace: >= sz_compress_workspace_bytes[_batched] bytes, contents
  * need not be initialised, clobbered (the encode workspace followed by
  * 256 bytes plus 2176 bytes per tensor of counters).  Calls sharing a

@@ -146,6 +146,10 @@ def test_compress_sizes_and_host_errors(sz):
     assert sz.sz_compress_batched(FAKE, 2, n, 2, FAKE, FAKE, FAKE, cap, None, None, FAKE, ws, stream=0) == E_SMALL
     assert sz.sz_compress_batched(FAKE, 2048, (1 << 32) - 1, 1, FAKE, FAKE, FAKE, 1 << 40, None, None, FAKE,
                                   1 << 62, stream=0) == E_ARG
+    # tiny tensors: two work items each (counting + codebook) -- 2^30 of them would overflow the grid
+    cap1 = sz.sz_max_compressed_bytes(1, 1)
+    assert sz.sz_compress_batched(FAKE, 1 << 30, 1, 1, FAKE, FAKE, FAKE, cap1, None, None, FAKE, 1 << 62,
+                                  stream=0) == E_ARG
 
 
 def test_compress_spin_limit_setting(sz):

@@ -86,6 +86,34 @@ def test_fused_batched(sz, dt, n):
         assert np.array_equal(to_host(one.output(i), dt), x), i
 
 
+@pytest.mark.parametrize("count,n", [(2, 16 * 4096 * 3 + 5), (5, 200705), (300, 3 * 16 * 4096 + 4097)])
+def test_fused_schedule_shapes(sz, count, n):
+    """Tensor counts below, at and far above the counting-to-encoding lag
+    (so the stage schedule's first, middle and last regions all occur),
+    with ragged counting items, ragged encode items and a partial last
+    block: everything equal to the three separate calls, and a sample of
+    tensors equal to the oracle."""
+    rng = np.random.default_rng(count)
+    xs = [kvsynth.stress(n, seed=int(s)) for s in rng.integers(0, 1 << 30, count)]
+    say("fused schedule shapes", count, n)
+    dev = [to_dev(x) for x in xs]
+    one = sz.codec.BatchCodec(count, n, BF16)
+    one.set_inputs(dev)
+    one.compress_fused()
+    three = sz.codec.BatchCodec(count, n, BF16)
+    three.set_inputs(dev)
+    three.compress()
+    torch.cuda.synchronize()
+    assert (one.fused_status.cpu().numpy() == 0).all()
+    assert torch.equal(one.sizes, three.sizes)
+    assert torch.equal(one.hists, three.hists)
+    assert torch.equal(one.codebooks, three.codebooks)
+    for i in range(count):
+        assert torch.equal(one.stream(i), three.stream(i)), i
+    for i in sorted({0, count // 2, count - 1}):
+        _check_against_oracle(xs[i], BF16, one.stream(i), one.hists[i], one.codebooks[i])
+
+
 def test_fused_is_deterministic(sz):
     x = to_dev(kvsynth.stress(3 << 20, seed=19))
     say("fused determinism")

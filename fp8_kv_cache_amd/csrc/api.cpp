@@ -80,8 +80,8 @@ sz_status encode_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, const
 sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint64_t* d_hists,
                         uint8_t* d_codebooks, DstRef dst, uint64_t* d_out_bytes, int32_t* d_status,
                         void* d_workspace, hipStream_t s) {
-    if (d_status && launch_fill_i32(d_status, count, SZ_OK, s) != hipSuccess) return SZ_ERR_HIP;
     if (n == 0 || dt != SZ_DTYPE_BF16) {
+        if (d_status && launch_fill_i32(d_status, count, SZ_OK, s) != hipSuccess) return SZ_ERR_HIP;
         sz_status st = histogram_impl(src, count, n, dt, 1, d_hists, s);
         if (st != SZ_OK) return st;
         CodebookArgs c{d_hists, d_codebooks, count};

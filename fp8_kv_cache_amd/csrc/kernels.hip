@@ -91,6 +91,17 @@ __global__ void k_fill_u64(uint64_t* p, uint64_t words, uint64_t value) {
         p[i] = value;
 }
 
+// Zero two ranges in one launch (u64 words of a, i32 words of b; b may be
+// null): the fused compress clears its synchronisation area and its status
+// words (SZ_OK is 0) with one kernel instead of two.
+__global__ void k_zero_two(uint64_t* a, uint64_t na, int32_t* b, uint64_t nb) {
+    const uint64_t first = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = first; i < na; i += stride) a[i] = 0;
+    if (b)
+        for (uint64_t i = first; i < nb; i += stride) b[i] = 0;
+}
+
 __global__ void k_fill_i32(int32_t* p, uint64_t words, int32_t value) {
     for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < words;
          i += (uint64_t)gridDim.x * blockDim.x)
@@ -1430,7 +1441,12 @@ void enqueue_compress(const CompressArgs& a, hipStream_t s) {
 
 hipError_t launch_compress(const CompressArgs& a, uint32_t dtype, hipStream_t s) {
     if (dtype != kDtypeBF16) return hipErrorInvalidValue;   // E5M2 takes the separate kernels
-    const hipError_t e = launch_fill_u64(reinterpret_cast<uint64_t*>(a.sync), sync_area_bytes(a.enc.count) / 8, 0, s);
+    const uint64_t words = sync_area_bytes(a.enc.count) / 8;
+    const uint64_t most = words > a.enc.count ? words : a.enc.count;
+    const uint32_t groups = grid_for(most < 4096ull * 256 ? most : 4096ull * 256, 256);
+    hipLaunchKernelGGL(k_zero_two, dim3(groups), dim3(256), 0, s, reinterpret_cast<uint64_t*>(a.sync), words, a.status,
+                       static_cast<uint64_t>(a.enc.count));
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     enqueue_compress<kDtypeBF16>(a, s);
     return hipGetLastError();

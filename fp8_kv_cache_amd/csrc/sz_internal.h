@@ -185,9 +185,9 @@ hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s)
 // encode = three kernels: planes + staged escapes, offsets + header, escape scatter
 hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
-// compress (BF16) = fill of the synchronisation area, the counting/encoding
-// kernel, the partial-block encode, then the same offsets and escape
-// scatter as encode
+// compress (BF16) = one clear of the synchronisation area and the status
+// words, the counting/encoding kernel, the partial-block encode, then the
+// same offsets and escape scatter as encode
 hipError_t launch_compress(const CompressArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_decode_empty(const DecodeArgs& a, uint32_t dtype, hipStream_t s);

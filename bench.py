@@ -43,7 +43,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 LAYERS, SHAPE = 32, (8192, 8, 128)
-KERNEL_SOURCE = os.path.join(ROOT, "fp8_kv_cache_amd", "csrc", "kernels.hip")
+# the sources that decide what the exponent codec's kernels do and how they are launched
+KERNEL_SOURCES = [os.path.join(ROOT, "fp8_kv_cache_amd", "csrc", f)
+                  for f in ("kernels.hip", "sz_internal.h", "device_common.h", "api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -60,19 +62,24 @@ def parse():
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_for(kernels):
     """HBM bytes per launch of the given kernels (summed), from the committed
-    rocprofv3 counter summary; None if missing or taken on other kernel source."""
+    rocprofv3 counter summary; None if missing or taken on other kernel
+    sources (the hash covers the kernels, their shared headers and the
+    launch code)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_sources_sha256") != kernel_source_hash():
         return None
     total = 0.0
     for k in kernels:

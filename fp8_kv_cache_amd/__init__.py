@@ -25,7 +25,7 @@ __all__ = [
     "sz_histogram_sampled_batched",
     "sz_histogram_batched", "sz_build_codebook_batched", "sz_encode_batched", "sz_decode_batched",
     "sz_compress_workspace_bytes", "sz_compress_workspace_bytes_batched", "sz_compress",
-    "sz_compress_batched", "sz_compress_spin_limit",
+    "sz_compress_batched", "sz_compress_spin_limit", "sz_compress_fused_min_elements",
     "sz_status_string", "check", "pointer_table", "library_path",
     "lc_max_compressed_bytes", "lc_encode_workspace_bytes", "lc_encode_workspace_bytes_batched",
     "lc_encode", "lc_decode", "lc_encode_batched", "lc_decode_batched",
@@ -68,6 +68,7 @@ _SIGNATURES = {
     "sz_compress": (_i32, [_vp, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp]),
     "sz_compress_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp]),
     "sz_compress_spin_limit": (_u32, [_u32]),
+    "sz_compress_fused_min_elements": (_u64, [_u64]),
     "sz_status_string": (ctypes.c_char_p, [_i32]),
     "lc_max_compressed_bytes": (_u64, [_u64]),
     "lc_encode_workspace_bytes": (_u64, [_u64]),
@@ -209,6 +210,10 @@ def sz_compress_batched(srcs, count, n, dtype, hists, codebooks, dsts, dst_capac
 
 def sz_compress_spin_limit(polls):
     return _lib.sz_compress_spin_limit(polls)
+
+
+def sz_compress_fused_min_elements(n):
+    return _lib.sz_compress_fused_min_elements(n)
 
 
 def lc_max_compressed_bytes(n):

@@ -43,6 +43,7 @@ uint64_t compress_workspace_bytes(uint32_t count, uint64_t n) {
 }
 
 std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
+std::atomic<uint64_t> g_fused_min{kDefaultFusedMin};
 
 sz_status histogram_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint32_t stride,
                          uint64_t* d_hists, hipStream_t s) {
@@ -73,14 +74,17 @@ sz_status encode_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, const
 }
 
 // Histogram, codebook and encode in one launch (plus the short offset and
-// scatter launches) for BF16.  E5M2 tensors (half the bytes per element, so
-// twice the per-item overhead per byte) measured slower fused than with the
-// separate calls' kernels (0.38 against 0.34 ms on the 64-tensor cache), so
-// they take those, as does n = 0; the results are the same either way.
+// scatter launches) for BF16 tensors of at least g_fused_min elements.
+// E5M2 tensors (half the bytes per element, so twice the per-item overhead
+// per byte) measured slower fused than with the separate calls' kernels
+// (0.37 against 0.34 ms on the 64-tensor cache), and so did BF16 tensors
+// of 2 MiB and less (4 MiB: 15% faster fused, 2 MiB: 10% slower); those
+// take the separate kernels, as does n = 0.  The results are the same
+// either way.
 sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint64_t* d_hists,
                         uint8_t* d_codebooks, DstRef dst, uint64_t* d_out_bytes, int32_t* d_status,
                         void* d_workspace, hipStream_t s) {
-    if (n == 0 || dt != SZ_DTYPE_BF16) {
+    if (n == 0 || dt != SZ_DTYPE_BF16 || n < g_fused_min.load(std::memory_order_relaxed)) {
         if (d_status && launch_fill_i32(d_status, count, SZ_OK, s) != hipSuccess) return SZ_ERR_HIP;
         sz_status st = histogram_impl(src, count, n, dt, 1, d_hists, s);
         if (st != SZ_OK) return st;
@@ -106,7 +110,18 @@ sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uin
     a.encode_items = static_cast<uint32_t>((n / kBlockElems + kPassWaves - 1) / kPassWaves);
     // (compress_items(n, dt) = count_items + 1 + encode_items; the entry points
     // keep count * that below 2^31, the launch's workgroup count)
-    a.lag = count < kPassLag ? count : kPassLag;
+    // Re-read each tensor once about kPassLagBytes of further input has been
+    // counted: long enough for its codebook to be published before its
+    // encode items arrive, short enough for the re-read to hit the
+    // last-level cache.  Measured optima (lags 6-8, 3 and 2 for tensors of
+    // 8, 16 and 32 MiB) all sit near 48 MiB.  Never below 2 when there are
+    // two tensors: at lag 1 the encode items arrive right behind their
+    // codebook item and stall on it.
+    const uint64_t tensor_bytes = 2 * n;
+    uint64_t lag = (kPassLagBytes + tensor_bytes / 2) / tensor_bytes;
+    lag = lag < 2 ? 2 : lag;
+    lag = lag > count ? count : lag;
+    a.lag = static_cast<uint32_t>(lag);
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     return from_hip(launch_compress(a, dt, s));
 }
@@ -261,6 +276,10 @@ SZ_EXPORT sz_status sz_compress_batched(const void* const* d_srcs, uint32_t coun
 
 SZ_EXPORT uint32_t sz_compress_spin_limit(uint32_t polls) {
     return g_spin_limit.exchange(polls ? polls : kDefaultSpinLimit, std::memory_order_relaxed);
+}
+
+SZ_EXPORT uint64_t sz_compress_fused_min_elements(uint64_t n) {
+    return g_fused_min.exchange(n ? n : kDefaultFusedMin, std::memory_order_relaxed);
 }
 
 SZ_EXPORT sz_status sz_decode(const void* d_src, uint64_t src_bytes, uint64_t n, sz_dtype dtype,

@@ -107,9 +107,11 @@ struct EncodeArgs {
 //   published
 constexpr uint32_t kPassWaves = 16;                         // blocks per encode item, one per wave
 constexpr uint32_t kPassThreads = kPassWaves * kWaveSize;   // 1024
-constexpr uint32_t kPassLag = 4;                            // stages between counting and encoding a tensor
+constexpr uint64_t kPassLagBytes = 48ull << 20;             // input counted between a tensor's counting and its
+                                                            // re-read: the lag in stages is this over the tensor size
 constexpr uint32_t kCountIters = 1;                         // 128 KB input iterations per counting item
 constexpr uint32_t kDefaultSpinLimit = 1u << 20;            // polls before a waiting workgroup gives up
+constexpr uint64_t kDefaultFusedMin = 1ull << 21;           // smallest BF16 tensor (elements) the fused kernel takes
 
 __host__ __device__ inline uint64_t sync_area_bytes(uint32_t count) {
     return 2048ull * count + 256 + 128ull * count;
@@ -123,7 +125,7 @@ struct CompressArgs {
     int32_t* status;          // count, may be null
     uint32_t count_items;     // per tensor: ceil(n / elements per counting item)
     uint32_t encode_items;    // per tensor: ceil(full blocks / kPassWaves); plus one codebook item
-    uint32_t lag;             // stages between counting and encoding a tensor, 1..count
+    uint32_t lag;             // stages between counting and encoding a tensor, 1..count (see kPassLagBytes)
     uint32_t spin_limit;
 };
 

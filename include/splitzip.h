@@ -172,10 +172,11 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * while it encodes tensor s - 4, so the second read of a tensor follows
  * the first closely enough to be served mostly from the GPU's last-level
  * cache, and the codebook is built and published inside the kernel (on
- * the Llama-shaped 64-tensor BF16 cache about 17% faster than the three
+ * the Llama-shaped 64-tensor BF16 cache about 15% faster than the three
  * calls).  E5M2 tensors have half the bytes per element, so the fused
  * kernel's fixed costs per work item weigh twice as much; measured slower
- * fused, they run the separate calls' kernels (the results are the same).
+ * fused, they run the separate calls' kernels, as do BF16 tensors below
+ * sz_compress_fused_min_elements() (the results are the same).
  *
  * Work inside the kernel waits only for work handed out before it, so a
  * call always makes progress, whatever else shares the GPU.  Waits are
@@ -208,6 +209,14 @@ sz_status sz_compress_batched(const void* const* d_srcs, uint32_t count, uint64_
                               uint64_t* d_hists, uint8_t* d_codebooks, void* const* d_dsts,
                               uint64_t dst_capacity, uint64_t* d_out_bytes, int32_t* d_status,
                               void* d_workspace, uint64_t workspace_bytes, hipStream_t stream);
+
+/* Smallest BF16 tensor (in elements) that later sz_compress* calls run
+ * through the fused kernel; smaller tensors take the separate calls'
+ * kernels (same results).  0 restores the default, 2^21 (4 MiB: measured
+ * 15% faster fused; 2 MiB tensors measured 10% slower).  Returns the
+ * previous value.  Host-side setting, read when a call is enqueued; a
+ * value of 1 sends every tensor through the fused kernel. */
+uint64_t sz_compress_fused_min_elements(uint64_t n);
 
 /* Polls a waiting workgroup of later sz_compress* calls makes before it
  * gives up (0 restores the default, 2^20); returns the previous value.

@@ -152,6 +152,16 @@ def test_compress_sizes_and_host_errors(sz):
                                   stream=0) == E_ARG
 
 
+def test_compress_fused_threshold_setting(sz):
+    before = sz.sz_compress_fused_min_elements(1)
+    try:
+        assert before == 1 << 21
+        assert sz.sz_compress_fused_min_elements(0) == 1     # 0 restores the default
+        assert sz.sz_compress_fused_min_elements(0) == 1 << 21
+    finally:
+        sz.sz_compress_fused_min_elements(0)
+
+
 def test_compress_spin_limit_setting(sz):
     before = sz.sz_compress_spin_limit(7)
     try:

@@ -25,11 +25,16 @@ def say(*a):
 
 @pytest.fixture(scope="module")
 def sz():
+    """The library with every BF16 tensor sent through the fused kernel
+    (by default tensors under 2^21 elements take the separate kernels), so
+    the small cases below exercise it; restored afterwards."""
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import fp8_kv_cache_amd
     from fp8_kv_cache_amd import codec
     fp8_kv_cache_amd.codec = codec
-    return fp8_kv_cache_amd
+    previous = fp8_kv_cache_amd.sz_compress_fused_min_elements(1)
+    yield fp8_kv_cache_amd
+    fp8_kv_cache_amd.sz_compress_fused_min_elements(previous)
 
 
 def _check_against_oracle(x, dt, stream, hist, cb):
@@ -112,6 +117,23 @@ def test_fused_schedule_shapes(sz, count, n):
         assert torch.equal(one.stream(i), three.stream(i)), i
     for i in sorted({0, count // 2, count - 1}):
         _check_against_oracle(xs[i], BF16, one.stream(i), one.hists[i], one.codebooks[i])
+
+
+@pytest.mark.parametrize("n", [(1 << 21) - 4096, 1 << 21])
+def test_default_size_threshold(sz, n):
+    """With the default threshold, a tensor just under 2^21 elements takes
+    the separate kernels and one at 2^21 the fused kernel: both give the
+    oracle's histogram, codebook and stream."""
+    previous = sz.sz_compress_fused_min_elements(0)
+    try:
+        x = kvsynth.stress(n, seed=n)
+        say("fused threshold", n)
+        stream, hist, cb, status = sz.codec.compress_fused(to_dev(x), BF16)
+        torch.cuda.synchronize()
+        assert status == 0
+        _check_against_oracle(x, BF16, stream, hist, cb)
+    finally:
+        sz.sz_compress_fused_min_elements(previous)
 
 
 def test_fused_is_deterministic(sz):

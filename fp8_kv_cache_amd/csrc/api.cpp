@@ -31,11 +31,20 @@ bool grid_ok(uint32_t count, uint64_t n) {
 
 uint64_t workspace_bytes(uint32_t count, uint64_t n) { return workspace_bytes_for(count, n); }
 
-// Work items of the fused compress kernel per tensor: counting items, one
-// codebook item, encode items.
+// The fused compress kernel's sample items per tensor: every
+// kSampleStride-th counting chunk.
+uint64_t sample_items(uint64_t n, sz_dtype dt) {
+    const uint64_t chunk = sample_chunk_elems(dt);
+    const uint64_t chunks = (n + chunk - 1) / chunk;
+    return (chunks + kSampleStride - 1) / kSampleStride;
+}
+
+// Its work items per tensor: sample items, the provisional codebook item,
+// main items (kPassWaves blocks each, the partial block included), the
+// final codebook item.
 uint64_t compress_items(uint64_t n, sz_dtype dt) {
-    const uint64_t chunk = kCountIters * 8ull * kPassThreads * (dt == SZ_DTYPE_BF16 ? 8 : 16);
-    return (n + chunk - 1) / chunk + 1 + (n / kBlockElems + kPassWaves - 1) / kPassWaves;
+    const uint64_t blocks = (n + kBlockElems - 1) / kBlockElems;
+    return sample_items(n, dt) + 1 + (blocks + kPassWaves - 1) / kPassWaves + 1;
 }
 
 uint64_t compress_workspace_bytes(uint32_t count, uint64_t n) {
@@ -73,14 +82,14 @@ sz_status encode_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, const
     return from_hip(launch_encode(a, dt, s));
 }
 
-// Histogram, codebook and encode in one launch (plus the short offset and
-// scatter launches) for BF16 tensors of at least g_fused_min elements.
-// E5M2 tensors (half the bytes per element, so twice the per-item overhead
-// per byte) measured slower fused than with the separate calls' kernels
-// (0.37 against 0.34 ms on the 64-tensor cache), and so did BF16 tensors
-// of 2 MiB and less (4 MiB: 15% faster fused, 2 MiB: 10% slower); those
-// take the separate kernels, as does n = 0.  The results are the same
-// either way.
+// Histogram, codebook and encode in one launch that reads the input once
+// (plus the short transcode, offset and scatter launches) for BF16 tensors
+// of at least g_fused_min elements.  E5M2 tensors measured slower fused
+// than with the separate calls' kernels (0.41 against 0.35 ms on the
+// 64-tensor cache: counting a byte per element in the same pass costs more
+// than a second read of half the bytes), and small BF16 tensors take the
+// separate kernels too, as does n = 0.  The results are the same either
+// way.
 sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint64_t* d_hists,
                         uint8_t* d_codebooks, DstRef dst, uint64_t* d_out_bytes, int32_t* d_status,
                         void* d_workspace, hipStream_t s) {
@@ -105,23 +114,17 @@ sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uin
     a.codebooks = d_codebooks;
     a.sync = static_cast<uint8_t*>(d_workspace) + workspace_bytes_for(count, n);
     a.status = d_status;
-    const uint64_t chunk = kCountIters * 8ull * kPassThreads * (dt == SZ_DTYPE_BF16 ? 8 : 16);
-    a.count_items = static_cast<uint32_t>((n + chunk - 1) / chunk);
-    a.encode_items = static_cast<uint32_t>((n / kBlockElems + kPassWaves - 1) / kPassWaves);
-    // (compress_items(n, dt) = count_items + 1 + encode_items; the entry points
+    const uint64_t chunk = sample_chunk_elems(dt);
+    a.sample_items = static_cast<uint32_t>(sample_items(n, dt));
+    a.sample_total = 0;
+    for (uint64_t i = 0; i < a.sample_items; ++i) {
+        const uint64_t begin = i * kSampleStride * chunk;
+        a.sample_total += n - begin < chunk ? n - begin : chunk;
+    }
+    a.main_items = static_cast<uint32_t>((layout_of(n, dt).blocks + kPassWaves - 1) / kPassWaves);
+    // (compress_items(n, dt) is the item count per tensor; the entry points
     // keep count * that below 2^31, the launch's workgroup count)
-    // Re-read each tensor once about kPassLagBytes of further input has been
-    // counted: long enough for its codebook to be published before its
-    // encode items arrive, short enough for the re-read to hit the
-    // last-level cache.  Measured optima (lags 6-8, 3 and 2 for tensors of
-    // 8, 16 and 32 MiB) all sit near 48 MiB.  Never below 2 when there are
-    // two tensors: at lag 1 the encode items arrive right behind their
-    // codebook item and stall on it.
-    const uint64_t tensor_bytes = 2 * n;
-    uint64_t lag = (kPassLagBytes + tensor_bytes / 2) / tensor_bytes;
-    lag = lag < 2 ? 2 : lag;
-    lag = lag > count ? count : lag;
-    a.lag = static_cast<uint32_t>(lag);
+    a.lag = kPassLag;
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     return from_hip(launch_compress(a, dt, s));
 }

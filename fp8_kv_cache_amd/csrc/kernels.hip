@@ -28,6 +28,16 @@ __device__ inline uint32_t valid_nibbles(int32_t valid) {
     return valid >= 8 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : ((1u << (4 * valid)) - 1u));
 }
 
+// four code nibbles (one per byte of x) -> the four codebook bytes; the
+// codebook is held in four registers cbw[0..3]
+__device__ inline uint32_t lookup4(uint32_t x, const uint32_t (&cbw)[4]) {
+    const uint32_t sel = x & 0x07070707u;
+    const uint32_t lo = perm(cbw[1], cbw[0], sel);
+    const uint32_t hi = perm(cbw[3], cbw[2], sel);
+    const uint32_t m = ((x >> 3) & 0x01010101u) * 0xFFu;
+    return (hi & m) | (lo & ~m);
+}
+
 template <uint32_t DT>
 struct Geometry;
 template <>
@@ -178,14 +188,15 @@ __device__ inline void hist_clear(uint32_t* bins, uint32_t tid) {
         *reinterpret_cast<uint4*>(bins + i) = make_uint4(0, 0, 0, 0);
 }
 
-// Fold the copies and add the sums to the tensor's u64 histogram.  Every
+// Fold the copies and add the sums to the tensor's u64 histogram (bins
+// kStride words apart).  Every
 // thread of the NT-thread workgroup calls it, after a barrier; the first
 // 256 do the folding.  `unpaired` is the number of phantom zero exponents
 // the workgroup counted (E5M2: elements counted one at a time as the pair
 // (e, 0); both types: zero padding counted past the end of a tensor); they
 // are taken off bin 0.  Rotating the start keeps the lanes of a wave on
 // distinct banks.
-template <uint32_t DT, uint32_t NT = kThreads>
+template <uint32_t DT, uint32_t NT = kThreads, uint32_t kStride = 1>
 __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64_t* hist, uint32_t unpaired) {
     static_assert(NT >= 256, "one folding thread per bin");
     const bool folds = NT == 256 || tid < 256;
@@ -194,7 +205,7 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
         uint32_t sum = tid == 0 ? 0u - unpaired : 0u;
 #pragma unroll 8
         for (uint32_t j = 0; j < 32; ++j) sum += bins[tid * 32 + ((j + tid) & 31u)];
-        if (sum) __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
+        if (sum) __hip_atomic_fetch_add(hist + tid * kStride, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
     } else {
         // thread t folds pairs 4t..4t+3 (dwords 2t, 2t+1): their first exponents
@@ -221,9 +232,21 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
         __syncthreads();
         const uint32_t sum = tid < 32 ? bins[tid] - (tid == 0 ? unpaired : 0u) : 0u;
         if (sum)
-            __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
+            __hip_atomic_fetch_add(hist + tid * kStride, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+// Count elements [begin, end) one at a time (a ragged end; NT threads).
+// Returns the phantom zero exponents to take off bin 0: E5M2 counts each
+// element as the pair (e, 0); BF16 counts exactly.
+template <uint32_t DT, uint32_t NT>
+__device__ inline uint32_t count_ragged(char* lds, const SZ_GLOBAL uint8_t* src, uint64_t begin, uint64_t end,
+                                        uint32_t tid) {
+    const uint32_t copy4 = hist_lane_bytes<DT>(tid);
+    for (uint64_t i = begin + tid; i < end; i += NT)
+        count_one<DT>(lds, DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i], copy4);
+    return DT == kDtypeE5M2 ? static_cast<uint32_t>(end - begin) : 0u;
 }
 
 // Count elements [begin, end) of src into the workgroup's LDS copies (NT
@@ -253,10 +276,7 @@ __device__ inline uint32_t count_range(char* lds, const SZ_GLOBAL uint8_t* src, 
             count_dword<DT>(lds, v[p].w, copy4);
         }
     }
-    // ragged end of the range: element-wise guarded reads
-    for (uint64_t i = base + tid; i < end; i += NT)
-        count_one<DT>(lds, DT == kDtypeBF16 ? ((const SZ_GLOBAL uint16_t*)src)[i] : src[i], copy4);
-    return DT == kDtypeE5M2 ? static_cast<uint32_t>(end - base) : 0u;
+    return count_ragged<DT, NT>(lds, src, base, end, tid);
 }
 
 // Each workgroup counts one contiguous chunk of one tensor.  The grid
@@ -399,13 +419,20 @@ __device__ inline void write_header(SZ_GLOBAL uint8_t* dst, const Layout& L, uin
 // BF16: eight elements d[0..3] -> 8 sign|mantissa bytes and 8 code
 // nibbles; elements at index >= valid get code 0 and zero bytes (they are
 // zero in d already).  Returns the escape nibble mask in esc[0].
+template <bool kCount = false>
 __device__ inline void encode_lane_bf16(const uint32_t (&d)[4], uint32_t valid, const uint8_t* tbl,
-                                        uint32_t (&sm)[2], uint32_t (&cw)[1], uint32_t (&esc)[1]) {
+                                        uint32_t (&sm)[2], uint32_t (&cw)[1], uint32_t (&esc)[1],
+                                        char* bins = nullptr, uint32_t copy4 = 0) {
     uint32_t c[8];
 #pragma unroll
     for (uint32_t k = 0; k < 4; ++k) {
-        c[2 * k] = tbl[(d[k] >> 7) & 0xFFu];
-        c[2 * k + 1] = tbl[(d[k] >> 23) & 0xFFu];
+        const uint32_t e0 = (d[k] >> 7) & 0xFFu, e1 = (d[k] >> 23) & 0xFFu;
+        c[2 * k] = tbl[e0];
+        c[2 * k + 1] = tbl[e1];
+        if (kCount) {   // the exponent histogram, from the same fields (full blocks only)
+            atomicAdd(reinterpret_cast<uint32_t*>(bins + ((e0 << 7) | copy4)), 1u);
+            atomicAdd(reinterpret_cast<uint32_t*>(bins + ((e1 << 7) | copy4)), 1u);
+        }
     }
     if (valid < 8) {
 #pragma unroll
@@ -490,20 +517,10 @@ __device__ inline void load_block(const SZ_GLOBAL uint8_t* src, uint64_t n, uint
     }
 }
 
-// Encode block b from its registers into stream dst: planes, the block's
-// escape count and its staged escape bytes (flat = the block's index over
-// all tensors).  `mine` is codebook entry cb[lane] for lanes below 15 (any
-// value above 255 elsewhere).
-template <uint32_t DT, bool kFull>
-__device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b,
-                                     uint64_t flat, uint32_t lane, uint32_t* tbl_words, uint32_t mine,
-                                     const BlockRegs<DT>& d) {
-    using G = Geometry<DT>;
-    constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
-    constexpr uint32_t kSmWords = G::kSmWords;
-    const uint64_t blk0 = b * kBlockElems;
-
-    // Code of every exponent value: the lowest c with cb[c] == v, else 15.
+// The wave's table of codes (256 bytes in tbl_words): the code of value v
+// is the lowest c with cb[c] == v, else 15.  `mine` is cb[lane] for lanes
+// below 15 (any value above 255 elsewhere).
+__device__ inline const uint8_t* build_code_table(uint32_t* tbl_words, uint32_t lane, uint32_t mine) {
     uint8_t* tbl = reinterpret_cast<uint8_t*>(tbl_words);
     tbl_words[lane] = 0x0F0F0F0Fu;
     bool lowest = lane < kCodes;
@@ -514,6 +531,23 @@ __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GL
     }
     if (lowest) tbl[mine] = static_cast<uint8_t>(lane);
     __builtin_amdgcn_wave_barrier();
+    return tbl;
+}
+
+// Encode block b from its registers into stream dst with the code table
+// tbl: planes, the block's escape count and its staged escape bytes (flat
+// = the block's index over all tensors).  kCount (full blocks): the
+// block's exponents are also counted into the LDS histogram copies `bins`
+// (copy4: this lane's copy), BF16 from the fields the lookups extract.
+template <uint32_t DT, bool kFull, bool kCount = false>
+__device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b,
+                                     uint64_t flat, uint32_t lane, const uint8_t* tbl, const BlockRegs<DT>& d,
+                                     char* bins = nullptr, uint32_t copy4 = 0) {
+    static_assert(!kCount || kFull, "counting in the encode covers full blocks only");
+    using G = Geometry<DT>;
+    constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
+    constexpr uint32_t kSmWords = G::kSmWords;
+    const uint64_t blk0 = b * kBlockElems;
 
     uint32_t sm[G::kSubs][kSmWords];
     uint32_t cw[G::kSubs][G::kCodeWords];
@@ -526,10 +560,15 @@ __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GL
                                : elem0 >= a.n ? 0u
                                : (a.n - elem0 >= G::kLaneElems ? G::kLaneElems
                                                                  : static_cast<uint32_t>(a.n - elem0));
-        if constexpr (DT == kDtypeBF16)
-            encode_lane_bf16(d[j], valid, tbl, sm[j], cw[j], esc[j]);
-        else
+        if constexpr (DT == kDtypeBF16) {
+            encode_lane_bf16<kCount>(d[j], valid, tbl, sm[j], cw[j], esc[j], bins, copy4);
+        } else {
             encode_lane_e5m2(d[j], valid, tbl, sm[j], cw[j], esc[j]);
+            if (kCount) {
+#pragma unroll
+                for (uint32_t i = 0; i < G::kInWords; ++i) count_dword<DT>(bins, d[j][i], copy4);
+            }
+        }
         cnt[j] = 0;
 #pragma unroll
         for (uint32_t q = 0; q < G::kCodeWords; ++q) cnt[j] += __builtin_popcount(esc[j][q]);
@@ -619,7 +658,7 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
     BlockRegs<DT> d;
     load_block<DT, kFull>(src, a.n, b, lane, d);
     __builtin_amdgcn_sched_barrier(0);
-    encode_loaded<DT, kFull>(a, L, dst, b, flat, lane, tbl_words, mine, d);
+    encode_loaded<DT, kFull>(a, L, dst, b, flat, lane, build_code_table(tbl_words, lane, mine), d);
 }
 
 // Full blocks only: wave i of the grid takes the i-th full block in
@@ -757,68 +796,78 @@ __global__ void k_encode_empty(EncodeArgs a) {
 
 // ---------------------------------------------------- one-launch compress
 //
-// Histogram, codebook and encode of every tensor in one launch.  A tensor's
-// codebook depends on all of its exponents, so its input is read twice; the
-// launch orders the work so that the second read follows the first closely
-// enough to be served mostly from the GPU's 256 MB last-level cache (MALL),
-// and without the separate calls' launch boundaries.
+// Histogram, codebook and encode of every tensor in one launch that reads
+// the input once.  A tensor's codebook depends on all of its exponents, but
+// a sample of them nearly always ranks the same values first, so each
+// tensor is coded with a provisional codebook built from a sample and
+// checked against the final codebook afterwards.  Work items:
+//   sample item (every kSampleStride-th 128 KB chunk of the tensor): counts
+//     its chunk into the tensor's sample histogram.  It never waits.
+//   provisional item: polls the sample histogram until it is complete (its
+//     bins sum to the sampled element count; counts only grow), ranks the
+//     values (count descending, then value ascending) and publishes the
+//     first 15 as the provisional codebook.
+//   main item (16 blocks, one per wave): loads its blocks, counts them into
+//     the tensor's full histogram (the item that holds a partial last block
+//     counts that block too), then waits for the provisional codebook and
+//     encodes its full blocks with it exactly as k_encode does.
+//   final item: polls the full histogram until it is complete, writes the
+//     histogram and codebook outputs and records whether the provisional
+//     codebook is the final one.
+// Where it is not, k_transcode rewrites the tensor's code nibbles and
+// staged escapes for the final codebook from what the main items wrote,
+// without reading the input again.  It is a separate launch, so what this
+// kernel wrote is visible to it without cache maintenance.  The partial
+// last block of a tensor is left to k_encode_tail, which runs with the
+// final codebook.
 //
 // Work items are handed out by a ticket counter in the order workgroups
-// start, in stages: stage s holds the counting items of tensor s (one
-// 128 KB chunk each), then the codebook item of tensor s - 1, then the
-// encode items of tensor s - lag (16 blocks, one per wave of the 1024-thread
-// workgroup).  So tensor t is
-// re-read `lag` stages after it was counted.
-//   counting item: counts its chunk in LDS and adds the counts to the
-//     tensor's u64 histogram in the workspace.  It never waits.
-//   codebook item: polls the tensor's histogram until it is complete --
-//     counts only grow and add up to n, so a reading of the bins that sums
-//     to n is the final histogram -- then writes the histogram output,
-//     ranks the values (count descending, then value ascending) and
-//     publishes the codebook.
-//   encode item: issues its blocks' loads, waits for the publication
-//     (normally long done), reads the codebook and encodes its full blocks
-//     exactly as k_encode does; a partial last block is left to
-//     k_encode_tail.
-// A codebook item waits only for counting items and an encode item only
-// for a codebook item; both hold earlier tickets, so they belong to running
-// workgroups, and none of them waits on a later ticket: the launch always
-// makes progress, whatever else shares the GPU.  The wait is still bounded: after
-// spin_limit polls, or once any workgroup has given up, a workgroup sets its
-// tensor's status, zeroes its blocks' escape counts and leaves.
+// start, in stages (pass_plan): stage s holds the sample items of tensor s,
+// the provisional item of tensor s - 1, the main items of tensor s - lag
+// and the final item of tensor s - lag - 1.  Every wait is for items with
+// earlier tickets (a provisional item for sample items, a main item for
+// the provisional item, a final item for main items and the provisional
+// item), and sample items never wait, so every awaited workgroup is already
+// running or done: the launch always makes progress, whatever else shares
+// the GPU.  The waits are still bounded: after spin_limit polls, or once
+// any workgroup has given up, a workgroup sets its tensor's status, zeroes
+// its blocks' escape counts and leaves.
 //
 // Signalling between workgroups uses no cache-wide maintenance.  Everything
-// one workgroup tells another inside the kernel travels through
+// one workgroup tells another inside the kernel travels through relaxed
 // agent-scope atomics, which are coherent across the XCDs' L2 caches:
-// read-modify-writes (histogram counts, tickets) or sc1 loads and stores
-// (the published flags, the abort word, the codebook).  A flag is raised
-// only after the codebook stores have completed (the storing waves wait for
-// their memory counter to drain, then the workgroup barriers).  Agent-scope
-// acquire/release orderings would instead write back or invalidate a whole
-// L2 at every publication and at every poll of every waiting workgroup.
+// read-modify-writes (histogram counts, tickets, the list) or sc1 loads and
+// stores (the abort word, the provisional codebook).  The provisional
+// codebook needs no separate flag and no store order: a reading of its
+// four words is complete exactly when its 15 bytes differ (see
+// codebook_complete).  Agent-scope acquire/release orderings would instead
+// write back or invalidate a whole L2 at every publication and at every
+// poll of every waiting workgroup.
 
 struct SyncView {
-    SZ_GLOBAL uint64_t* hist;   // count x 256
+    SZ_GLOBAL uint64_t* hist;     // count x 256 bins (kHistStride apart), whole tensors
+    SZ_GLOBAL uint64_t* sample;   // count x 256 bins (kHistStride apart), sampled chunks
     SZ_GLOBAL uint32_t* ticket;
     SZ_GLOBAL uint32_t* abort;
-    SZ_GLOBAL uint32_t* flags;  // per tensor a 128-byte record; word 0: codebook published
+    SZ_GLOBAL uint32_t* listed;   // entries of `list` in use
+    SZ_GLOBAL uint32_t* records;  // per tensor 32 words, see kRec*
+    SZ_GLOBAL uint32_t* list;     // count: tensors to transcode
 };
+
+constexpr uint32_t kRecProvisional = 0;  // 4 words: the provisional codebook (complete once 15 bytes differ)
+constexpr uint32_t kRecVerdict = 8;      // kProvisionalSame / kProvisionalDiffers
 
 __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     SyncView v;
     v.hist = gptr(reinterpret_cast<uint64_t*>(base));
-    SZ_GLOBAL uint32_t* w = gptr(reinterpret_cast<uint32_t*>(base + 2048ull * count));
+    v.sample = v.hist + 256ull * kHistStride * count;
+    SZ_GLOBAL uint32_t* w = gptr(reinterpret_cast<uint32_t*>(base + 4096ull * kHistStride * count));
     v.ticket = w;
     v.abort = w + 1;
-    v.flags = w + 64;
+    v.listed = w + 2;
+    v.records = w + 64;
+    v.list = v.records + 32ull * count;
     return v;
-}
-
-// This wave's global loads, stores and atomics so far have completed.
-__device__ inline void drain_memory() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited on
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 __device__ inline uint32_t load_agent(const SZ_GLOBAL uint32_t* p) {
@@ -835,145 +884,229 @@ __device__ inline void store_agent(SZ_GLOBAL uint32_t* p, uint32_t v) {
 
 constexpr int32_t kStatusGaveUp = 5;   // SZ_ERR_TIMEOUT
 
-// Elements per counting item: kCountIters iterations of count_range (each
-// 8 passes of a 16-byte vector per lane of the 1024-thread workgroup,
-// 128 KB of input).
+// A reading of a tensor's provisional codebook (lanes 0..3 of a wave each
+// hold one of its words) is complete when bytes 0..14 are 15 distinct
+// values: the record starts zeroed and every published codebook lists 15
+// distinct values, so a reading that mixes published and still-zero words
+// repeats a byte.  No flag, and no order among the four word stores, is
+// needed.  Every lane of the wave calls it and gets the same result; lane c
+// below 15 also gets byte c in `mine`.
+__device__ inline bool codebook_complete(uint32_t word, uint32_t lane, uint32_t& mine) {
+    const uint32_t w0 = __builtin_amdgcn_readlane(word, 0), w1 = __builtin_amdgcn_readlane(word, 1);
+    const uint32_t w2 = __builtin_amdgcn_readlane(word, 2), w3 = __builtin_amdgcn_readlane(word, 3);
+    const uint32_t c = lane < kCodes ? lane : 0u;
+    const uint32_t w = c < 4 ? w0 : (c < 8 ? w1 : (c < 12 ? w2 : w3));
+    mine = (w >> (8 * (c & 3u))) & 0xFFu;
+    bool dup = false;
+#pragma unroll
+    for (uint32_t k = 0; k + 1 < kCodes; ++k) {
+        const uint32_t other = __builtin_amdgcn_readlane(mine, k);
+        if (k < c && other == mine) dup = true;
+    }
+    return __ballot(dup) == 0;
+}
+
+// One wave waits for a complete reading of the provisional codebook at
+// `words`, starting from the reading it holds (`word`, lanes 0..3; updated
+// by every poll).  Returns true with lane c's byte in `mine` (c < 15),
+// false after spin_limit polls (raising the abort word) or once the abort
+// word is up.  Every lane of the wave calls it and gets the same result.
+__device__ inline bool wait_codebook(const SZ_GLOBAL uint32_t* words, uint32_t& word, const SyncView& sv,
+                                     uint32_t spin_limit, uint32_t lane, uint32_t& mine) {
+    for (uint32_t polls = 0;; ++polls) {
+        if (codebook_complete(word, lane, mine)) return true;
+        if (polls >= spin_limit) {
+            if (lane == 0) store_agent(sv.abort, 1u);
+            return false;
+        }
+        if (uniform(load_agent(sv.abort))) return false;
+        __builtin_amdgcn_s_sleep(8);
+        if (lane < 4) word = load_agent(words + lane);
+    }
+}
+
+// Every thread of the workgroup polls a tensor's histogram until its bins
+// sum to `total` (counts only grow, so that reading is final).  Returns 1
+// with c = this thread's bin (0 for threads past the domain), or 2 after
+// giving up.  Uses s_word[8..12].
 template <uint32_t DT>
-constexpr uint64_t count_chunk() {
-    return kCountIters * 8ull * kPassThreads * (16 / Geometry<DT>::kElemBytes);
+__device__ inline uint32_t wait_histogram(const SZ_GLOBAL uint64_t* hist, uint64_t total, const SyncView& sv,
+                                          uint32_t spin_limit, uint32_t* s_word, uint32_t tid, uint32_t lane,
+                                          uint32_t wave, uint64_t& c) {
+    constexpr uint32_t D = Geometry<DT>::kDomain;
+    for (uint32_t polls = 0;; ++polls) {
+        c = tid < D ? load_agent(hist + tid * kHistStride) : 0;
+        const uint32_t sum = __builtin_amdgcn_readlane(wave_scan_incl(static_cast<uint32_t>(c)), 63);
+        if (lane == 0 && wave < 4) s_word[8 + wave] = sum;   // counts are at most n < 2^32
+        __syncthreads();
+        if (tid == 0) {
+            const uint64_t got = static_cast<uint64_t>(s_word[8]) + s_word[9] + s_word[10] + s_word[11];
+            uint32_t st = got == total ? 1u : 0u;
+            if (!st && polls >= spin_limit) {
+                store_agent(sv.abort, 1u);
+                st = 2;
+            }
+            if (!st && load_agent(sv.abort)) st = 2;
+            s_word[12] = st;
+        }
+        __syncthreads();
+        const uint32_t state = s_word[12];
+        if (state) return state;
+        __syncthreads();   // every thread has read this round's words before the next round rewrites them
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+// Rank the values of the domain by (count descending, value ascending);
+// the values of rank 0..14 become the codebook, left in s_word[2..5] (byte
+// 15 zero).  c: this thread's bin.  The workgroup's kParts groups of 256
+// threads each compare against a share of the keys; bins holds the keys
+// and the partial ranks.  Ends with a barrier.
+template <uint32_t DT>
+__device__ inline void rank_codebook(uint64_t c, uint32_t* bins, uint32_t* s_word, uint32_t tid) {
+    constexpr uint32_t D = Geometry<DT>::kDomain;
+    constexpr uint32_t kParts = kPassThreads / 256;
+    uint64_t* keys = reinterpret_cast<uint64_t*>(bins);
+    uint32_t* parts = bins + 2 * 256;   // [kParts][256] partial ranks, after the keys
+    if (tid < D) keys[tid] = (c << 8) | (255u - tid);
+    if (tid < 4) s_word[2 + tid] = 0;
+    __syncthreads();
+    const uint32_t v = tid & 255u, q = tid >> 8;
+    if (v < D) {
+        const uint64_t key = keys[v];
+        uint32_t part = 0;
+        for (uint32_t u = q * (D / kParts); u < (q + 1) * (D / kParts); ++u) part += keys[u] > key ? 1u : 0u;
+        parts[q * 256 + v] = part;
+    }
+    __syncthreads();
+    if (q == 0 && v < D) {
+        uint32_t rank = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kParts; ++k) rank += parts[k * 256 + v];
+        if (rank < kCodes) reinterpret_cast<uint8_t*>(s_word + 2)[rank] = static_cast<uint8_t>(v);
+    }
+    __syncthreads();
 }
 
 // One work item; every thread of the workgroup calls it and every return
-// is taken by all of them.  LDS: bins (counting and ranking), s_tbl (one
-// code table per wave), s_word ([2..5] codebook, [8..12] poll words).
+// is taken by all of them.  LDS: bins (counting and ranking), s_tbl (the
+// code table, 256 bytes), s_word ([2..5] codebook, [8..13] poll words,
+// [16..19] the provisional codebook in the final item; [0], [14], [15]
+// hold the item and are not written).
 template <uint32_t DT>
 __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const PassItem& it, uint32_t* bins,
-                                uint32_t (*s_tbl)[64], uint32_t* s_word, uint32_t tid, uint32_t lane,
-                                uint32_t wave) {
-    using G = Geometry<DT>;
-    constexpr uint32_t D = G::kDomain;
+                                uint32_t* s_tbl, uint32_t* s_word, uint32_t tid, uint32_t lane, uint32_t wave) {
     const uint32_t t = it.t;
+    const uint64_t n = a.enc.n;
     const SZ_GLOBAL uint8_t* src = src_of(a.enc.src, t);
+    char* lds = reinterpret_cast<char*>(bins);
+    SZ_GLOBAL uint32_t* rec = sv.records + 32ull * t;
 
-    if (it.kind == kItemCount) {
-        // ---- counting item
+    if (it.kind == kItemSample) {
+        // ---- sample item: chunk idx * kSampleStride
         hist_clear<DT, kPassThreads>(bins, tid);
         __syncthreads();
-        const uint64_t begin = static_cast<uint64_t>(it.idx) * count_chunk<DT>();
-        const uint64_t end = begin + count_chunk<DT>() < a.enc.n ? begin + count_chunk<DT>() : a.enc.n;
-        const uint32_t phantom = count_range<DT, kPassThreads>(reinterpret_cast<char*>(bins), src, begin, end, tid);
+        const uint64_t chunk = sample_chunk_elems(DT);
+        const uint64_t begin = static_cast<uint64_t>(it.idx) * kSampleStride * chunk;
+        const uint64_t end = n - begin < chunk ? n : begin + chunk;
+        const uint32_t phantom = count_range<DT, kPassThreads>(lds, src, begin, end, tid);
         __syncthreads();
-        hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * t, phantom);
+        hist_flush<DT, kPassThreads, kHistStride>(bins, tid, sv.sample + 256ull * kHistStride * t, phantom);
         return;
     }
-    SZ_GLOBAL uint32_t* published = sv.flags + 32ull * t;
-    SZ_GLOBAL uint32_t* cbw = gptr(reinterpret_cast<uint32_t*>(a.codebooks + 16ull * t));
 
-    if (it.kind == kItemCodebook) {
-        // ---- codebook item: wait until the histogram is complete
-        const SZ_GLOBAL uint64_t* hist = sv.hist + 256ull * t;
+    if (it.kind == kItemProvisional) {
+        // ---- provisional item: rank the sample, publish the codebook
         uint64_t c = 0;
-        uint32_t state = 0;   // 1 complete (c holds this thread's bin), 2 give up
-        for (uint32_t polls = 0;; ++polls) {
-            c = tid < D ? load_agent(hist + tid) : 0;
-            const uint32_t sum = __builtin_amdgcn_readlane(wave_scan_incl(static_cast<uint32_t>(c)), 63);
-            if (lane == 0 && wave < 4) s_word[8 + wave] = sum;   // counts are at most n < 2^32
-            __syncthreads();
-            if (tid == 0) {
-                const uint64_t total = static_cast<uint64_t>(s_word[8]) + s_word[9] + s_word[10] + s_word[11];
-                uint32_t st = total == a.enc.n ? 1u : 0u;
-                if (!st && polls >= a.spin_limit) {
-                    store_agent(sv.abort, 1u);
-                    st = 2;
-                }
-                if (!st && load_agent(sv.abort)) st = 2;
-                s_word[12] = st;
-            }
-            __syncthreads();
-            state = s_word[12];
-            if (state) break;
-            __syncthreads();   // every thread has read this round's words before the next round rewrites them
-            __builtin_amdgcn_s_sleep(8);
-        }
-        if (state != 1) {
+        if (wait_histogram<DT>(sv.sample + 256ull * kHistStride * t, a.sample_total, sv, a.spin_limit, s_word, tid, lane, wave,
+                               c) != 1) {
             if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
             return;
         }
-        // rank of value v = number of keys above its own; the workgroup's
-        // kParts groups of 256 threads each compare against a share of the keys
-        constexpr uint32_t kParts = kPassThreads / 256;
-        if (tid < 256) gptr(a.hists)[256ull * t + tid] = c;
-        uint64_t* keys = reinterpret_cast<uint64_t*>(bins);
-        uint32_t* parts = bins + 2 * 256;   // [kParts][256] partial ranks, after the keys
-        if (tid < D) keys[tid] = (c << 8) | (255u - tid);
-        if (tid < 4) s_word[2 + tid] = 0;
-        __syncthreads();
-        const uint32_t v = tid & 255u, q = tid >> 8;
-        if (v < D) {
-            const uint64_t key = keys[v];
-            uint32_t part = 0;
-            for (uint32_t u = q * (D / kParts); u < (q + 1) * (D / kParts); ++u) part += keys[u] > key ? 1u : 0u;
-            parts[q * 256 + v] = part;
-        }
-        __syncthreads();
-        if (q == 0 && v < D) {
-            uint32_t rank = 0;
-#pragma unroll
-            for (uint32_t k = 0; k < kParts; ++k) rank += parts[k * 256 + v];
-            if (rank < kCodes) reinterpret_cast<uint8_t*>(s_word + 2)[rank] = static_cast<uint8_t>(v);
-        }
-        __syncthreads();
-        if (tid < 4) store_agent(cbw + tid, s_word[2 + tid]);
-        drain_memory();    // the codebook is out before the flag
-        __syncthreads();
-        if (tid == 0) store_agent(published, 1u);
+        rank_codebook<DT>(c, bins, s_word, tid);
+        if (tid < 4) store_agent(rec + kRecProvisional + tid, s_word[2 + tid]);   // the publication itself
         return;
     }
-    if (it.kind != kItemEncode) return;
 
-    // ---- encode item: blocks 16 * idx + wave of tensor t, full blocks only;
-    // the loads are issued before the wait for the codebook
-    const Layout L = layout_of(a.enc.n, DT);
-    const uint64_t full_blocks = a.enc.n / kBlockElems;
+    if (it.kind == kItemFinal) {
+        // ---- final item: rank the whole histogram, compare with the provisional codebook
+        uint64_t c = 0;
+        uint32_t ok = wait_histogram<DT>(sv.hist + 256ull * kHistStride * t, n, sv, a.spin_limit, s_word, tid, lane, wave, c) == 1;
+        if (ok) {
+            if (wave == 0) {
+                uint32_t word = lane < 4 ? load_agent(rec + kRecProvisional + lane) : 0u, mine;
+                const bool got = wait_codebook(rec + kRecProvisional, word, sv, a.spin_limit, lane, mine);
+                if (got && lane < 4) s_word[16 + lane] = word;
+                if (lane == 0) s_word[13] = got ? 1u : 0u;
+            }
+            __syncthreads();
+            ok = s_word[13];
+        }
+        if (!ok) {
+            if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
+            return;
+        }
+        if (tid < 256) gptr(a.hists)[256ull * t + tid] = c;
+        rank_codebook<DT>(c, bins, s_word, tid);
+        if (tid < 4) gptr(reinterpret_cast<uint32_t*>(a.codebooks + 16ull * t))[tid] = s_word[2 + tid];
+        if (tid == 0) {
+            bool same = true;
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) same &= s_word[16 + k] == s_word[2 + k];
+            store_agent(rec + kRecVerdict, same ? kProvisionalSame : kProvisionalDiffers);
+            if (!same) {
+                const uint32_t at = __hip_atomic_fetch_add(sv.listed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sv.list[at] = t;   // read by the next launch; at most count tensors are listed
+            }
+        }
+        return;
+    }
+    if (it.kind != kItemMain) return;
+
+    // ---- main item: blocks 16 * idx + wave of tensor t.  Block loads and
+    // the provisional codebook first (it is normally complete long before);
+    // wave 0 checks the codebook and builds the one code table all 16 waves
+    // share, while the LDS histogram is cleared; then every wave encodes its
+    // block and counts its exponents in the same pass, and the item adds
+    // its counts to the tensor's histogram.
+    const Layout L = layout_of(n, DT);
+    const uint64_t full_blocks = n / kBlockElems;
     const uint64_t b = static_cast<uint64_t>(it.idx) * kPassWaves + wave;
     const bool mine_full = b < full_blocks;
     const uint64_t flat = static_cast<uint64_t>(t) * L.blocks + b;
-    SZ_GLOBAL uint8_t* dst = dst_of(a.enc.dst, t);
+    uint32_t word = wave == 0 && lane < 4 ? load_agent(rec + kRecProvisional + lane) : 0u;
     BlockRegs<DT> d;
-    if (mine_full) load_block<DT, true>(src, a.enc.n, b, lane, d);
-    if (tid == 0) {
-        uint32_t ok = 0;
-        for (uint32_t polls = 0;; ++polls) {
-            if (load_agent(published)) {
-                ok = 1;
-                break;
-            }
-            if (polls >= a.spin_limit) {
-                store_agent(sv.abort, 1u);
-                break;
-            }
-            if (load_agent(sv.abort)) break;
-            __builtin_amdgcn_s_sleep(8);
-        }
-        if (ok) {
-            drain_memory();    // the codebook is read only after the flag was seen
-#pragma unroll
-            for (uint32_t k = 0; k < 4; ++k) s_word[2 + k] = load_agent(cbw + k);
-        }
-        s_word[12] = ok;
+    if (mine_full) load_block<DT, true>(src, n, b, lane, d);
+    hist_clear<DT, kPassThreads>(bins, tid);
+    if (wave == 0) {
+        uint32_t mine;
+        const bool got = wait_codebook(rec + kRecProvisional, word, sv, a.spin_limit, lane, mine);
+        if (got) build_code_table(s_tbl, lane, lane < kCodes ? mine : 0xFFFFu);
+        if (lane == 0) s_word[12] = got ? 1u : 0u;
     }
     __syncthreads();
-    if (!s_word[12]) {
-        // gave up: no escapes for these blocks (so the scatter that follows
+    if (mine_full) {
+        const uint32_t copy4 = hist_lane_bytes<DT>(tid);
+#pragma unroll
+        for (uint32_t j = 0; j < Geometry<DT>::kSubs; ++j)
+#pragma unroll
+            for (uint32_t i = 0; i < Geometry<DT>::kInWords; ++i) count_dword<DT>(lds, d[j][i], copy4);
+    }
+    if (s_word[12]) {
+        if (mine_full)
+            encode_loaded<DT, true>(a.enc, L, dst_of(a.enc.dst, t), b, flat, lane,
+                                    reinterpret_cast<const uint8_t*>(s_tbl), d);
+    } else {
+        // gave up: no escapes for this block (so the scatter that follows
         // stays inside the stream) and an error for the tensor
         if (mine_full && lane == 0) gptr(a.enc.counts)[flat] = 0;
         if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
-        return;
     }
-    if (mine_full) {
-        const uint32_t mine = lane < kCodes ? reinterpret_cast<const uint8_t*>(s_word + 2)[lane] : 0xFFFFu;
-        encode_loaded<DT, true>(a.enc, L, dst, b, flat, lane, s_tbl[wave], mine, d);
-    }
+    uint32_t phantom = 0;
+    if (n % kBlockElems && full_blocks / kPassWaves == it.idx)   // the partial last block is in this item
+        phantom = count_ragged<DT, kPassThreads>(lds, src, full_blocks * kBlockElems, n, tid);
+    __syncthreads();
+    hist_flush<DT, kPassThreads, kHistStride>(bins, tid, sv.hist + 256ull * kHistStride * t, phantom);
 }
 
 // One workgroup per item: the ticket taken at the start fixes the item.
@@ -981,28 +1114,248 @@ template <uint32_t DT>
 __global__ __launch_bounds__(kPassThreads, 8) void k_compress(CompressArgs a) {
     static_assert(kPassThreads % 256 == 0 && Geometry<DT>::kDomain % (kPassThreads / 256) == 0, "rank split");
     __shared__ uint32_t bins[HistLds<DT>::kWords];
-    __shared__ uint32_t s_tbl[kPassWaves][64];
-    __shared__ uint32_t s_word[16];   // [0] ticket
+    __shared__ uint32_t s_tbl[64];    // the code table of a main item, shared by its waves
+    __shared__ uint32_t s_word[20];   // [0], [14], [15] the item
     const uint32_t tid = threadIdx.x, lane = lane_id();
     const uint32_t wave = uniform(tid / kWaveSize);
     const SyncView sv = sync_view(a.sync, a.enc.count);
-    if (tid == 0) s_word[0] = __hip_atomic_fetch_add(sv.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        // one thread locates the item (the schedule arithmetic stays out of
+        // the scalar registers the rest of the kernel needs)
+        const uint32_t ticket = __hip_atomic_fetch_add(sv.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const PassItem it = pass_item(ticket, pass_plan(a));
+        s_word[0] = it.kind;
+        s_word[14] = it.t;
+        s_word[15] = it.idx;
+    }
     __syncthreads();
-    const PassItem it = pass_item(s_word[0], a.enc.count, a.count_items, a.encode_items, a.lag);
+    const PassItem it{uniform(s_word[0]), uniform(s_word[14]), uniform(s_word[15])};
     run_item<DT>(a, sv, it, bins, s_tbl, s_word, tid, lane, wave);
 }
 
-// ----------------------------------------------------------------- decode
-
-// four code nibbles (one per byte of x) -> the four codebook bytes; the
-// codebook is held in four registers cbw[0..3]
-__device__ inline uint32_t lookup4(uint32_t x, const uint32_t (&cbw)[4]) {
-    const uint32_t sel = x & 0x07070707u;
-    const uint32_t lo = perm(cbw[1], cbw[0], sel);
-    const uint32_t hi = perm(cbw[3], cbw[2], sel);
-    const uint32_t m = ((x >> 3) & 0x01010101u) * 0xFFu;
-    return (hi & m) | (lo & ~m);
+// Byte c (0..15) of a 16-byte table held in four registers; c may differ
+// between lanes (a byte permute, not an indexed register array).
+__device__ inline uint32_t table_byte(const uint32_t (&w)[4], uint32_t c) {
+    return lookup4(c & 0xFu, w) & 0xFFu;
 }
+
+// What a wave reads of block b before recoding it: the code words, the
+// escape count and the first 256 staged escape bytes (16 bytes in each of
+// lanes 0..15; most blocks have fewer escapes, and the rest, if any, is
+// read when the block is recoded).  None of it depends on the count, so
+// the reads of the next block are in flight while this one is recoded.
+template <uint32_t DT>
+struct TranscodeIn {
+    uint32_t cw[Geometry<DT>::kSubs][Geometry<DT>::kCodeWords];
+    uint32_t count;
+    u32x4 head;
+};
+
+template <uint32_t DT>
+__device__ inline void transcode_read(const EncodeArgs& a, const Layout& L, const SZ_GLOBAL uint8_t* dst, uint64_t b,
+                                      uint64_t flat, uint32_t lane, TranscodeIn<DT>& in) {
+    using G = Geometry<DT>;
+    constexpr uint32_t kSubBytes = kWaveSize * G::kLaneElems / 2;   // code bytes per sub-chunk
+    const SZ_GLOBAL uint8_t* codes = dst + L.code_at + b * (kBlockElems / 2) + lane * (G::kLaneElems / 2);
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        if constexpr (G::kCodeWords == 1) {
+            in.cw[j][0] = *(const SZ_GLOBAL uint32_t*)(codes + j * kSubBytes);
+        } else {
+            const u32x4 v = *(const SZ_GLOBAL u32x4*)(codes + j * kSubBytes);
+            in.cw[j][0] = v.x; in.cw[j][1] = v.y; in.cw[j][2] = v.z; in.cw[j][3] = v.w;
+        }
+    }
+    in.count = gptr(a.counts)[flat];
+    in.head = lane < 16 ? *(const SZ_GLOBAL u32x4*)(gptr(a.staging) + flat * kBlockElems + 16 * lane)
+                        : u32x4{0, 0, 0, 0};
+}
+
+// Block b, coded with codebook P (bytes pw), recoded for the codebook whose
+// code table is tbl.  map: P's code c -> the new code of value P[c] (15 ->
+// 15).  The block's P escapes are copied to LDS (esc) first, so the new
+// escapes can be staged in their place.  An escape count or code plane that
+// was never written (a tensor that gave up) is harmless: every rank stays
+// below 4096, inside the block's LDS copy and staging slot.
+template <uint32_t DT>
+__device__ inline void transcode_block(const EncodeArgs& a, const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b,
+                                       uint64_t flat, uint32_t lane, const uint8_t* tbl, const uint32_t (&map)[4],
+                                       const uint32_t (&pw)[4], uint32_t* esc_words, const TranscodeIn<DT>& in) {
+    using G = Geometry<DT>;
+    constexpr uint32_t kCW = G::kCodeWords;
+    SZ_GLOBAL uint8_t* stage = gptr(a.staging) + flat * kBlockElems;
+    uint32_t old_total = uniform(in.count);
+    old_total = old_total < kBlockElems ? old_total : kBlockElems;
+    if (lane < 16) {
+        esc_words[4 * lane] = in.head.x; esc_words[4 * lane + 1] = in.head.y;
+        esc_words[4 * lane + 2] = in.head.z; esc_words[4 * lane + 3] = in.head.w;
+    }
+    for (uint32_t i = 256 + lane * 16; i < old_total; i += kWaveSize * 16) {
+        const u32x4 v = *(const SZ_GLOBAL u32x4*)(stage + i);
+        esc_words[i / 4] = v.x; esc_words[i / 4 + 1] = v.y; esc_words[i / 4 + 2] = v.z; esc_words[i / 4 + 3] = v.w;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint8_t* esc = reinterpret_cast<const uint8_t*>(esc_words);
+
+    // Element order is (sub-chunk, lane, element), so sub-chunks are taken
+    // in order, two at a time, with running old and new escape ranks.
+    constexpr uint32_t kSubBytes = kWaveSize * G::kLaneElems / 2;
+    SZ_GLOBAL uint8_t* codes = dst + L.code_at + b * (kBlockElems / 2) + lane * (G::kLaneElems / 2);
+    uint32_t orun = 0, nrun = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; j += 2) {
+        // old ranks of this lane's first escape in sub-chunks j and j + 1
+        uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+        for (uint32_t q = 0; q < kCW; ++q) {
+            c0 += __builtin_popcount(escape_nibbles(in.cw[j][q]));
+            c1 += __builtin_popcount(escape_nibbles(in.cw[j + 1][q]));
+        }
+        uint32_t packed = c0 | (c1 << 16);
+        uint32_t incl = wave_scan_incl(packed);
+        uint32_t excl = incl - packed;
+        uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+        const uint32_t ob[2] = {orun + (excl & 0xFFFFu), orun + (tot & 0xFFFFu) + (excl >> 16)};
+        orun += (tot & 0xFFFFu) + (tot >> 16);
+        // new code words: P codes through the map, P escapes through the table
+        uint32_t nw[2][kCW];
+        c0 = 0;
+        c1 = 0;
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h) {
+            uint32_t r = ob[h];
+#pragma unroll
+            for (uint32_t q = 0; q < kCW; ++q) {
+                const uint32_t w = in.cw[j + h][q];
+                uint32_t x = lookup4(w & 0x0F0F0F0Fu, map) | (lookup4((w >> 4) & 0x0F0F0F0Fu, map) << 4);
+                uint32_t m = escape_nibbles(w);
+                while (m) {
+                    const uint32_t sh = __builtin_ctz(m);   // 4 * nibble index
+                    const uint32_t v = esc[r < kBlockElems ? r : kBlockElems - 1];
+                    ++r;
+                    x = (x & ~(0xFu << sh)) | (static_cast<uint32_t>(tbl[v]) << sh);
+                    m &= m - 1;
+                }
+                nw[h][q] = x;
+                (h ? c1 : c0) += __builtin_popcount(escape_nibbles(x));
+            }
+            if constexpr (kCW == 1)
+                *(SZ_GLOBAL uint32_t*)(codes + (j + h) * kSubBytes) = nw[h][0];
+            else
+                *(SZ_GLOBAL u32x4*)(codes + (j + h) * kSubBytes) = u32x4{nw[h][0], nw[h][1], nw[h][2], nw[h][3]};
+        }
+        // new ranks, then the new escape bytes: a P code that lost its place
+        // escapes with its value P[c]; a P escape that stays one keeps its byte
+        packed = c0 | (c1 << 16);
+        incl = wave_scan_incl(packed);
+        excl = incl - packed;
+        tot = __builtin_amdgcn_readlane(incl, 63);
+        const uint32_t nb[2] = {nrun + (excl & 0xFFFFu), nrun + (tot & 0xFFFFu) + (excl >> 16)};
+        nrun += (tot & 0xFFFFu) + (tot >> 16);
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h) {
+            uint32_t rank = nb[h];
+            uint32_t before = ob[h];   // P escapes of this lane in the sub-chunk ahead of word q
+#pragma unroll
+            for (uint32_t q = 0; q < kCW; ++q) {
+                const uint32_t w = in.cw[j + h][q];
+                const uint32_t oe = escape_nibbles(w);
+                uint32_t m = escape_nibbles(nw[h][q]);
+                while (m) {
+                    const uint32_t sh = __builtin_ctz(m);
+                    const uint32_t c = (w >> sh) & 0xFu;
+                    uint32_t v;
+                    if (c < kEscape) {
+                        v = table_byte(pw, c);
+                    } else {
+                        const uint32_t r = before + __builtin_popcount(oe & ((1u << sh) - 1u));
+                        v = esc[r < kBlockElems ? r : kBlockElems - 1];
+                    }
+                    stage[rank < kBlockElems ? rank : kBlockElems - 1] = static_cast<uint8_t>(v);
+                    ++rank;
+                    m &= m - 1;
+                }
+                before += __builtin_popcount(oe);
+            }
+        }
+    }
+    if (lane == 0) gptr(a.counts)[flat] = uniform(nrun);
+}
+
+// A listed tensor's tables: its index, stream, provisional codebook P,
+// and map[c] = the new code of P[c] (lanes 0..15 each compute one byte;
+// P's code 15 stays 15).  The wave's LDS table tbl_words receives the code
+// of every value under the final codebook.
+struct TranscodeTables {
+    uint32_t t;
+    SZ_GLOBAL uint8_t* dst;
+    uint32_t pw[4];
+    uint32_t map[4];
+};
+
+__device__ inline TranscodeTables transcode_tables(const CompressArgs& a, const SyncView& sv, uint64_t entry,
+                                                   uint32_t* tbl_words, uint32_t lane) {
+    TranscodeTables r;
+    r.t = uniform(sv.list[entry]);
+    const SZ_GLOBAL uint32_t* rec = sv.records + 32ull * r.t;
+    const SZ_GLOBAL uint8_t* fcb = gptr(a.codebooks) + 16ull * r.t;
+    const uint8_t* tbl = build_code_table(tbl_words, lane, lane < kCodes ? fcb[lane] : 0xFFFFu);
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) r.pw[k] = uniform(rec[kRecProvisional + k]);
+    const uint32_t mc = lane < kCodes ? tbl[table_byte(r.pw, lane & 15u)] : kEscape;
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k)
+        r.map[k] = __builtin_amdgcn_readlane(mc, 4 * k) | (__builtin_amdgcn_readlane(mc, 4 * k + 1) << 8) |
+                   (__builtin_amdgcn_readlane(mc, 4 * k + 2) << 16) | (__builtin_amdgcn_readlane(mc, 4 * k + 3) << 24);
+    r.dst = dst_of(a.enc.dst, r.t);
+    return r;
+}
+
+// Tensors whose provisional codebook was not the final one (the final
+// items list them): every full block of a listed tensor is recoded for the
+// final codebook.  The listed blocks, tensor by tensor, are split into
+// equal contiguous runs, one per wave of the grid, so a short list still
+// spreads over the whole GPU; with an empty list every workgroup leaves at
+// once.  A wave reads its next block while it recodes the current one.
+template <uint32_t DT>
+__global__ __launch_bounds__(kThreads, 8) void k_transcode(CompressArgs a) {
+    __shared__ uint32_t s_tbl[kWavesPerGroup][64];
+    __shared__ uint32_t s_esc[kWavesPerGroup][kBlockElems / 4];
+    const uint32_t lane = lane_id(), wave = uniform(threadIdx.x / kWaveSize);
+    const SyncView sv = sync_view(a.sync, a.enc.count);
+    const uint32_t listed = uniform(*sv.listed);
+    const uint64_t full_blocks = a.enc.n / kBlockElems;
+    const uint64_t total = static_cast<uint64_t>(listed < a.enc.count ? listed : a.enc.count) * full_blocks;
+    const uint64_t waves = static_cast<uint64_t>(gridDim.x) * kWavesPerGroup;
+    const uint64_t per = (total + waves - 1) / waves;
+    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave) * per;
+    const uint64_t last = first + per < total ? first + per : total;
+    if (first >= last) return;
+    const Layout L = layout_of(a.enc.n, DT);
+    const uint8_t* tbl = reinterpret_cast<const uint8_t*>(s_tbl[wave]);
+    TranscodeTables tt = transcode_tables(a, sv, first / full_blocks, s_tbl[wave], lane);
+    TranscodeIn<DT> cur, next;
+    transcode_read<DT>(a.enc, L, tt.dst, first % full_blocks,
+                       static_cast<uint64_t>(tt.t) * L.blocks + first % full_blocks, lane, cur);
+    for (uint64_t i = first; i < last; ++i) {
+        const uint64_t b = i % full_blocks;
+        const bool ahead = i + 1 < last && (i + 1) / full_blocks == i / full_blocks;   // same tensor
+        if (ahead)
+            transcode_read<DT>(a.enc, L, tt.dst, b + 1, static_cast<uint64_t>(tt.t) * L.blocks + b + 1, lane, next);
+        transcode_block<DT>(a.enc, L, tt.dst, b, static_cast<uint64_t>(tt.t) * L.blocks + b, lane, tbl, tt.map, tt.pw,
+                            s_esc[wave], cur);
+        if (i + 1 < last) {
+            if (!ahead) {
+                __builtin_amdgcn_wave_barrier();   // the previous tensor's table is no longer read
+                tt = transcode_tables(a, sv, (i + 1) / full_blocks, s_tbl[wave], lane);
+                transcode_read<DT>(a.enc, L, tt.dst, 0, static_cast<uint64_t>(tt.t) * L.blocks, lane, next);
+            }
+            cur = next;
+        }
+    }
+}
+
+// ----------------------------------------------------------------- decode
 
 // The 16 header dwords of a stream (caller guarantees src_bytes >= 64).
 __device__ inline void load_header(const SZ_GLOBAL uint8_t* src, uint32_t (&w)[16]) {
@@ -1433,9 +1786,17 @@ hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t 
 
 template <uint32_t DT>
 void enqueue_compress(const CompressArgs& a, hipStream_t s) {
-    const uint32_t grid = a.enc.count * (a.count_items + 1 + a.encode_items);   // one workgroup per item
+    const uint32_t grid = a.enc.count * (a.sample_items + 1 + a.main_items + 1);   // one workgroup per item
     hipLaunchKernelGGL(k_compress<DT>, dim3(grid), dim3(kPassThreads), 0, s, a);
     if (a.enc.n % kBlockElems) hipLaunchKernelGGL(k_encode_tail<DT>, dim3(a.enc.count), dim3(kWaveSize), 0, s, a.enc);
+    const uint64_t full_blocks = a.enc.n / kBlockElems;
+    if (full_blocks) {
+        // about one block per wave when every tensor is listed, capped
+        const uint64_t blocks = static_cast<uint64_t>(a.enc.count) * full_blocks;
+        const uint64_t groups = (blocks + kWavesPerGroup - 1) / kWavesPerGroup;
+        hipLaunchKernelGGL(k_transcode<DT>, dim3(static_cast<uint32_t>(groups < kTranscodeGroups ? groups : kTranscodeGroups)),
+                           dim3(kThreads), 0, s, a);
+    }
     enqueue_encode_finish<DT>(a.enc, s);
 }
 

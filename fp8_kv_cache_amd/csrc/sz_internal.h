@@ -6,6 +6,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Full unrolling of the fixed-size loops below keeps their arrays in
+// registers on the GPU; other host compilers (the g++ schedule check) just
+// run the loops.
+#if defined(__clang__)
+#define SZ_UNROLL _Pragma("unroll")
+#else
+#define SZ_UNROLL
+#endif
+
 namespace sz {
 
 constexpr uint32_t kBlockElems = 4096;      // elements per format block
@@ -101,20 +110,35 @@ struct EncodeArgs {
 // One-launch compress (histogram, codebook and encode).  Its workspace is
 // the encode workspace followed by a synchronisation area that a fill
 // kernel zeroes before every launch:
-//   u64 hist[count][256]   exponent counts accumulated by all workgroups
-//   u32 ticket, u32 abort  (padded to 256 bytes)
-//   per tensor t a 128-byte record: u32 at byte 0, 1 once t's codebook is
-//   published
-constexpr uint32_t kPassWaves = 16;                         // blocks per encode item, one per wave
+//   u64 hist[count][256]     exponent counts of the whole tensor (bins
+//                            kHistStride words apart)
+//   u64 sample[count][256]   exponent counts of the sampled chunks (same)
+//   u32 ticket, u32 abort, u32 listed   (padded to 256 bytes)
+//   per tensor t a 128-byte record of u32 words: [0..3] the provisional
+//   codebook (published once its 15 bytes are distinct), [8] the verdict
+//   on it once the final codebook is known (kProvisionalSame or
+//   kProvisionalDiffers; 0 if the tensor gave up)
+//   u32 list[count]          the first `listed` entries: the tensors whose
+//                            provisional codebook differs, in no set order
+constexpr uint32_t kPassWaves = 16;                         // blocks per main item, one per wave
 constexpr uint32_t kPassThreads = kPassWaves * kWaveSize;   // 1024
-constexpr uint64_t kPassLagBytes = 48ull << 20;             // input counted between a tensor's counting and its
-                                                            // re-read: the lag in stages is this over the tensor size
-constexpr uint32_t kCountIters = 1;                         // 128 KB input iterations per counting item
+constexpr uint32_t kSampleStride = 16;                      // one counting chunk in 16 feeds the provisional codebook
+constexpr uint32_t kPassLag = 4;                            // stages between a tensor's sample and its main items
 constexpr uint32_t kDefaultSpinLimit = 1u << 20;            // polls before a waiting workgroup gives up
 constexpr uint64_t kDefaultFusedMin = 1ull << 21;           // smallest BF16 tensor (elements) the fused kernel takes
+constexpr uint32_t kProvisionalSame = 1;
+constexpr uint32_t kProvisionalDiffers = 2;
+constexpr uint32_t kTranscodeGroups = 2048;                 // workgroups of the transcode kernel, at most
+constexpr uint32_t kHistStride = 1;                         // u64 words from one workspace bin to the next
+
+// Elements one sample item counts: 8 passes of a 16-byte vector per lane
+// of the 1024-thread workgroup (128 KB of input).
+__host__ __device__ inline uint64_t sample_chunk_elems(uint32_t dtype) {
+    return 8ull * kPassThreads * (dtype == kDtypeBF16 ? 8 : 16);
+}
 
 __host__ __device__ inline uint64_t sync_area_bytes(uint32_t count) {
-    return 2048ull * count + 256 + 128ull * count;
+    return 4096ull * kHistStride * count + 256 + 128ull * count + 8ull * ((count + 1) / 2);
 }
 
 struct CompressArgs {
@@ -123,14 +147,16 @@ struct CompressArgs {
     uint8_t* codebooks;       // count x 16, written (same memory as enc.codebooks)
     uint8_t* sync;            // the synchronisation area
     int32_t* status;          // count, may be null
-    uint32_t count_items;     // per tensor: ceil(n / elements per counting item)
-    uint32_t encode_items;    // per tensor: ceil(full blocks / kPassWaves); plus one codebook item
-    uint32_t lag;             // stages between counting and encoding a tensor, 1..count (see kPassLagBytes)
+    uint32_t sample_items;    // per tensor: ceil(chunks / kSampleStride), chunks = ceil(n / sample chunk)
+    uint32_t main_items;      // per tensor: ceil(blocks / kPassWaves)
+    uint32_t lag;             // stage of a tensor's main items after its sample items, >= 1
     uint32_t spin_limit;
+    uint64_t sample_total;    // elements the sample items of one tensor count
 };
 
 // Work items of the one-launch compress, in ticket order (see k_compress).
-enum : uint32_t { kItemCount = 0, kItemCodebook = 1, kItemEncode = 2, kItemNone = 3 };
+enum : uint32_t { kItemSample = 0, kItemProvisional = 1, kItemMain = 2, kItemFinal = 3, kItemNone = 4 };
+constexpr uint32_t kItemKinds = 4;
 
 struct PassItem {
     uint32_t kind;
@@ -138,18 +164,56 @@ struct PassItem {
     uint32_t idx;
 };
 
-// Ticket k -> item, for T tensors, H counting and E encode items per
-// tensor and 1 <= lag <= T.  Stage s holds, in this order: the H counting
-// items of tensor s (s < T), the codebook item of tensor s - 1
-// (1 <= s <= T), the E encode items of tensor s - lag (lag <= s < T + lag).
-// Stage sizes are constant between the boundaries 0, 1, lag, T, T + 1,
-// T + lag, so the ticket is located region by region.
-__host__ __device__ inline PassItem pass_item(uint64_t k, uint32_t T, uint32_t H, uint32_t E, uint32_t lag) {
-    const uint32_t edge[6] = {0, 1, lag, T, T + 1, T + lag};
-    for (uint32_t r = 0; r < 5; ++r) {
+// The schedule: T tensors; in stage s, kind j (in kind order) has per[j]
+// items for tensor s - delay[j] when delay[j] <= s < delay[j] + T.
+struct PassPlan {
+    uint32_t T;
+    uint32_t per[kItemKinds];
+    uint32_t delay[kItemKinds];
+};
+
+__host__ __device__ inline PassPlan pass_plan(const CompressArgs& a) {
+    PassPlan p;
+    p.T = a.enc.count;
+    p.per[kItemSample] = a.sample_items;
+    p.per[kItemProvisional] = 1;
+    p.per[kItemMain] = a.main_items;
+    p.per[kItemFinal] = 1;
+    p.delay[kItemSample] = 0;
+    p.delay[kItemProvisional] = 1;
+    p.delay[kItemMain] = a.lag;
+    p.delay[kItemFinal] = a.lag + 1;
+    return p;
+}
+
+// Ticket k -> item.  Stage sizes are constant between consecutive values
+// of {delay[j], delay[j] + T}, so the ticket is located region by region
+// (fixed-size loops: no dynamically indexed arrays in device code).
+__host__ __device__ inline PassItem pass_item(uint64_t k, const PassPlan& p) {
+    constexpr uint32_t kEdges = 2 * kItemKinds;
+    uint32_t edge[kEdges];
+SZ_UNROLL
+    for (uint32_t j = 0; j < kItemKinds; ++j) {
+        edge[2 * j] = p.delay[j];
+        edge[2 * j + 1] = p.delay[j] + p.T;
+    }
+SZ_UNROLL
+    for (uint32_t i = 0; i + 1 < kEdges; ++i)
+SZ_UNROLL
+        for (uint32_t j = 0; j + 1 < kEdges - i; ++j) {
+            const uint32_t x = edge[j], y = edge[j + 1];
+            edge[j] = x < y ? x : y;
+            edge[j + 1] = x < y ? y : x;
+        }
+SZ_UNROLL
+    for (uint32_t r = 0; r + 1 < kEdges; ++r) {
         const uint32_t lo = edge[r], hi = edge[r + 1];
         if (hi <= lo) continue;
-        const uint64_t size = (lo < T ? H : 0u) + (lo >= 1 && lo <= T ? 1u : 0u) + (lo >= lag ? E : 0u);
+        uint64_t size = 0;
+SZ_UNROLL
+        for (uint32_t j = 0; j < kItemKinds; ++j)
+            if (p.delay[j] <= lo && lo < p.delay[j] + p.T) size += p.per[j];
+        if (size == 0) continue;
         const uint64_t span = static_cast<uint64_t>(hi - lo) * size;
         if (k >= span) {
             k -= span;
@@ -157,15 +221,12 @@ __host__ __device__ inline PassItem pass_item(uint64_t k, uint32_t T, uint32_t H
         }
         const uint32_t s = lo + static_cast<uint32_t>(k / size);
         uint64_t q = k % size;
-        if (s < T) {
-            if (q < H) return {kItemCount, s, static_cast<uint32_t>(q)};
-            q -= H;
+SZ_UNROLL
+        for (uint32_t j = 0; j < kItemKinds; ++j) {
+            if (!(p.delay[j] <= s && s < p.delay[j] + p.T)) continue;
+            if (q < p.per[j]) return {j, s - p.delay[j], static_cast<uint32_t>(q)};
+            q -= p.per[j];
         }
-        if (s >= 1 && s <= T) {
-            if (q == 0) return {kItemCodebook, s - 1, 0};
-            q -= 1;
-        }
-        return {kItemEncode, s - lag, static_cast<uint32_t>(q)};
     }
     return {kItemNone, 0, 0};
 }
@@ -187,9 +248,10 @@ hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s)
 // encode = three kernels: planes + staged escapes, offsets + header, escape scatter
 hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
-// compress (BF16) = one clear of the synchronisation area and the status
-// words, the counting/encoding kernel, the partial-block encode, then the
-// same offsets and escape scatter as encode
+// compress = one clear of the synchronisation area and the status words,
+// the counting/encoding kernel, the partial-block encode, the transcode of
+// tensors whose provisional codebook was not the final one, then the same
+// offsets and escape scatter as encode
 hipError_t launch_compress(const CompressArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_decode_empty(const DecodeArgs& a, uint32_t dtype, hipStream_t s);

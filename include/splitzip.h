@@ -166,17 +166,21 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * for T tensors of the same n and dtype.
  *
  * The codebook of a tensor needs all of its exponents ("Abstract": the
- * most frequent exponent values get the codes), so each input is read
- * twice.  The separate calls read the whole cache twice, with a launch
- * boundary between; here one kernel hands out counting work for tensor s
- * while it encodes tensor s - 4, so the second read of a tensor follows
- * the first closely enough to be served mostly from the GPU's last-level
- * cache, and the codebook is built and published inside the kernel (on
- * the Llama-shaped 64-tensor BF16 cache about 15% faster than the three
- * calls).  E5M2 tensors have half the bytes per element, so the fused
- * kernel's fixed costs per work item weigh twice as much; measured slower
- * fused, they run the separate calls' kernels, as do BF16 tensors below
- * sz_compress_fused_min_elements() (the results are the same).
+ * most frequent exponent values get the codes), so the separate calls read
+ * every input twice: a histogram pass, then the encode.  This call reads
+ * it once.  One kernel counts a 1/16 sample of each tensor (every 16th
+ * 128 KB chunk) and ranks it into a provisional codebook; then it encodes
+ * every full 4096-element block with that codebook while counting the
+ * block into the tensor's full histogram; then it ranks the full histogram
+ * into the final codebook.  The sample nearly always ranks the same values
+ * in the same order.  Where it does not (12 of the 64 tensors of the
+ * Llama-shaped BF16 cache), a short second kernel recodes that tensor's
+ * code nibbles and staged escapes for the final codebook from what was
+ * written, without reading the input again; the partial last block is
+ * encoded with the final codebook afterwards.  The bytes written are the
+ * same as the separate calls'.  E5M2 tensors (measured slower fused) and
+ * BF16 tensors below sz_compress_fused_min_elements() run the separate
+ * calls' kernels, with the same results.
  *
  * Work inside the kernel waits only for work handed out before it, so a
  * call always makes progress, whatever else shares the GPU.  Waits are
@@ -189,13 +193,14 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * d_hist(s): 256 (count x 256) u64, written.  d_codebook(s): 16 (count x
  * 16) bytes, written.  d_dst(s), dst_capacity, d_out_bytes: as sz_encode.
  * d_status: 1 (count) int32, SZ_OK or SZ_ERR_TIMEOUT, may be NULL.
- * Batched: T x (ceil(n / 65536) + 1 + ceil(floor(n / 4096) / 16)), the
- * kernel's work items, must stay below 2^31 as well, else
+ * Batched: T x (ceil(ceil(n / 65536) / 16) + ceil(ceil(n / 4096) / 16) + 2),
+ * the kernel's work items, must stay below 2^31 as well, else
  * SZ_ERR_INVALID_ARGUMENT.
  * d_workspace: >= sz_compress_workspace_bytes[_batched] bytes, contents
- * need not be initialised, clobbered (the encode workspace followed by
- * 256 bytes plus 2176 bytes per tensor of counters).  Calls sharing a
- * workspace must not overlap in time. ---- */
+ * need not be initialised, clobbered (the encode workspace followed by a
+ * synchronisation area: 256 bytes plus 4228 bytes per tensor, rounded up
+ * to a multiple of 8).  Calls sharing a workspace must not overlap in
+ * time. ---- */
 
 uint64_t sz_compress_workspace_bytes(uint64_t n, sz_dtype dtype);
 uint64_t sz_compress_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype dtype);

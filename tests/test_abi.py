@@ -113,11 +113,12 @@ def test_host_argument_errors_return_before_launch(sz):
 
 
 def test_compress_sizes_and_host_errors(sz):
-    """Single-pass calls: workspace = the encode workspace plus 2048 bytes of
-    histogram per tensor, 256 bytes of counters and a 128-byte flag record
-    per tensor; argument errors return before any launch."""
+    """Single-pass calls: workspace = the encode workspace plus two 2048-byte
+    histograms per tensor (whole tensor and sample), 256 bytes of counters
+    and a 128-byte record per tensor; argument errors return before any
+    launch."""
     for count, n in [(1, 0), (1, 4097), (64, 1 << 23), (3, 100)]:
-        sync = 2048 * count + 256 + 128 * count
+        sync = 4096 * count + 256 + 128 * count + 8 * ((count + 1) // 2)
         assert sz.sz_compress_workspace_bytes_batched(count, n, 1) == \
             sz.sz_encode_workspace_bytes_batched(count, n, 1) + sync
     assert sz.sz_compress_workspace_bytes(1 << 32, 1) == 0
@@ -146,7 +147,8 @@ def test_compress_sizes_and_host_errors(sz):
     assert sz.sz_compress_batched(FAKE, 2, n, 2, FAKE, FAKE, FAKE, cap, None, None, FAKE, ws, stream=0) == E_SMALL
     assert sz.sz_compress_batched(FAKE, 2048, (1 << 32) - 1, 1, FAKE, FAKE, FAKE, 1 << 40, None, None, FAKE,
                                   1 << 62, stream=0) == E_ARG
-    # tiny tensors: two work items each (counting + codebook) -- 2^30 of them would overflow the grid
+    # tiny tensors: four work items each (sample, provisional codebook, main,
+    # final codebook) -- 2^30 of them would overflow the grid
     cap1 = sz.sz_max_compressed_bytes(1, 1)
     assert sz.sz_compress_batched(FAKE, 1 << 30, 1, 1, FAKE, FAKE, FAKE, cap1, None, None, FAKE, 1 << 62,
                                   stream=0) == E_ARG

@@ -1,7 +1,8 @@
 """The one-launch compress hands out work items through a ticket counter in
 a fixed schedule (pass_item in fp8_kv_cache_amd/csrc/sz_internal.h).  Its
 waits are deadlock-free only if every item appears once and each tensor's
-counting items precede its codebook item, which precedes its encode items.
+sample items precede its provisional codebook item, which precedes its main
+items, which precede its final codebook item.
 The same header the kernel is built from is compiled for the host with g++
 and the schedule is enumerated over a grid of shapes (no GPU needed)."""
 import os
@@ -23,4 +24,4 @@ def test_schedule_orders_and_covers_every_item(tmp_path):
     assert r.returncode == 0, r.stderr
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
-    assert out.stdout.strip() == "ok 900"
+    assert out.stdout.strip() == "ok 1260"

@@ -111,7 +111,6 @@ sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uin
     a.enc.counts = static_cast<uint32_t*>(d_workspace);
     a.enc.staging = static_cast<uint8_t*>(d_workspace) + workspace_counts_bytes(count, layout_of(n, dt).blocks);
     a.hists = d_hists;
-    a.codebooks = d_codebooks;
     a.sync = static_cast<uint8_t*>(d_workspace) + workspace_bytes_for(count, n);
     a.status = d_status;
     const uint64_t chunk = sample_chunk_elems(dt);
@@ -119,12 +118,22 @@ sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uin
     a.sample_total = 0;
     for (uint64_t i = 0; i < a.sample_items; ++i) {
         const uint64_t begin = i * kSampleStride * chunk;
-        a.sample_total += n - begin < chunk ? n - begin : chunk;
+        a.sample_total += static_cast<uint32_t>(n - begin < chunk ? n - begin : chunk);
     }
     a.main_items = static_cast<uint32_t>((layout_of(n, dt).blocks + kPassWaves - 1) / kPassWaves);
     // (compress_items(n, dt) is the item count per tensor; the entry points
     // keep count * that below 2^31, the launch's workgroup count)
-    a.lag = kPassLag;
+    // Main items of a tensor come lag stages after its sample items: long
+    // enough for the sample items to finish and the provisional codebook to
+    // be ranked before the main items start (a main item that has to wait
+    // holds its CU slot idle).  That takes about the same time whatever the
+    // tensor size, and a stage's time is proportional to it, so the lag
+    // spans kPassLagBytes of input (measured on 1 GB caches: 2^21-element
+    // tensors need 16 stages or more, 2^23-element ones 8; 4 stages cost
+    // them 70% and 3%), and is never below kPassLag.
+    const uint64_t tensor_bytes = static_cast<uint64_t>(n) * (dt == SZ_DTYPE_BF16 ? 2 : 1);
+    const uint64_t lag = (kPassLagBytes + tensor_bytes - 1) / tensor_bytes;
+    a.lag = static_cast<uint32_t>(lag < kPassLag ? kPassLag : (lag > count + 1u ? count + 1u : lag));
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     return from_hip(launch_compress(a, dt, s));
 }

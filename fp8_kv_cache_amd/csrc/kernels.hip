@@ -849,13 +849,13 @@ struct SyncView {
     SZ_GLOBAL uint64_t* sample;   // count x 256 bins (kHistStride apart), sampled chunks
     SZ_GLOBAL uint32_t* ticket;
     SZ_GLOBAL uint32_t* abort;
-    SZ_GLOBAL uint32_t* listed;   // entries of `list` in use
+    SZ_GLOBAL uint32_t* listed;   // [2]: entries in use of the two lists
     SZ_GLOBAL uint32_t* records;  // per tensor 32 words, see kRec*
-    SZ_GLOBAL uint32_t* list;     // count: tensors to transcode
+    SZ_GLOBAL uint32_t* list;     // [2][count]: tensors to recode, reordered ones, then the others
 };
 
 constexpr uint32_t kRecProvisional = 0;  // 4 words: the provisional codebook (complete once 15 bytes differ)
-constexpr uint32_t kRecVerdict = 8;      // kProvisionalSame / kProvisionalDiffers
+constexpr uint32_t kRecVerdict = 8;      // kProvisionalSame / Reordered / Differs
 
 __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     SyncView v;
@@ -990,9 +990,10 @@ __device__ inline void rank_codebook(uint64_t c, uint32_t* bins, uint32_t* s_wor
 
 // One work item; every thread of the workgroup calls it and every return
 // is taken by all of them.  LDS: bins (counting and ranking), s_tbl (the
-// code table, 256 bytes), s_word ([2..5] codebook, [8..13] poll words,
-// [16..19] the provisional codebook in the final item; [0], [14], [15]
-// hold the item and are not written).
+// code table, 256 bytes), s_word ([2..5] codebook, [6] the final item's
+// "other values" flag, [8..13] poll words, [16..19] the provisional
+// codebook in the final item; [0], [14], [15] hold the item and are not
+// written).
 template <uint32_t DT>
 __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const PassItem& it, uint32_t* bins,
                                 uint32_t* s_tbl, uint32_t* s_word, uint32_t tid, uint32_t lane, uint32_t wave) {
@@ -1048,15 +1049,34 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
         }
         if (tid < 256) gptr(a.hists)[256ull * t + tid] = c;
         rank_codebook<DT>(c, bins, s_word, tid);
-        if (tid < 4) gptr(reinterpret_cast<uint32_t*>(a.codebooks + 16ull * t))[tid] = s_word[2 + tid];
+        if (tid < 4) gptr(reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(a.enc.codebooks) + 16ull * t))[tid] =
+            s_word[2 + tid];
+        // same values in the same order, the same values in another order
+        // (thread v < D: is v in both codebooks or in neither?), or others
+        if (tid == 0) s_word[6] = 0;
+        __syncthreads();
+        if (tid < Geometry<DT>::kDomain) {
+            const uint8_t* pb = reinterpret_cast<const uint8_t*>(s_word + 16);
+            const uint8_t* fb = reinterpret_cast<const uint8_t*>(s_word + 2);
+            bool in_p = false, in_f = false;
+#pragma unroll
+            for (uint32_t k = 0; k < kCodes; ++k) {
+                in_p |= pb[k] == tid;
+                in_f |= fb[k] == tid;
+            }
+            if (in_p != in_f) s_word[6] = 1;   // benign race: every writer stores 1
+        }
+        __syncthreads();
         if (tid == 0) {
             bool same = true;
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) same &= s_word[16 + k] == s_word[2 + k];
-            store_agent(rec + kRecVerdict, same ? kProvisionalSame : kProvisionalDiffers);
+            store_agent(rec + kRecVerdict,
+                        same ? kProvisionalSame : (s_word[6] ? kProvisionalDiffers : kProvisionalReordered));
             if (!same) {
-                const uint32_t at = __hip_atomic_fetch_add(sv.listed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sv.list[at] = t;   // read by the next launch; at most count tensors are listed
+                const uint32_t k = s_word[6] ? 1u : 0u;   // list 0: reordered, 1: other values
+                const uint32_t at = __hip_atomic_fetch_add(sv.listed + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sv.list[k * a.enc.count + at] = t;   // read by the next launch; a tensor is listed at most once
             }
         }
         return;
@@ -1153,7 +1173,7 @@ struct TranscodeIn {
 
 template <uint32_t DT>
 __device__ inline void transcode_read(const EncodeArgs& a, const Layout& L, const SZ_GLOBAL uint8_t* dst, uint64_t b,
-                                      uint64_t flat, uint32_t lane, TranscodeIn<DT>& in) {
+                                      uint64_t flat, uint32_t lane, bool codes_only, TranscodeIn<DT>& in) {
     using G = Geometry<DT>;
     constexpr uint32_t kSubBytes = kWaveSize * G::kLaneElems / 2;   // code bytes per sub-chunk
     const SZ_GLOBAL uint8_t* codes = dst + L.code_at + b * (kBlockElems / 2) + lane * (G::kLaneElems / 2);
@@ -1166,9 +1186,34 @@ __device__ inline void transcode_read(const EncodeArgs& a, const Layout& L, cons
             in.cw[j][0] = v.x; in.cw[j][1] = v.y; in.cw[j][2] = v.z; in.cw[j][3] = v.w;
         }
     }
+    in.count = 0;
+    in.head = u32x4{0, 0, 0, 0};
+    if (codes_only) return;
     in.count = gptr(a.counts)[flat];
-    in.head = lane < 16 ? *(const SZ_GLOBAL u32x4*)(gptr(a.staging) + flat * kBlockElems + 16 * lane)
-                        : u32x4{0, 0, 0, 0};
+    if (lane < 16) in.head = *(const SZ_GLOBAL u32x4*)(gptr(a.staging) + flat * kBlockElems + 16 * lane);
+}
+
+// A block of a reordered tensor: only its code nibbles change (escapes
+// keep their codes, values and places).
+template <uint32_t DT>
+__device__ inline void transcode_codes(const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b, uint32_t lane,
+                                       const uint32_t (&map)[4], const TranscodeIn<DT>& in) {
+    using G = Geometry<DT>;
+    constexpr uint32_t kSubBytes = kWaveSize * G::kLaneElems / 2;
+    SZ_GLOBAL uint8_t* codes = dst + L.code_at + b * (kBlockElems / 2) + lane * (G::kLaneElems / 2);
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        uint32_t x[G::kCodeWords];
+#pragma unroll
+        for (uint32_t q = 0; q < G::kCodeWords; ++q) {
+            const uint32_t w = in.cw[j][q];
+            x[q] = lookup4(w & 0x0F0F0F0Fu, map) | (lookup4((w >> 4) & 0x0F0F0F0Fu, map) << 4);
+        }
+        if constexpr (G::kCodeWords == 1)
+            *(SZ_GLOBAL uint32_t*)(codes + j * kSubBytes) = x[0];
+        else
+            *(SZ_GLOBAL u32x4*)(codes + j * kSubBytes) = u32x4{x[0], x[1], x[2], x[3]};
+    }
 }
 
 // Block b, coded with codebook P (bytes pw), recoded for the codebook whose
@@ -1293,12 +1338,13 @@ struct TranscodeTables {
     uint32_t map[4];
 };
 
-__device__ inline TranscodeTables transcode_tables(const CompressArgs& a, const SyncView& sv, uint64_t entry,
-                                                   uint32_t* tbl_words, uint32_t lane) {
+__device__ inline TranscodeTables transcode_tables(const CompressArgs& a, const SyncView& sv,
+                                                   const SZ_GLOBAL uint32_t* list, uint64_t entry, uint32_t* tbl_words,
+                                                   uint32_t lane) {
     TranscodeTables r;
-    r.t = uniform(sv.list[entry]);
+    r.t = uniform(list[entry]);
     const SZ_GLOBAL uint32_t* rec = sv.records + 32ull * r.t;
-    const SZ_GLOBAL uint8_t* fcb = gptr(a.codebooks) + 16ull * r.t;
+    const SZ_GLOBAL uint8_t* fcb = gptr(a.enc.codebooks) + 16ull * r.t;
     const uint8_t* tbl = build_code_table(tbl_words, lane, lane < kCodes ? fcb[lane] : 0xFFFFu);
 #pragma unroll
     for (uint32_t k = 0; k < 4; ++k) r.pw[k] = uniform(rec[kRecProvisional + k]);
@@ -1311,48 +1357,67 @@ __device__ inline TranscodeTables transcode_tables(const CompressArgs& a, const 
     return r;
 }
 
+// The full blocks of the `listed` tensors of one list, split into equal
+// contiguous runs, one per wave of the grid (wave w of `waves`).  A wave
+// reads its next block while it recodes the current one.  kCodesOnly: the
+// list of reordered tensors, whose escapes stay as they are.
+template <uint32_t DT, bool kCodesOnly>
+__device__ inline void transcode_list(const CompressArgs& a, const SyncView& sv, const SZ_GLOBAL uint32_t* list,
+                                      uint32_t listed, uint64_t w, uint64_t waves, uint32_t* tbl_words,
+                                      uint32_t* esc_words, uint32_t lane) {
+    const uint64_t full_blocks = a.enc.n / kBlockElems;
+    const uint64_t total = static_cast<uint64_t>(listed < a.enc.count ? listed : a.enc.count) * full_blocks;
+    const uint64_t per = (total + waves - 1) / waves;
+    const uint64_t first = w * per;
+    const uint64_t last = first + per < total ? first + per : total;
+    if (first >= last) return;
+    const Layout L = layout_of(a.enc.n, DT);
+    const uint8_t* tbl = reinterpret_cast<const uint8_t*>(tbl_words);
+    __builtin_amdgcn_wave_barrier();   // a table of an earlier list is no longer read
+    TranscodeTables tt = transcode_tables(a, sv, list, first / full_blocks, tbl_words, lane);
+    TranscodeIn<DT> cur, next;
+    transcode_read<DT>(a.enc, L, tt.dst, first % full_blocks,
+                       static_cast<uint64_t>(tt.t) * L.blocks + first % full_blocks, lane, kCodesOnly, cur);
+    for (uint64_t i = first; i < last; ++i) {
+        const uint64_t b = i % full_blocks;
+        const bool ahead = i + 1 < last && (i + 1) / full_blocks == i / full_blocks;   // same tensor
+        if (ahead)
+            transcode_read<DT>(a.enc, L, tt.dst, b + 1, static_cast<uint64_t>(tt.t) * L.blocks + b + 1, lane,
+                               kCodesOnly, next);
+        if (kCodesOnly)
+            transcode_codes<DT>(L, tt.dst, b, lane, tt.map, cur);
+        else
+            transcode_block<DT>(a.enc, L, tt.dst, b, static_cast<uint64_t>(tt.t) * L.blocks + b, lane, tbl, tt.map,
+                                tt.pw, esc_words, cur);
+        if (i + 1 < last) {
+            if (!ahead) {
+                __builtin_amdgcn_wave_barrier();   // the previous tensor's table is no longer read
+                tt = transcode_tables(a, sv, list, (i + 1) / full_blocks, tbl_words, lane);
+                transcode_read<DT>(a.enc, L, tt.dst, 0, static_cast<uint64_t>(tt.t) * L.blocks, lane, kCodesOnly,
+                                   next);
+            }
+            cur = next;
+        }
+    }
+}
+
 // Tensors whose provisional codebook was not the final one (the final
 // items list them): every full block of a listed tensor is recoded for the
-// final codebook.  The listed blocks, tensor by tensor, are split into
-// equal contiguous runs, one per wave of the grid, so a short list still
-// spreads over the whole GPU; with an empty list every workgroup leaves at
-// once.  A wave reads its next block while it recodes the current one.
+// final codebook, first the reordered tensors' code nibbles, then the other
+// tensors' codes and escapes, each list spread over every wave of the grid
+// so a short list still covers the whole GPU; with empty lists every
+// workgroup leaves at once.
 template <uint32_t DT>
 __global__ __launch_bounds__(kThreads, 8) void k_transcode(CompressArgs a) {
     __shared__ uint32_t s_tbl[kWavesPerGroup][64];
     __shared__ uint32_t s_esc[kWavesPerGroup][kBlockElems / 4];
     const uint32_t lane = lane_id(), wave = uniform(threadIdx.x / kWaveSize);
     const SyncView sv = sync_view(a.sync, a.enc.count);
-    const uint32_t listed = uniform(*sv.listed);
-    const uint64_t full_blocks = a.enc.n / kBlockElems;
-    const uint64_t total = static_cast<uint64_t>(listed < a.enc.count ? listed : a.enc.count) * full_blocks;
     const uint64_t waves = static_cast<uint64_t>(gridDim.x) * kWavesPerGroup;
-    const uint64_t per = (total + waves - 1) / waves;
-    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave) * per;
-    const uint64_t last = first + per < total ? first + per : total;
-    if (first >= last) return;
-    const Layout L = layout_of(a.enc.n, DT);
-    const uint8_t* tbl = reinterpret_cast<const uint8_t*>(s_tbl[wave]);
-    TranscodeTables tt = transcode_tables(a, sv, first / full_blocks, s_tbl[wave], lane);
-    TranscodeIn<DT> cur, next;
-    transcode_read<DT>(a.enc, L, tt.dst, first % full_blocks,
-                       static_cast<uint64_t>(tt.t) * L.blocks + first % full_blocks, lane, cur);
-    for (uint64_t i = first; i < last; ++i) {
-        const uint64_t b = i % full_blocks;
-        const bool ahead = i + 1 < last && (i + 1) / full_blocks == i / full_blocks;   // same tensor
-        if (ahead)
-            transcode_read<DT>(a.enc, L, tt.dst, b + 1, static_cast<uint64_t>(tt.t) * L.blocks + b + 1, lane, next);
-        transcode_block<DT>(a.enc, L, tt.dst, b, static_cast<uint64_t>(tt.t) * L.blocks + b, lane, tbl, tt.map, tt.pw,
-                            s_esc[wave], cur);
-        if (i + 1 < last) {
-            if (!ahead) {
-                __builtin_amdgcn_wave_barrier();   // the previous tensor's table is no longer read
-                tt = transcode_tables(a, sv, (i + 1) / full_blocks, s_tbl[wave], lane);
-                transcode_read<DT>(a.enc, L, tt.dst, 0, static_cast<uint64_t>(tt.t) * L.blocks, lane, next);
-            }
-            cur = next;
-        }
-    }
+    const uint64_t w = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave;
+    transcode_list<DT, true>(a, sv, sv.list, uniform(sv.listed[0]), w, waves, s_tbl[wave], s_esc[wave], lane);
+    transcode_list<DT, false>(a, sv, sv.list + a.enc.count, uniform(sv.listed[1]), w, waves, s_tbl[wave],
+                              s_esc[wave], lane);
 }
 
 // ----------------------------------------------------------------- decode

@@ -113,21 +113,25 @@ struct EncodeArgs {
 //   u64 hist[count][256]     exponent counts of the whole tensor (bins
 //                            kHistStride words apart)
 //   u64 sample[count][256]   exponent counts of the sampled chunks (same)
-//   u32 ticket, u32 abort, u32 listed   (padded to 256 bytes)
+//   u32 ticket, u32 abort, u32 listed[2]   (padded to 256 bytes)
 //   per tensor t a 128-byte record of u32 words: [0..3] the provisional
 //   codebook (published once its 15 bytes are distinct), [8] the verdict
-//   on it once the final codebook is known (kProvisionalSame or
-//   kProvisionalDiffers; 0 if the tensor gave up)
-//   u32 list[count]          the first `listed` entries: the tensors whose
-//                            provisional codebook differs, in no set order
+//   on it once the final codebook is known (kProvisional*; 0 if the
+//   tensor gave up)
+//   u32 list[2][count]       the first listed[k] entries of list k: the
+//                            tensors whose provisional codebook is not the
+//                            final one, [0] kProvisionalReordered, [1]
+//                            kProvisionalDiffers, in no set order
 constexpr uint32_t kPassWaves = 16;                         // blocks per main item, one per wave
 constexpr uint32_t kPassThreads = kPassWaves * kWaveSize;   // 1024
 constexpr uint32_t kSampleStride = 16;                      // one counting chunk in 16 feeds the provisional codebook
-constexpr uint32_t kPassLag = 4;                            // stages between a tensor's sample and its main items
+constexpr uint32_t kPassLag = 4;                            // fewest stages between a tensor's sample and its main items
+constexpr uint64_t kPassLagBytes = 128ull << 20;            // input bytes those stages span at least
 constexpr uint32_t kDefaultSpinLimit = 1u << 20;            // polls before a waiting workgroup gives up
 constexpr uint64_t kDefaultFusedMin = 1ull << 21;           // smallest BF16 tensor (elements) the fused kernel takes
-constexpr uint32_t kProvisionalSame = 1;
-constexpr uint32_t kProvisionalDiffers = 2;
+constexpr uint32_t kProvisionalSame = 1;       // no recoding
+constexpr uint32_t kProvisionalReordered = 2;  // same 15 values, other codes: code nibbles recoded
+constexpr uint32_t kProvisionalDiffers = 3;    // other values: code nibbles and escapes recoded
 constexpr uint32_t kTranscodeGroups = 2048;                 // workgroups of the transcode kernel, at most
 constexpr uint32_t kHistStride = 1;                         // u64 words from one workspace bin to the next
 
@@ -138,20 +142,19 @@ __host__ __device__ inline uint64_t sample_chunk_elems(uint32_t dtype) {
 }
 
 __host__ __device__ inline uint64_t sync_area_bytes(uint32_t count) {
-    return 4096ull * kHistStride * count + 256 + 128ull * count + 8ull * ((count + 1) / 2);
+    return 4096ull * kHistStride * count + 256 + 128ull * count + 8ull * count;
 }
 
 struct CompressArgs {
-    EncodeArgs enc;           // enc.codebooks is written by the compress kernel
+    EncodeArgs enc;           // enc.codebooks (count x 16) is written by the compress kernel
     uint64_t* hists;          // count x 256, written
-    uint8_t* codebooks;       // count x 16, written (same memory as enc.codebooks)
     uint8_t* sync;            // the synchronisation area
     int32_t* status;          // count, may be null
     uint32_t sample_items;    // per tensor: ceil(chunks / kSampleStride), chunks = ceil(n / sample chunk)
     uint32_t main_items;      // per tensor: ceil(blocks / kPassWaves)
     uint32_t lag;             // stage of a tensor's main items after its sample items, >= 1
     uint32_t spin_limit;
-    uint64_t sample_total;    // elements the sample items of one tensor count
+    uint32_t sample_total;    // elements the sample items of one tensor count (n < 2^32)
 };
 
 // Work items of the one-launch compress, in ticket order (see k_compress).

@@ -198,9 +198,8 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * SZ_ERR_INVALID_ARGUMENT.
  * d_workspace: >= sz_compress_workspace_bytes[_batched] bytes, contents
  * need not be initialised, clobbered (the encode workspace followed by a
- * synchronisation area: 256 bytes plus 4228 bytes per tensor, rounded up
- * to a multiple of 8).  Calls sharing a workspace must not overlap in
- * time. ---- */
+ * synchronisation area: 256 bytes plus 4232 bytes per tensor).  Calls
+ * sharing a workspace must not overlap in time. ---- */
 
 uint64_t sz_compress_workspace_bytes(uint64_t n, sz_dtype dtype);
 uint64_t sz_compress_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype dtype);

@@ -301,3 +301,92 @@ def test_give_up_path_is_reported_and_bounded(sz):
     assert (bc.fused_status.cpu().numpy() == 0).all()
     for i, x in enumerate(xs):
         assert np.array_equal(bc.stream(i).cpu().numpy(), oracle.encode(x, BF16)), i
+
+
+# The fused kernel ranks a provisional codebook from a sample (every 16th
+# chunk of 65536 BF16 elements) and recodes a tensor when the full
+# histogram ranks differently.  These inputs are built so that the sample
+# and the whole tensor rank differently in a known way (checked with the
+# oracle on the CPU first), which drives the recoding path.
+SAMPLE_CHUNK, SAMPLE_STRIDE = 1 << 16, 16
+
+
+def _sample_mask(n):
+    m = np.zeros(n, dtype=bool)
+    for c in range(0, -(-n // SAMPLE_CHUNK), SAMPLE_STRIDE):
+        m[c * SAMPLE_CHUNK:(c + 1) * SAMPLE_CHUNK] = True
+    return m
+
+
+def _set_exponent(bits, where, e):
+    bits[where] = (bits[where] & 0x807F) | (e << 7)
+
+
+def _skewed(n, seed, kind):
+    """single_tensor(n) with its sampled chunks altered: 'order' swaps the
+    sample's two most frequent exponents (same 15 values, other codes),
+    'members' moves the sample's 15th exponent to a value outside the full
+    top 15 (other values: codes and escapes both change)."""
+    x = kvsynth.single_tensor(n, seed=seed).copy()
+    s = _sample_mask(n)
+    e = (x >> 7) & 0xFF
+    top = oracle.codebook(oracle.histogram(x, BF16), BF16)[:15]
+    if kind == "order":
+        first, second = int(top[0]), int(top[1])
+        idx = np.flatnonzero(s & (e == first))
+        gap = int((e[s] == first).sum() - (e[s] == second).sum())
+        _set_exponent(x, idx[:gap // 2 + gap // 8 + 1], second)
+    else:
+        out = int(top[14])
+        unused = next(v for v in range(1, 255) if not (e == v).any())
+        _set_exponent(x, s & (e == out), unused)
+    return x
+
+
+def _codebooks(x):
+    full = oracle.codebook(oracle.histogram(x, BF16), BF16)[:15]
+    part = oracle.codebook(oracle.histogram(x[_sample_mask(x.size)], BF16), BF16)[:15]
+    return full, part
+
+
+@pytest.mark.parametrize("kind", ["order", "members"])
+@pytest.mark.parametrize("n", [1 << 21, (1 << 21) + 12345])
+def test_fused_recodes_when_the_sample_ranks_differently(sz, kind, n):
+    """Three tensors, the middle one skewed: its provisional codebook is not
+    the final one (same values in another order, or other values), so its
+    codes -- and for 'members' its escapes -- are recoded after the main
+    pass.  Every stream equals the oracle's."""
+    xs = [kvsynth.single_tensor(n, seed=703), _skewed(n, 701, kind), kvsynth.single_tensor(n, seed=702)]
+    full, part = _codebooks(xs[1])
+    assert not np.array_equal(full, part)
+    assert (set(full.tolist()) == set(part.tolist())) == (kind == "order")
+    for x in (xs[0], xs[2]):
+        f, p = _codebooks(x)
+        assert np.array_equal(f, p)   # these two need no recoding
+    say("fused recode", kind, n)
+    bc = sz.codec.BatchCodec(len(xs), n, BF16)
+    bc.set_inputs([to_dev(x) for x in xs])
+    bc.compress_fused()
+    bc.decompress()
+    torch.cuda.synchronize()
+    assert (bc.fused_status.cpu().numpy() == 0).all()
+    for i, x in enumerate(xs):
+        _check_against_oracle(x, BF16, bc.stream(i), bc.hists[i], bc.codebooks[i])
+        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i
+
+
+def test_fused_recodes_escape_heavy_tensors(sz):
+    """Heavy-tailed tensors (most elements escape, ~150 exponent values):
+    samples and whole tensors rank differently, so recoding rewrites many
+    staged escapes per block; a ragged last block too."""
+    n = (1 << 22) + 777
+    xs = [kvsynth.stress(n, seed=710 + i) for i in range(3)]
+    assert any(not np.array_equal(*_codebooks(x)) for x in xs)
+    say("fused recode escape-heavy", n)
+    bc = sz.codec.BatchCodec(len(xs), n, BF16)
+    bc.set_inputs([to_dev(x) for x in xs])
+    bc.compress_fused()
+    torch.cuda.synchronize()
+    assert (bc.fused_status.cpu().numpy() == 0).all()
+    for i, x in enumerate(xs):
+        _check_against_oracle(x, BF16, bc.stream(i), bc.hists[i], bc.codebooks[i])

@@ -188,15 +188,14 @@ __device__ inline void hist_clear(uint32_t* bins, uint32_t tid) {
         *reinterpret_cast<uint4*>(bins + i) = make_uint4(0, 0, 0, 0);
 }
 
-// Fold the copies and add the sums to the tensor's u64 histogram (bins
-// kStride words apart).  Every
+// Fold the copies and add the sums to the tensor's u64 histogram.  Every
 // thread of the NT-thread workgroup calls it, after a barrier; the first
 // 256 do the folding.  `unpaired` is the number of phantom zero exponents
 // the workgroup counted (E5M2: elements counted one at a time as the pair
 // (e, 0); both types: zero padding counted past the end of a tensor); they
 // are taken off bin 0.  Rotating the start keeps the lanes of a wave on
 // distinct banks.
-template <uint32_t DT, uint32_t NT = kThreads, uint32_t kStride = 1>
+template <uint32_t DT, uint32_t NT = kThreads>
 __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64_t* hist, uint32_t unpaired) {
     static_assert(NT >= 256, "one folding thread per bin");
     const bool folds = NT == 256 || tid < 256;
@@ -205,7 +204,7 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
         uint32_t sum = tid == 0 ? 0u - unpaired : 0u;
 #pragma unroll 8
         for (uint32_t j = 0; j < 32; ++j) sum += bins[tid * 32 + ((j + tid) & 31u)];
-        if (sum) __hip_atomic_fetch_add(hist + tid * kStride, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
+        if (sum) __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
     } else {
         // thread t folds pairs 4t..4t+3 (dwords 2t, 2t+1): their first exponents
@@ -232,7 +231,7 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
         __syncthreads();
         const uint32_t sum = tid < 32 ? bins[tid] - (tid == 0 ? unpaired : 0u) : 0u;
         if (sum)
-            __hip_atomic_fetch_add(hist + tid * kStride, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
+            __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -419,20 +418,13 @@ __device__ inline void write_header(SZ_GLOBAL uint8_t* dst, const Layout& L, uin
 // BF16: eight elements d[0..3] -> 8 sign|mantissa bytes and 8 code
 // nibbles; elements at index >= valid get code 0 and zero bytes (they are
 // zero in d already).  Returns the escape nibble mask in esc[0].
-template <bool kCount = false>
 __device__ inline void encode_lane_bf16(const uint32_t (&d)[4], uint32_t valid, const uint8_t* tbl,
-                                        uint32_t (&sm)[2], uint32_t (&cw)[1], uint32_t (&esc)[1],
-                                        char* bins = nullptr, uint32_t copy4 = 0) {
+                                        uint32_t (&sm)[2], uint32_t (&cw)[1], uint32_t (&esc)[1]) {
     uint32_t c[8];
 #pragma unroll
     for (uint32_t k = 0; k < 4; ++k) {
-        const uint32_t e0 = (d[k] >> 7) & 0xFFu, e1 = (d[k] >> 23) & 0xFFu;
-        c[2 * k] = tbl[e0];
-        c[2 * k + 1] = tbl[e1];
-        if (kCount) {   // the exponent histogram, from the same fields (full blocks only)
-            atomicAdd(reinterpret_cast<uint32_t*>(bins + ((e0 << 7) | copy4)), 1u);
-            atomicAdd(reinterpret_cast<uint32_t*>(bins + ((e1 << 7) | copy4)), 1u);
-        }
+        c[2 * k] = tbl[(d[k] >> 7) & 0xFFu];
+        c[2 * k + 1] = tbl[(d[k] >> 23) & 0xFFu];
     }
     if (valid < 8) {
 #pragma unroll
@@ -536,14 +528,10 @@ __device__ inline const uint8_t* build_code_table(uint32_t* tbl_words, uint32_t 
 
 // Encode block b from its registers into stream dst with the code table
 // tbl: planes, the block's escape count and its staged escape bytes (flat
-// = the block's index over all tensors).  kCount (full blocks): the
-// block's exponents are also counted into the LDS histogram copies `bins`
-// (copy4: this lane's copy), BF16 from the fields the lookups extract.
-template <uint32_t DT, bool kFull, bool kCount = false>
+// = the block's index over all tensors).
+template <uint32_t DT, bool kFull>
 __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b,
-                                     uint64_t flat, uint32_t lane, const uint8_t* tbl, const BlockRegs<DT>& d,
-                                     char* bins = nullptr, uint32_t copy4 = 0) {
-    static_assert(!kCount || kFull, "counting in the encode covers full blocks only");
+                                     uint64_t flat, uint32_t lane, const uint8_t* tbl, const BlockRegs<DT>& d) {
     using G = Geometry<DT>;
     constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
     constexpr uint32_t kSmWords = G::kSmWords;
@@ -560,15 +548,10 @@ __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GL
                                : elem0 >= a.n ? 0u
                                : (a.n - elem0 >= G::kLaneElems ? G::kLaneElems
                                                                  : static_cast<uint32_t>(a.n - elem0));
-        if constexpr (DT == kDtypeBF16) {
-            encode_lane_bf16<kCount>(d[j], valid, tbl, sm[j], cw[j], esc[j], bins, copy4);
-        } else {
+        if constexpr (DT == kDtypeBF16)
+            encode_lane_bf16(d[j], valid, tbl, sm[j], cw[j], esc[j]);
+        else
             encode_lane_e5m2(d[j], valid, tbl, sm[j], cw[j], esc[j]);
-            if (kCount) {
-#pragma unroll
-                for (uint32_t i = 0; i < G::kInWords; ++i) count_dword<DT>(bins, d[j][i], copy4);
-            }
-        }
         cnt[j] = 0;
 #pragma unroll
         for (uint32_t q = 0; q < G::kCodeWords; ++q) cnt[j] += __builtin_popcount(esc[j][q]);
@@ -845,8 +828,8 @@ __global__ void k_encode_empty(EncodeArgs a) {
 // poll of every waiting workgroup.
 
 struct SyncView {
-    SZ_GLOBAL uint64_t* hist;     // count x 256 bins (kHistStride apart), whole tensors
-    SZ_GLOBAL uint64_t* sample;   // count x 256 bins (kHistStride apart), sampled chunks
+    SZ_GLOBAL uint64_t* hist;     // count x 256, whole tensors
+    SZ_GLOBAL uint64_t* sample;   // count x 256, sampled chunks
     SZ_GLOBAL uint32_t* ticket;
     SZ_GLOBAL uint32_t* abort;
     SZ_GLOBAL uint32_t* listed;   // [2]: entries in use of the two lists
@@ -860,8 +843,8 @@ constexpr uint32_t kRecVerdict = 8;      // kProvisionalSame / Reordered / Diffe
 __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     SyncView v;
     v.hist = gptr(reinterpret_cast<uint64_t*>(base));
-    v.sample = v.hist + 256ull * kHistStride * count;
-    SZ_GLOBAL uint32_t* w = gptr(reinterpret_cast<uint32_t*>(base + 4096ull * kHistStride * count));
+    v.sample = v.hist + 256ull * count;
+    SZ_GLOBAL uint32_t* w = gptr(reinterpret_cast<uint32_t*>(base + 4096ull * count));
     v.ticket = w;
     v.abort = w + 1;
     v.listed = w + 2;
@@ -935,7 +918,7 @@ __device__ inline uint32_t wait_histogram(const SZ_GLOBAL uint64_t* hist, uint64
                                           uint32_t wave, uint64_t& c) {
     constexpr uint32_t D = Geometry<DT>::kDomain;
     for (uint32_t polls = 0;; ++polls) {
-        c = tid < D ? load_agent(hist + tid * kHistStride) : 0;
+        c = tid < D ? load_agent(hist + tid) : 0;
         const uint32_t sum = __builtin_amdgcn_readlane(wave_scan_incl(static_cast<uint32_t>(c)), 63);
         if (lane == 0 && wave < 4) s_word[8 + wave] = sum;   // counts are at most n < 2^32
         __syncthreads();
@@ -1012,14 +995,14 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
         const uint64_t end = n - begin < chunk ? n : begin + chunk;
         const uint32_t phantom = count_range<DT, kPassThreads>(lds, src, begin, end, tid);
         __syncthreads();
-        hist_flush<DT, kPassThreads, kHistStride>(bins, tid, sv.sample + 256ull * kHistStride * t, phantom);
+        hist_flush<DT, kPassThreads>(bins, tid, sv.sample + 256ull * t, phantom);
         return;
     }
 
     if (it.kind == kItemProvisional) {
         // ---- provisional item: rank the sample, publish the codebook
         uint64_t c = 0;
-        if (wait_histogram<DT>(sv.sample + 256ull * kHistStride * t, a.sample_total, sv, a.spin_limit, s_word, tid, lane, wave,
+        if (wait_histogram<DT>(sv.sample + 256ull * t, a.sample_total, sv, a.spin_limit, s_word, tid, lane, wave,
                                c) != 1) {
             if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
             return;
@@ -1032,7 +1015,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     if (it.kind == kItemFinal) {
         // ---- final item: rank the whole histogram, compare with the provisional codebook
         uint64_t c = 0;
-        uint32_t ok = wait_histogram<DT>(sv.hist + 256ull * kHistStride * t, n, sv, a.spin_limit, s_word, tid, lane, wave, c) == 1;
+        uint32_t ok = wait_histogram<DT>(sv.hist + 256ull * t, n, sv, a.spin_limit, s_word, tid, lane, wave, c) == 1;
         if (ok) {
             if (wave == 0) {
                 uint32_t word = lane < 4 ? load_agent(rec + kRecProvisional + lane) : 0u, mine;
@@ -1126,7 +1109,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     if (n % kBlockElems && full_blocks / kPassWaves == it.idx)   // the partial last block is in this item
         phantom = count_ragged<DT, kPassThreads>(lds, src, full_blocks * kBlockElems, n, tid);
     __syncthreads();
-    hist_flush<DT, kPassThreads, kHistStride>(bins, tid, sv.hist + 256ull * kHistStride * t, phantom);
+    hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * t, phantom);
 }
 
 // One workgroup per item: the ticket taken at the start fixes the item.

@@ -110,9 +110,8 @@ struct EncodeArgs {
 // One-launch compress (histogram, codebook and encode).  Its workspace is
 // the encode workspace followed by a synchronisation area that a fill
 // kernel zeroes before every launch:
-//   u64 hist[count][256]     exponent counts of the whole tensor (bins
-//                            kHistStride words apart)
-//   u64 sample[count][256]   exponent counts of the sampled chunks (same)
+//   u64 hist[count][256]     exponent counts of the whole tensor
+//   u64 sample[count][256]   exponent counts of the sampled chunks
 //   u32 ticket, u32 abort, u32 listed[2]   (padded to 256 bytes)
 //   per tensor t a 128-byte record of u32 words: [0..3] the provisional
 //   codebook (published once its 15 bytes are distinct), [8] the verdict
@@ -133,7 +132,6 @@ constexpr uint32_t kProvisionalSame = 1;       // no recoding
 constexpr uint32_t kProvisionalReordered = 2;  // same 15 values, other codes: code nibbles recoded
 constexpr uint32_t kProvisionalDiffers = 3;    // other values: code nibbles and escapes recoded
 constexpr uint32_t kTranscodeGroups = 2048;                 // workgroups of the transcode kernel, at most
-constexpr uint32_t kHistStride = 1;                         // u64 words from one workspace bin to the next
 
 // Elements one sample item counts: 8 passes of a 16-byte vector per lane
 // of the 1024-thread workgroup (128 KB of input).
@@ -142,7 +140,7 @@ __host__ __device__ inline uint64_t sample_chunk_elems(uint32_t dtype) {
 }
 
 __host__ __device__ inline uint64_t sync_area_bytes(uint32_t count) {
-    return 4096ull * kHistStride * count + 256 + 128ull * count + 8ull * count;
+    return 4096ull * count + 256 + 128ull * count + 8ull * count;
 }
 
 struct CompressArgs {

@@ -834,8 +834,14 @@ struct SyncView {
     SZ_GLOBAL uint32_t* abort;
     SZ_GLOBAL uint32_t* listed;   // [2]: entries in use of the two lists
     SZ_GLOBAL uint32_t* records;  // per tensor 32 words, see kRec*
-    SZ_GLOBAL uint32_t* list;     // [2][count]: tensors to recode, reordered ones, then the others
+    SZ_GLOBAL uint32_t* list;     // [2][count] entries of kEntryWords: tensors to recode, reordered ones, then the others
 };
+
+// A list entry: everything the recode of one tensor needs, in one 64-byte
+// line: [0] tensor, [1..2] its stream's address, [4..7] the provisional
+// codebook P, [8..11] the final codebook F, [12..15] map[c] = the code F
+// gives the value P[c] (15 when F does not hold it; 15 -> 15).
+constexpr uint32_t kEntryWords = 16;
 
 constexpr uint32_t kRecProvisional = 0;  // 4 words: the provisional codebook (complete once 15 bytes differ)
 constexpr uint32_t kRecVerdict = 8;      // kProvisionalSame / Reordered / Differs
@@ -849,7 +855,7 @@ __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     v.abort = w + 1;
     v.listed = w + 2;
     v.records = w + 64;
-    v.list = v.records + 32ull * count;
+    v.list = v.records + 32ull * count;   // 2 x count entries
     return v;
 }
 
@@ -1035,9 +1041,21 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
         if (tid < 4) gptr(reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(a.enc.codebooks) + 16ull * t))[tid] =
             s_word[2 + tid];
         // same values in the same order, the same values in another order
-        // (thread v < D: is v in both codebooks or in neither?), or others
+        // (thread v < D: is v in both codebooks or in neither?), or others;
+        // threads c < 16 also find the code F gives P[c] (the recode map)
         if (tid == 0) s_word[6] = 0;
         __syncthreads();
+        if (tid < 16) {
+            const uint8_t* pb = reinterpret_cast<const uint8_t*>(s_word + 16);
+            const uint8_t* fb = reinterpret_cast<const uint8_t*>(s_word + 2);
+            uint32_t m = kEscape;
+            if (tid < kCodes) {
+#pragma unroll
+                for (uint32_t k = kCodes; k-- > 0;)
+                    if (fb[k] == pb[tid]) m = k;
+            }
+            reinterpret_cast<uint8_t*>(s_word + 8)[tid] = static_cast<uint8_t>(m);
+        }
         if (tid < Geometry<DT>::kDomain) {
             const uint8_t* pb = reinterpret_cast<const uint8_t*>(s_word + 16);
             const uint8_t* fb = reinterpret_cast<const uint8_t*>(s_word + 2);
@@ -1056,11 +1074,26 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
             for (uint32_t k = 0; k < 4; ++k) same &= s_word[16 + k] == s_word[2 + k];
             store_agent(rec + kRecVerdict,
                         same ? kProvisionalSame : (s_word[6] ? kProvisionalDiffers : kProvisionalReordered));
+            uint32_t slot = ~0u;
             if (!same) {
                 const uint32_t k = s_word[6] ? 1u : 0u;   // list 0: reordered, 1: other values
-                const uint32_t at = __hip_atomic_fetch_add(sv.listed + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sv.list[k * a.enc.count + at] = t;   // read by the next launch; a tensor is listed at most once
+                slot = k * a.enc.count +
+                       __hip_atomic_fetch_add(sv.listed + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            s_word[7] = slot;   // a tensor is listed at most once, so a slot stays below 2 x count
+        }
+        __syncthreads();
+        const uint32_t slot = s_word[7];
+        if (slot != ~0u && tid < kEntryWords) {   // the entry, read by the next launch
+            const uint64_t d = reinterpret_cast<uint64_t>(dst_of(a.enc.dst, t));
+            const uint32_t word = tid == 0   ? t
+                                  : tid == 1 ? static_cast<uint32_t>(d)
+                                  : tid == 2 ? static_cast<uint32_t>(d >> 32)
+                                  : tid < 4  ? 0u
+                                  : tid < 8  ? s_word[16 + tid - 4]
+                                  : tid < 12 ? s_word[2 + tid - 8]
+                                             : s_word[8 + tid - 12];
+            sv.list[static_cast<uint64_t>(slot) * kEntryWords + tid] = word;
         }
         return;
     }
@@ -1310,10 +1343,10 @@ __device__ inline void transcode_block(const EncodeArgs& a, const Layout& L, SZ_
     if (lane == 0) gptr(a.counts)[flat] = uniform(nrun);
 }
 
-// A listed tensor's tables: its index, stream, provisional codebook P,
-// and map[c] = the new code of P[c] (lanes 0..15 each compute one byte;
-// P's code 15 stays 15).  The wave's LDS table tbl_words receives the code
-// of every value under the final codebook.
+// A listed tensor's tables, from its list entry (one 64-byte load): its
+// index, stream, provisional codebook P and recode map.  The wave's LDS
+// table tbl_words receives the code of every value under the final
+// codebook F.
 struct TranscodeTables {
     uint32_t t;
     SZ_GLOBAL uint8_t* dst;
@@ -1321,22 +1354,24 @@ struct TranscodeTables {
     uint32_t map[4];
 };
 
-__device__ inline TranscodeTables transcode_tables(const CompressArgs& a, const SyncView& sv,
-                                                   const SZ_GLOBAL uint32_t* list, uint64_t entry, uint32_t* tbl_words,
-                                                   uint32_t lane) {
+__device__ inline TranscodeTables transcode_tables(const SZ_GLOBAL uint32_t* list, uint64_t entry,
+                                                   uint32_t* tbl_words, uint32_t lane) {
+    const uint32_t word = lane < kEntryWords ? list[entry * kEntryWords + lane] : 0u;
     TranscodeTables r;
-    r.t = uniform(list[entry]);
-    const SZ_GLOBAL uint32_t* rec = sv.records + 32ull * r.t;
-    const SZ_GLOBAL uint8_t* fcb = gptr(a.enc.codebooks) + 16ull * r.t;
-    const uint8_t* tbl = build_code_table(tbl_words, lane, lane < kCodes ? fcb[lane] : 0xFFFFu);
+    // (readlane returns a signed int: each word is taken as unsigned before
+    // it is widened, or a set bit 31 would fill the high half)
+    r.t = static_cast<uint32_t>(__builtin_amdgcn_readlane(word, 0));
+    const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(word, 1));
+    const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(word, 2));
+    r.dst = reinterpret_cast<SZ_GLOBAL uint8_t*>(lo | (hi << 32));
+    uint32_t fw[4];
 #pragma unroll
-    for (uint32_t k = 0; k < 4; ++k) r.pw[k] = uniform(rec[kRecProvisional + k]);
-    const uint32_t mc = lane < kCodes ? tbl[table_byte(r.pw, lane & 15u)] : kEscape;
-#pragma unroll
-    for (uint32_t k = 0; k < 4; ++k)
-        r.map[k] = __builtin_amdgcn_readlane(mc, 4 * k) | (__builtin_amdgcn_readlane(mc, 4 * k + 1) << 8) |
-                   (__builtin_amdgcn_readlane(mc, 4 * k + 2) << 16) | (__builtin_amdgcn_readlane(mc, 4 * k + 3) << 24);
-    r.dst = dst_of(a.enc.dst, r.t);
+    for (uint32_t k = 0; k < 4; ++k) {
+        r.pw[k] = __builtin_amdgcn_readlane(word, 4 + k);
+        fw[k] = __builtin_amdgcn_readlane(word, 8 + k);
+        r.map[k] = __builtin_amdgcn_readlane(word, 12 + k);
+    }
+    build_code_table(tbl_words, lane, lane < kCodes ? table_byte(fw, lane) : 0xFFFFu);
     return r;
 }
 
@@ -1357,7 +1392,7 @@ __device__ inline void transcode_list(const CompressArgs& a, const SyncView& sv,
     const Layout L = layout_of(a.enc.n, DT);
     const uint8_t* tbl = reinterpret_cast<const uint8_t*>(tbl_words);
     __builtin_amdgcn_wave_barrier();   // a table of an earlier list is no longer read
-    TranscodeTables tt = transcode_tables(a, sv, list, first / full_blocks, tbl_words, lane);
+    TranscodeTables tt = transcode_tables(list, first / full_blocks, tbl_words, lane);
     TranscodeIn<DT> cur, next;
     transcode_read<DT>(a.enc, L, tt.dst, first % full_blocks,
                        static_cast<uint64_t>(tt.t) * L.blocks + first % full_blocks, lane, kCodesOnly, cur);
@@ -1375,7 +1410,7 @@ __device__ inline void transcode_list(const CompressArgs& a, const SyncView& sv,
         if (i + 1 < last) {
             if (!ahead) {
                 __builtin_amdgcn_wave_barrier();   // the previous tensor's table is no longer read
-                tt = transcode_tables(a, sv, list, (i + 1) / full_blocks, tbl_words, lane);
+                tt = transcode_tables(list, (i + 1) / full_blocks, tbl_words, lane);
                 transcode_read<DT>(a.enc, L, tt.dst, 0, static_cast<uint64_t>(tt.t) * L.blocks, lane, kCodesOnly,
                                    next);
             }
@@ -1399,7 +1434,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_transcode(CompressArgs a) {
     const uint64_t waves = static_cast<uint64_t>(gridDim.x) * kWavesPerGroup;
     const uint64_t w = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave;
     transcode_list<DT, true>(a, sv, sv.list, uniform(sv.listed[0]), w, waves, s_tbl[wave], s_esc[wave], lane);
-    transcode_list<DT, false>(a, sv, sv.list + a.enc.count, uniform(sv.listed[1]), w, waves, s_tbl[wave],
+    transcode_list<DT, false>(a, sv, sv.list + static_cast<uint64_t>(a.enc.count) * kEntryWords, uniform(sv.listed[1]), w, waves, s_tbl[wave],
                               s_esc[wave], lane);
 }
 
@@ -1565,7 +1600,10 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
 #pragma unroll
     for (uint32_t i = 0; i < 16; ++i) hdr[i] = __builtin_amdgcn_readlane(meta, i);
     const int64_t escapes = check_header<DT>(hdr, src_bytes, L, cbw);
-    const uint64_t next = b + 1 < L.blocks ? __builtin_amdgcn_readlane(meta, 17) : static_cast<uint64_t>(escapes);
+    // (offsets are unsigned 32-bit: readlane's signed result is taken as
+    // unsigned before widening, so offsets from 2^31 on stay what they are)
+    const uint64_t next = b + 1 < L.blocks ? static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(meta, 17)))
+                                           : static_cast<uint64_t>(escapes);
     if (escapes < 0 || (b == 0 && first != 0) || next < first || next > static_cast<uint64_t>(escapes)) {
         mark_corrupt(status, lane);
         return;

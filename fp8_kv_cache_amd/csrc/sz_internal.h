@@ -117,10 +117,11 @@ struct EncodeArgs {
 //   codebook (published once its 15 bytes are distinct), [8] the verdict
 //   on it once the final codebook is known (kProvisional*; 0 if the
 //   tensor gave up)
-//   u32 list[2][count]       the first listed[k] entries of list k: the
-//                            tensors whose provisional codebook is not the
-//                            final one, [0] kProvisionalReordered, [1]
-//                            kProvisionalDiffers, in no set order
+//   list[2][count]           64-byte entries; the first listed[k] of list k
+//                            describe the tensors whose provisional
+//                            codebook is not the final one, [0]
+//                            kProvisionalReordered, [1] kProvisionalDiffers,
+//                            in no set order
 constexpr uint32_t kPassWaves = 16;                         // blocks per main item, one per wave
 constexpr uint32_t kPassThreads = kPassWaves * kWaveSize;   // 1024
 constexpr uint32_t kSampleStride = 16;                      // one counting chunk in 16 feeds the provisional codebook
@@ -140,7 +141,7 @@ __host__ __device__ inline uint64_t sample_chunk_elems(uint32_t dtype) {
 }
 
 __host__ __device__ inline uint64_t sync_area_bytes(uint32_t count) {
-    return 4096ull * count + 256 + 128ull * count + 8ull * count;
+    return 4096ull * count + 256 + 128ull * count + 128ull * count;
 }
 
 struct CompressArgs {

@@ -198,7 +198,7 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * SZ_ERR_INVALID_ARGUMENT.
  * d_workspace: >= sz_compress_workspace_bytes[_batched] bytes, contents
  * need not be initialised, clobbered (the encode workspace followed by a
- * synchronisation area: 256 bytes plus 4232 bytes per tensor).  Calls
+ * synchronisation area: 256 bytes plus 4352 bytes per tensor).  Calls
  * sharing a workspace must not overlap in time. ---- */
 
 uint64_t sz_compress_workspace_bytes(uint64_t n, sz_dtype dtype);

@@ -139,3 +139,12 @@ def stress_device(device, n=1 << 28, seed=5, special_fraction=0.01):
               torch.where(kind == 2, zero + 0x7F80, payload | 0x7F80)))
     bits[idx] = (sign | pattern).to(torch.int16)
     return bits
+
+
+def uniform_bits_device(device, n, seed=9):
+    """n uniformly random 16-bit patterns (BF16 bit patterns of every kind,
+    all 256 exponents about equally often) drawn on `device` with torch's
+    Philox; an int16 tensor."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randint(-32768, 32768, (n,), generator=g, device=device, dtype=torch.int16)

@@ -407,3 +407,25 @@ def test_graph_replay_matches_eager(sz, dt):
             assert int(bc.status[i]) == 0, (replay, i)
             assert torch.equal(bc.stream(i), ref_streams[i]), (replay, i)
             assert np.array_equal(to_host(bc.output(i), dt), x), (replay, i)
+
+
+def test_round_trip_with_escape_offsets_beyond_2_31(sz):
+    """Uniformly random BF16 bit patterns: about 241 of every 256 elements
+    escape, so in a tensor of 2^31 + 2^29 elements the per-block escape
+    offsets pass 2^31 (they are unsigned 32-bit in the stream).  Compressed
+    (the one-launch call) and decoded on the GPU, the tensor must come back
+    bit for bit, and the header must count more than 2^31 escapes.  At this
+    size the oracle would take minutes, so the stream bytes are not compared
+    with it (the smaller parity cases cover the same kernels)."""
+    n = (1 << 31) + (1 << 29)
+    say("escape offsets beyond 2^31", n)
+    x = kvsynth.uniform_bits_device("cuda", n)
+    stream, _, _, status = sz.codec.compress_fused(x, BF16)
+    assert status == 0
+    escapes = int(stream[16:24].cpu().numpy().view(np.uint64)[0])
+    assert escapes > (1 << 31)
+    y, st = sz.codec.decompress(stream, n, BF16)
+    assert st == 0
+    assert torch.equal(y, x)
+    del x, y, stream
+    torch.cuda.empty_cache()

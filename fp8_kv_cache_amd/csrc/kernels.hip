@@ -266,7 +266,7 @@ __device__ inline uint32_t count_range(char* lds, const SZ_GLOBAL uint8_t* src, 
         const SZ_GLOBAL u32x4* q = (const SZ_GLOBAL u32x4*)(src + base * G::kElemBytes);
         u32x4 v[kPasses];
 #pragma unroll
-        for (uint32_t p = 0; p < kPasses; ++p) v[p] = q[p * NT + tid];
+        for (uint32_t p = 0; p < kPasses; ++p) v[p] = __builtin_nontemporal_load(q + p * NT + tid);
 #pragma unroll
         for (uint32_t p = 0; p < kPasses; ++p) {
             count_dword<DT>(lds, v[p].x, copy4);
@@ -384,6 +384,11 @@ __global__ __launch_bounds__(256) void k_codebook(CodebookArgs a) {
 //              table and writes the header, and
 //   k_scatter  copies each block's staged escapes.
 
+// Inputs, planes and outputs are each read or written once per call, so
+// the bulk loads and stores are non-temporal (streaming past the caches):
+// on the Llama-shaped cache the stores made compress 5% and decode 4%
+// faster, and the loads a further 3.5% and 3%.
+
 // Header (64 bytes), the zero padding after the offset table and the
 // stream size; `lane` is the calling thread's index (0..63 used).
 __device__ inline void write_header(SZ_GLOBAL uint8_t* dst, const Layout& L, uint32_t dtype,
@@ -500,7 +505,7 @@ __device__ inline void load_block(const SZ_GLOBAL uint8_t* src, uint64_t n, uint
             const SZ_GLOBAL u32x4* p = (const SZ_GLOBAL u32x4*)(src + elem0 * G::kElemBytes);
 #pragma unroll
             for (uint32_t v = 0; v < G::kInWords / 4; ++v) {
-                const u32x4 x = p[v];
+                const u32x4 x = __builtin_nontemporal_load(p + v);
                 d[j][4 * v] = x.x; d[j][4 * v + 1] = x.y; d[j][4 * v + 2] = x.z; d[j][4 * v + 3] = x.w;
             }
         } else {
@@ -564,18 +569,18 @@ __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GL
         const uint64_t code_off = elem0 / 2;
         if constexpr (DT == kDtypeBF16) {
             if (kFull || elem0 < L.sm_region)
-                *(SZ_GLOBAL u32x2*)(dst + L.sm_at + elem0) = u32x2{sm[j][0], sm[j][1]};
+                __builtin_nontemporal_store(u32x2{sm[j][0], sm[j][1]}, (SZ_GLOBAL u32x2*)(dst + L.sm_at + elem0));
             if (kFull || code_off < L.code_region)
-                *(SZ_GLOBAL uint32_t*)(dst + L.code_at + code_off) = cw[j][0];
+                __builtin_nontemporal_store(cw[j][0], (SZ_GLOBAL uint32_t*)(dst + L.code_at + code_off));
         } else {
             const uint64_t sm_off = elem0 / 32 * 12;
             SZ_GLOBAL uint32_t* smp = (SZ_GLOBAL uint32_t*)(dst + L.sm_at + sm_off);
 #pragma unroll
             for (uint32_t i = 0; i < 3; ++i)
-                if (kFull || sm_off + 4 * i < L.sm_region) smp[i] = sm[j][i];
+                if (kFull || sm_off + 4 * i < L.sm_region) __builtin_nontemporal_store(sm[j][i], smp + i);
             if (kFull || code_off < L.code_region)
-                *(SZ_GLOBAL u32x4*)(dst + L.code_at + code_off) =
-                    u32x4{cw[j][0], cw[j][1], cw[j][2], cw[j][3]};
+                __builtin_nontemporal_store(u32x4{cw[j][0], cw[j][1], cw[j][2], cw[j][3]},
+                                            (SZ_GLOBAL u32x4*)(dst + L.code_at + code_off));
         }
     }
 
@@ -1196,9 +1201,9 @@ __device__ inline void transcode_read(const EncodeArgs& a, const Layout& L, cons
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; ++j) {
         if constexpr (G::kCodeWords == 1) {
-            in.cw[j][0] = *(const SZ_GLOBAL uint32_t*)(codes + j * kSubBytes);
+            in.cw[j][0] = __builtin_nontemporal_load((const SZ_GLOBAL uint32_t*)(codes + j * kSubBytes));
         } else {
-            const u32x4 v = *(const SZ_GLOBAL u32x4*)(codes + j * kSubBytes);
+            const u32x4 v = __builtin_nontemporal_load((const SZ_GLOBAL u32x4*)(codes + j * kSubBytes));
             in.cw[j][0] = v.x; in.cw[j][1] = v.y; in.cw[j][2] = v.z; in.cw[j][3] = v.w;
         }
     }
@@ -1226,9 +1231,9 @@ __device__ inline void transcode_codes(const Layout& L, SZ_GLOBAL uint8_t* dst, 
             x[q] = lookup4(w & 0x0F0F0F0Fu, map) | (lookup4((w >> 4) & 0x0F0F0F0Fu, map) << 4);
         }
         if constexpr (G::kCodeWords == 1)
-            *(SZ_GLOBAL uint32_t*)(codes + j * kSubBytes) = x[0];
+            __builtin_nontemporal_store(x[0], (SZ_GLOBAL uint32_t*)(codes + j * kSubBytes));
         else
-            *(SZ_GLOBAL u32x4*)(codes + j * kSubBytes) = u32x4{x[0], x[1], x[2], x[3]};
+            __builtin_nontemporal_store(u32x4{x[0], x[1], x[2], x[3]}, (SZ_GLOBAL u32x4*)(codes + j * kSubBytes));
     }
 }
 
@@ -1301,9 +1306,10 @@ __device__ inline void transcode_block(const EncodeArgs& a, const Layout& L, SZ_
                 (h ? c1 : c0) += __builtin_popcount(escape_nibbles(x));
             }
             if constexpr (kCW == 1)
-                *(SZ_GLOBAL uint32_t*)(codes + (j + h) * kSubBytes) = nw[h][0];
+                __builtin_nontemporal_store(nw[h][0], (SZ_GLOBAL uint32_t*)(codes + (j + h) * kSubBytes));
             else
-                *(SZ_GLOBAL u32x4*)(codes + (j + h) * kSubBytes) = u32x4{nw[h][0], nw[h][1], nw[h][2], nw[h][3]};
+                __builtin_nontemporal_store(u32x4{nw[h][0], nw[h][1], nw[h][2], nw[h][3]},
+                                            (SZ_GLOBAL u32x4*)(codes + (j + h) * kSubBytes));
         }
         // new ranks, then the new escape bytes: a P code that lost its place
         // escapes with its value P[c]; a P escape that stays one keeps its byte
@@ -1565,15 +1571,15 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
         const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
         if (kFull || elem0 < L.n) {
             if constexpr (DT == kDtypeBF16) {
-                cw[j][0] = *(const SZ_GLOBAL uint32_t*)(src + L.code_at + elem0 / 2);
-                const u32x2 v = *(const SZ_GLOBAL u32x2*)(src + L.sm_at + elem0);
+                cw[j][0] = __builtin_nontemporal_load((const SZ_GLOBAL uint32_t*)(src + L.code_at + elem0 / 2));
+                const u32x2 v = __builtin_nontemporal_load((const SZ_GLOBAL u32x2*)(src + L.sm_at + elem0));
                 sm[j][0] = v.x; sm[j][1] = v.y;
             } else {
-                const u32x2 c = *(const SZ_GLOBAL u32x2*)(src + L.code_at + elem0 / 2);
+                const u32x2 c = __builtin_nontemporal_load((const SZ_GLOBAL u32x2*)(src + L.code_at + elem0 / 2));
                 cw[j][0] = c.x; cw[j][1] = c.y;
                 // the lane's 6 field bytes start 0 or 2 bytes into this dword pair
                 const uint64_t sm_off = elem0 / 16 * 6;
-                const u32x2 v = *(const SZ_GLOBAL u32x2*)(src + L.sm_at + (sm_off & ~3ull));
+                const u32x2 v = __builtin_nontemporal_load((const SZ_GLOBAL u32x2*)(src + L.sm_at + (sm_off & ~3ull)));
                 sm[j][0] = v.x; sm[j][1] = v.y;
             }
         } else {
@@ -1701,7 +1707,7 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
         }
         SZ_GLOBAL uint8_t* p = dst + elem0 * (DT == kDtypeBF16 ? 2 : 1);
         if (kFull || elem0 + G::kLaneElems <= L.n) {
-            *(SZ_GLOBAL u32x4*)p = u32x4{out[0], out[1], out[2], out[3]};
+            __builtin_nontemporal_store(u32x4{out[0], out[1], out[2], out[3]}, (SZ_GLOBAL u32x4*)p);
         } else {
             const uint32_t valid = static_cast<uint32_t>(L.n - elem0);
 #pragma unroll

@@ -106,13 +106,17 @@ __device__ inline void mark_corrupt(int32_t* status, uint32_t t, uint32_t tid) {
 
 // ------------------------------------------------------------- full chunk
 
+// Chunk inputs, payloads and decoded chunks are each read or written once
+// per call, so their bulk accesses are non-temporal, as in the exponent
+// codec's kernels (so that the two codecs are compared on equal terms).
+
 // x (16384 bytes, global) -> LDS rows of 512 bytes at stride kRowStride.
 // `keep` receives the thread's four 16-byte vectors.
 __device__ inline void stage_input(const SZ_GLOBAL uint8_t* x, Lds& s, uint32_t tid, u32x4 (&keep)[4]) {
 #pragma unroll
     for (uint32_t v = 0; v < 4; ++v) {
         const uint32_t o = 16 * (tid + kThreads * v);
-        keep[v] = *(const SZ_GLOBAL u32x4*)(x + o);
+        keep[v] = __builtin_nontemporal_load((const SZ_GLOBAL u32x4*)(x + o));
         uint8_t* d = s.buf + (o / 512) * kRowStride + (o % 512);
         *reinterpret_cast<u32x2*>(d) = u32x2{keep[v].x, keep[v].y};
         *reinterpret_cast<u32x2*>(d + 8) = u32x2{keep[v].z, keep[v].w};
@@ -166,7 +170,7 @@ __device__ inline void inverse_full(Lds& s, uint32_t tid, SZ_GLOBAL uint8_t* out
         const uint8_t* d = s.buf + (o / 512) * kRowStride + (o % 512);
         const u32x2 lo = *reinterpret_cast<const u32x2*>(d);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(d + 8);
-        *(SZ_GLOBAL u32x4*)(out + o) = u32x4{lo.x, lo.y, hi.x, hi.y};
+        __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, (SZ_GLOBAL u32x4*)(out + o));
     }
 }
 
@@ -363,7 +367,8 @@ __global__ __launch_bounds__(kThreads) void k_lc_write(EncodeArgs a) {
 #pragma unroll
             for (uint32_t v = 0; v < 4; ++v) {
                 const uint32_t o = 16 * (tid + kThreads * v);
-                *(SZ_GLOBAL u32x4*)(out + o) = *(const SZ_GLOBAL u32x4*)(x + o);
+                __builtin_nontemporal_store(__builtin_nontemporal_load((const SZ_GLOBAL u32x4*)(x + o)),
+                                            (SZ_GLOBAL u32x4*)(out + o));
             }
             return;
         }
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_lc_write(EncodeArgs a) {
     }
     // the payload and its padding sit in buf[0, A16(size))
     for (uint32_t v = tid; v < align16(size) / 16; v += kThreads)
-        *(SZ_GLOBAL u32x4*)(out + 16 * v) = reinterpret_cast<const u32x4*>(s.buf)[v];
+        __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(s.buf)[v], (SZ_GLOBAL u32x4*)(out + 16 * v));
 }
 
 // ----------------------------------------------------------------- decode
@@ -411,7 +416,8 @@ __global__ __launch_bounds__(kThreads, 8) void k_lc_decode(DecodeArgs a) {
 #pragma unroll
             for (uint32_t v = 0; v < 4; ++v) {
                 const uint32_t o = 16 * (tid + kThreads * v);
-                *(SZ_GLOBAL u32x4*)(out + o) = *(const SZ_GLOBAL u32x4*)(in + o);
+                __builtin_nontemporal_store(__builtin_nontemporal_load((const SZ_GLOBAL u32x4*)(in + o)),
+                                            (SZ_GLOBAL u32x4*)(out + o));
             }
         } else {
             for (uint32_t p = tid; p < L; p += kThreads) out[p] = in[p];
@@ -419,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_lc_decode(DecodeArgs a) {
         return;
     }
     for (uint32_t v = tid; v < align16(size) / 16; v += kThreads)
-        reinterpret_cast<u32x4*>(s.buf)[v] = *(const SZ_GLOBAL u32x4*)(in + 16 * v);
+        reinterpret_cast<u32x4*>(s.buf)[v] = __builtin_nontemporal_load((const SZ_GLOBAL u32x4*)(in + 16 * v));
     __syncthreads();
     const uint32_t V = L / 2, nb = (V + 7) / 8;
     // this thread's 32 words m = 32t + i: flags from the bitmap (bits m >= V cleared)

@@ -252,8 +252,11 @@ __device__ inline uint32_t count_ragged(char* lds, const SZ_GLOBAL uint8_t* src,
 // threads).  Every pass a lane reads one 16-byte vector (a wave one
 // contiguous kilobyte); eight passes are in flight per iteration.  Returns
 // the number of phantom zero exponents to take off bin 0 (E5M2 counts the
-// ragged end as pairs (e, 0); BF16 counts it exactly).
-template <uint32_t DT, uint32_t NT>
+// ragged end as pairs (e, 0); BF16 counts it exactly).  kStream selects
+// non-temporal loads, for data read once; the one-launch compress's sample
+// reads pass false so that the chunks they read may still be in the
+// last-level cache when the main items read them again.
+template <uint32_t DT, uint32_t NT, bool kStream = true>
 __device__ inline uint32_t count_range(char* lds, const SZ_GLOBAL uint8_t* src, uint64_t begin, uint64_t end,
                                        uint32_t tid) {
     using G = Geometry<DT>;
@@ -266,7 +269,7 @@ __device__ inline uint32_t count_range(char* lds, const SZ_GLOBAL uint8_t* src, 
         const SZ_GLOBAL u32x4* q = (const SZ_GLOBAL u32x4*)(src + base * G::kElemBytes);
         u32x4 v[kPasses];
 #pragma unroll
-        for (uint32_t p = 0; p < kPasses; ++p) v[p] = __builtin_nontemporal_load(q + p * NT + tid);
+        for (uint32_t p = 0; p < kPasses; ++p) v[p] = kStream ? __builtin_nontemporal_load(q + p * NT + tid) : q[p * NT + tid];
 #pragma unroll
         for (uint32_t p = 0; p < kPasses; ++p) {
             count_dword<DT>(lds, v[p].x, copy4);
@@ -1004,7 +1007,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
         const uint64_t chunk = sample_chunk_elems(DT);
         const uint64_t begin = static_cast<uint64_t>(it.idx) * kSampleStride * chunk;
         const uint64_t end = n - begin < chunk ? n : begin + chunk;
-        const uint32_t phantom = count_range<DT, kPassThreads>(lds, src, begin, end, tid);
+        const uint32_t phantom = count_range<DT, kPassThreads, false>(lds, src, begin, end, tid);
         __syncthreads();
         hist_flush<DT, kPassThreads>(bins, tid, sv.sample + 256ull * t, phantom);
         return;

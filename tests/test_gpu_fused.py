@@ -390,3 +390,43 @@ def test_fused_recodes_escape_heavy_tensors(sz):
     assert (bc.fused_status.cpu().numpy() == 0).all()
     for i, x in enumerate(xs):
         _check_against_oracle(x, BF16, bc.stream(i), bc.hists[i], bc.codebooks[i])
+
+
+def _degenerate(n, kind):
+    """'zeros' and 'ones': a single exponent value.  'unsampled': exponents
+    127 and 126 everywhere, and 200 only in chunks the sample skips, so the
+    provisional codebook lacks a value the final one ranks third: its
+    elements are staged as escapes and recoded to code 2."""
+    if kind == "zeros":
+        return np.zeros(n, np.uint16)
+    if kind == "ones":
+        return np.full(n, 0x3F80, np.uint16)
+    rng = np.random.default_rng(720)
+    e = np.where(rng.random(n) < 0.7, 127, 126)
+    e[~_sample_mask(n) & (rng.random(n) < 0.1)] = 200
+    sign = rng.integers(0, 2, n)
+    mant = rng.integers(0, 1 << 7, n)
+    return ((sign << 15) | (e << 7) | mant).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kind", ["zeros", "ones", "unsampled"])
+def test_fused_degenerate_alphabets(sz, kind):
+    """Tensors with one to three exponent values over several items and a
+    ragged end, between two ordinary tensors."""
+    n = (1 << 21) + 777
+    xs = [kvsynth.single_tensor(n, seed=721), _degenerate(n, kind), kvsynth.single_tensor(n, seed=722)]
+    full, part = _codebooks(xs[1])
+    if kind == "unsampled":
+        assert 200 in full.tolist() and 200 not in part.tolist()
+    else:
+        assert np.array_equal(full, part)
+    say("fused degenerate", kind, n)
+    bc = sz.codec.BatchCodec(len(xs), n, BF16)
+    bc.set_inputs([to_dev(x) for x in xs])
+    bc.compress_fused()
+    bc.decompress()
+    torch.cuda.synchronize()
+    assert (bc.fused_status.cpu().numpy() == 0).all()
+    for i, x in enumerate(xs):
+        _check_against_oracle(x, BF16, bc.stream(i), bc.hists[i], bc.codebooks[i])
+        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i

@@ -52,6 +52,12 @@ def _inputs():
         "llama_k_small": (lambda: kvsynth.llama_kv(1, 0, shape=(512, 8, 128)), BF16),
         "llama_v_small": (lambda: kvsynth.llama_kv(1, 1, shape=(512, 8, 128)), BF16),
         "e5m2_stress": (lambda: kvsynth.e5m2_of(kvsynth.stress(1 << 17, seed=8)), E5M2),
+        # one exponent value only: the other 14 codebook entries are unused
+        # values in ascending order, and nothing escapes
+        "bf16_zeros_65537": (lambda: np.zeros(65537, np.uint16), BF16),
+        "bf16_ones_65537": (lambda: np.full(65537, 0x3F80, np.uint16), BF16),
+        "e5m2_zeros_65537": (lambda: np.zeros(65537, np.uint8), E5M2),
+        "e5m2_ones_65537": (lambda: np.full(65537, 0x3C, np.uint8), E5M2),
     }
     for n in (1, 2, 3, 15, 16, 17, 31, 33, 1023, 1025, 2049, 4095, 4096, 4097, 8191, 12289, 65537, 100003):
         cases[f"bf16_n{n}"] = (lambda n=n: kvsynth.stress(n, seed=n), BF16)

@@ -85,7 +85,7 @@ sz_status encode_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, const
 // Histogram, codebook and encode in one launch that reads the input once
 // (plus the short transcode, offset and scatter launches) for BF16 tensors
 // of at least g_fused_min elements.  E5M2 tensors measured slower fused
-// than with the separate calls' kernels (0.41 against 0.35 ms on the
+// than with the separate calls' kernels (0.37 against 0.28 ms on the
 // 64-tensor cache: counting a byte per element in the same pass costs more
 // than a second read of half the bytes), and small BF16 tensors take the
 // separate kernels too, as does n = 0.  The results are the same either

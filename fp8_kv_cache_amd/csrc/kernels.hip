@@ -120,8 +120,8 @@ __global__ void k_fill_i32(int32_t* p, uint64_t words, int32_t value) {
 
 // -------------------------------------------------------------- histogram
 //
-// Each workgroup counts one contiguous chunk of one tensor into 32
-// Histogram bins in LDS.
+// Each workgroup counts one contiguous chunk of one tensor into
+// lane-striped copies of the histogram in LDS.
 //   BF16: 256 bins x 32 lane-striped copies, laid out [bin][copy]; lane l
 //         adds into copy l & 31, so the 32 lanes of a half-wave hit 32
 //         different banks whatever their exponents.  The byte address of
@@ -269,7 +269,8 @@ __device__ inline uint32_t count_range(char* lds, const SZ_GLOBAL uint8_t* src, 
         const SZ_GLOBAL u32x4* q = (const SZ_GLOBAL u32x4*)(src + base * G::kElemBytes);
         u32x4 v[kPasses];
 #pragma unroll
-        for (uint32_t p = 0; p < kPasses; ++p) v[p] = kStream ? __builtin_nontemporal_load(q + p * NT + tid) : q[p * NT + tid];
+        for (uint32_t p = 0; p < kPasses; ++p)
+            v[p] = kStream ? __builtin_nontemporal_load(q + p * NT + tid) : q[p * NT + tid];
 #pragma unroll
         for (uint32_t p = 0; p < kPasses; ++p) {
             count_dword<DT>(lds, v[p].x, copy4);
@@ -798,10 +799,11 @@ __global__ void k_encode_empty(EncodeArgs a) {
 //     bins sum to the sampled element count; counts only grow), ranks the
 //     values (count descending, then value ascending) and publishes the
 //     first 15 as the provisional codebook.
-//   main item (16 blocks, one per wave): loads its blocks, counts them into
-//     the tensor's full histogram (the item that holds a partial last block
-//     counts that block too), then waits for the provisional codebook and
-//     encodes its full blocks with it exactly as k_encode does.
+//   main item (16 blocks, one per wave): loads its blocks and the
+//     provisional codebook (waiting for it if it is not complete yet), counts
+//     the blocks into the tensor's full histogram (the item that holds a
+//     partial last block counts that block too) and encodes its full blocks
+//     with the provisional codebook exactly as k_encode does.
 //   final item: polls the full histogram until it is complete, writes the
 //     histogram and codebook outputs and records whether the provisional
 //     codebook is the final one.
@@ -1443,8 +1445,8 @@ __global__ __launch_bounds__(kThreads, 8) void k_transcode(CompressArgs a) {
     const uint64_t waves = static_cast<uint64_t>(gridDim.x) * kWavesPerGroup;
     const uint64_t w = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave;
     transcode_list<DT, true>(a, sv, sv.list, uniform(sv.listed[0]), w, waves, s_tbl[wave], s_esc[wave], lane);
-    transcode_list<DT, false>(a, sv, sv.list + static_cast<uint64_t>(a.enc.count) * kEntryWords, uniform(sv.listed[1]), w, waves, s_tbl[wave],
-                              s_esc[wave], lane);
+    transcode_list<DT, false>(a, sv, sv.list + static_cast<uint64_t>(a.enc.count) * kEntryWords,
+                              uniform(sv.listed[1]), w, waves, s_tbl[wave], s_esc[wave], lane);
 }
 
 // ----------------------------------------------------------------- decode
@@ -1611,8 +1613,8 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
     const int64_t escapes = check_header<DT>(hdr, src_bytes, L, cbw);
     // (offsets are unsigned 32-bit: readlane's signed result is taken as
     // unsigned before widening, so offsets from 2^31 on stay what they are)
-    const uint64_t next = b + 1 < L.blocks ? static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(meta, 17)))
-                                           : static_cast<uint64_t>(escapes);
+    const uint32_t next_word = static_cast<uint32_t>(__builtin_amdgcn_readlane(meta, 17));
+    const uint64_t next = b + 1 < L.blocks ? static_cast<uint64_t>(next_word) : static_cast<uint64_t>(escapes);
     if (escapes < 0 || (b == 0 && first != 0) || next < first || next > static_cast<uint64_t>(escapes)) {
         mark_corrupt(status, lane);
         return;
@@ -1889,8 +1891,8 @@ void enqueue_compress(const CompressArgs& a, hipStream_t s) {
         // about one block per wave when every tensor is listed, capped
         const uint64_t blocks = static_cast<uint64_t>(a.enc.count) * full_blocks;
         const uint64_t groups = (blocks + kWavesPerGroup - 1) / kWavesPerGroup;
-        hipLaunchKernelGGL(k_transcode<DT>, dim3(static_cast<uint32_t>(groups < kTranscodeGroups ? groups : kTranscodeGroups)),
-                           dim3(kThreads), 0, s, a);
+        const uint32_t grid = static_cast<uint32_t>(groups < kTranscodeGroups ? groups : kTranscodeGroups);
+        hipLaunchKernelGGL(k_transcode<DT>, dim3(grid), dim3(kThreads), 0, s, a);
     }
     enqueue_encode_finish<DT>(a.enc, s);
 }

@@ -247,7 +247,9 @@ hipError_t launch_fill_u64(uint64_t* p, uint64_t words, uint64_t value, hipStrea
 hipError_t launch_fill_i32(int32_t* p, uint64_t words, int32_t value, hipStream_t s);
 hipError_t launch_histogram(const HistArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s);
-// encode = three kernels: planes + staged escapes, offsets + header, escape scatter
+// encode = planes and staged escapes (full blocks, then a partial last
+// block), then offsets, header and escape scatter (one kernel, or two for
+// tensors of more than 2^16 blocks)
 hipError_t launch_encode(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
 hipError_t launch_encode_empty(const EncodeArgs& a, uint32_t dtype, hipStream_t s);
 // compress = one clear of the synchronisation area and the status words,

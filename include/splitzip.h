@@ -106,8 +106,9 @@ sz_status sz_build_codebook(const uint64_t* d_hist, sz_dtype dtype,
  * cb[15] is ignored and stored as 0).  d_dst receives the whole stream;
  * dst_capacity must be >= sz_max_compressed_bytes(n, dtype), else
  * SZ_ERR_BUFFER_TOO_SMALL.  d_out_bytes (u64 in device memory or in
- * device-accessible pinned host memory, may be NULL) receives C.  d_workspace: >= sz_encode_workspace_bytes(n, dtype) bytes (may be
- * NULL when n = 0), contents need not be initialised, clobbered. */
+ * device-accessible pinned host memory, may be NULL) receives C.
+ * d_workspace: >= sz_encode_workspace_bytes(n, dtype) bytes (may be NULL
+ * when n = 0), contents need not be initialised, clobbered. */
 sz_status sz_encode(const void* d_src, uint64_t n, sz_dtype dtype,
                     const uint8_t* d_codebook, void* d_dst, uint64_t dst_capacity,
                     uint64_t* d_out_bytes, void* d_workspace, uint64_t workspace_bytes,
@@ -193,8 +194,9 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * d_hist(s): 256 (count x 256) u64, written.  d_codebook(s): 16 (count x
  * 16) bytes, written.  d_dst(s), dst_capacity, d_out_bytes: as sz_encode.
  * d_status: 1 (count) int32, SZ_OK or SZ_ERR_TIMEOUT, may be NULL.
- * Batched: T x (ceil(ceil(n / 65536) / 16) + ceil(ceil(n / 4096) / 16) + 2),
- * the kernel's work items, must stay below 2^31 as well, else
+ * Batched: T x (ceil(ceil(n / K) / 16) + ceil(ceil(n / 4096) / 16) + 2),
+ * the kernel's work items (K = 65536 for BF16, 131072 for E5M2: one
+ * 128 KB sample chunk), must stay below 2^31 as well, else
  * SZ_ERR_INVALID_ARGUMENT.
  * d_workspace: >= sz_compress_workspace_bytes[_batched] bytes, contents
  * need not be initialised, clobbered (the encode workspace followed by a

@@ -1,0 +1,71 @@
+"""Host-side parts of bench.py, on the CPU: the one-GPU guard, and the
+counter-derived traffic lookup (profiles/traffic.json), which is tied to a
+hash of the kernel sources so that counters taken on other kernels are
+never reported."""
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+ROOFLINE_KERNELS = ["k_zero_two", "k_compress<bf16>", "k_transcode<bf16>", "k_offsets_scatter<bf16>"]
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _traffic_file(tmp_path, sha, kernels):
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps({"kernel_sources_sha256": sha,
+                             "kernels": {k: {"hbm_bytes_per_launch": v} for k, v in kernels.items()}}))
+    return str(p)
+
+
+def test_traffic_is_summed_over_the_call_kernels(tmp_path, monkeypatch):
+    path = _traffic_file(tmp_path, bench.kernel_source_hash(), {"a": 10.0, "b": 32.5, "c": 1.0})
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", path)
+    assert bench.traffic_for(["a", "b"]) == 42.5
+
+
+def test_traffic_is_null_for_other_sources_a_missing_kernel_or_no_file(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", _traffic_file(tmp_path, "0" * 64, {"a": 10.0}))
+    assert bench.traffic_for(["a"]) is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", _traffic_file(tmp_path, bench.kernel_source_hash(), {"a": 10.0}))
+    assert bench.traffic_for(["a", "b"]) is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
+    assert bench.traffic_for(["a"]) is None
+
+
+def test_source_hash_changes_with_every_kernel_source(tmp_path, monkeypatch):
+    copies = []
+    for src in bench.KERNEL_SOURCES:
+        dst = tmp_path / os.path.basename(src)
+        shutil.copyfile(src, dst)
+        copies.append(str(dst))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", copies)
+    base = bench.kernel_source_hash()
+    assert base == bench.kernel_source_hash()
+    for path in copies:
+        with open(path, "ab") as f:
+            f.write(b"\n")
+        changed = bench.kernel_source_hash()
+        assert changed != base
+        base = changed
+
+
+def test_committed_traffic_covers_the_roofline_kernels():
+    with open(bench.TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    assert len(rec["kernel_sources_sha256"]) == 64
+    for k in ROOFLINE_KERNELS:
+        assert rec["kernels"][k]["hbm_bytes_per_launch"] > 0, k

@@ -306,14 +306,19 @@ def test_stress_full_size(sz, n):
     assert stream.numel() <= sz.sz_max_compressed_bytes(x.size, BF16)
     y, status = sz.codec.decompress(stream, x.size, BF16)
     assert status == 0 and torch.equal(y, x_dev)
+    say("stress full: one-launch compress")
+    fstream, fhist, fcb, fstatus = sz.codec.compress_fused(x_dev, BF16)
+    assert fstatus == 0
+    assert torch.equal(fhist, hist) and torch.equal(fcb, cb) and torch.equal(fstream, stream)
 
 
 def test_long_context_kv_full_size(sz):
     """Qwen3-32B-shaped long-context cache: 64 layers x {K, V} x
     [131072, 8, 128], encoded layer by layer with a per-layer codebook.
     Every layer: bit-exact round trip, histogram equal to a torch bincount of
-    the exponent field, exact stream size; two layers also byte-equal to the
-    oracle's stream."""
+    the exponent field, exact stream size, and the one-launch compress gives
+    the same histogram, codebook and stream; two layers also byte-equal to
+    the oracle's stream."""
     n = 131072 * 8 * 128
     oracle_layers = {(0, 0), (63, 1)}
     for layer in range(64):
@@ -330,6 +335,10 @@ def test_long_context_kv_full_size(sz):
             assert stream.numel() == oracle.exact_bytes(n, BF16, escapes)
             y, status = sz.codec.decompress(stream, n, BF16)
             assert status == 0 and torch.equal(y, x)
+            fstream, fhist, fcb, fstatus = sz.codec.compress_fused(x, BF16)
+            assert fstatus == 0
+            assert torch.equal(fhist, hist) and torch.equal(fcb, cb) and torch.equal(fstream, stream)
+            del fstream
             if (layer, kv) in oracle_layers:
                 xh = x.cpu().numpy().view(np.uint16)
                 assert np.array_equal(stream.cpu().numpy(), oracle.encode(xh, BF16))

@@ -1,7 +1,9 @@
 // Host check of the one-launch compress schedule (pass_item and pass_plan
 // in sz_internal.h, the functions the kernel calls): for every shape in a
-// grid of (tensors, sample items, main items, lag), every work item appears
-// exactly once among the tickets, nothing lies past the last ticket, and
+// grid of (tensors, sample items, main items, lag -- up to 5 stages more
+// than the tensor count, since a lone large tensor runs with the minimum
+// lag of 4), every work item appears exactly once among the tickets,
+// nothing lies past the last ticket, and
 // for each tensor its sample items come before its provisional item, which
 // comes before its main items, which come before its final item -- the
 // order the kernel's waits rely on (each waits only for earlier tickets).
@@ -17,7 +19,7 @@ int main() {
     for (uint32_t T = 1; T <= 9; ++T)
         for (uint32_t S = 1; S <= 4; ++S)
             for (uint32_t M = 1; M <= 5; ++M)
-                for (uint32_t lag = 1; lag <= T + 2; ++lag) {
+                for (uint32_t lag = 1; lag <= T + 5; ++lag) {
                     sz::CompressArgs a{};
                     a.enc.count = T;
                     a.sample_items = S;

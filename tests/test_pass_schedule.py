@@ -24,4 +24,4 @@ def test_schedule_orders_and_covers_every_item(tmp_path):
     assert r.returncode == 0, r.stderr
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
-    assert out.stdout.strip() == "ok 1260"
+    assert out.stdout.strip() == "ok 1800"

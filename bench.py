@@ -17,21 +17,24 @@ the three separate calls' first.  The same step replayed from one captured
 HIP graph, checked against the eager step, is reported beside it.
 The same JSON line also carries the step as the three separate calls,
 cold-cache steps, the E5M2-quantised cache, single-read encode variants,
-the LC-style comparison codec, the runtime's copy rate and the CPU
-oracle's rate on the host.
+the LC-style comparison codec, the runtime's copy rate, this GPU's HBM
+streaming ceilings (read, copy and the compress's read/write mix, plain
+and non-temporal) and the CPU oracle's rate on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-                    [--mode bench|profile|copy|transfer|lc] [--no-cpu-baseline]
+                    [--mode bench|profile|copy|transfer|lc|ceiling] [--no-cpu-baseline]
                     [--dtype bf16|e5m2]   (profile mode)
 
 --mode profile   a short eager run for rocprofv3 (BF16 or E5M2 cache);
 --mode copy      a 1 GiB copy, for scaling rocprofv3's byte counters;
 --mode transfer  the layer-pipelined transfer (encode -> PCIe send and
                  receive -> decode) against shipping the raw layers;
---mode lc        only the LC-style comparison codec.
+--mode lc        only the LC-style comparison codec;
+--mode ceiling   only the HBM streaming ceilings (libszprobe).
 """
 import argparse
 import concurrent.futures as cf
+import ctypes
 import hashlib
 import json
 import os
@@ -56,7 +59,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--mode", choices=["bench", "profile", "copy", "transfer", "lc"], default="bench")
+    p.add_argument("--mode", choices=["bench", "profile", "copy", "transfer", "lc", "ceiling"], default="bench")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--dtype", choices=["bf16", "e5m2"], default="bf16",
                    help="profile mode only: run the step on the cache as BF16 or quantised to FP8 E5M2")
@@ -330,6 +333,47 @@ def graph_replay(torch, bc, steps, warmup, fused=True):
             "ms_per_step_cold": float(np.median([e[0].elapsed_time(e[1]) for e in cold_ev])), "wall_s_timed": wall}
 
 
+PROBE_LIB = os.path.join(ROOT, "fp8_kv_cache_amd", "libszprobe.so")
+PROBE_GROUPS = 4096
+
+
+def hbm_ceilings(torch, reps=15):
+    """Context for the roofline, measured on this GPU in this run with
+    libszprobe's grid-stride kernels (16-byte vectors, 8 loads in flight per
+    lane, 4096 workgroups of 256): a 1 GiB read-only pass, a 1 GiB copy, and
+    the one-launch compress's mix (read 1 GiB, write back 3 of every 4
+    vectors), each with plain and with non-temporal accesses.  GB/s of
+    bytes read plus written, median of `reps` passes after two warm-ups."""
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.szp_stream.restype = ctypes.c_int
+    lib.szp_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                               ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(0x5A)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, mix, moved in (("read", 0, 1.0), ("copy", 4, 2.0), ("compress_mix", 3, 1.75)):
+        for nt in (0, 1):
+            times = []
+            for i in range(reps + 2):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = lib.szp_stream(src.data_ptr(), dst.data_ptr(), nbytes, nbytes, mix, nt, PROBE_GROUPS,
+                                    stream.cuda_stream)
+                e1.record(stream)
+                assert rc == 0, rc
+                torch.cuda.synchronize()
+                if i >= 2:
+                    times.append(e0.elapsed_time(e1))
+            ms = float(np.median(times))
+            out[f"{name}_{'nt' if nt else 'plain'}_GBps"] = moved * nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    out["how"] = ("libszprobe grid-stride kernels, 4096 x 256 threads, 16-byte vectors; read = 1 GiB read, "
+                  "copy = 1 GiB read + 1 GiB written, compress_mix = 1 GiB read + 0.75 GiB written")
+    return out
+
+
 def copy_ceiling(torch):
     """Context for the roofline: this GPU's device-to-device copy rate
     through the HIP runtime (1 GiB read + 1 GiB written), median of 10."""
@@ -459,6 +503,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.mode == "copy":
         copy_calibration(torch)
+        return
+    if args.mode == "ceiling":
+        print(json.dumps({"mode": "ceiling", "hbm_ceilings": hbm_ceilings(torch)}))
         return
 
     xs = make_inputs()
@@ -650,6 +697,7 @@ def main():
         result["e5m2"] = e5m2_cache(torch, xs)
         result["lc_comparison"] = lc_comparison(torch, xs)
         result["copy_ceiling"] = copy_ceiling(torch)
+        result["hbm_ceilings"] = hbm_ceilings(torch)
     if args.mode == "bench" and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(xs)
     print(json.dumps(result))

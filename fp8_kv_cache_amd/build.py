@@ -1,4 +1,5 @@
-"""Build libsplitzip.so (gfx950) in-tree with hipcc.
+"""Build libsplitzip.so (gfx950) in-tree with hipcc, and libszprobe.so, the
+HBM streaming-rate probes the benchmark measures its ceilings with.
 
     python fp8_kv_cache_amd/build.py
 
@@ -14,6 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsplitzip.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "api.cpp", "lc_kernels.hip", "lc_api.cpp")]
+PROBE_LIB = os.path.join(HERE, "libszprobe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "probe.hip")]
 ARCH = "gfx950"
 
 
@@ -36,13 +39,19 @@ def flags():
 
 
 def build(verbose=False):
-    """Compile every source (device code for gfx950 only) and link the
-    shared library next to this file."""
+    """Compile every source (device code for gfx950 only) and link both
+    shared libraries next to this file.  Returns the codec library's path."""
+    _link(SOURCES, LIB, verbose)
+    _link(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _link(sources, lib, verbose):
     cc = hipcc()
     objs = []
     tmpdir = os.path.join(ROOT, "_build")
     os.makedirs(tmpdir, exist_ok=True)
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         cmd = [cc, *flags(), *lang, "-c", src, "-o", obj]
@@ -50,13 +59,12 @@ def build(verbose=False):
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -1,7 +1,8 @@
-"""Host-side parts of bench.py, on the CPU: the one-GPU guard, and the
+"""Host-side parts of bench.py, on the CPU: the one-GPU guard, the
 counter-derived traffic lookup (profiles/traffic.json), which is tied to a
 hash of the kernel sources so that counters taken on other kernels are
-never reported."""
+never reported, and the probe library's argument checks."""
+import ctypes
 import json
 import os
 import shutil
@@ -69,3 +70,28 @@ def test_committed_traffic_covers_the_roofline_kernels():
     assert len(rec["kernel_sources_sha256"]) == 64
     for k in ROOFLINE_KERNELS:
         assert rec["kernels"][k]["hbm_bytes_per_launch"] > 0, k
+
+
+def test_probe_rejects_invalid_arguments_before_any_launch():
+    """libszprobe.so's argument checks run on the host, so every call below
+    returns -1 without touching a GPU."""
+    lib = ctypes.CDLL(bench.PROBE_LIB)
+    lib.szp_stream.restype = ctypes.c_int
+    lib.szp_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                               ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    a, b = 1 << 20, 2 << 20          # aligned stand-in addresses, never dereferenced
+    bad = [
+        (None, b, 4096, 4096, 4, 0, 8),        # null source
+        (a + 8, b, 4096, 4096, 4, 0, 8),       # misaligned source
+        (a, b + 4, 4096, 4096, 4, 0, 8),       # misaligned destination
+        (a, b, 4096 + 16, 8192, 4, 0, 8),      # size not a multiple of 64
+        (a, b, 0, 4096, 4, 0, 8),              # empty
+        (a, b, 4096, 4096, 2, 0, 8),           # unknown mix
+        (a, b, 4096, 4096, 4, 0, 0),           # no workgroups
+        (a, b, 4096, 4096, 4, 0, 65536),       # too many workgroups
+        (a, b, 4096, 4095, 4, 0, 8),           # copy into a smaller buffer
+        (a, b, 4096, 3071, 3, 1, 8),           # mix into less than 3/4 of the size
+        (a, b, 4096, 8 * 4096 - 1, 0, 0, 8),   # read-only sink below 4 KB per workgroup
+    ]
+    for args in bad:
+        assert lib.szp_stream(*args, None) == -1, args

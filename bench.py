@@ -698,6 +698,11 @@ def main():
         result["lc_comparison"] = lc_comparison(torch, xs)
         result["copy_ceiling"] = copy_ceiling(torch)
         result["hbm_ceilings"] = hbm_ceilings(torch)
+        # the same achieved rate against the measured ceiling for the fused
+        # compress's mix of reads and writes, beside frac (the published peak)
+        if dominant == "sz_compress_batched":
+            roofline["frac_of_measured_mix_ceiling"] = (
+                roofline["achieved"] / result["hbm_ceilings"]["compress_mix_nt_GBps"])
     if args.mode == "bench" and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(xs)
     print(json.dumps(result))

@@ -491,6 +491,9 @@ def transfer(torch, xs):
 
 def main():
     args = parse()
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the codec is per-tensor data-parallel with no cross-GPU exchange)", file=sys.stderr)
@@ -557,7 +560,7 @@ def main():
         if ev:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, 1)):   # at least one untimed step: its results are checked below
         three_call_step()
     torch.cuda.synchronize()
     # correctness of the timed configuration: every tensor round-trips, and

@@ -25,6 +25,14 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
+def test_step_counts_are_checked_before_anything_runs():
+    for flags in (["--steps", "0"], ["--warmup", "-1"]):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags],
+                           capture_output=True, text=True, timeout=300)
+        assert r.returncode == 2, flags
+        assert "--steps >= 1" in r.stderr and r.stdout == ""
+
+
 def _traffic_file(tmp_path, sha, kernels):
     p = tmp_path / "traffic.json"
     p.write_text(json.dumps({"kernel_sources_sha256": sha,

@@ -709,72 +709,195 @@ __global__ __launch_bounds__(256) void k_offsets(EncodeArgs a) {
                  a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid);
 }
 
-// Staged escapes -> the stream's escape region; one thread per block,
-// reading the staged bytes 16 at a time (a block's staging slot is
-// 4096-byte aligned) and writing them to their unaligned destination.
-template <uint32_t DT>
-__global__ __launch_bounds__(kThreads) void k_scatter(EncodeArgs a) {
-    const Layout L = layout_of(a.n, DT);
-    const uint64_t flat = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (flat >= static_cast<uint64_t>(a.count) * L.blocks) return;
-    const uint32_t t = static_cast<uint32_t>(flat / L.blocks);
-    const uint64_t b = flat - static_cast<uint64_t>(t) * L.blocks;
-    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
-    const uint32_t cnt = gptr(a.counts)[flat];
-    const uint32_t off = ((const SZ_GLOBAL uint32_t*)(dst + 64))[b];
-    const SZ_GLOBAL u32x4* from = (const SZ_GLOBAL u32x4*)(gptr(a.staging) + flat * kBlockElems);
-    SZ_GLOBAL uint8_t* to = dst + L.esc_at + off;
-    for (uint32_t i = 0; i < cnt; i += 16) {
-        const u32x4 v = from[i / 16];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// ---- escape copy: staged escapes -> the stream's escape region
+//
+// A group of kGroupBlocks consecutive blocks of one tensor is copied by one
+// kScatterThreads-thread workgroup.  Block i of the group has c_i staged
+// escapes (16-byte aligned slot) that go to byte off_i of the escape region
+// (the region starts 256-byte aligned; off_i has any alignment).  The copy is
+// cut into 16-byte destination windows aligned in the stream: block i covers
+// ceil(((off_i & 15) + c_i) / 16) of them.  A prefix scan numbers the
+// windows of the group, and all threads take windows in turn, kCopyUnroll at
+// a time, so their loads are in flight together whatever the escape counts
+// (a few windows per block in a KV cache, 225 in an escape-heavy tensor).
+// A window gets its 16 bytes from two adjacent staged vectors, joined by a
+// byte funnel shift.  A window wholly inside its block's range is one
+// 16-byte store; the first and last window of a range may be shared with the
+// neighbouring blocks' escapes and are written byte by byte.
+constexpr uint32_t kGroupBlocks = 256;
+constexpr uint32_t kScatterThreads = 1024;
+constexpr uint32_t kCopyUnroll = 4;
+
+struct CopyGroup {
+    uint32_t off[kGroupBlocks];       // escape-region byte offset of each block's first escape
+    uint32_t cnt[kGroupBlocks];       // escapes of each block
+    uint32_t win[kGroupBlocks + 1];   // first window of each block; win[nb] = windows of the group
+    uint32_t sums[kScatterThreads / kWaveSize];
+};
+
+// Bytes [16 - s, 32 - s) of the 32-byte sequence prev ++ cur (0 < s < 16).
+__device__ inline u32x4 funnel16(const u32x4& prev, const u32x4& cur, uint32_t s) {
+    const uint32_t q[8] = {prev.x, prev.y, prev.z, prev.w, cur.x, cur.y, cur.z, cur.w};
+    const uint32_t k = 16 - s, j = k >> 2, r = k & 3;   // j in 0..3 (per lane)
+    uint32_t x[5];
 #pragma unroll
-        for (uint32_t k = 0; k < 16; ++k)
-            if (i + k < cnt) to[i + k] = static_cast<uint8_t>(w[k / 4] >> (8 * (k & 3)));
+    for (uint32_t i = 0; i < 5; ++i)
+        x[i] = j == 0 ? q[i] : j == 1 ? q[i + 1] : j == 2 ? q[i + 2] : q[i + 3];
+    return u32x4{__builtin_amdgcn_alignbyte(x[1], x[0], r), __builtin_amdgcn_alignbyte(x[2], x[1], r),
+                 __builtin_amdgcn_alignbyte(x[3], x[2], r), __builtin_amdgcn_alignbyte(x[4], x[3], r)};
+}
+
+// Window w of the group (w < cg.win[nb]): its block by binary search, then
+// the staged vectors it needs.  `slot0` is the staging slot of the group's
+// first block, `esc` the stream's escape region.
+struct CopyWindow {
+    SZ_GLOBAL uint8_t* to;   // 16-byte aligned destination
+    uint32_t lo, hi;         // bytes [lo, hi) of the window belong to the block
+    uint32_t s;              // the block's misalignment
+    u32x4 prev, cur;
+};
+
+__device__ inline CopyWindow copy_window_load(const CopyGroup& cg, uint32_t nb, uint32_t w,
+                                              const SZ_GLOBAL uint8_t* slot0, SZ_GLOBAL uint8_t* esc) {
+    uint32_t lo = 0, hi = nb;   // the block i with win[i] <= w < win[i + 1]
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) / 2;
+        if (cg.win[mid] <= w) lo = mid; else hi = mid;
+    }
+    const uint32_t i = lo, lw = w - cg.win[i];
+    const uint32_t off = cg.off[i], cnt = cg.cnt[i], s = off & 15;
+    CopyWindow c;
+    c.to = esc + (off - s) + 16ull * lw;
+    c.lo = lw == 0 ? s : 0;
+    const uint32_t end = s + cnt - 16 * lw;   // > 0: the window holds at least one byte of the block
+    c.hi = end < 16 ? end : 16;
+    c.s = s;
+    const SZ_GLOBAL u32x4* slot = (const SZ_GLOBAL u32x4*)(slot0 + static_cast<uint64_t>(i) * kBlockElems);
+    c.cur = 16 * lw < cnt ? slot[lw] : u32x4{0, 0, 0, 0};
+    c.prev = s && lw ? slot[lw - 1] : u32x4{0, 0, 0, 0};
+    return c;
+}
+
+__device__ inline void copy_window_store(const CopyWindow& c) {
+    const u32x4 v = c.s ? funnel16(c.prev, c.cur, c.s) : c.cur;
+    if (c.lo == 0 && c.hi == 16) {
+        __builtin_nontemporal_store(v, (SZ_GLOBAL u32x4*)c.to);
+        return;
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (uint32_t k = 0; k < 16; ++k)
+        if (k >= c.lo && k < c.hi) c.to[k] = static_cast<uint8_t>(w[k / 4] >> (8 * (k & 3)));
+}
+
+// Every thread of the workgroup calls it after cg is complete (a barrier).
+__device__ inline void copy_escapes(const CopyGroup& cg, uint32_t nb, const SZ_GLOBAL uint8_t* slot0,
+                                    SZ_GLOBAL uint8_t* esc, uint32_t tid) {
+    const uint32_t total = cg.win[nb];
+    for (uint32_t w0 = tid; w0 < total; w0 += kScatterThreads * kCopyUnroll) {
+        CopyWindow c[kCopyUnroll];
+#pragma unroll
+        for (uint32_t k = 0; k < kCopyUnroll; ++k) {
+            const uint32_t w = w0 + k * kScatterThreads;
+            if (w < total) c[k] = copy_window_load(cg, nb, w, slot0, esc);
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < kCopyUnroll; ++k)
+            if (w0 + k * kScatterThreads < total) copy_window_store(c[k]);
     }
 }
 
+// Sum of x over the kScatterThreads threads (every thread gets it).
+// Contains barriers; `sums` is reusable after it returns.
+__device__ inline uint32_t group_sum(uint32_t x, uint32_t tid, uint32_t* sums) {
+    const uint32_t incl = wave_scan_incl(x);
+    if ((tid & 63) == 63) sums[tid / 64] = incl;
+    __syncthreads();
+    uint32_t total = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kScatterThreads / kWaveSize; ++w) total += sums[w];
+    __syncthreads();
+    return total;
+}
+
+// Threads 0..255 (waves 0..3) hold the group's blocks: exclusive prefix of x
+// over them, and `total`.  Every thread calls it (contains barriers).
+__device__ inline uint32_t group_blocks_scan(uint32_t x, uint32_t tid, uint32_t* sums, uint32_t& total) {
+    const uint32_t incl = wave_scan_incl(x);
+    if (tid < kGroupBlocks && (tid & 63) == 63) sums[tid / 64] = incl;
+    __syncthreads();
+    uint32_t base = 0;
+    for (uint32_t w = 0; w < tid / 64 && w < kGroupBlocks / kWaveSize; ++w) base += sums[w];
+    total = sums[0] + sums[1] + sums[2] + sums[3];
+    __syncthreads();
+    return base + incl - x;
+}
+
+// Fills cg for the group's nb blocks from their offsets and counts (held by
+// threads 0..nb-1).  Every thread calls it; ends with a barrier.
+__device__ inline void plan_copy(CopyGroup& cg, uint32_t off, uint32_t cnt, uint32_t nb, uint32_t tid) {
+    const uint32_t windows = tid < nb && cnt ? ((off & 15) + cnt + 15) / 16 : 0u;
+    uint32_t total;
+    const uint32_t first = group_blocks_scan(windows, tid, cg.sums, total);
+    if (tid < nb) {
+        cg.off[tid] = off;
+        cg.cnt[tid] = cnt;
+        cg.win[tid] = first;
+    }
+    if (tid == 0) cg.win[nb] = total;
+    __syncthreads();
+}
+
+// Beyond 2^16 blocks per tensor: k_offsets wrote the offset table; one
+// workgroup per group of kGroupBlocks blocks copies their staged escapes.
+template <uint32_t DT>
+__global__ __launch_bounds__(kScatterThreads) void k_scatter(EncodeArgs a) {
+    __shared__ CopyGroup cg;
+    const Layout L = layout_of(a.n, DT);
+    const uint32_t groups = static_cast<uint32_t>((L.blocks + kGroupBlocks - 1) / kGroupBlocks);
+    const uint32_t t = blockIdx.x / groups, g = blockIdx.x - t * groups, tid = threadIdx.x;
+    const uint64_t b0 = static_cast<uint64_t>(g) * kGroupBlocks;
+    const uint32_t nb = static_cast<uint32_t>(L.blocks - b0 < kGroupBlocks ? L.blocks - b0 : kGroupBlocks);
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+    const uint64_t flat0 = static_cast<uint64_t>(t) * L.blocks + b0;
+    const uint32_t cnt = tid < nb ? gptr(a.counts)[flat0 + tid] : 0u;
+    const uint32_t off = tid < nb ? ((const SZ_GLOBAL uint32_t*)(dst + 64))[b0 + tid] : 0u;
+    plan_copy(cg, off, cnt, nb, tid);
+    copy_escapes(cg, nb, gptr(a.staging) + flat0 * kBlockElems, dst + L.esc_at, tid);
+}
+
 // k_offsets and k_scatter in one launch, for tensors of at most
-// kFusedGroups x 256 blocks.  Workgroup g of tensor t takes blocks
+// kFusedGroups x kGroupBlocks blocks.  Workgroup g of tensor t takes blocks
 // [256g, 256g + 256): its base offset is the sum of the counts of every
-// earlier block, read directly (fewer than 256 x 256 reads, from L2), so no
-// workgroup waits for another; an in-group scan gives each block its offset,
-// which it writes to the table before copying its staged escapes.  The last
-// workgroup of a tensor writes the header.
+// earlier block, read directly (fewer than 2^16 reads, from L2), so no
+// workgroup waits for another; an in-group scan gives each block its
+// offset, which goes to the table, and the group's escapes are copied.  The
+// last workgroup of a tensor writes the header.
 constexpr uint64_t kFusedGroups = 256;
 
 template <uint32_t DT>
-__global__ __launch_bounds__(kThreads) void k_offsets_scatter(EncodeArgs a) {
-    __shared__ uint32_t s_sums[kWavesPerGroup];
+__global__ __launch_bounds__(kScatterThreads) void k_offsets_scatter(EncodeArgs a) {
+    __shared__ CopyGroup cg;
     const Layout L = layout_of(a.n, DT);
-    const uint32_t groups = static_cast<uint32_t>((L.blocks + kThreads - 1) / kThreads);
+    const uint32_t groups = static_cast<uint32_t>((L.blocks + kGroupBlocks - 1) / kGroupBlocks);
     const uint32_t t = blockIdx.x / groups, g = blockIdx.x - t * groups, tid = threadIdx.x;
+    const uint64_t b0 = static_cast<uint64_t>(g) * kGroupBlocks;
+    const uint32_t nb = static_cast<uint32_t>(L.blocks - b0 < kGroupBlocks ? L.blocks - b0 : kGroupBlocks);
     const SZ_GLOBAL uint32_t* counts = gptr(a.counts) + static_cast<uint64_t>(t) * L.blocks;
+    const uint32_t cnt = tid < nb ? counts[b0 + tid] : 0u;
     uint32_t before = 0;
-    for (uint32_t k = tid; k < g * kThreads; k += kThreads) before += counts[k];
-    uint32_t base;
-    block_scan_excl(before, tid, s_sums, base);
-    __syncthreads();
-    const uint64_t b = static_cast<uint64_t>(g) * kThreads + tid;
-    const uint32_t cnt = b < L.blocks ? counts[b] : 0u;
+    for (uint32_t k = tid; k < g * kGroupBlocks; k += kScatterThreads) before += counts[k];
+    const uint32_t base = group_sum(before, tid, cg.sums);
     uint32_t in_group;
-    const uint32_t off = base + block_scan_excl(cnt, tid, s_sums, in_group);
+    const uint32_t off = base + group_blocks_scan(cnt, tid, cg.sums, in_group);
     SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
-    if (b < L.blocks) {
-        ((SZ_GLOBAL uint32_t*)(dst + 64))[b] = off;
-        const SZ_GLOBAL u32x4* from =
-            (const SZ_GLOBAL u32x4*)(gptr(a.staging) + (static_cast<uint64_t>(t) * L.blocks + b) * kBlockElems);
-        SZ_GLOBAL uint8_t* to = dst + L.esc_at + off;
-        for (uint32_t i = 0; i < cnt; i += 16) {
-            const u32x4 v = from[i / 16];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (uint32_t k = 0; k < 16; ++k)
-                if (i + k < cnt) to[i + k] = static_cast<uint8_t>(w[k / 4] >> (8 * (k & 3)));
-        }
-    }
+    if (tid < nb) ((SZ_GLOBAL uint32_t*)(dst + 64))[b0 + tid] = off;
     if (g == groups - 1)
         write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, base + in_group,
                      a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid);
+    plan_copy(cg, off, cnt, nb, tid);
+    copy_escapes(cg, nb, gptr(a.staging) + (static_cast<uint64_t>(t) * L.blocks + b0) * kBlockElems,
+                 dst + L.esc_at, tid);
 }
 
 // n == 0: a header-only stream per tensor
@@ -1520,25 +1643,44 @@ struct DecodeGeometry<kDtypeE5M2> {
     static constexpr uint32_t kOutWords = 4;
 };
 
-constexpr uint32_t kPrefetch = 2 * kWaveSize;   // escape bytes staged in LDS per block
+// A block's escapes are staged in LDS before they are merged: up to 4096
+// bytes, read as 16-byte vectors from the aligned window around them (257
+// vectors at most, since the first escape may sit 15 bytes into a vector).
+constexpr uint32_t kEscVecs = kBlockElems / 16 + 1;
+constexpr uint32_t kEscWords = kEscVecs * 4;
+
+// Stage `vecs` 16-byte vectors of the stream, from byte `at` (16-byte
+// aligned) on, into LDS words esc_words[0 .. 4 vecs).  Vectors wholly below
+// `limit` go straight from memory to LDS (gfx950's 16-byte load-to-LDS,
+// which writes lane l's vector at the instruction's LDS base + 16 l); a
+// vector that crosses `limit` is assembled from byte loads below it, so no
+// byte at or past `limit` is read.  The caller waits for the loads (vmcnt)
+// before reading the words.
+__device__ inline void stage_vectors(const SZ_GLOBAL uint8_t* src, uint64_t at, uint32_t vecs, uint64_t limit,
+                                     uint32_t* esc_words, uint32_t lane) {
+    for (uint32_t k = 0; k * kWaveSize < vecs; ++k) {
+        const uint32_t v = k * kWaveSize + lane;
+        const uint64_t pos = at + 16ull * v;
+        if (v < vecs && pos + 16 <= limit)
+            __builtin_amdgcn_global_load_lds((const SZ_GLOBAL void*)(src + pos),
+                                             (__attribute__((address_space(3))) void*)(esc_words + 4 * k * kWaveSize),
+                                             16, 0, 0);
+        if (v < vecs && pos + 16 > limit) {
+            uint32_t w[4] = {0, 0, 0, 0};
+            for (uint32_t i = 0; i < 16; ++i)
+                if (pos + i < limit) w[i / 4] |= static_cast<uint32_t>(src[pos + i]) << (8 * (i & 3));
+            *reinterpret_cast<uint4*>(esc_words + 4 * v) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
 
 // Replace the exponent bytes of this lane's escaped elements (escape nibble
-// mask m over the 8 elements held in e0/e1) with the next escape bytes.
-// `near` is wave-uniform: when every escape of the block sits in the LDS
-// copy, the loop touches no global memory, so it never waits on the
-// block's outstanding stores.
-__device__ inline void patch_escapes(uint32_t& e0, uint32_t& e1, uint32_t m, uint32_t& rank, bool near,
-                                     const uint8_t* esc_near, const SZ_GLOBAL uint8_t* esc_in) {
-    if (near) {
-        while (m) {
-            put_byte(e0, e1, __builtin_ctz(m) >> 2, esc_near[rank++]);
-            m &= m - 1;
-        }
-    } else {
-        while (m) {
-            put_byte(e0, e1, __builtin_ctz(m) >> 2, esc_in[rank++]);
-            m &= m - 1;
-        }
+// mask m over the 8 elements held in e0/e1) with the next escape bytes,
+// read from the block's LDS copy.
+__device__ inline void patch_escapes(uint32_t& e0, uint32_t& e1, uint32_t m, uint32_t& rank, const uint8_t* esc) {
+    while (m) {
+        put_byte(e0, e1, __builtin_ctz(m) >> 2, esc[rank++]);
+        m &= m - 1;
     }
 }
 
@@ -1546,7 +1688,7 @@ __device__ inline void patch_escapes(uint32_t& e0, uint32_t& e1, uint32_t m, uin
 // exist), so the loads and stores need no per-lane guards.
 template <uint32_t DT, bool kFull>
 __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32_t t, uint64_t b,
-                                    uint32_t lane, uint8_t* esc_near) {
+                                    uint32_t lane, uint32_t* esc_words) {
     using G = DecodeGeometry<DT>;
     constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
     const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
@@ -1598,23 +1740,27 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
     // keep every plane load ahead of the wait for the offset below
     __builtin_amdgcn_sched_barrier(0);
 
-    // The block's first escape bytes, fetched as soon as its offset is known
-    // (addresses clamped into the buffer; bytes past the block are unused).
-    const uint32_t first = __builtin_amdgcn_readlane(meta, 16);
+    // The block's escapes [first, next), fetched as soon as the offsets are
+    // known: the aligned window of 16-byte vectors around them, at most
+    // kEscVecs, every byte read below src_bytes.  The span is not validated
+    // yet, so it is clamped; it is checked before any staged byte is used.
+    // (Offsets are unsigned 32-bit: readlane's signed result is taken as
+    // unsigned before widening, so offsets from 2^31 on stay what they are.)
+    const uint32_t first = static_cast<uint32_t>(__builtin_amdgcn_readlane(meta, 16));
+    const uint32_t next_word = static_cast<uint32_t>(__builtin_amdgcn_readlane(meta, 17));
+    const uint64_t hdr_escapes = static_cast<uint32_t>(__builtin_amdgcn_readlane(meta, 4)) |
+                                 (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(meta, 5))) << 32);
+    const uint64_t next = b + 1 < L.blocks ? static_cast<uint64_t>(next_word) : hdr_escapes;
     const uint64_t esc_first = L.esc_at + first;
-    const uint64_t last = src_bytes - 1;
-    const uint64_t p0 = esc_first + lane, p1 = esc_first + kWaveSize + lane;
-    const uint32_t pre0 = src[p0 < last ? p0 : last];
-    const uint32_t pre1 = src[p1 < last ? p1 : last];
+    const uint32_t skew = static_cast<uint32_t>(esc_first & 15);
+    const uint64_t span = next > first ? (next - first < kBlockElems ? next - first : kBlockElems) : 0;
+    const uint32_t vecs = static_cast<uint32_t>((skew + span + 15) / 16);
+    stage_vectors(src, esc_first - skew, vecs, src_bytes, esc_words, lane);
 
     uint32_t hdr[16], cbw[4];
 #pragma unroll
     for (uint32_t i = 0; i < 16; ++i) hdr[i] = __builtin_amdgcn_readlane(meta, i);
     const int64_t escapes = check_header<DT>(hdr, src_bytes, L, cbw);
-    // (offsets are unsigned 32-bit: readlane's signed result is taken as
-    // unsigned before widening, so offsets from 2^31 on stay what they are)
-    const uint32_t next_word = static_cast<uint32_t>(__builtin_amdgcn_readlane(meta, 17));
-    const uint64_t next = b + 1 < L.blocks ? static_cast<uint64_t>(next_word) : static_cast<uint64_t>(escapes);
     if (escapes < 0 || (b == 0 && first != 0) || next < first || next > static_cast<uint64_t>(escapes)) {
         mark_corrupt(status, lane);
         return;
@@ -1656,12 +1802,10 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
         mark_corrupt(status, lane);
         return;
     }
-    esc_near[lane] = static_cast<uint8_t>(pre0);
-    esc_near[kWaveSize + lane] = static_cast<uint8_t>(pre1);
+    // (block_total = next - first <= 4096 now, so every escape was staged)
+    __builtin_amdgcn_s_waitcnt(0);   // the staging loads have landed in LDS
     __builtin_amdgcn_wave_barrier();
-
-    const SZ_GLOBAL uint8_t* esc_in = src + esc_first;
-    const bool near = block_total <= kPrefetch;   // all escapes of the block are in LDS
+    const uint8_t* esc_lds = reinterpret_cast<const uint8_t*>(esc_words) + skew;
     SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
 #pragma unroll
     for (uint32_t j = 0; j < G::kSubs; ++j) {
@@ -1675,7 +1819,7 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
             const uint32_t od = lookup4((c >> 4) & 0x0F0F0F0Fu, cbw);  // elements 1,3,5,7
             uint32_t e0 = perm(od, ev, 0x05010400u);                    // elements 0..3
             uint32_t e1 = perm(od, ev, 0x07030602u);                    // elements 4..7
-            patch_escapes(e0, e1, esc[j][0], rank, near, esc_near, esc_in);
+            patch_escapes(e0, e1, esc[j][0], rank, esc_lds);
             // (sign|mantissa byte s, exponent byte e) pairs -> BF16 words
 #pragma unroll
             for (uint32_t h = 0; h < 4; ++h) {
@@ -1700,7 +1844,7 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
                 const uint32_t od = lookup4((c >> 4) & 0x0F0F0F0Fu, cbw);
                 uint32_t e0 = perm(od, ev, 0x05010400u);
                 uint32_t e1 = perm(od, ev, 0x07030602u);
-                patch_escapes(e0, e1, esc[j][q], rank, near, esc_near, esc_in);
+                patch_escapes(e0, e1, esc[j][q], rank, esc_lds);
 #pragma unroll
                 for (uint32_t h = 0; h < 2; ++h) {
                     const uint32_t v = f[2 * q + h];
@@ -1733,7 +1877,7 @@ __device__ inline void decode_block(const DecodeArgs& a, const Layout& L, uint32
 // the 5 waves the unbounded BF16 instance fits; 8 waves would spill.
 template <uint32_t DT>
 __global__ __launch_bounds__(kThreads, 6) void k_decode(DecodeArgs a) {
-    __shared__ uint8_t s_esc[kWavesPerGroup][kPrefetch];
+    __shared__ uint32_t s_esc[kWavesPerGroup][kEscWords];
     const uint32_t wave = uniform(threadIdx.x / kWaveSize);
     const Layout L = layout_of(a.n, DT);
     const uint64_t full = a.n / kBlockElems;
@@ -1746,7 +1890,7 @@ __global__ __launch_bounds__(kThreads, 6) void k_decode(DecodeArgs a) {
 
 template <uint32_t DT>
 __global__ __launch_bounds__(kWaveSize) void k_decode_tail(DecodeArgs a) {
-    __shared__ uint8_t s_esc[kPrefetch];
+    __shared__ uint32_t s_esc[kEscWords];
     const Layout L = layout_of(a.n, DT);
     decode_block<DT, false>(a, L, blockIdx.x, L.blocks - 1, lane_id(), s_esc);
 }
@@ -1845,15 +1989,13 @@ hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s)
 template <uint32_t DT>
 void enqueue_encode_finish(const EncodeArgs& a, hipStream_t s) {
     const Layout L = layout_of(a.n, DT);
-    const uint64_t blocks = static_cast<uint64_t>(a.count) * L.blocks;
-    const uint32_t scatter_groups = grid_for(blocks, kThreads);
-    const uint64_t groups = (L.blocks + kThreads - 1) / kThreads;     // 256-block groups per tensor
+    const uint64_t groups = (L.blocks + kGroupBlocks - 1) / kGroupBlocks;   // block groups per tensor
+    const dim3 grid(static_cast<uint32_t>(a.count * groups));
     if (groups <= kFusedGroups) {
-        hipLaunchKernelGGL(k_offsets_scatter<DT>, dim3(static_cast<uint32_t>(a.count * groups)), dim3(kThreads), 0,
-                           s, a);
+        hipLaunchKernelGGL(k_offsets_scatter<DT>, grid, dim3(kScatterThreads), 0, s, a);
     } else {
         hipLaunchKernelGGL(k_offsets<DT>, dim3(a.count), dim3(256), 0, s, a);
-        hipLaunchKernelGGL(k_scatter<DT>, dim3(scatter_groups), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(k_scatter<DT>, grid, dim3(kScatterThreads), 0, s, a);
     }
 }
 

@@ -112,6 +112,7 @@ sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uin
     a.enc.staging = static_cast<uint8_t*>(d_workspace) + workspace_counts_bytes(count, layout_of(n, dt).blocks);
     a.hists = d_hists;
     a.sync = static_cast<uint8_t*>(d_workspace) + workspace_bytes_for(count, n);
+    a.enc.records = reinterpret_cast<const uint32_t*>(a.sync + sync_records_offset(count));
     a.status = d_status;
     const uint64_t chunk = sample_chunk_elems(dt);
     a.sample_items = static_cast<uint32_t>(sample_items(n, dt));

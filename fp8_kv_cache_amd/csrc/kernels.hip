@@ -394,15 +394,20 @@ __global__ __launch_bounds__(256) void k_codebook(CodebookArgs a) {
 // faster, and the loads a further 3.5% and 3%.
 
 // Header (64 bytes), the zero padding after the offset table and the
-// stream size; `lane` is the calling thread's index (0..63 used).
+// stream size; `lane` is the calling thread's index (0..63 used).  A
+// stream the one-launch compress gave up on (its record shows no verdict or
+// a give-up) gets a zero magic, so that decoding it reports a corrupt
+// stream instead of returning wrong data.
+__device__ inline bool compress_gave_up(const EncodeArgs& a, uint32_t t);
+
 __device__ inline void write_header(SZ_GLOBAL uint8_t* dst, const Layout& L, uint32_t dtype,
                                     const SZ_GLOBAL uint8_t* cb, uint64_t escapes, SZ_GLOBAL uint64_t* out_bytes,
-                                    uint32_t lane) {
+                                    uint32_t lane, bool gave_up = false) {
     const uint64_t total = L.esc_at + escapes;
     const SZ_GLOBAL uint32_t* cbw = (const SZ_GLOBAL uint32_t*)cb;
     uint32_t v = 0;
     switch (lane) {
-        case 0: v = kMagic; break;
+        case 0: v = gave_up ? 0u : kMagic; break;
         case 1: v = kVersion | (dtype << 8) | (kLog2Block << 16) | (kCodes << 24); break;
         case 2: v = static_cast<uint32_t>(L.n); break;
         case 3: v = static_cast<uint32_t>(L.n >> 32); break;
@@ -488,6 +493,81 @@ __device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, 
     sm[2] = (f[5] >> 4) | (f[6] << 8) | (f[7] << 20);
 }
 
+// Escape bytes of a block go to its staging slot at their rank inside the
+// block.  A sparse block (a KV cache block has a few dozen escapes) walks
+// each lane's escape mask and stores each escape byte to the slot.  A dense
+// block (wave-uniform choice: more than kSparseEscapes) would make that a
+// byte store per escape, each wave instruction spread over several lines;
+// instead every element slot of the lane is taken in turn, its rank a
+// masked popcount, the bytes are gathered in the wave's 4 KB of LDS, and
+// the slot is written with 16-byte vectors.
+constexpr uint32_t kSparseEscapes = 256;
+
+template <uint32_t DT>
+__device__ inline uint32_t exponent_of(const uint32_t (&d)[Geometry<DT>::kInWords], uint32_t k) {
+    if constexpr (DT == kDtypeBF16) {
+        uint32_t word = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < Geometry<DT>::kInWords; ++i)
+            if (i == (k >> 1)) word = d[i];
+        return (k & 1) ? (word >> 23) & 0xFFu : (word >> 7) & 0xFFu;
+    } else {
+        uint32_t word = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < Geometry<DT>::kInWords; ++i)
+            if (i == (k >> 2)) word = d[i];
+        return (word >> (8 * (k & 3) + 2)) & 0x1Fu;
+    }
+}
+
+template <uint32_t DT>
+__device__ inline void stage_escapes(SZ_GLOBAL uint8_t* esc_out, uint32_t* esc_lds,
+                                     const uint32_t (&d)[Geometry<DT>::kSubs][Geometry<DT>::kInWords],
+                                     const uint32_t (&esc)[Geometry<DT>::kSubs][Geometry<DT>::kCodeWords],
+                                     const uint32_t (&cnt)[Geometry<DT>::kSubs], const uint32_t (&base)[Geometry<DT>::kSubs],
+                                     uint32_t block_total, uint32_t lane) {
+    using G = Geometry<DT>;
+    if (block_total <= kSparseEscapes) {
+#pragma unroll
+        for (uint32_t j = 0; j < G::kSubs; ++j) {
+            if (cnt[j] == 0) continue;
+            uint32_t rank = base[j];
+#pragma unroll
+            for (uint32_t q = 0; q < G::kCodeWords; ++q) {
+                uint32_t m = esc[j][q];
+                while (m) {
+                    esc_out[rank++] = static_cast<uint8_t>(exponent_of<DT>(d[j], 8 * q + (__builtin_ctz(m) >> 2)));
+                    m &= m - 1;
+                }
+            }
+        }
+        return;
+    }
+    uint8_t* gather = reinterpret_cast<uint8_t*>(esc_lds);
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        uint32_t rank = base[j];
+#pragma unroll
+        for (uint32_t q = 0; q < G::kCodeWords; ++q) {
+            const uint32_t m = esc[j][q];
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) {
+                const uint32_t bit = 1u << (4 * k);
+                if (m & bit)
+                    gather[rank + __builtin_popcount(m & (bit - 1))] =
+                        static_cast<uint8_t>(exponent_of<DT>(d[j], 8 * q + k));
+            }
+            rank += __builtin_popcount(m);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (uint32_t v = lane; 16 * v < block_total; v += kWaveSize) {
+        const uint4 x = *reinterpret_cast<const uint4*>(esc_lds + 4 * v);
+        *(SZ_GLOBAL u32x4*)(esc_out + 16 * v) = u32x4{x.x, x.y, x.z, x.w};
+    }
+    __builtin_amdgcn_wave_barrier();   // the buffer may be reused once every lane has read it
+}
+
 // A wave's share of block b: sub-chunk j, lane l holds elements
 // [4096b + j * 64 * kLaneElems + l * kLaneElems, ... + kLaneElems).
 template <uint32_t DT>
@@ -537,10 +617,12 @@ __device__ inline const uint8_t* build_code_table(uint32_t* tbl_words, uint32_t 
 
 // Encode block b from its registers into stream dst with the code table
 // tbl: planes, the block's escape count and its staged escape bytes (flat
-// = the block's index over all tensors).
+// = the block's index over all tensors).  esc_lds: the wave's 4096 bytes
+// of LDS for gathering a dense block's escapes (16-byte aligned).
 template <uint32_t DT, bool kFull>
 __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b,
-                                     uint64_t flat, uint32_t lane, const uint8_t* tbl, const BlockRegs<DT>& d) {
+                                     uint64_t flat, uint32_t lane, const uint8_t* tbl, const BlockRegs<DT>& d,
+                                     uint32_t* esc_lds) {
     using G = Geometry<DT>;
     constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
     constexpr uint32_t kSmWords = G::kSmWords;
@@ -607,42 +689,14 @@ __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GL
     if (lane == 0) gptr(a.counts)[flat] = uniform(block_total);
 
     // escape bytes, in element order, staged at their rank inside the block
-    SZ_GLOBAL uint8_t* esc_out = gptr(a.staging) + flat * kBlockElems;
-#pragma unroll
-    for (uint32_t j = 0; j < G::kSubs; ++j) {
-        if (cnt[j] == 0) continue;
-        uint32_t rank = base[j];
-#pragma unroll
-        for (uint32_t q = 0; q < G::kCodeWords; ++q) {
-            uint32_t m = esc[j][q];
-            while (m) {
-                const uint32_t k = 8 * q + (__builtin_ctz(m) >> 2);   // element within the lane
-                uint32_t e;
-                if constexpr (DT == kDtypeBF16) {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (uint32_t i = 0; i < G::kInWords; ++i)
-                        if (i == (k >> 1)) word = d[j][i];
-                    e = (k & 1) ? (word >> 23) & 0xFFu : (word >> 7) & 0xFFu;
-                } else {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (uint32_t i = 0; i < 8; ++i)
-                        if (i == (k >> 2)) word = d[j][i];
-                    e = (word >> (8 * (k & 3) + 2)) & 0x1Fu;
-                }
-                esc_out[rank++] = static_cast<uint8_t>(e);
-                m &= m - 1;
-            }
-        }
-    }
+    stage_escapes<DT>(gptr(a.staging) + flat * kBlockElems, esc_lds, d, esc, cnt, base, uniform(block_total), lane);
 }
 
 // One block with the codebook given in memory: the lane's codebook entry
 // first, then the block's input, then the encode.
 template <uint32_t DT, bool kFull>
 __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32_t t, uint64_t b,
-                                    uint64_t flat, uint32_t lane, uint32_t* tbl_words) {
+                                    uint64_t flat, uint32_t lane, uint32_t* tbl_words, uint32_t* esc_lds) {
     const SZ_GLOBAL uint8_t* cb = gptr(a.codebooks) + 16ull * t;
     const uint32_t mine = lane < kCodes ? cb[lane] : 0xFFFFu;
     const SZ_GLOBAL uint8_t* src = src_of(a.src, t);
@@ -650,7 +704,7 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
     BlockRegs<DT> d;
     load_block<DT, kFull>(src, a.n, b, lane, d);
     __builtin_amdgcn_sched_barrier(0);
-    encode_loaded<DT, kFull>(a, L, dst, b, flat, lane, build_code_table(tbl_words, lane, mine), d);
+    encode_loaded<DT, kFull>(a, L, dst, b, flat, lane, build_code_table(tbl_words, lane, mine), d, esc_lds);
 }
 
 // Full blocks only: wave i of the grid takes the i-th full block in
@@ -659,6 +713,7 @@ __device__ inline void encode_block(const EncodeArgs& a, const Layout& L, uint32
 template <uint32_t DT>
 __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
     __shared__ uint32_t s_tbl[kWavesPerGroup][64];   // 256 one-byte codes per wave
+    __shared__ uint32_t s_esc[kWavesPerGroup][kBlockElems / 4];
     const uint32_t wave = uniform(threadIdx.x / kWaveSize);
     const Layout L = layout_of(a.n, DT);
     const uint64_t full = a.n / kBlockElems;          // full blocks per tensor
@@ -666,17 +721,18 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
     if (i >= static_cast<uint64_t>(a.count) * full) return;
     const uint32_t t = static_cast<uint32_t>(i / full);
     const uint64_t b = i - static_cast<uint64_t>(t) * full;
-    encode_block<DT, true>(a, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane_id(), s_tbl[wave]);
+    encode_block<DT, true>(a, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane_id(), s_tbl[wave], s_esc[wave]);
 }
 
 // The partial last block of every tensor, one wave each.
 template <uint32_t DT>
 __global__ __launch_bounds__(kWaveSize) void k_encode_tail(EncodeArgs a) {
     __shared__ uint32_t s_tbl[64];
+    __shared__ uint32_t s_esc[kBlockElems / 4];
     const Layout L = layout_of(a.n, DT);
     const uint32_t t = blockIdx.x;
     const uint64_t b = L.blocks - 1;
-    encode_block<DT, false>(a, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane_id(), s_tbl);
+    encode_block<DT, false>(a, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane_id(), s_tbl, s_esc);
 }
 
 // One workgroup per tensor: off[b] = escapes in blocks [0, b), then the
@@ -706,24 +762,25 @@ __global__ __launch_bounds__(256) void k_offsets(EncodeArgs a) {
         run += counts[b];
     }
     write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, escapes,
-                 a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid);
+                 a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid, compress_gave_up(a, t));
 }
 
 // ---- escape copy: staged escapes -> the stream's escape region
 //
-// A group of kGroupBlocks consecutive blocks of one tensor is copied by one
-// kScatterThreads-thread workgroup.  Block i of the group has c_i staged
-// escapes (16-byte aligned slot) that go to byte off_i of the escape region
-// (the region starts 256-byte aligned; off_i has any alignment).  The copy is
-// cut into 16-byte destination windows aligned in the stream: block i covers
-// ceil(((off_i & 15) + c_i) / 16) of them.  A prefix scan numbers the
-// windows of the group, and all threads take windows in turn, kCopyUnroll at
-// a time, so their loads are in flight together whatever the escape counts
-// (a few windows per block in a KV cache, 225 in an escape-heavy tensor).
-// A window gets its 16 bytes from two adjacent staged vectors, joined by a
-// byte funnel shift.  A window wholly inside its block's range is one
-// 16-byte store; the first and last window of a range may be shared with the
-// neighbouring blocks' escapes and are written byte by byte.
+// A group of kGroupBlocks consecutive blocks of one tensor is copied by
+// scatter_splits() workgroups of kScatterThreads threads.  Block i of the
+// group has c_i staged escapes (16-byte aligned slot) that go to byte off_i
+// of the escape region (the region starts 256-byte aligned; off_i has any
+// alignment).  In the stream's 16-byte windows, block i's range
+// [off_i, off_i + c_i) covers whole windows, stored as 16-byte vectors, and
+// at most two partial ones at its ends, shared with the neighbouring
+// blocks' escapes and written byte by byte.  A prefix scan numbers the
+// whole windows of the group, and all threads of the group's workgroups
+// take them in turn, kCopyUnroll at a time, so their loads are in flight
+// together whatever the escape counts (one or two windows per block in a
+// KV cache, about 224 in an escape-heavy tensor); two threads per block
+// take its partial windows.  A window gets its 16 bytes from two adjacent
+// staged vectors, joined by a byte funnel shift.
 constexpr uint32_t kGroupBlocks = 256;
 constexpr uint32_t kScatterThreads = 1024;
 constexpr uint32_t kCopyUnroll = 4;
@@ -731,7 +788,7 @@ constexpr uint32_t kCopyUnroll = 4;
 struct CopyGroup {
     uint32_t off[kGroupBlocks];       // escape-region byte offset of each block's first escape
     uint32_t cnt[kGroupBlocks];       // escapes of each block
-    uint32_t win[kGroupBlocks + 1];   // first window of each block; win[nb] = windows of the group
+    uint32_t win[kGroupBlocks + 1];   // first whole window of each block; win[nb] = whole windows of the group
     uint32_t sums[kScatterThreads / kWaveSize];
 };
 
@@ -747,64 +804,86 @@ __device__ inline u32x4 funnel16(const u32x4& prev, const u32x4& cur, uint32_t s
                  __builtin_amdgcn_alignbyte(x[3], x[2], r), __builtin_amdgcn_alignbyte(x[4], x[3], r)};
 }
 
-// Window w of the group (w < cg.win[nb]): its block by binary search, then
-// the staged vectors it needs.  `slot0` is the staging slot of the group's
-// first block, `esc` the stream's escape region.
-struct CopyWindow {
-    SZ_GLOBAL uint8_t* to;   // 16-byte aligned destination
-    uint32_t lo, hi;         // bytes [lo, hi) of the window belong to the block
-    uint32_t s;              // the block's misalignment
-    u32x4 prev, cur;
-};
-
-__device__ inline CopyWindow copy_window_load(const CopyGroup& cg, uint32_t nb, uint32_t w,
-                                              const SZ_GLOBAL uint8_t* slot0, SZ_GLOBAL uint8_t* esc) {
-    uint32_t lo = 0, hi = nb;   // the block i with win[i] <= w < win[i + 1]
-    while (hi - lo > 1) {
-        const uint32_t mid = (lo + hi) / 2;
-        if (cg.win[mid] <= w) lo = mid; else hi = mid;
-    }
-    const uint32_t i = lo, lw = w - cg.win[i];
-    const uint32_t off = cg.off[i], cnt = cg.cnt[i], s = off & 15;
-    CopyWindow c;
-    c.to = esc + (off - s) + 16ull * lw;
-    c.lo = lw == 0 ? s : 0;
-    const uint32_t end = s + cnt - 16 * lw;   // > 0: the window holds at least one byte of the block
-    c.hi = end < 16 ? end : 16;
-    c.s = s;
-    const SZ_GLOBAL u32x4* slot = (const SZ_GLOBAL u32x4*)(slot0 + static_cast<uint64_t>(i) * kBlockElems);
-    c.cur = 16 * lw < cnt ? slot[lw] : u32x4{0, 0, 0, 0};
-    c.prev = s && lw ? slot[lw - 1] : u32x4{0, 0, 0, 0};
-    return c;
+// Window lw of a block whose range starts s = off & 15 bytes into its first
+// window: the two staged vectors it draws on (a vector wholly outside
+// [0, cnt) is not read), funnelled into the window's 16 bytes.
+__device__ inline u32x4 window_bytes(const SZ_GLOBAL u32x4* slot, uint32_t lw, uint32_t s, uint32_t cnt) {
+    const u32x4 cur = 16 * lw < cnt ? slot[lw] : u32x4{0, 0, 0, 0};
+    if (s == 0) return cur;
+    const u32x4 prev = lw ? slot[lw - 1] : u32x4{0, 0, 0, 0};
+    return funnel16(prev, cur, s);
 }
 
-__device__ inline void copy_window_store(const CopyWindow& c) {
-    const u32x4 v = c.s ? funnel16(c.prev, c.cur, c.s) : c.cur;
-    if (c.lo == 0 && c.hi == 16) {
-        __builtin_nontemporal_store(v, (SZ_GLOBAL u32x4*)c.to);
-        return;
-    }
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (uint32_t k = 0; k < 16; ++k)
-        if (k >= c.lo && k < c.hi) c.to[k] = static_cast<uint8_t>(w[k / 4] >> (8 * (k & 3)));
+// Whole windows of block i: lw in [first_whole, (s + cnt) / 16).
+__device__ inline uint32_t first_whole(uint32_t s) { return s ? 1u : 0u; }
+__device__ inline uint32_t whole_windows(uint32_t off, uint32_t cnt) {
+    const uint32_t s = off & 15, end = (s + cnt) / 16, a = first_whole(s);
+    return cnt && end > a ? end - a : 0u;
 }
 
-// Every thread of the workgroup calls it after cg is complete (a barrier).
+// Every thread of the group's workgroups calls it after cg is complete (a
+// barrier); split `split` of `splits` takes every splits-th round of
+// whole windows, and split 0 also writes the partial windows.
 __device__ inline void copy_escapes(const CopyGroup& cg, uint32_t nb, const SZ_GLOBAL uint8_t* slot0,
-                                    SZ_GLOBAL uint8_t* esc, uint32_t tid) {
+                                    SZ_GLOBAL uint8_t* esc, uint32_t tid, uint32_t split, uint32_t splits) {
     const uint32_t total = cg.win[nb];
-    for (uint32_t w0 = tid; w0 < total; w0 += kScatterThreads * kCopyUnroll) {
-        CopyWindow c[kCopyUnroll];
+    constexpr uint32_t kRound = kScatterThreads * kCopyUnroll;
+    for (uint32_t w0 = split * kRound + tid; w0 < total; w0 += splits * kRound) {
+        uint32_t blk[kCopyUnroll];
+#pragma unroll
+        for (uint32_t k = 0; k < kCopyUnroll; ++k) {   // the block of each window (binary search over win)
+            const uint32_t w = w0 + k * kScatterThreads;
+            uint32_t lo = 0, hi = nb;
+            while (hi - lo > 1) {
+                const uint32_t mid = (lo + hi) / 2;
+                if (cg.win[mid] <= w) lo = mid; else hi = mid;
+            }
+            blk[k] = lo;
+        }
+        // every load of the round is issued before any is used: a window
+        // past the end reads vector 0 of the group's first slot and stores
+        // nothing; a whole window always needs its `cur` vector, and its
+        // `prev` one when s > 0 (then lw >= 1); with lw = 0 vector 0 is
+        // read and unused (the index never goes below 0)
+        u32x4 cur[kCopyUnroll], prev[kCopyUnroll];
+        uint32_t skew[kCopyUnroll];
+        SZ_GLOBAL uint8_t* to[kCopyUnroll];
 #pragma unroll
         for (uint32_t k = 0; k < kCopyUnroll; ++k) {
             const uint32_t w = w0 + k * kScatterThreads;
-            if (w < total) c[k] = copy_window_load(cg, nb, w, slot0, esc);
+            const bool live = w < total;
+            const uint32_t i = live ? blk[k] : 0u, off = cg.off[i], s = off & 15;
+            const uint32_t lw = live ? first_whole(s) + (w - cg.win[i]) : 0u;
+            const SZ_GLOBAL u32x4* slot = (const SZ_GLOBAL u32x4*)(slot0 + static_cast<uint64_t>(i) * kBlockElems);
+            to[k] = esc + (off - s) + 16ull * lw;
+            skew[k] = s;
+            cur[k] = slot[lw];
+            prev[k] = slot[lw ? lw - 1 : 0u];
         }
 #pragma unroll
         for (uint32_t k = 0; k < kCopyUnroll; ++k)
-            if (w0 + k * kScatterThreads < total) copy_window_store(c[k]);
+            if (w0 + k * kScatterThreads < total)
+                __builtin_nontemporal_store(skew[k] ? funnel16(prev[k], cur[k], skew[k]) : cur[k],
+                                            (SZ_GLOBAL u32x4*)to[k]);
     }
+    // partial windows: thread 2i takes block i's first window when its range
+    // starts inside it, thread 2i + 1 the last one when the range ends inside
+    // it (unless that is the same window)
+    if (split != 0 || tid >= 2 * nb) return;
+    const uint32_t i = tid / 2, off = cg.off[i], cnt = cg.cnt[i], s = off & 15, end = (s + cnt) / 16;
+    if (cnt == 0) return;
+    const bool head = (tid & 1) == 0;
+    if (head ? s == 0 : ((s + cnt) % 16 == 0 || (end == 0 && s != 0))) return;
+    const uint32_t lw = head ? 0u : end;
+    const uint32_t lo = lw == 0 ? s : 0u;
+    const uint32_t stop = s + cnt - 16 * lw;
+    const uint32_t hi = stop < 16 ? stop : 16u;
+    const u32x4 v = window_bytes((const SZ_GLOBAL u32x4*)(slot0 + static_cast<uint64_t>(i) * kBlockElems), lw, s, cnt);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    SZ_GLOBAL uint8_t* to = esc + (off - s) + 16ull * lw;
+#pragma unroll
+    for (uint32_t k = 0; k < 16; ++k)
+        if (k >= lo && k < hi) to[k] = static_cast<uint8_t>(w[k / 4] >> (8 * (k & 3)));
 }
 
 // Sum of x over the kScatterThreads threads (every thread gets it).
@@ -836,7 +915,7 @@ __device__ inline uint32_t group_blocks_scan(uint32_t x, uint32_t tid, uint32_t*
 // Fills cg for the group's nb blocks from their offsets and counts (held by
 // threads 0..nb-1).  Every thread calls it; ends with a barrier.
 __device__ inline void plan_copy(CopyGroup& cg, uint32_t off, uint32_t cnt, uint32_t nb, uint32_t tid) {
-    const uint32_t windows = tid < nb && cnt ? ((off & 15) + cnt + 15) / 16 : 0u;
+    const uint32_t windows = tid < nb ? whole_windows(off, cnt) : 0u;
     uint32_t total;
     const uint32_t first = group_blocks_scan(windows, tid, cg.sums, total);
     if (tid < nb) {
@@ -848,14 +927,47 @@ __device__ inline void plan_copy(CopyGroup& cg, uint32_t off, uint32_t cnt, uint
     __syncthreads();
 }
 
-// Beyond 2^16 blocks per tensor: k_offsets wrote the offset table; one
-// workgroup per group of kGroupBlocks blocks copies their staged escapes.
+// Sum of counts[0 .. len) (u32, device memory) over the workgroup's
+// threads: 16-byte loads for the aligned middle, eight in flight per thread.
+__device__ inline uint32_t sum_counts(const SZ_GLOBAL uint32_t* counts, uint64_t len, uint32_t tid, uint32_t* sums) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(counts);
+    uint64_t head = ((16 - (addr & 15)) & 15) / 4;   // words before the first 16-byte boundary
+    if (head > len) head = len;
+    const uint64_t vecs = (len - head) / 4;
+    uint32_t x = 0;
+    if (tid < head) x += counts[tid];
+    const SZ_GLOBAL u32x4* v = (const SZ_GLOBAL u32x4*)(counts + head);
+    for (uint64_t k = tid; k < vecs; k += 8 * kScatterThreads) {
+        u32x4 r[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u)
+            r[u] = k + u * kScatterThreads < vecs ? v[k + u * kScatterThreads] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) x += r[u].x + r[u].y + r[u].z + r[u].w;
+    }
+    const uint64_t tail = head + 4 * vecs;
+    if (tail + tid < len) x += counts[tail + tid];
+    return group_sum(x, tid, sums);
+}
+
+// Workgroups per block group of the escape copy: enough for about 1024
+// workgroups in all, at most 8 (each split recomputes the group's offsets).
+__host__ __device__ inline uint32_t scatter_splits(uint32_t count, uint64_t blocks) {
+    const uint64_t groups = static_cast<uint64_t>(count) * ((blocks + kGroupBlocks - 1) / kGroupBlocks);
+    const uint64_t want = (1024 + groups - 1) / groups;
+    return static_cast<uint32_t>(want < 1 ? 1 : (want > 8 ? 8 : want));
+}
+
+// Beyond 2^16 blocks per tensor: k_offsets wrote the offset table; the
+// workgroups of each group of kGroupBlocks blocks copy their staged escapes.
 template <uint32_t DT>
 __global__ __launch_bounds__(kScatterThreads) void k_scatter(EncodeArgs a) {
     __shared__ CopyGroup cg;
     const Layout L = layout_of(a.n, DT);
     const uint32_t groups = static_cast<uint32_t>((L.blocks + kGroupBlocks - 1) / kGroupBlocks);
-    const uint32_t t = blockIdx.x / groups, g = blockIdx.x - t * groups, tid = threadIdx.x;
+    const uint32_t splits = scatter_splits(a.count, L.blocks);
+    const uint32_t unit = blockIdx.x / splits, split = blockIdx.x - unit * splits;
+    const uint32_t t = unit / groups, g = unit - t * groups, tid = threadIdx.x;
     const uint64_t b0 = static_cast<uint64_t>(g) * kGroupBlocks;
     const uint32_t nb = static_cast<uint32_t>(L.blocks - b0 < kGroupBlocks ? L.blocks - b0 : kGroupBlocks);
     SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
@@ -863,16 +975,16 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(EncodeArgs a) {
     const uint32_t cnt = tid < nb ? gptr(a.counts)[flat0 + tid] : 0u;
     const uint32_t off = tid < nb ? ((const SZ_GLOBAL uint32_t*)(dst + 64))[b0 + tid] : 0u;
     plan_copy(cg, off, cnt, nb, tid);
-    copy_escapes(cg, nb, gptr(a.staging) + flat0 * kBlockElems, dst + L.esc_at, tid);
+    copy_escapes(cg, nb, gptr(a.staging) + flat0 * kBlockElems, dst + L.esc_at, tid, split, splits);
 }
 
 // k_offsets and k_scatter in one launch, for tensors of at most
-// kFusedGroups x kGroupBlocks blocks.  Workgroup g of tensor t takes blocks
-// [256g, 256g + 256): its base offset is the sum of the counts of every
-// earlier block, read directly (fewer than 2^16 reads, from L2), so no
-// workgroup waits for another; an in-group scan gives each block its
-// offset, which goes to the table, and the group's escapes are copied.  The
-// last workgroup of a tensor writes the header.
+// kFusedGroups x kGroupBlocks blocks.  The workgroups of group g of tensor
+// t take blocks [256g, 256g + 256): their base offset is the sum of the
+// counts of every earlier block, read directly (fewer than 2^16 reads, from
+// L2), so no workgroup waits for another; an in-group scan gives each block
+// its offset, which split 0 writes to the table, and the group's escapes
+// are copied.  Split 0 of the last group of a tensor writes the header.
 constexpr uint64_t kFusedGroups = 256;
 
 template <uint32_t DT>
@@ -880,24 +992,26 @@ __global__ __launch_bounds__(kScatterThreads) void k_offsets_scatter(EncodeArgs 
     __shared__ CopyGroup cg;
     const Layout L = layout_of(a.n, DT);
     const uint32_t groups = static_cast<uint32_t>((L.blocks + kGroupBlocks - 1) / kGroupBlocks);
-    const uint32_t t = blockIdx.x / groups, g = blockIdx.x - t * groups, tid = threadIdx.x;
+    const uint32_t splits = scatter_splits(a.count, L.blocks);
+    const uint32_t unit = blockIdx.x / splits, split = blockIdx.x - unit * splits;
+    const uint32_t t = unit / groups, g = unit - t * groups, tid = threadIdx.x;
     const uint64_t b0 = static_cast<uint64_t>(g) * kGroupBlocks;
     const uint32_t nb = static_cast<uint32_t>(L.blocks - b0 < kGroupBlocks ? L.blocks - b0 : kGroupBlocks);
     const SZ_GLOBAL uint32_t* counts = gptr(a.counts) + static_cast<uint64_t>(t) * L.blocks;
     const uint32_t cnt = tid < nb ? counts[b0 + tid] : 0u;
-    uint32_t before = 0;
-    for (uint32_t k = tid; k < g * kGroupBlocks; k += kScatterThreads) before += counts[k];
-    const uint32_t base = group_sum(before, tid, cg.sums);
+    const uint32_t base = sum_counts(counts, b0, tid, cg.sums);
     uint32_t in_group;
     const uint32_t off = base + group_blocks_scan(cnt, tid, cg.sums, in_group);
     SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
-    if (tid < nb) ((SZ_GLOBAL uint32_t*)(dst + 64))[b0 + tid] = off;
-    if (g == groups - 1)
-        write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, base + in_group,
-                     a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid);
+    if (split == 0) {
+        if (tid < nb) ((SZ_GLOBAL uint32_t*)(dst + 64))[b0 + tid] = off;
+        if (g == groups - 1)
+            write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, base + in_group,
+                         a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid, compress_gave_up(a, t));
+    }
     plan_copy(cg, off, cnt, nb, tid);
     copy_escapes(cg, nb, gptr(a.staging) + (static_cast<uint64_t>(t) * L.blocks + b0) * kBlockElems,
-                 dst + L.esc_at, tid);
+                 dst + L.esc_at, tid, split, splits);
 }
 
 // n == 0: a header-only stream per tensor
@@ -965,9 +1079,10 @@ struct SyncView {
     SZ_GLOBAL uint64_t* sample;   // count x 256, sampled chunks
     SZ_GLOBAL uint32_t* ticket;
     SZ_GLOBAL uint32_t* abort;
-    SZ_GLOBAL uint32_t* listed;   // [2]: entries in use of the two lists
+    SZ_GLOBAL uint32_t* listed;   // [kLists]: entries in use of the lists
     SZ_GLOBAL uint32_t* records;  // per tensor 32 words, see kRec*
-    SZ_GLOBAL uint32_t* list;     // [2][count] entries of kEntryWords: tensors to recode, reordered ones, then the others
+    SZ_GLOBAL uint32_t* list;     // [kLists][count] entries of kEntryWords: reordered tensors, tensors with other
+                                  // values, escape-heavy tensors (encoded from the input)
 };
 
 // A list entry: everything the recode of one tensor needs, in one 64-byte
@@ -977,7 +1092,8 @@ struct SyncView {
 constexpr uint32_t kEntryWords = 16;
 
 constexpr uint32_t kRecProvisional = 0;  // 4 words: the provisional codebook (complete once 15 bytes differ)
-constexpr uint32_t kRecVerdict = 8;      // kProvisionalSame / Reordered / Differs
+constexpr uint32_t kRecVerdict = 8;      // kProvisionalSame / Reordered / Differs / CountOnly
+constexpr uint32_t kRecGaveUp = 9;       // 1 once any work item of the tensor gave up
 
 __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     SyncView v;
@@ -988,8 +1104,14 @@ __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     v.abort = w + 1;
     v.listed = w + 2;
     v.records = w + 64;
-    v.list = v.records + 32ull * count;   // 2 x count entries
+    v.list = v.records + 32ull * count;   // kLists x count entries
     return v;
+}
+
+__device__ inline bool compress_gave_up(const EncodeArgs& a, uint32_t t) {
+    if (!a.records) return false;
+    const SZ_GLOBAL uint32_t* rec = gptr(a.records) + 32ull * t;
+    return rec[kRecVerdict] == 0 || rec[kRecGaveUp] != 0;
 }
 
 __device__ inline uint32_t load_agent(const SZ_GLOBAL uint32_t* p) {
@@ -1005,6 +1127,15 @@ __device__ inline void store_agent(SZ_GLOBAL uint32_t* p, uint32_t v) {
 }
 
 constexpr int32_t kStatusGaveUp = 5;   // SZ_ERR_TIMEOUT
+
+// A work item of tensor t gave up (thread 0 of its workgroup records it):
+// SZ_ERR_TIMEOUT in the status word and the give-up mark in the record,
+// which the header writer turns into a stream that does not decode.
+__device__ inline void mark_gave_up(const CompressArgs& a, SZ_GLOBAL uint32_t* rec, uint32_t t, uint32_t tid) {
+    if (tid != 0) return;
+    if (a.status) gptr(a.status)[t] = kStatusGaveUp;
+    store_agent(rec + kRecGaveUp, 1u);
+}
 
 // A reading of a tensor's provisional codebook (lanes 0..3 of a wave each
 // hold one of its words) is complete when bytes 0..14 are 15 distinct
@@ -1143,11 +1274,29 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
         uint64_t c = 0;
         if (wait_histogram<DT>(sv.sample + 256ull * t, a.sample_total, sv, a.spin_limit, s_word, tid, lane, wave,
                                c) != 1) {
-            if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
+            mark_gave_up(a, rec, t, tid);
             return;
         }
         rank_codebook<DT>(c, bins, s_word, tid);
-        if (tid < 4) store_agent(rec + kRecProvisional + tid, s_word[2 + tid]);   // the publication itself
+        // the sample's escapes under P: escape-heavy tensors are only counted
+        // by their main items (byte 15 of the published codebook says so)
+        uint32_t covered = 0;
+        if (tid < Geometry<DT>::kDomain) {
+            const uint8_t* pb = reinterpret_cast<const uint8_t*>(s_word + 2);
+            bool in_p = false;
+#pragma unroll
+            for (uint32_t k = 0; k < kCodes; ++k) in_p |= pb[k] == tid;
+            covered = in_p ? static_cast<uint32_t>(c) : 0u;
+        }
+        covered = __builtin_amdgcn_readlane(wave_scan_incl(covered), 63);
+        if (lane == 0 && wave < 4) s_word[8 + wave] = covered;
+        __syncthreads();
+        if (tid < 4) {
+            const uint32_t in_sample = s_word[8] + s_word[9] + s_word[10] + s_word[11];
+            const uint32_t heavy = (a.sample_total - in_sample) > a.sample_total / kCountOnlyRatio ? 1u : 0u;
+            const uint32_t word = tid == 3 ? s_word[5] | (heavy << 24) : s_word[2 + tid];
+            store_agent(rec + kRecProvisional + tid, word);   // the publication itself
+        }
         return;
     }
 
@@ -1166,9 +1315,13 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
             ok = s_word[13];
         }
         if (!ok) {
-            if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
+            mark_gave_up(a, rec, t, tid);
             return;
         }
+        // byte 15 of the provisional codebook: the escape-heavy mark, not a code
+        const uint32_t count_only = s_word[19] >> 24;
+        __syncthreads();   // every thread has read the mark before it is cleared
+        if (tid == 0) s_word[19] &= 0x00FFFFFFu;
         if (tid < 256) gptr(a.hists)[256ull * t + tid] = c;
         rank_codebook<DT>(c, bins, s_word, tid);
         if (tid < 4) gptr(reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(a.enc.codebooks) + 16ull * t))[tid] =
@@ -1205,15 +1358,18 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
             bool same = true;
 #pragma unroll
             for (uint32_t k = 0; k < 4; ++k) same &= s_word[16 + k] == s_word[2 + k];
-            store_agent(rec + kRecVerdict,
-                        same ? kProvisionalSame : (s_word[6] ? kProvisionalDiffers : kProvisionalReordered));
+            const uint32_t verdict = count_only ? kProvisionalCountOnly
+                                     : same     ? kProvisionalSame
+                                     : s_word[6] ? kProvisionalDiffers : kProvisionalReordered;
+            store_agent(rec + kRecVerdict, verdict);
             uint32_t slot = ~0u;
-            if (!same) {
-                const uint32_t k = s_word[6] ? 1u : 0u;   // list 0: reordered, 1: other values
+            if (verdict != kProvisionalSame) {
+                // list 0: reordered, 1: other values, 2: escape-heavy (encoded from the input)
+                const uint32_t k = verdict == kProvisionalReordered ? 0u : verdict == kProvisionalDiffers ? 1u : 2u;
                 slot = k * a.enc.count +
                        __hip_atomic_fetch_add(sv.listed + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            s_word[7] = slot;   // a tensor is listed at most once, so a slot stays below 2 x count
+            s_word[7] = slot;   // a tensor is listed at most once, so a slot stays below kLists x count
         }
         __syncthreads();
         const uint32_t slot = s_word[7];
@@ -1250,8 +1406,10 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     if (wave == 0) {
         uint32_t mine;
         const bool got = wait_codebook(rec + kRecProvisional, word, sv, a.spin_limit, lane, mine);
-        if (got) build_code_table(s_tbl, lane, lane < kCodes ? mine : 0xFFFFu);
-        if (lane == 0) s_word[12] = got ? 1u : 0u;
+        // byte 15 of P marks an escape-heavy tensor: count only
+        const uint32_t heavy = static_cast<uint32_t>(__builtin_amdgcn_readlane(word, 3)) >> 24;
+        if (got && !heavy) build_code_table(s_tbl, lane, lane < kCodes ? mine : 0xFFFFu);
+        if (lane == 0) s_word[12] = got ? (heavy ? 2u : 1u) : 0u;
     }
     __syncthreads();
     if (mine_full) {
@@ -1261,28 +1419,34 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
 #pragma unroll
             for (uint32_t i = 0; i < Geometry<DT>::kInWords; ++i) count_dword<DT>(lds, d[j][i], copy4);
     }
-    if (s_word[12]) {
-        if (mine_full)
-            encode_loaded<DT, true>(a.enc, L, dst_of(a.enc.dst, t), b, flat, lane,
-                                    reinterpret_cast<const uint8_t*>(s_tbl), d);
-    } else {
-        // gave up: no escapes for this block (so the scatter that follows
-        // stays inside the stream) and an error for the tensor
-        if (mine_full && lane == 0) gptr(a.enc.counts)[flat] = 0;
-        if (tid == 0 && a.status) gptr(a.status)[t] = kStatusGaveUp;
-    }
     uint32_t phantom = 0;
     if (n % kBlockElems && full_blocks / kPassWaves == it.idx)   // the partial last block is in this item
         phantom = count_ragged<DT, kPassThreads>(lds, src, full_blocks * kBlockElems, n, tid);
     __syncthreads();
     hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * t, phantom);
+    __syncthreads();   // the histogram copies are read: their LDS now stages the waves' escapes
+    const uint32_t state = s_word[12];   // 1: encode with P, 2: escape-heavy, count only, 0: gave up
+    if (state == 1) {
+        if (mine_full)
+            encode_loaded<DT, true>(a.enc, L, dst_of(a.enc.dst, t), b, flat, lane,
+                                    reinterpret_cast<const uint8_t*>(s_tbl), d, bins + wave * (kBlockElems / 4));
+    } else {
+        // no escapes for this block yet (so the scatter that follows stays
+        // inside the stream if the tensor is never encoded); an escape-heavy
+        // tensor is encoded by the recode launch, a give-up is recorded
+        if (mine_full && lane == 0) gptr(a.enc.counts)[flat] = 0;
+        if (state == 0) mark_gave_up(a, rec, t, tid);
+    }
 }
 
 // One workgroup per item: the ticket taken at the start fixes the item.
 template <uint32_t DT>
 __global__ __launch_bounds__(kPassThreads, 8) void k_compress(CompressArgs a) {
     static_assert(kPassThreads % 256 == 0 && Geometry<DT>::kDomain % (kPassThreads / 256) == 0, "rank split");
-    __shared__ uint32_t bins[HistLds<DT>::kWords];
+    // the histogram copies, and after a main item's flush its waves' escape
+    // staging (4 KB each)
+    constexpr uint32_t kStageWords = kPassWaves * (kBlockElems / 4);
+    __shared__ uint32_t bins[HistLds<DT>::kWords > kStageWords ? HistLds<DT>::kWords : kStageWords];
     __shared__ uint32_t s_tbl[64];    // the code table of a main item, shared by its waves
     __shared__ uint32_t s_word[20];   // [0], [14], [15] the item
     const uint32_t tid = threadIdx.x, lane = lane_id();
@@ -1553,11 +1717,32 @@ __device__ inline void transcode_list(const CompressArgs& a, const SyncView& sv,
     }
 }
 
-// Tensors whose provisional codebook was not the final one (the final
-// items list them): every full block of a listed tensor is recoded for the
-// final codebook, first the reordered tensors' code nibbles, then the other
-// tensors' codes and escapes, each list spread over every wave of the grid
-// so a short list still covers the whole GPU; with empty lists every
+// The full blocks of the escape-heavy tensors (list 2), encoded from the
+// input with their final codebooks exactly as k_encode does, split into
+// equal contiguous runs over the waves of the grid.
+template <uint32_t DT>
+__device__ inline void encode_list(const CompressArgs& a, const SZ_GLOBAL uint32_t* list, uint32_t listed, uint64_t w,
+                                   uint64_t waves, uint32_t* tbl_words, uint32_t* esc_words, uint32_t lane) {
+    const uint64_t full_blocks = a.enc.n / kBlockElems;
+    const uint64_t total = static_cast<uint64_t>(listed < a.enc.count ? listed : a.enc.count) * full_blocks;
+    const uint64_t per = (total + waves - 1) / waves;
+    const uint64_t first = w * per;
+    const uint64_t last = first + per < total ? first + per : total;
+    const Layout L = layout_of(a.enc.n, DT);
+    for (uint64_t i = first; i < last; ++i) {
+        const uint32_t t = uniform(list[i / full_blocks * kEntryWords]);
+        const uint64_t b = i % full_blocks;
+        __builtin_amdgcn_wave_barrier();   // the previous block's code table is no longer read
+        encode_block<DT, true>(a.enc, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane, tbl_words, esc_words);
+    }
+}
+
+// Tensors whose provisional codebook was not used as the final one (the
+// final items list them): every full block of a listed tensor is recoded
+// for the final codebook, first the reordered tensors' code nibbles, then
+// the other tensors' codes and escapes, then the escape-heavy tensors are
+// encoded from their input; each list is spread over every wave of the
+// grid so a short list still covers the whole GPU.  With empty lists every
 // workgroup leaves at once.
 template <uint32_t DT>
 __global__ __launch_bounds__(kThreads, 8) void k_transcode(CompressArgs a) {
@@ -1567,9 +1752,11 @@ __global__ __launch_bounds__(kThreads, 8) void k_transcode(CompressArgs a) {
     const SyncView sv = sync_view(a.sync, a.enc.count);
     const uint64_t waves = static_cast<uint64_t>(gridDim.x) * kWavesPerGroup;
     const uint64_t w = static_cast<uint64_t>(blockIdx.x) * kWavesPerGroup + wave;
+    const uint64_t entries = static_cast<uint64_t>(a.enc.count) * kEntryWords;
     transcode_list<DT, true>(a, sv, sv.list, uniform(sv.listed[0]), w, waves, s_tbl[wave], s_esc[wave], lane);
-    transcode_list<DT, false>(a, sv, sv.list + static_cast<uint64_t>(a.enc.count) * kEntryWords,
-                              uniform(sv.listed[1]), w, waves, s_tbl[wave], s_esc[wave], lane);
+    transcode_list<DT, false>(a, sv, sv.list + entries, uniform(sv.listed[1]), w, waves, s_tbl[wave], s_esc[wave],
+                              lane);
+    encode_list<DT>(a, sv.list + 2 * entries, uniform(sv.listed[2]), w, waves, s_tbl[wave], s_esc[wave], lane);
 }
 
 // ----------------------------------------------------------------- decode
@@ -1990,7 +2177,7 @@ template <uint32_t DT>
 void enqueue_encode_finish(const EncodeArgs& a, hipStream_t s) {
     const Layout L = layout_of(a.n, DT);
     const uint64_t groups = (L.blocks + kGroupBlocks - 1) / kGroupBlocks;   // block groups per tensor
-    const dim3 grid(static_cast<uint32_t>(a.count * groups));
+    const dim3 grid(static_cast<uint32_t>(a.count * groups * scatter_splits(a.count, L.blocks)));
     if (groups <= kFusedGroups) {
         hipLaunchKernelGGL(k_offsets_scatter<DT>, grid, dim3(kScatterThreads), 0, s, a);
     } else {

@@ -103,6 +103,9 @@ struct EncodeArgs {
     uint64_t* out_bytes;      // count, may be null
     uint32_t* counts;         // count x blocks escape counts (workspace)
     uint8_t* staging;         // count x blocks x 4096 staged escape bytes (workspace)
+    const uint32_t* records;  // the one-launch compress's per-tensor records (null for the separate calls):
+                              // a tensor whose record shows no verdict or a give-up gets a header that
+                              // does not decode
     uint32_t count;
     uint64_t n;
 };
@@ -112,16 +115,17 @@ struct EncodeArgs {
 // kernel zeroes before every launch:
 //   u64 hist[count][256]     exponent counts of the whole tensor
 //   u64 sample[count][256]   exponent counts of the sampled chunks
-//   u32 ticket, u32 abort, u32 listed[2]   (padded to 256 bytes)
+//   u32 ticket, u32 abort, u32 listed[3]   (padded to 256 bytes)
 //   per tensor t a 128-byte record of u32 words: [0..3] the provisional
-//   codebook (published once its 15 bytes are distinct), [8] the verdict
-//   on it once the final codebook is known (kProvisional*; 0 if the
-//   tensor gave up)
-//   list[2][count]           64-byte entries; the first listed[k] of list k
+//   codebook (published once its bytes 0..14 are distinct; byte 15 is 1
+//   when the tensor is escape-heavy, see kProvisionalCountOnly), [8] the
+//   verdict on it once the final codebook is known (kProvisional*; 0 if
+//   the tensor gave up), [9] 1 once any of its work gave up
+//   list[3][count]           64-byte entries; the first listed[k] of list k
 //                            describe the tensors whose provisional
-//                            codebook is not the final one, [0]
+//                            codebook was not used as the final one, [0]
 //                            kProvisionalReordered, [1] kProvisionalDiffers,
-//                            in no set order
+//                            [2] kProvisionalCountOnly, in no set order
 constexpr uint32_t kPassWaves = 16;                         // blocks per main item, one per wave
 constexpr uint32_t kPassThreads = kPassWaves * kWaveSize;   // 1024
 constexpr uint32_t kSampleStride = 16;                      // one counting chunk in 16 feeds the provisional codebook
@@ -132,6 +136,14 @@ constexpr uint64_t kDefaultFusedMin = 1ull << 21;           // smallest BF16 ten
 constexpr uint32_t kProvisionalSame = 1;       // no recoding
 constexpr uint32_t kProvisionalReordered = 2;  // same 15 values, other codes: code nibbles recoded
 constexpr uint32_t kProvisionalDiffers = 3;    // other values: code nibbles and escapes recoded
+// Escape-heavy tensors: when more than 1/kCountOnlyRatio of the sample
+// escapes under its own provisional codebook, the final codebook would
+// nearly always differ and a recode would rewrite most of the stream, so
+// the main items only count such a tensor and the recode launch encodes it
+// from the input with the final codebook.
+constexpr uint32_t kProvisionalCountOnly = 4;
+constexpr uint32_t kCountOnlyRatio = 4;
+constexpr uint32_t kLists = 3;
 constexpr uint32_t kTranscodeGroups = 2048;                 // workgroups of the transcode kernel, at most
 
 // Elements one sample item counts: 8 passes of a 16-byte vector per lane
@@ -141,8 +153,11 @@ __host__ __device__ inline uint64_t sample_chunk_elems(uint32_t dtype) {
 }
 
 __host__ __device__ inline uint64_t sync_area_bytes(uint32_t count) {
-    return 4096ull * count + 256 + 128ull * count + 128ull * count;
+    return 4096ull * count + 256 + 128ull * count + 64ull * kLists * count;
 }
+
+// The per-tensor records inside the synchronisation area (32 u32 words each).
+__host__ __device__ inline uint64_t sync_records_offset(uint32_t count) { return 4096ull * count + 256; }
 
 struct CompressArgs {
     EncodeArgs enc;           // enc.codebooks (count x 16) is written by the compress kernel

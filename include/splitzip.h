@@ -178,18 +178,24 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * Llama-shaped BF16 cache), a short second kernel recodes that tensor's
  * code nibbles and staged escapes for the final codebook from what was
  * written, without reading the input again; the partial last block is
- * encoded with the final codebook afterwards.  The bytes written are the
- * same as the separate calls'.  E5M2 tensors (measured slower fused) and
- * BF16 tensors below sz_compress_fused_min_elements() run the separate
- * calls' kernels, with the same results.
+ * encoded with the final codebook afterwards.  A tensor of which more than
+ * a quarter of the sample escapes under its own provisional codebook (an
+ * escape-heavy tensor, where the final codebook nearly always differs and a
+ * recode would rewrite most of the stream) is only counted in the first
+ * kernel and encoded from its input by the second, with the final codebook.
+ * The bytes written are the same as the separate calls'.  E5M2 tensors
+ * (measured slower fused) and BF16 tensors below
+ * sz_compress_fused_min_elements() run the separate calls' kernels, with the
+ * same results.
  *
  * Work inside the kernel waits only for work handed out before it, so a
  * call always makes progress, whatever else shares the GPU.  Waits are
  * bounded nonetheless: a workgroup that has polled sz_compress_spin_limit()
  * times without progress (about a second) gives up, and so does every
  * workgroup after it; each tensor they belong to gets SZ_ERR_TIMEOUT in
- * d_status and unspecified outputs (its stream still stays inside
- * dst_capacity).
+ * d_status, unspecified histogram and codebook, and a stream that stays
+ * inside dst_capacity and starts with a zero magic, so that sz_decode
+ * reports it as SZ_ERR_CORRUPT_STREAM even when d_status is NULL.
  *
  * d_hist(s): 256 (count x 256) u64, written.  d_codebook(s): 16 (count x
  * 16) bytes, written.  d_dst(s), dst_capacity, d_out_bytes: as sz_encode.
@@ -200,7 +206,7 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * SZ_ERR_INVALID_ARGUMENT.
  * d_workspace: >= sz_compress_workspace_bytes[_batched] bytes, contents
  * need not be initialised, clobbered (the encode workspace followed by a
- * synchronisation area: 256 bytes plus 4352 bytes per tensor).  Calls
+ * synchronisation area: 256 bytes plus 4416 bytes per tensor).  Calls
  * sharing a workspace must not overlap in time. ---- */
 
 uint64_t sz_compress_workspace_bytes(uint64_t n, sz_dtype dtype);

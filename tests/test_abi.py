@@ -115,10 +115,10 @@ def test_host_argument_errors_return_before_launch(sz):
 def test_compress_sizes_and_host_errors(sz):
     """Single-pass calls: workspace = the encode workspace plus two 2048-byte
     histograms per tensor (whole tensor and sample), 256 bytes of counters,
-    a 128-byte record per tensor and two 64-byte list entries per tensor;
+    a 128-byte record per tensor and three 64-byte list entries per tensor;
     argument errors return before any launch."""
     for count, n in [(1, 0), (1, 4097), (64, 1 << 23), (3, 100)]:
-        sync = 4096 * count + 256 + 128 * count + 128 * count
+        sync = 4096 * count + 256 + 128 * count + 3 * 64 * count
         assert sz.sz_compress_workspace_bytes_batched(count, n, 1) == \
             sz.sz_encode_workspace_bytes_batched(count, n, 1) + sync
     assert sz.sz_compress_workspace_bytes(1 << 32, 1) == 0

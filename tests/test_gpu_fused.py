@@ -292,10 +292,18 @@ def test_give_up_path_is_reported_and_bounded(sz):
     sizes = bc.sizes.cpu().numpy()
     assert set(status.tolist()) <= {0, sz.SZ_ERR_TIMEOUT}
     say("give-up statuses", status.tolist())
+    bc.decompress()
+    torch.cuda.synchronize()
+    decoded = bc.status.cpu().numpy()
     for i, x in enumerate(xs):
         assert 0 < sizes[i] <= bc.capacity
         if status[i] == 0:
             assert np.array_equal(bc.stream(i).cpu().numpy(), oracle.encode(x, BF16)), i
+        else:
+            # a stream the call gave up on carries no valid header: decoding
+            # it reports a corrupt stream rather than returning wrong data
+            assert bc.stream(i)[:4].cpu().tolist() == [0, 0, 0, 0], i
+            assert decoded[i] == sz.SZ_ERR_CORRUPT_STREAM, i
     bc.compress_fused()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
@@ -375,21 +383,66 @@ def test_fused_recodes_when_the_sample_ranks_differently(sz, kind, n):
         assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i
 
 
-def test_fused_recodes_escape_heavy_tensors(sz):
+def _sample_escape_fraction(x):
+    """Fraction of the sampled elements that escape under the sample's own
+    codebook (the fused kernel encodes a tensor from its input, after
+    counting it, when this exceeds 1/4)."""
+    h = oracle.histogram(x[_sample_mask(x.size)], BF16)
+    cb = oracle.codebook(h, BF16)[:15]
+    return 1.0 - h[cb].sum() / h.sum()
+
+
+def test_fused_escape_heavy_tensors_encoded_after_counting(sz):
     """Heavy-tailed tensors (most elements escape, ~150 exponent values):
-    samples and whole tensors rank differently, so recoding rewrites many
-    staged escapes per block; a ragged last block too."""
+    more than a quarter of the sample escapes, so the main items only count
+    them and the recode launch encodes them from the input with the final
+    codebook; between two ordinary tensors, with a ragged last block."""
     n = (1 << 22) + 777
-    xs = [kvsynth.stress(n, seed=710 + i) for i in range(3)]
-    assert any(not np.array_equal(*_codebooks(x)) for x in xs)
-    say("fused recode escape-heavy", n)
+    xs = [kvsynth.single_tensor(n, seed=709)] + [kvsynth.stress(n, seed=710 + i) for i in range(2)] + \
+         [kvsynth.single_tensor(n, seed=713)]
+    assert [_sample_escape_fraction(x) > 0.25 for x in xs] == [False, True, True, False]
+    say("fused escape-heavy", n)
     bc = sz.codec.BatchCodec(len(xs), n, BF16)
     bc.set_inputs([to_dev(x) for x in xs])
     bc.compress_fused()
+    bc.decompress()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
     for i, x in enumerate(xs):
         _check_against_oracle(x, BF16, bc.stream(i), bc.hists[i], bc.codebooks[i])
+        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i
+
+
+def _dense_escapes_outside_sample(n, seed):
+    """_skewed(..., 'members') with some blocks outside the sample replaced
+    by uniformly random bit patterns: the sample escapes rarely (so the
+    tensor is encoded with its provisional codebook), the final codebook
+    holds other values, and those blocks hold thousands of escapes each, so
+    the recode rewrites dense runs of staged escapes."""
+    x = _skewed(n, seed, "members")
+    rng = np.random.default_rng(seed)
+    outside = np.flatnonzero(~_sample_mask(n)[::4096][:n // 4096]) * 4096
+    for b in rng.choice(outside, 24, replace=False):
+        x[b:b + 4096] = rng.integers(0, 1 << 16, 4096, dtype=np.uint32).astype(np.uint16)
+    return x
+
+
+def test_fused_recodes_dense_escape_blocks(sz):
+    """The 'other values' recode on blocks with thousands of escapes."""
+    n = (1 << 21) + 4096 * 3 + 5
+    xs = [_dense_escapes_outside_sample(n, 730), kvsynth.single_tensor(n, seed=731)]
+    full, part = _codebooks(xs[0])
+    assert set(full.tolist()) != set(part.tolist()) and _sample_escape_fraction(xs[0]) < 0.25
+    say("fused recode dense escapes", n)
+    bc = sz.codec.BatchCodec(len(xs), n, BF16)
+    bc.set_inputs([to_dev(x) for x in xs])
+    bc.compress_fused()
+    bc.decompress()
+    torch.cuda.synchronize()
+    assert (bc.fused_status.cpu().numpy() == 0).all()
+    for i, x in enumerate(xs):
+        _check_against_oracle(x, BF16, bc.stream(i), bc.hists[i], bc.codebooks[i])
+        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i
 
 
 def _degenerate(n, kind):

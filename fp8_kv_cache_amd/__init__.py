@@ -25,7 +25,7 @@ __all__ = [
     "sz_histogram_sampled_batched",
     "sz_histogram_batched", "sz_build_codebook_batched", "sz_encode_batched", "sz_decode_batched",
     "sz_compress_workspace_bytes", "sz_compress_workspace_bytes_batched", "sz_compress",
-    "sz_compress_batched", "sz_compress_spin_limit", "sz_compress_fused_min_elements",
+    "sz_compress_batched", "SzCompressOptions", "compress_options",
     "sz_status_string", "check", "pointer_table", "library_path",
     "lc_max_compressed_bytes", "lc_encode_workspace_bytes", "lc_encode_workspace_bytes_batched",
     "lc_encode", "lc_decode", "lc_encode_batched", "lc_decode_batched",
@@ -65,10 +65,8 @@ _SIGNATURES = {
     "sz_decode_batched": (_i32, [_vp, _vp, _u32, _u64, _i32, _vp, _vp, _vp]),
     "sz_compress_workspace_bytes": (_u64, [_u64, _i32]),
     "sz_compress_workspace_bytes_batched": (_u64, [_u32, _u64, _i32]),
-    "sz_compress": (_i32, [_vp, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp]),
-    "sz_compress_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp]),
-    "sz_compress_spin_limit": (_u32, [_u32]),
-    "sz_compress_fused_min_elements": (_u64, [_u64]),
+    "sz_compress": (_i32, [_vp, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp]),
+    "sz_compress_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp]),
     "sz_status_string": (ctypes.c_char_p, [_i32]),
     "lc_max_compressed_bytes": (_u64, [_u64]),
     "lc_encode_workspace_bytes": (_u64, [_u64]),
@@ -195,25 +193,36 @@ def sz_compress_workspace_bytes_batched(count, n, dtype):
     return _lib.sz_compress_workspace_bytes_batched(count, n, dtype)
 
 
+class SzCompressOptions(ctypes.Structure):
+    """sz_compress_options: per-call settings of sz_compress[_batched]
+    (0 in a field means its default)."""
+    _fields_ = [("fused_min_elements", ctypes.c_uint64), ("spin_limit", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+def compress_options(fused_min_elements=0, spin_limit=0):
+    """An SzCompressOptions, or None (the defaults) when every field is 0."""
+    if not fused_min_elements and not spin_limit:
+        return None
+    return SzCompressOptions(fused_min_elements, spin_limit, 0)
+
+
+def _opts(o):
+    return None if o is None else ctypes.addressof(o)
+
+
 def sz_compress(src, n, dtype, hist, codebook, dst, dst_capacity, out_bytes, status, workspace,
-                workspace_bytes, stream=None):
+                workspace_bytes, options=None, stream=None):
     return _lib.sz_compress(_ptr(src), n, dtype, _ptr(hist), _ptr(codebook), _ptr(dst), dst_capacity,
-                            _ptr(out_bytes), _ptr(status), _ptr(workspace), workspace_bytes, _stream(stream))
+                            _ptr(out_bytes), _ptr(status), _ptr(workspace), workspace_bytes, _opts(options),
+                            _stream(stream))
 
 
 def sz_compress_batched(srcs, count, n, dtype, hists, codebooks, dsts, dst_capacity, out_bytes, status,
-                        workspace, workspace_bytes, stream=None):
+                        workspace, workspace_bytes, options=None, stream=None):
     return _lib.sz_compress_batched(_ptr(srcs), count, n, dtype, _ptr(hists), _ptr(codebooks), _ptr(dsts),
                                     dst_capacity, _ptr(out_bytes), _ptr(status), _ptr(workspace),
-                                    workspace_bytes, _stream(stream))
-
-
-def sz_compress_spin_limit(polls):
-    return _lib.sz_compress_spin_limit(polls)
-
-
-def sz_compress_fused_min_elements(n):
-    return _lib.sz_compress_fused_min_elements(n)
+                                    workspace_bytes, _opts(options), _stream(stream))
 
 
 def lc_max_compressed_bytes(n):

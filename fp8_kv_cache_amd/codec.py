@@ -5,7 +5,7 @@ patterns, dtype int16/bfloat16) or bytes (E5M2, dtype uint8/float8_e5m2).
 """
 import torch
 
-from . import (SZ_DTYPE_BF16, SZ_DTYPE_FP8_E5M2, check, pointer_table, sz_build_codebook, sz_histogram_sampled,
+from . import (SZ_DTYPE_BF16, SZ_DTYPE_FP8_E5M2, SZ_ERR_TIMEOUT, SZ_OK, check, pointer_table, sz_build_codebook, sz_histogram_sampled,
                sz_histogram_sampled_batched, sz_compress, sz_compress_batched, sz_compress_workspace_bytes,
                sz_compress_workspace_bytes_batched,
                sz_build_codebook_batched, sz_decode, sz_decode_batched, sz_encode, sz_encode_batched,
@@ -47,10 +47,13 @@ def compress(x, dtype, codebook=None, stream=None, block_stride=1):
     return dst[:size], hist, codebook
 
 
-def compress_fused(x, dtype, stream=None):
+def compress_fused(x, dtype, stream=None, options=None, retry=True):
     """Histogram, codebook and encode of one tensor in one launch
     (sz_compress).  Returns (stream bytes, histogram int64[256], codebook
-    uint8[16], device status); the results equal compress()'s."""
+    uint8[16], device status); the results equal compress()'s.  options: an
+    SzCompressOptions (compress_options()) or None for the defaults.  If the
+    kernel gave up (SZ_ERR_TIMEOUT) and `retry`, the tensor is encoded again
+    with the separate calls and their results are returned with SZ_OK."""
     dev = x.device
     n = x.numel()
     hist = torch.empty(256, dtype=torch.int64, device=dev)
@@ -62,9 +65,15 @@ def compress_fused(x, dtype, stream=None):
     ws_bytes = sz_compress_workspace_bytes(n, dtype)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     check(sz_compress(x if n else None, n, dtype, hist, codebook, dst, cap, out_bytes, status, ws, ws_bytes,
-                      stream), "sz_compress")
+                      options, stream), "sz_compress")
+    st = int(status.item())
+    if st == SZ_ERR_TIMEOUT and retry:
+        # the one-launch kernel gave up waiting (its stream does not decode):
+        # the separate calls' kernels compute the same results without waits
+        stream_bytes, hist, codebook = compress(x, dtype, stream=stream)
+        return stream_bytes, hist, codebook, SZ_OK
     size = int(out_bytes.item())
-    return dst[:size], hist, codebook, int(status.item())
+    return dst[:size], hist, codebook, st
 
 
 def decompress(stream_bytes, n, dtype, src_bytes=None, stream=None):
@@ -130,12 +139,26 @@ class BatchCodec:
         self.build_codebooks(stream)
         self.encode(stream)
 
-    def compress_fused(self, stream=None):
+    def compress_fused(self, stream=None, options=None):
         """Same histograms, codebooks and streams as compress(), in one
-        launch (sz_compress_batched); per-tensor status in fused_status."""
+        launch (sz_compress_batched); per-tensor status in fused_status
+        (asynchronous: see settle()).  options: an SzCompressOptions or None
+        for the defaults."""
         check(sz_compress_batched(self.src_ptrs, self.count, self.n, self.dtype, self.hists, self.codebooks,
                                   self.stream_ptrs, self.capacity, self.sizes, self.fused_status, self.workspace,
-                                  self.fused_ws_bytes, stream), "sz_compress_batched")
+                                  self.fused_ws_bytes, options, stream), "sz_compress_batched")
+
+    def settle(self, stream=None):
+        """After compress_fused(): waits for it, and if any tensor gave up
+        (SZ_ERR_TIMEOUT; its stream does not decode) encodes the whole batch
+        again with the separate calls, which compute the same results
+        without waits.  Returns the number of tensors that had given up."""
+        torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+        gave_up = int((self.fused_status == SZ_ERR_TIMEOUT).sum().item())
+        if gave_up:
+            self.compress(stream)
+            self.fused_status.fill_(SZ_OK)
+        return gave_up
 
     def decompress(self, stream=None):
         check(sz_decode_batched(self.stream_ptrs, self.sizes, self.count, self.n, self.dtype,

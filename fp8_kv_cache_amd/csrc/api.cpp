@@ -4,8 +4,6 @@
 // never allocates, frees or synchronises.
 #include "splitzip.h"
 
-#include <atomic>
-
 #include "sz_internal.h"
 
 #define SZ_EXPORT extern "C" __attribute__((visibility("default")))
@@ -51,8 +49,17 @@ uint64_t compress_workspace_bytes(uint32_t count, uint64_t n) {
     return workspace_bytes_for(count, n) + sync_area_bytes(count);
 }
 
-std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
-std::atomic<uint64_t> g_fused_min{kDefaultFusedMin};
+// Per-call settings of the one-launch compress, defaults filled in.
+struct CompressSettings {
+    uint64_t fused_min;
+    uint32_t spin_limit;
+};
+
+bool settings_of(const sz_compress_options* o, CompressSettings& c) {
+    c.fused_min = o && o->fused_min_elements ? o->fused_min_elements : kDefaultFusedMin;
+    c.spin_limit = o && o->spin_limit ? o->spin_limit : kDefaultSpinLimit;
+    return !o || o->reserved == 0;
+}
 
 sz_status histogram_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint32_t stride,
                          uint64_t* d_hists, hipStream_t s) {
@@ -84,7 +91,7 @@ sz_status encode_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, const
 
 // Histogram, codebook and encode in one launch that reads the input once
 // (plus the short transcode, offset and scatter launches) for BF16 tensors
-// of at least g_fused_min elements.  E5M2 tensors measured slower fused
+// of at least cs.fused_min elements.  E5M2 tensors measured slower fused
 // than with the separate calls' kernels (0.37 against 0.28 ms on the
 // 64-tensor cache: counting a byte per element in the same pass costs more
 // than a second read of half the bytes), and small BF16 tensors take the
@@ -92,8 +99,8 @@ sz_status encode_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, const
 // way.
 sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint64_t* d_hists,
                         uint8_t* d_codebooks, DstRef dst, uint64_t* d_out_bytes, int32_t* d_status,
-                        void* d_workspace, hipStream_t s) {
-    if (n == 0 || dt != SZ_DTYPE_BF16 || n < g_fused_min.load(std::memory_order_relaxed)) {
+                        void* d_workspace, const CompressSettings& cs, hipStream_t s) {
+    if (n == 0 || dt != SZ_DTYPE_BF16 || n < cs.fused_min) {
         if (d_status && launch_fill_i32(d_status, count, SZ_OK, s) != hipSuccess) return SZ_ERR_HIP;
         sz_status st = histogram_impl(src, count, n, dt, 1, d_hists, s);
         if (st != SZ_OK) return st;
@@ -135,7 +142,7 @@ sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uin
     const uint64_t tensor_bytes = static_cast<uint64_t>(n) * (dt == SZ_DTYPE_BF16 ? 2 : 1);
     const uint64_t lag = (kPassLagBytes + tensor_bytes - 1) / tensor_bytes;
     a.lag = static_cast<uint32_t>(lag < kPassLag ? kPassLag : (lag > count + 1u ? count + 1u : lag));
-    a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    a.spin_limit = cs.spin_limit;
     return from_hip(launch_compress(a, dt, s));
 }
 
@@ -259,23 +266,26 @@ SZ_EXPORT uint64_t sz_compress_workspace_bytes(uint64_t n, sz_dtype dtype) {
 SZ_EXPORT sz_status sz_compress(const void* d_src, uint64_t n, sz_dtype dtype, uint64_t* d_hist,
                                 uint8_t* d_codebook, void* d_dst, uint64_t dst_capacity, uint64_t* d_out_bytes,
                                 int32_t* d_status, void* d_workspace, uint64_t workspace_bytes_given,
-                                hipStream_t stream) {
-    if (!dtype_ok(dtype) || n >= kMaxElems || !usable(d_hist) || !usable(d_codebook) || !usable(d_dst) ||
-        !usable(d_workspace) || (n && !usable(d_src)) ||
+                                const sz_compress_options* options, hipStream_t stream) {
+    CompressSettings cs;
+    if (!settings_of(options, cs) || !dtype_ok(dtype) || n >= kMaxElems || !usable(d_hist) || !usable(d_codebook) ||
+        !usable(d_dst) || !usable(d_workspace) || (n && !usable(d_src)) ||
         (d_out_bytes && (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)) ||
         (d_status && (reinterpret_cast<uintptr_t>(d_status) & 3u)))
         return SZ_ERR_INVALID_ARGUMENT;
     if (dst_capacity < sz_max_compressed_bytes(n, dtype)) return SZ_ERR_BUFFER_TOO_SMALL;
     if (workspace_bytes_given < compress_workspace_bytes(1, n)) return SZ_ERR_BUFFER_TOO_SMALL;
     return compress_impl(SrcRef{nullptr, d_src}, 1, n, dtype, d_hist, d_codebook, DstRef{nullptr, d_dst},
-                         d_out_bytes, d_status, d_workspace, stream);
+                         d_out_bytes, d_status, d_workspace, cs, stream);
 }
 
 SZ_EXPORT sz_status sz_compress_batched(const void* const* d_srcs, uint32_t count, uint64_t n, sz_dtype dtype,
                                         uint64_t* d_hists, uint8_t* d_codebooks, void* const* d_dsts,
                                         uint64_t dst_capacity, uint64_t* d_out_bytes, int32_t* d_status,
-                                        void* d_workspace, uint64_t workspace_bytes_given, hipStream_t stream) {
-    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n) ||
+                                        void* d_workspace, uint64_t workspace_bytes_given,
+                                        const sz_compress_options* options, hipStream_t stream) {
+    CompressSettings cs;
+    if (!settings_of(options, cs) || !dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n) ||
         static_cast<uint64_t>(count) * compress_items(n, dtype) >= (uint64_t(1) << 31) || !usable(d_srcs) ||
         !usable(d_hists) || !usable(d_codebooks) || !usable(d_dsts) || !usable(d_workspace) ||
         (d_out_bytes && (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)) ||
@@ -284,15 +294,7 @@ SZ_EXPORT sz_status sz_compress_batched(const void* const* d_srcs, uint32_t coun
     if (dst_capacity < sz_max_compressed_bytes(n, dtype)) return SZ_ERR_BUFFER_TOO_SMALL;
     if (workspace_bytes_given < compress_workspace_bytes(count, n)) return SZ_ERR_BUFFER_TOO_SMALL;
     return compress_impl(SrcRef{d_srcs, nullptr}, count, n, dtype, d_hists, d_codebooks, DstRef{d_dsts, nullptr},
-                         d_out_bytes, d_status, d_workspace, stream);
-}
-
-SZ_EXPORT uint32_t sz_compress_spin_limit(uint32_t polls) {
-    return g_spin_limit.exchange(polls ? polls : kDefaultSpinLimit, std::memory_order_relaxed);
-}
-
-SZ_EXPORT uint64_t sz_compress_fused_min_elements(uint64_t n) {
-    return g_fused_min.exchange(n ? n : kDefaultFusedMin, std::memory_order_relaxed);
+                         d_out_bytes, d_status, d_workspace, cs, stream);
 }
 
 SZ_EXPORT sz_status sz_decode(const void* d_src, uint64_t src_bytes, uint64_t n, sz_dtype dtype,

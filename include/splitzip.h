@@ -184,13 +184,13 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * recode would rewrite most of the stream) is only counted in the first
  * kernel and encoded from its input by the second, with the final codebook.
  * The bytes written are the same as the separate calls'.  E5M2 tensors
- * (measured slower fused) and BF16 tensors below
- * sz_compress_fused_min_elements() run the separate calls' kernels, with the
- * same results.
+ * (measured slower fused) and BF16 tensors below the options'
+ * fused_min_elements run the separate calls' kernels, with the same
+ * results.
  *
  * Work inside the kernel waits only for work handed out before it, so a
  * call always makes progress, whatever else shares the GPU.  Waits are
- * bounded nonetheless: a workgroup that has polled sz_compress_spin_limit()
+ * bounded nonetheless: a workgroup that has polled the options' spin_limit
  * times without progress (about a second) gives up, and so does every
  * workgroup after it; each tensor they belong to gets SZ_ERR_TIMEOUT in
  * d_status, unspecified histogram and codebook, and a stream that stays
@@ -207,7 +207,23 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * d_workspace: >= sz_compress_workspace_bytes[_batched] bytes, contents
  * need not be initialised, clobbered (the encode workspace followed by a
  * synchronisation area: 256 bytes plus 4416 bytes per tensor).  Calls
- * sharing a workspace must not overlap in time. ---- */
+ * sharing a workspace must not overlap in time.
+ * options: per-call settings (host memory, read when the call is enqueued),
+ * or NULL for the defaults; an options struct with a non-zero reserved
+ * field is SZ_ERR_INVALID_ARGUMENT. ---- */
+
+typedef struct {
+    /* Smallest BF16 tensor (in elements) run through the one-launch kernel;
+     * smaller ones take the separate calls' kernels (same results).  0 means
+     * the default, 2^21 (4 MiB tensors measured 15% faster fused, 2 MiB ones
+     * 10% slower); 1 sends every BF16 tensor through the one-launch kernel. */
+    uint64_t fused_min_elements;
+    /* Polls a waiting workgroup makes before it gives up; 0 means the
+     * default, 2^20 (about a second).  A small value reaches the give-up
+     * path. */
+    uint32_t spin_limit;
+    uint32_t reserved;   /* must be 0 */
+} sz_compress_options;
 
 uint64_t sz_compress_workspace_bytes(uint64_t n, sz_dtype dtype);
 uint64_t sz_compress_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype dtype);
@@ -215,26 +231,13 @@ uint64_t sz_compress_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtyp
 sz_status sz_compress(const void* d_src, uint64_t n, sz_dtype dtype, uint64_t* d_hist,
                       uint8_t* d_codebook, void* d_dst, uint64_t dst_capacity, uint64_t* d_out_bytes,
                       int32_t* d_status, void* d_workspace, uint64_t workspace_bytes,
-                      hipStream_t stream);
+                      const sz_compress_options* options, hipStream_t stream);
 
 sz_status sz_compress_batched(const void* const* d_srcs, uint32_t count, uint64_t n, sz_dtype dtype,
                               uint64_t* d_hists, uint8_t* d_codebooks, void* const* d_dsts,
                               uint64_t dst_capacity, uint64_t* d_out_bytes, int32_t* d_status,
-                              void* d_workspace, uint64_t workspace_bytes, hipStream_t stream);
-
-/* Smallest BF16 tensor (in elements) that later sz_compress* calls run
- * through the fused kernel; smaller tensors take the separate calls'
- * kernels (same results).  0 restores the default, 2^21 (4 MiB: measured
- * 15% faster fused; 2 MiB tensors measured 10% slower).  Returns the
- * previous value.  Host-side setting, read when a call is enqueued; a
- * value of 1 sends every tensor through the fused kernel. */
-uint64_t sz_compress_fused_min_elements(uint64_t n);
-
-/* Polls a waiting workgroup of later sz_compress* calls makes before it
- * gives up (0 restores the default, 2^20); returns the previous value.
- * Host-side setting, read when a call is enqueued; a small value lets a
- * test reach the give-up path. */
-uint32_t sz_compress_spin_limit(uint32_t polls);
+                              void* d_workspace, uint64_t workspace_bytes,
+                              const sz_compress_options* options, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* sz_status_string(sz_status status);

@@ -154,24 +154,26 @@ def test_compress_sizes_and_host_errors(sz):
                                   stream=0) == E_ARG
 
 
-def test_compress_fused_threshold_setting(sz):
-    before = sz.sz_compress_fused_min_elements(1)
-    try:
-        assert before == 1 << 21
-        assert sz.sz_compress_fused_min_elements(0) == 1     # 0 restores the default
-        assert sz.sz_compress_fused_min_elements(0) == 1 << 21
-    finally:
-        sz.sz_compress_fused_min_elements(0)
-
-
-def test_compress_spin_limit_setting(sz):
-    before = sz.sz_compress_spin_limit(7)
-    try:
-        assert before == 1 << 20
-        assert sz.sz_compress_spin_limit(0) == 7       # 0 restores the default
-        assert sz.sz_compress_spin_limit(0) == 1 << 20
-    finally:
-        sz.sz_compress_spin_limit(0)
+def test_compress_options_are_per_call(sz):
+    """The one-launch compress takes its settings per call: NULL or zero
+    fields mean the defaults, a non-zero reserved field is an argument error
+    returned before any launch, and the library keeps no process-wide
+    setting (the old setters are not exported)."""
+    n = 5000
+    cap = sz.sz_max_compressed_bytes(n, 1)
+    ws = sz.sz_compress_workspace_bytes(n, 1)
+    bad = sz.SzCompressOptions(1, 1, 7)
+    args = (FAKE, n, 1, FAKE, FAKE, FAKE, cap, None, None, FAKE, ws)
+    assert sz.sz_compress(*args, options=bad, stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.sz_compress_batched(FAKE, 2, n, 1, FAKE, FAKE, FAKE, cap, None, None, FAKE,
+                                  sz.sz_compress_workspace_bytes_batched(2, n, 1), options=bad,
+                                  stream=0) == sz.SZ_ERR_INVALID_ARGUMENT
+    assert sz.compress_options() is None
+    o = sz.compress_options(fused_min_elements=1, spin_limit=3)
+    assert (o.fused_min_elements, o.spin_limit, o.reserved) == (1, 3, 0)
+    lib = ctypes.CDLL(sz.library_path())
+    for gone in ("sz_compress_spin_limit", "sz_compress_fused_min_elements"):
+        assert not hasattr(lib, gone), gone
 
 
 def test_status_strings(sz):

@@ -25,16 +25,18 @@ def say(*a):
 
 @pytest.fixture(scope="module")
 def sz():
-    """The library with every BF16 tensor sent through the fused kernel
-    (by default tensors under 2^21 elements take the separate kernels), so
-    the small cases below exercise it; restored afterwards."""
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import fp8_kv_cache_amd
     from fp8_kv_cache_amd import codec
     fp8_kv_cache_amd.codec = codec
-    previous = fp8_kv_cache_amd.sz_compress_fused_min_elements(1)
-    yield fp8_kv_cache_amd
-    fp8_kv_cache_amd.sz_compress_fused_min_elements(previous)
+    return fp8_kv_cache_amd
+
+
+def every(sz, **more):
+    """Options that send every BF16 tensor through the fused kernel (by
+    default tensors under 2^21 elements take the separate kernels), so the
+    small cases below exercise it."""
+    return sz.compress_options(fused_min_elements=1, **more)
 
 
 def _check_against_oracle(x, dt, stream, hist, cb):
@@ -52,7 +54,7 @@ def test_fused_parity(sz, name):
     make, dt = CASES[name]
     x = make()
     say("fused parity", name, "n", x.size, "dtype", dt)
-    stream, hist, cb, status = sz.codec.compress_fused(to_dev(x), dt)
+    stream, hist, cb, status = sz.codec.compress_fused(to_dev(x), dt, options=every(sz))
     torch.cuda.synchronize()
     assert status == 0
     _check_against_oracle(x, dt, stream, hist, cb)
@@ -72,7 +74,7 @@ def test_fused_batched(sz, dt, n):
     dev = [to_dev(x) for x in xs]
     one = sz.codec.BatchCodec(len(xs), n, dt)
     one.set_inputs(dev)
-    one.compress_fused()
+    one.compress_fused(options=every(sz))
     three = sz.codec.BatchCodec(len(xs), n, dt)
     three.set_inputs(dev)
     three.compress()
@@ -104,7 +106,7 @@ def test_fused_schedule_shapes(sz, count, n):
     dev = [to_dev(x) for x in xs]
     one = sz.codec.BatchCodec(count, n, BF16)
     one.set_inputs(dev)
-    one.compress_fused()
+    one.compress_fused(options=every(sz))
     three = sz.codec.BatchCodec(count, n, BF16)
     three.set_inputs(dev)
     three.compress()
@@ -124,16 +126,12 @@ def test_default_size_threshold(sz, n):
     """With the default threshold, a tensor just under 2^21 elements takes
     the separate kernels and one at 2^21 the fused kernel: both give the
     oracle's histogram, codebook and stream."""
-    previous = sz.sz_compress_fused_min_elements(0)
-    try:
-        x = kvsynth.stress(n, seed=n)
-        say("fused threshold", n)
-        stream, hist, cb, status = sz.codec.compress_fused(to_dev(x), BF16)
-        torch.cuda.synchronize()
-        assert status == 0
-        _check_against_oracle(x, BF16, stream, hist, cb)
-    finally:
-        sz.sz_compress_fused_min_elements(previous)
+    x = kvsynth.stress(n, seed=n)
+    say("fused threshold", n)
+    stream, hist, cb, status = sz.codec.compress_fused(to_dev(x), BF16)   # default options
+    torch.cuda.synchronize()
+    assert status == 0
+    _check_against_oracle(x, BF16, stream, hist, cb)
 
 
 def test_fused_is_deterministic(sz):
@@ -141,7 +139,7 @@ def test_fused_is_deterministic(sz):
     say("fused determinism")
     first = None
     for _ in range(6):
-        s, _, _, status = sz.codec.compress_fused(x, BF16)
+        s, _, _, status = sz.codec.compress_fused(x, BF16, options=every(sz))
         assert status == 0
         s = s.cpu().numpy()
         if first is None:
@@ -160,7 +158,7 @@ def test_llama_kv_cache_full_size_fused(sz):
     bc = sz.codec.BatchCodec(64, n, BF16)
     bc.set_inputs([to_dev(x) for x in xs])
     say("llama fused: encode+decode")
-    bc.compress_fused()
+    bc.compress_fused(options=every(sz))
     bc.decompress()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
@@ -193,7 +191,7 @@ def test_fused_large_tensor(sz, dt):
     if dt == E5M2:
         x_dev = to_dev(kvsynth.e5m2_of(x_dev.cpu().numpy().view(np.uint16)))
     say("fused large", dt, n)
-    stream, hist, cb, status = sz.codec.compress_fused(x_dev, dt)
+    stream, hist, cb, status = sz.codec.compress_fused(x_dev, dt, options=every(sz))
     ref, ref_hist, ref_cb = sz.codec.compress(x_dev, dt)
     torch.cuda.synchronize()
     assert status == 0
@@ -214,7 +212,7 @@ def test_fused_graph_replay(sz, dt):
     say("fused graph", dt, n, count)
     bc = sz.codec.BatchCodec(count, n, dt)
     bc.set_inputs([to_dev(x) for x in xs])
-    bc.compress_fused()
+    bc.compress_fused(options=every(sz))
     bc.decompress()
     torch.cuda.synchronize()
     ref_sizes = bc.sizes.clone()
@@ -224,7 +222,7 @@ def test_fused_graph_replay(sz, dt):
         assert np.array_equal(ref_streams[i].cpu().numpy(), oracle.encode(x, dt)), i
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        bc.compress_fused()
+        bc.compress_fused(options=every(sz))
         bc.decompress()
     for replay in range(3):
         bc.outputs.zero_()
@@ -263,7 +261,7 @@ def test_two_fused_calls_on_two_streams(sz):
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     for (xs, bc), s in zip(groups, streams):
         with torch.cuda.stream(s):
-            bc.compress_fused()
+            bc.compress_fused(options=every(sz))
     torch.cuda.synchronize()
     for xs, bc in groups:
         assert (bc.fused_status.cpu().numpy() == 0).all()
@@ -282,12 +280,8 @@ def test_give_up_path_is_reported_and_bounded(sz):
     bc = sz.codec.BatchCodec(count, n, BF16)
     bc.set_inputs([to_dev(x) for x in xs])
     say("fused give-up")
-    previous = sz.sz_compress_spin_limit(1)
-    try:
-        bc.compress_fused()
-        torch.cuda.synchronize()
-    finally:
-        sz.sz_compress_spin_limit(previous)
+    bc.compress_fused(options=every(sz, spin_limit=1))
+    torch.cuda.synchronize()
     status = bc.fused_status.cpu().numpy()
     sizes = bc.sizes.cpu().numpy()
     assert set(status.tolist()) <= {0, sz.SZ_ERR_TIMEOUT}
@@ -304,7 +298,7 @@ def test_give_up_path_is_reported_and_bounded(sz):
             # it reports a corrupt stream rather than returning wrong data
             assert bc.stream(i)[:4].cpu().tolist() == [0, 0, 0, 0], i
             assert decoded[i] == sz.SZ_ERR_CORRUPT_STREAM, i
-    bc.compress_fused()
+    bc.compress_fused(options=every(sz))
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
     for i, x in enumerate(xs):
@@ -374,7 +368,7 @@ def test_fused_recodes_when_the_sample_ranks_differently(sz, kind, n):
     say("fused recode", kind, n)
     bc = sz.codec.BatchCodec(len(xs), n, BF16)
     bc.set_inputs([to_dev(x) for x in xs])
-    bc.compress_fused()
+    bc.compress_fused(options=every(sz))
     bc.decompress()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
@@ -404,7 +398,7 @@ def test_fused_escape_heavy_tensors_encoded_after_counting(sz):
     say("fused escape-heavy", n)
     bc = sz.codec.BatchCodec(len(xs), n, BF16)
     bc.set_inputs([to_dev(x) for x in xs])
-    bc.compress_fused()
+    bc.compress_fused(options=every(sz))
     bc.decompress()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
@@ -436,7 +430,7 @@ def test_fused_recodes_dense_escape_blocks(sz):
     say("fused recode dense escapes", n)
     bc = sz.codec.BatchCodec(len(xs), n, BF16)
     bc.set_inputs([to_dev(x) for x in xs])
-    bc.compress_fused()
+    bc.compress_fused(options=every(sz))
     bc.decompress()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
@@ -476,7 +470,7 @@ def test_fused_degenerate_alphabets(sz, kind):
     say("fused degenerate", kind, n)
     bc = sz.codec.BatchCodec(len(xs), n, BF16)
     bc.set_inputs([to_dev(x) for x in xs])
-    bc.compress_fused()
+    bc.compress_fused(options=every(sz))
     bc.decompress()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()

@@ -25,7 +25,8 @@ __all__ = [
     "sz_histogram_sampled_batched",
     "sz_histogram_batched", "sz_build_codebook_batched", "sz_encode_batched", "sz_decode_batched",
     "sz_compress_workspace_bytes", "sz_compress_workspace_bytes_batched", "sz_compress",
-    "sz_compress_batched", "SzCompressOptions", "compress_options",
+    "sz_compress_batched", "SzCompressOptions", "compress_options", "sz_compress_noalloc",
+    "SZ_NOALLOC_MAX_ELEMENTS", "SZ_NOALLOC_SCRATCH_BYTES",
     "sz_status_string", "check", "pointer_table", "library_path",
     "lc_max_compressed_bytes", "lc_encode_workspace_bytes", "lc_encode_workspace_bytes_batched",
     "lc_encode", "lc_decode", "lc_encode_batched", "lc_decode_batched",
@@ -39,6 +40,8 @@ SZ_ERR_BUFFER_TOO_SMALL = 2
 SZ_ERR_CORRUPT_STREAM = 3
 SZ_ERR_HIP = 4
 SZ_ERR_TIMEOUT = 5
+SZ_NOALLOC_MAX_ELEMENTS = 1 << 24                  # include/splitzip.h
+SZ_NOALLOC_SCRATCH_BYTES = (16 << 20) + (32 << 10)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
@@ -67,6 +70,7 @@ _SIGNATURES = {
     "sz_compress_workspace_bytes_batched": (_u64, [_u32, _u64, _i32]),
     "sz_compress": (_i32, [_vp, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp]),
     "sz_compress_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp]),
+    "sz_compress_noalloc": (_i32, [_vp, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _vp]),
     "sz_status_string": (ctypes.c_char_p, [_i32]),
     "lc_max_compressed_bytes": (_u64, [_u64]),
     "lc_encode_workspace_bytes": (_u64, [_u64]),
@@ -216,6 +220,12 @@ def sz_compress(src, n, dtype, hist, codebook, dst, dst_capacity, out_bytes, sta
     return _lib.sz_compress(_ptr(src), n, dtype, _ptr(hist), _ptr(codebook), _ptr(dst), dst_capacity,
                             _ptr(out_bytes), _ptr(status), _ptr(workspace), workspace_bytes, _opts(options),
                             _stream(stream))
+
+
+def sz_compress_noalloc(src, n, dtype, hist, codebook, dst, dst_capacity, out_bytes, status, options=None,
+                        stream=None):
+    return _lib.sz_compress_noalloc(_ptr(src), n, dtype, _ptr(hist), _ptr(codebook), _ptr(dst), dst_capacity,
+                                    _ptr(out_bytes), _ptr(status), _opts(options), _stream(stream))
 
 
 def sz_compress_batched(srcs, count, n, dtype, hists, codebooks, dsts, dst_capacity, out_bytes, status,

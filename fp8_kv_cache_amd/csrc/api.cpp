@@ -4,9 +4,17 @@
 // never allocates, frees or synchronises.
 #include "splitzip.h"
 
+#include <mutex>
+
 #include "sz_internal.h"
 
 #define SZ_EXPORT extern "C" __attribute__((visibility("default")))
+
+// The workspace of sz_compress_noalloc: one array per device, held by the
+// library for the life of the process.  Host code never uses its name as an
+// address: the device address comes from hipGetSymbolAddress, once per
+// device (scratch_on_current_device).
+static __device__ __align__(256) uint8_t scratch[SZ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -146,6 +154,24 @@ sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uin
     return from_hip(launch_compress(a, dt, s));
 }
 
+// Device address of `scratch` on the current device, looked up with the
+// device current the first time the device is seen; null on a HIP error.
+constexpr int kScratchDevices = 1024;
+std::mutex g_scratch_lock;
+void* g_scratch_ptr[kScratchDevices];
+
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> hold(g_scratch_lock);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 sz_status decode_impl(SrcRef src, const uint64_t* d_src_bytes, uint64_t src_bytes, uint32_t count,
                       uint64_t n, sz_dtype dt, DstRef dst, int32_t* d_status, hipStream_t s) {
     if (d_status) {
@@ -277,6 +303,25 @@ SZ_EXPORT sz_status sz_compress(const void* d_src, uint64_t n, sz_dtype dtype, u
     if (workspace_bytes_given < compress_workspace_bytes(1, n)) return SZ_ERR_BUFFER_TOO_SMALL;
     return compress_impl(SrcRef{nullptr, d_src}, 1, n, dtype, d_hist, d_codebook, DstRef{nullptr, d_dst},
                          d_out_bytes, d_status, d_workspace, cs, stream);
+}
+
+SZ_EXPORT sz_status sz_compress_noalloc(const void* d_src, uint64_t n, sz_dtype dtype, uint64_t* d_hist,
+                                        uint8_t* d_codebook, void* d_dst, uint64_t dst_capacity,
+                                        uint64_t* d_out_bytes, int32_t* d_status,
+                                        const sz_compress_options* options, hipStream_t stream) {
+    static_assert(SZ_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch keeps the workspace alignment");
+    CompressSettings cs;
+    if (!settings_of(options, cs) || !dtype_ok(dtype) || n >= kMaxElems || !usable(d_hist) || !usable(d_codebook) ||
+        !usable(d_dst) || (n && !usable(d_src)) || (d_out_bytes && (reinterpret_cast<uintptr_t>(d_out_bytes) & 7u)) ||
+        (d_status && (reinterpret_cast<uintptr_t>(d_status) & 3u)))
+        return SZ_ERR_INVALID_ARGUMENT;
+    if (dst_capacity < sz_max_compressed_bytes(n, dtype)) return SZ_ERR_BUFFER_TOO_SMALL;
+    if (n > SZ_NOALLOC_MAX_ELEMENTS || compress_workspace_bytes(1, n) > SZ_NOALLOC_SCRATCH_BYTES)
+        return SZ_ERR_BUFFER_TOO_SMALL;
+    void* ws = scratch_on_current_device();
+    if (!ws) return SZ_ERR_HIP;
+    return compress_impl(SrcRef{nullptr, d_src}, 1, n, dtype, d_hist, d_codebook, DstRef{nullptr, d_dst},
+                         d_out_bytes, d_status, ws, cs, stream);
 }
 
 SZ_EXPORT sz_status sz_compress_batched(const void* const* d_srcs, uint32_t count, uint64_t n, sz_dtype dtype,

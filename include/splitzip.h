@@ -239,6 +239,26 @@ sz_status sz_compress_batched(const void* const* d_srcs, uint32_t count, uint64_
                               void* d_workspace, uint64_t workspace_bytes,
                               const sz_compress_options* options, hipStream_t stream);
 
+/* ---- sz_compress without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It computes exactly what sz_compress
+ * computes (same histogram, codebook, stream and status), for one tensor of
+ * n <= SZ_NOALLOC_MAX_ELEMENTS elements (else SZ_ERR_BUFFER_TOO_SMALL,
+ * before anything is enqueued), with its workspace in a scratch array of
+ * SZ_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends.  The current device's array is used, so `stream`
+ * must belong to the current device.  No call allocates or frees anything.
+ * Every call on one device shares that device's array and leaves its own
+ * contents there (the call clears what must start at zero), so calls that
+ * overlap in time on one device race: issue them on one stream, or order
+ * them.  Other arguments as sz_compress. ---- */
+#define SZ_NOALLOC_MAX_ELEMENTS (1ull << 24)
+#define SZ_NOALLOC_SCRATCH_BYTES ((16ull << 20) + (32ull << 10))
+
+sz_status sz_compress_noalloc(const void* d_src, uint64_t n, sz_dtype dtype, uint64_t* d_hist,
+                              uint8_t* d_codebook, void* d_dst, uint64_t dst_capacity, uint64_t* d_out_bytes,
+                              int32_t* d_status, const sz_compress_options* options, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* sz_status_string(sz_status status);
 

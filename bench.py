@@ -19,18 +19,23 @@ The same JSON line also carries the step as the three separate calls,
 cold-cache steps, the E5M2-quantised cache, single-read encode variants,
 the LC-style comparison codec, the runtime's copy rate, this GPU's HBM
 streaming ceilings (read, copy and the compress's read/write mix, plain
-and non-temporal) and the CPU oracle's rate on the host.
+and non-temporal), the layer-pipelined transfer, the other workloads
+("configs": one 2^20-element BF16 tensor, its E5M2 quantisation, the
+128-layer long-context cache layer by layer, the 2^28-element escape-heavy
+tensor; each with the oracle's rate in the same run) and the CPU oracle's
+rate on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-                    [--mode bench|profile|copy|transfer|lc|ceiling] [--no-cpu-baseline]
+                    [--mode bench|profile|copy|transfer|lc|ceiling|configs] [--no-cpu-baseline]
                     [--dtype bf16|e5m2]   (profile mode)
 
 --mode profile   a short eager run for rocprofv3 (BF16 or E5M2 cache);
 --mode copy      a 1 GiB copy, for scaling rocprofv3's byte counters;
---mode transfer  the layer-pipelined transfer (encode -> PCIe send and
+--mode transfer  the layer-pipelined transfer (compress -> PCIe send and
                  receive -> decode) against shipping the raw layers;
 --mode lc        only the LC-style comparison codec;
---mode ceiling   only the HBM streaming ceilings (libszprobe).
+--mode ceiling   only the HBM streaming ceilings (libszprobe);
+--mode configs   only the other workloads.
 """
 import argparse
 import concurrent.futures as cf
@@ -59,7 +64,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--mode", choices=["bench", "profile", "copy", "transfer", "lc", "ceiling"], default="bench")
+    p.add_argument("--mode", choices=["bench", "profile", "copy", "transfer", "lc", "ceiling", "configs"],
+                   default="bench")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--dtype", choices=["bf16", "e5m2"], default="bf16",
                    help="profile mode only: run the step on the cache as BF16 or quantised to FP8 E5M2")
@@ -394,12 +400,30 @@ def copy_ceiling(torch):
             "how": "1 GiB device-to-device copy through the HIP runtime"}
 
 
+# Host threads for the CPU oracle: the GPU machine gives one GPU a share of 16
+# host cores, whatever os.cpu_count() reports for the whole host, so the
+# multi-tensor oracle runs use min(16, cpu_count) threads.
+HOST_CORES = 16
+
+
+def host_threads(tensors):
+    return max(1, min(HOST_CORES, os.cpu_count() or 1, tensors))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
+    except (OSError, StopIteration):
+        return "unknown"
+
+
 def cpu_baseline(xs):
     """The CPU oracle (plain scalar C) on this host: encode + decode of
     every layer tensor, one tensor per thread."""
     import oracle
     oracle._load()
-    threads = min(16, os.cpu_count() or 1, len(xs))
+    threads = host_threads(len(xs))
 
     def round_trip(x):
         s = oracle.encode(x, oracle.BF16)
@@ -417,25 +441,24 @@ def cpu_baseline(xs):
             if dt * threads >= 10.0 or passes >= 20:
                 break
     raw = sum(x.nbytes for x in xs) * passes
-    model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
-    except (OSError, StopIteration):
-        pass
+    model = cpu_model()
     return {
         "value": raw / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
         "sample": f"{passes} pass(es) of encode+decode over all {len(xs)} layer tensors (2^23 BF16 "
                   f"each, {raw / passes / 1e9:.3f} GB raw per pass), one tensor per thread, "
                   f"{dt:.2f} s wall",
         "per_core_GBps": raw / dt / 1e9 / threads, "cpu_model": model,
+        "threads_why": f"the GPU box's host share for one GPU is {HOST_CORES} cores (os.cpu_count() reports "
+                       f"{os.cpu_count()} for the whole host)",
     }
 
 
-def transfer(torch, xs):
+def transfer(torch, xs, reps=5):
     """Raw vs compressed layer transfer over the PCIe link (device -> pinned
     host on the sending stream, pinned host -> device on the receiving
-    stream, layers overlapped), and the Equation-1 break-even link rate."""
+    stream, layers overlapped; compressed: one sz_compress_batched call per
+    group of layers, each layer decoded as it lands), and the Equation-1
+    break-even link rate from the codec's own time without overlap."""
     from fp8_kv_cache_amd.transfer import Link
     import fp8_kv_cache_amd as sz
     from fp8_kv_cache_amd.codec import BatchCodec
@@ -443,9 +466,8 @@ def transfer(torch, xs):
     dev = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in xs]
     n, count = xs[0].size, len(xs)
     raw_bytes = sum(x.nbytes for x in xs)
-    link = Link(count, n)
 
-    def timed(fn, reps=5):
+    def timed(fn):
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -458,35 +480,229 @@ def transfer(torch, xs):
             times.append(e0.elapsed_time(e1))
         return float(np.median(times))
 
+    link = Link(count, n, group=8)
     raw_ms = timed(lambda: link.ship_raw(dev))
     for t, landed in zip(dev, link.raw_landed):
         assert torch.equal(landed, t.view(torch.uint8).reshape(-1))
     by_group = {}
-    for group in (1, 4, 8, 16):
-        by_group[group] = timed(lambda: link.ship_compressed(dev, group=group))
-        assert all(st == 0 for st in link.statuses())
-        for t, L in zip(dev, link.layers):
+    for group in (4, 8, 16):
+        lk = link if group == 8 else Link(count, n, group=group)
+        by_group[group] = timed(lambda: lk.ship_compressed(dev))
+        assert all(st == 0 for st in lk.statuses()) and all(st == 0 for st in lk.compress_statuses())
+        for t, L in zip(dev, lk.layers):
             assert torch.equal(L.output, t.view(torch.uint8).reshape(-1))
-    comp_ms = by_group[8]                               # the default grouping
-    comp_bytes = link.compressed_bytes()
-
-    # codec cost without overlap: the batched hot path over the same layers
+        comp_bytes = lk.compressed_bytes()
+        if lk is not link:
+            del lk
+    comp_ms = by_group[8]
+    # codec cost without overlap: the batched fused compress + decode of all layers
     bc = BatchCodec(count, n, sz.SZ_DTYPE_BF16)
     bc.set_inputs(dev)
-    codec_ms = timed(lambda: (bc.compress(), bc.decompress()))
-    link_gbps = raw_bytes / (raw_ms * 1e-3) / 1e9            # bytes delivered per second
+    codec_ms = timed(lambda: (bc.compress_fused(), bc.decompress()))
+    link_gbps = raw_bytes / (raw_ms * 1e-3) / 1e9
     saved = raw_bytes - comp_bytes
-    print(json.dumps({
-        "mode": "transfer", "layers": count, "raw_bytes": raw_bytes, "compressed_bytes": comp_bytes,
+    return {
+        "layers": count, "raw_bytes": raw_bytes, "compressed_bytes": comp_bytes,
         "raw_ms": raw_ms, "compressed_pipelined_ms": comp_ms, "speedup": raw_ms / comp_ms,
-        "layers_per_group": 8, "compressed_ms_by_group": by_group,
+        "layers_per_compress_call": 8, "compressed_ms_by_group": by_group,
         "link": "device -> pinned host (send stream) then pinned host -> device (receive stream) per layer, "
                 "both directions busy at once (PCIe copy engines)",
         "link_GBps_measured": link_gbps,
         "codec_ms_unoverlapped": codec_ms,
         "break_even_link_GBps": saved / (codec_ms * 1e-3) / 1e9,
-        "note": "compression pays on any link slower than break_even_link_GBps even without overlap",
-    }))
+        "note": "compression pays on any link slower than break_even_link_GBps even without overlap "
+                "(encode + decode time < wire time saved)",
+    }
+
+
+# ---------------------------------------------------------------- configs
+#
+# The other workloads, each timed through the C ABI on one GPU: the
+# one-launch compress (sz_compress, histogram + codebook + encode), the same
+# as the three separate calls, and decode; a bit-exact round trip and the
+# fused stream equal to the separate calls' before timing; the CPU oracle on
+# the same input (its streams must equal the GPU's: a same-run parity check)
+# for its rate on 1 core (single-tensor workloads) or a pool of host threads
+# (the long-context cache, one layer per thread).
+
+def _hbm(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS
+
+
+class _One:
+    """Buffers and calls for one tensor of n elements."""
+
+    def __init__(self, torch, sz, n, dt):
+        self.sz, self.n, self.dt = sz, n, dt
+        self.cap = sz.sz_max_compressed_bytes(n, dt)
+        self.hist = torch.empty(256, dtype=torch.int64, device="cuda")
+        self.cb = torch.empty(16, dtype=torch.uint8, device="cuda")
+        self.dst = torch.empty(self.cap, dtype=torch.uint8, device="cuda")
+        self.size = torch.zeros(1, dtype=torch.int64, device="cuda")
+        self.status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        self.dstatus = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        self.ws_bytes = sz.sz_compress_workspace_bytes(n, dt)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.enc_ws_bytes = sz.sz_encode_workspace_bytes(n, dt)
+        self.out = torch.empty(n, dtype=torch.int16 if dt == 1 else torch.uint8, device="cuda")
+
+    def fused(self, x):
+        self.sz.check(self.sz.sz_compress(x, self.n, self.dt, self.hist, self.cb, self.dst, self.cap, self.size,
+                                          self.status, self.ws, self.ws_bytes), "sz_compress")
+
+    def three(self, x):
+        sz = self.sz
+        sz.check(sz.sz_histogram(x, self.n, self.dt, self.hist), "sz_histogram")
+        sz.check(sz.sz_build_codebook(self.hist, self.dt, self.cb), "sz_build_codebook")
+        sz.check(sz.sz_encode(x, self.n, self.dt, self.cb, self.dst, self.cap, self.size, self.ws,
+                              self.enc_ws_bytes), "sz_encode")
+
+    def decode(self, nbytes):
+        self.sz.check(self.sz.sz_decode(self.dst, nbytes, self.n, self.dt, self.out, self.dstatus), "sz_decode")
+
+
+def _time_one(torch, one, x, reps):
+    """Median event times of the fused compress, the three calls and decode
+    on tensor x, after checking the round trip and fused == three calls."""
+    one.three(x)
+    torch.cuda.synchronize()
+    ref_size = int(one.size.item())
+    ref = one.dst[:ref_size].clone()
+    one.fused(x)
+    torch.cuda.synchronize()
+    size = int(one.size.item())
+    assert int(one.status.item()) == 0 and size == ref_size and torch.equal(one.dst[:size], ref)
+    one.decode(size)
+    torch.cuda.synchronize()
+    assert int(one.dstatus.item()) == 0 and torch.equal(one.out, x)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        one.fused(x)
+        e[1].record()
+        one.three(x)
+        e[2].record()
+        one.decode(size)
+        e[3].record()
+    torch.cuda.synchronize()
+    assert int(one.status.item()) == 0 and int(one.dstatus.item()) == 0 and int(one.size.item()) == size
+    med = [float(np.median([e[k].elapsed_time(e[k + 1]) for e in ev])) for k in range(3)]
+    return med[0], med[1], med[2], size, one.dst[:size]
+
+
+def _config_row(workload, raw, stream, fused_ms, three_ms, dec_ms, oracle_row, launch_bound=False):
+    row = {
+        "workload": workload, "raw_bytes": raw, "stream_bytes": stream, "compression_ratio": raw / stream,
+        "encode_ms": fused_ms, "encode_GBps": raw / (fused_ms * 1e-3) / 1e9,
+        "encode_hbm_frac_strict": _hbm(raw + stream, fused_ms),
+        "encode_hbm_frac_two_pass": _hbm(2 * raw + stream, fused_ms),
+        "three_call_encode_ms": three_ms, "three_call_encode_GBps": raw / (three_ms * 1e-3) / 1e9,
+        "three_call_encode_hbm_frac_two_pass": _hbm(2 * raw + stream, three_ms),
+        "decode_ms": dec_ms, "decode_GBps": raw / (dec_ms * 1e-3) / 1e9,
+        "decode_hbm_frac": _hbm(raw + stream, dec_ms),
+        "oracle": oracle_row,
+    }
+    if launch_bound:
+        row["note"] = ("a few microseconds of data per call: launch latency, not HBM, sets these times, so the "
+                       "roofline fractions are not meaningful here")
+    return row
+
+
+def _oracle_single(x_host, dt, gpu_stream, min_s=1.0):
+    """The oracle's encode + decode of one tensor on 1 core, repeated to
+    about min_s seconds; its stream must equal the GPU's."""
+    import oracle
+    oracle._load()
+    t0, passes = time.perf_counter(), 0
+    while True:
+        s = oracle.encode(x_host, dt)
+        st, y = oracle.decode(s, x_host.size, dt)
+        assert st == oracle.OK and np.array_equal(y, x_host)
+        passes += 1
+        if passes == 1:
+            assert np.array_equal(s, gpu_stream), "the GPU stream differs from the oracle's"
+        if time.perf_counter() - t0 >= min_s:
+            break
+    dt_s = time.perf_counter() - t0
+    return {"GBps": x_host.nbytes * passes / dt_s / 1e9, "cores": 1, "kind": "oracle",
+            "sample": f"{passes} encode+decode pass(es) of the whole tensor, {dt_s:.2f} s",
+            "stream_equals_gpu": True}
+
+
+def measure_configs(torch, sz, reps=20, cpu=True):
+    import kvsynth
+    out = {}
+    # config 1: one BF16 tensor of 2^20 elements; config 4: its E5M2 quantisation
+    x1 = kvsynth.single_tensor()
+    x4 = kvsynth.e5m2_of(x1)
+    for name, host, dt, desc in (("cfg1", x1, 1, "single BF16 tensor, 2^20 elements, N(0,1) + 0.1% forced escapes"),
+                                 ("cfg4", x4, 2, "the same tensor quantised to FP8 E5M2 (RNE)")):
+        x = torch.from_numpy(host.view(np.int16) if dt == 1 else host).to("cuda")
+        one = _One(torch, sz, host.size, dt)
+        f, t3, d, size, stream = _time_one(torch, one, x, reps)
+        orc = _oracle_single(host, dt, stream.cpu().numpy()) if cpu else None
+        out[name] = _config_row(desc, host.nbytes, size, f, t3, d, orc, launch_bound=True)
+        del x, one
+    # config 5: escape-heavy stress tensor, 2^28 BF16 elements (drawn on the device)
+    x = kvsynth.stress_device("cuda")
+    one = _One(torch, sz, x.numel(), 1)
+    f, t3, d, size, stream = _time_one(torch, one, x, max(3, reps // 2))
+    orc = _oracle_single(x.cpu().numpy().view(np.uint16), 1, stream.cpu().numpy(), min_s=0.5) if cpu else None
+    out["cfg5"] = _config_row("escape-heavy stress: 2^28 BF16 (Cauchy x 2^U(-60,60) + 1% special patterns)",
+                              2 * x.numel(), size, f, t3, d, orc)
+    del x, one, stream
+    torch.cuda.empty_cache()
+    out["cfg3"] = long_context(torch, sz, cpu=cpu)
+    return out
+
+
+def long_context(torch, sz, cpu=True, reps=2):
+    """Config 3: the Qwen3-32B-shaped long-context cache, 64 layers x {K, V}
+    x [131072, 8, 128] (34 GB), layer by layer: each layer is drawn on the
+    device, then compressed (one-launch call and three calls) and decoded
+    on its own, with its own codebook; times add up over the 128 layers.
+    The oracle runs one layer per host thread on the first layers."""
+    import kvsynth
+    import oracle
+    n = 131072 * 8 * 128
+    one = _One(torch, sz, n, 1)
+    tot = [0.0, 0.0, 0.0]
+    raw = stream = 0
+    threads = host_threads(128)
+    sample = []
+    for layer in range(64):
+        for kv in (0, 1):
+            x = kvsynth.long_kv_device(layer, kv, "cuda")
+            f, t3, d, size, s = _time_one(torch, one, x, reps)
+            tot[0] += f
+            tot[1] += t3
+            tot[2] += d
+            raw += 2 * n
+            stream += size
+            if cpu and len(sample) < threads:
+                sample.append((x.cpu().numpy().view(np.uint16), s.cpu().numpy()))
+            del x, s
+    orc = None
+    if cpu:
+        oracle._load()
+
+        def round_trip(item):
+            xh, gpu = item
+            st = oracle.encode(xh, 1)
+            ok = np.array_equal(st, gpu)
+            code, y = oracle.decode(st, xh.size, 1)
+            return ok and code == oracle.OK and np.array_equal(y, xh)
+
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as pool:
+            oks = list(pool.map(round_trip, sample))
+        dt_s = time.perf_counter() - t0
+        assert all(oks), "an oracle stream differs from the GPU's"
+        orc = {"GBps": len(sample) * 2 * n / dt_s / 1e9, "cores": threads, "kind": "oracle",
+               "sample": f"encode+decode of the first {len(sample)} layer tensors, one per thread, {dt_s:.2f} s",
+               "stream_equals_gpu": True}
+    return _config_row("Qwen3-32B-shaped long-context KV cache, 128 x [131072, 8, 128] BF16 (34 GB), "
+                       "layer by layer", raw, stream, tot[0], tot[1], tot[2], orc)
 
 
 def main():
@@ -511,9 +727,12 @@ def main():
         print(json.dumps({"mode": "ceiling", "hbm_ceilings": hbm_ceilings(torch)}))
         return
 
+    if args.mode == "configs":
+        print(json.dumps({"mode": "configs", "configs": measure_configs(torch, sz, cpu=not args.no_cpu_baseline)}))
+        return
     xs = make_inputs()
     if args.mode == "transfer":
-        transfer(torch, xs)
+        print(json.dumps({"mode": "transfer", **transfer(torch, xs)}))
         return
     if args.mode == "lc":
         print(json.dumps({"mode": "lc", "lc_comparison": lc_comparison(torch, xs, reps=3)}))
@@ -593,6 +812,10 @@ def main():
 
     ev3, wall3 = timed(three_call_step, 5)
     evf, wall = timed(fused_step, 3)
+    # the timed steps' own results: every fused status, and one round trip
+    assert (bc.fused_status.cpu().numpy() == 0).all(), "the fused compress gave up in a timed step"
+    for i in range(count):
+        assert int(bc.status[i]) == 0 and torch.equal(bc.output(i), bc._inputs[i]), i
     ms = lambda ev, a, b: [e[a].elapsed_time(e[b]) for e in ev]
     hist_ms, cb_ms, enc_ms, dec3_ms, step3_ms = ms(ev3, 0, 1), ms(ev3, 1, 2), ms(ev3, 2, 3), ms(ev3, 3, 4), ms(ev3, 0, 4)
     comp_ms, dec_ms, step_ms = ms(evf, 0, 1), ms(evf, 1, 2), ms(evf, 0, 2)
@@ -706,6 +929,9 @@ def main():
         if dominant == "sz_compress_batched":
             roofline["frac_of_measured_mix_ceiling"] = (
                 roofline["achieved"] / result["hbm_ceilings"]["compress_mix_nt_GBps"])
+    if args.mode == "bench":
+        result["transfer"] = transfer(torch, [x for x in xs])
+        result["configs"] = measure_configs(torch, sz, cpu=not args.no_cpu_baseline)
     if args.mode == "bench" and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(xs)
     print(json.dumps(result))

@@ -463,28 +463,26 @@ __device__ inline void encode_lane_bf16(const uint32_t (&d)[4], uint32_t valid, 
 // fields (LSB-first) and 32 code nibbles.
 __device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, const uint8_t* tbl,
                                         uint32_t (&sm)[3], uint32_t (&cw)[4], uint32_t (&esc)[4]) {
-    uint32_t c[32];
     uint32_t f[8];
 #pragma unroll
     for (uint32_t k = 0; k < 8; ++k) {
-        const uint32_t e4 = (d[k] >> 2) & 0x1F1F1F1Fu;
-        c[4 * k + 0] = tbl[e4 & 0xFFu];
-        c[4 * k + 1] = tbl[(e4 >> 8) & 0xFFu];
-        c[4 * k + 2] = tbl[(e4 >> 16) & 0xFFu];
-        c[4 * k + 3] = tbl[e4 >> 24];
         const uint32_t s = ((d[k] >> 5) & 0x04040404u) | (d[k] & 0x03030303u);
         f[k] = (s & 0x7u) | ((s >> 5) & 0x38u) | ((s >> 10) & 0x1C0u) | ((s >> 15) & 0xE00u);
-    }
-    if (valid < 32) {
-#pragma unroll
-        for (uint32_t k = 0; k < 32; ++k)
-            if (k >= valid) c[k] = 0;
     }
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
         uint32_t w = 0;
 #pragma unroll
-        for (uint32_t k = 0; k < 8; ++k) w |= c[8 * q + k] << (4 * k);
+        for (uint32_t h = 0; h < 2; ++h) {   // dword 2q + h: elements 8q + 4h .. 8q + 4h + 3
+            const uint32_t e4 = (d[2 * q + h] >> 2) & 0x1F1F1F1Fu;
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i) {
+                const uint32_t e = (e4 >> (8 * i)) & 0xFFu;
+                uint32_t c = tbl[e];
+                if (valid < 32 && 8 * q + 4 * h + i >= valid) c = 0;
+                w |= c << (4 * (4 * h + i));
+            }
+        }
         cw[q] = w;
         esc[q] = escape_nibbles(w);
     }
@@ -496,11 +494,11 @@ __device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, 
 // Escape bytes of a block go to its staging slot at their rank inside the
 // block.  A sparse block (a KV cache block has a few dozen escapes) walks
 // each lane's escape mask and stores each escape byte to the slot.  A dense
-// block (wave-uniform choice: more than kSparseEscapes) would make that a
-// byte store per escape, each wave instruction spread over several lines;
-// instead every element slot of the lane is taken in turn, its rank a
-// masked popcount, the bytes are gathered in the wave's 4 KB of LDS, and
-// the slot is written with 16-byte vectors.
+// block (wave-uniform choice: more than kSparseEscapes) takes every element
+// slot of the lane in turn, its rank a masked popcount; with 4 KB of LDS
+// for the wave (esc_lds) the bytes are gathered there and the slot is
+// written with 16-byte vectors (a byte store per escape makes about 512
+// partial-line write requests per block), else they are stored one by one.
 constexpr uint32_t kSparseEscapes = 256;
 
 template <uint32_t DT>
@@ -539,6 +537,25 @@ __device__ inline void stage_escapes(SZ_GLOBAL uint8_t* esc_out, uint32_t* esc_l
                     esc_out[rank++] = static_cast<uint8_t>(exponent_of<DT>(d[j], 8 * q + (__builtin_ctz(m) >> 2)));
                     m &= m - 1;
                 }
+            }
+        }
+        return;
+    }
+    if (!esc_lds) {
+#pragma unroll
+        for (uint32_t j = 0; j < G::kSubs; ++j) {
+            uint32_t rank = base[j];
+#pragma unroll
+            for (uint32_t q = 0; q < G::kCodeWords; ++q) {
+                const uint32_t m = esc[j][q];
+#pragma unroll
+                for (uint32_t k = 0; k < 8; ++k) {
+                    const uint32_t bit = 1u << (4 * k);
+                    if (m & bit)
+                        esc_out[rank + __builtin_popcount(m & (bit - 1))] =
+                            static_cast<uint8_t>(exponent_of<DT>(d[j], 8 * q + k));
+                }
+                rank += __builtin_popcount(m);
             }
         }
         return;
@@ -618,7 +635,7 @@ __device__ inline const uint8_t* build_code_table(uint32_t* tbl_words, uint32_t 
 // Encode block b from its registers into stream dst with the code table
 // tbl: planes, the block's escape count and its staged escape bytes (flat
 // = the block's index over all tensors).  esc_lds: the wave's 4096 bytes
-// of LDS for gathering a dense block's escapes (16-byte aligned).
+// of LDS for gathering a dense block's escapes (16-byte aligned), or null.
 template <uint32_t DT, bool kFull>
 __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b,
                                      uint64_t flat, uint32_t lane, const uint8_t* tbl, const BlockRegs<DT>& d,
@@ -767,23 +784,24 @@ __global__ __launch_bounds__(256) void k_offsets(EncodeArgs a) {
 
 // ---- escape copy: staged escapes -> the stream's escape region
 //
-// A group of kGroupBlocks consecutive blocks of one tensor is copied by
-// scatter_splits() workgroups of kScatterThreads threads.  Block i of the
-// group has c_i staged escapes (16-byte aligned slot) that go to byte off_i
-// of the escape region (the region starts 256-byte aligned; off_i has any
-// alignment).  In the stream's 16-byte windows, block i's range
-// [off_i, off_i + c_i) covers whole windows, stored as 16-byte vectors, and
-// at most two partial ones at its ends, shared with the neighbouring
-// blocks' escapes and written byte by byte.  A prefix scan numbers the
-// whole windows of the group, and all threads of the group's workgroups
+// A group of kGroupBlocks consecutive blocks of one tensor is copied by one
+// workgroup of kScatterThreads threads.  Block i of the group has c_i
+// staged escapes (16-byte aligned slot) that go to byte off_i of the escape
+// region (the region starts 256-byte aligned; off_i has any alignment).
+// A light group (a KV cache's blocks hold a few dozen escapes each) is
+// copied one block per thread, 16-byte reads and byte stores.  In a dense
+// group, block i's range [off_i, off_i + c_i) covers whole 16-byte windows
+// of the stream, stored as 16-byte vectors, and at most two partial ones at
+// its ends, shared with the neighbouring blocks' escapes and written byte
+// by byte.  A prefix scan numbers the group's whole windows, and all threads
 // take them in turn, kCopyUnroll at a time, so their loads are in flight
-// together whatever the escape counts (one or two windows per block in a
-// KV cache, about 224 in an escape-heavy tensor); two threads per block
-// take its partial windows.  A window gets its 16 bytes from two adjacent
-// staged vectors, joined by a byte funnel shift.
+// together (about 224 windows per block in an escape-heavy tensor); two
+// threads per block take its partial windows.  A window gets its 16 bytes
+// from two adjacent staged vectors, joined by a byte funnel shift.
 constexpr uint32_t kGroupBlocks = 256;
 constexpr uint32_t kScatterThreads = 1024;
 constexpr uint32_t kCopyUnroll = 4;
+constexpr uint32_t kLightEscapes = 64;   // average escapes per block up to which a group is copied per block
 
 struct CopyGroup {
     uint32_t off[kGroupBlocks];       // escape-region byte offset of each block's first escape
@@ -821,14 +839,28 @@ __device__ inline uint32_t whole_windows(uint32_t off, uint32_t cnt) {
     return cnt && end > a ? end - a : 0u;
 }
 
-// Every thread of the group's workgroups calls it after cg is complete (a
-// barrier); split `split` of `splits` takes every splits-th round of
-// whole windows, and split 0 also writes the partial windows.
+// One block per thread (threads 0..nb-1, which hold the block's offset
+// and count): 16-byte reads of the staged bytes, byte stores.
+__device__ inline void copy_escapes_light(uint32_t off, uint32_t cnt, uint32_t nb, const SZ_GLOBAL uint8_t* slot0,
+                                          SZ_GLOBAL uint8_t* esc, uint32_t tid) {
+    if (tid >= nb || cnt == 0) return;
+    const SZ_GLOBAL u32x4* from = (const SZ_GLOBAL u32x4*)(slot0 + static_cast<uint64_t>(tid) * kBlockElems);
+    SZ_GLOBAL uint8_t* to = esc + off;
+    for (uint32_t i = 0; i < cnt; i += 16) {
+        const u32x4 v = from[i / 16];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k)
+            if (i + k < cnt) to[i + k] = static_cast<uint8_t>(w[k / 4] >> (8 * (k & 3)));
+    }
+}
+
+// Every thread of the workgroup calls it after cg is complete (a barrier).
 __device__ inline void copy_escapes(const CopyGroup& cg, uint32_t nb, const SZ_GLOBAL uint8_t* slot0,
-                                    SZ_GLOBAL uint8_t* esc, uint32_t tid, uint32_t split, uint32_t splits) {
+                                    SZ_GLOBAL uint8_t* esc, uint32_t tid) {
     const uint32_t total = cg.win[nb];
     constexpr uint32_t kRound = kScatterThreads * kCopyUnroll;
-    for (uint32_t w0 = split * kRound + tid; w0 < total; w0 += splits * kRound) {
+    for (uint32_t w0 = tid; w0 < total; w0 += kRound) {
         uint32_t blk[kCopyUnroll];
 #pragma unroll
         for (uint32_t k = 0; k < kCopyUnroll; ++k) {   // the block of each window (binary search over win)
@@ -869,7 +901,7 @@ __device__ inline void copy_escapes(const CopyGroup& cg, uint32_t nb, const SZ_G
     // partial windows: thread 2i takes block i's first window when its range
     // starts inside it, thread 2i + 1 the last one when the range ends inside
     // it (unless that is the same window)
-    if (split != 0 || tid >= 2 * nb) return;
+    if (tid >= 2 * nb) return;
     const uint32_t i = tid / 2, off = cg.off[i], cnt = cg.cnt[i], s = off & 15, end = (s + cnt) / 16;
     if (cnt == 0) return;
     const bool head = (tid & 1) == 0;
@@ -950,14 +982,6 @@ __device__ inline uint32_t sum_counts(const SZ_GLOBAL uint32_t* counts, uint64_t
     return group_sum(x, tid, sums);
 }
 
-// Workgroups per block group of the escape copy: enough for about 1024
-// workgroups in all, at most 8 (each split recomputes the group's offsets).
-__host__ __device__ inline uint32_t scatter_splits(uint32_t count, uint64_t blocks) {
-    const uint64_t groups = static_cast<uint64_t>(count) * ((blocks + kGroupBlocks - 1) / kGroupBlocks);
-    const uint64_t want = (1024 + groups - 1) / groups;
-    return static_cast<uint32_t>(want < 1 ? 1 : (want > 8 ? 8 : want));
-}
-
 // Beyond 2^16 blocks per tensor: k_offsets wrote the offset table; the
 // workgroups of each group of kGroupBlocks blocks copy their staged escapes.
 template <uint32_t DT>
@@ -965,26 +989,31 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(EncodeArgs a) {
     __shared__ CopyGroup cg;
     const Layout L = layout_of(a.n, DT);
     const uint32_t groups = static_cast<uint32_t>((L.blocks + kGroupBlocks - 1) / kGroupBlocks);
-    const uint32_t splits = scatter_splits(a.count, L.blocks);
-    const uint32_t unit = blockIdx.x / splits, split = blockIdx.x - unit * splits;
-    const uint32_t t = unit / groups, g = unit - t * groups, tid = threadIdx.x;
+    const uint32_t t = blockIdx.x / groups, g = blockIdx.x - t * groups, tid = threadIdx.x;
     const uint64_t b0 = static_cast<uint64_t>(g) * kGroupBlocks;
     const uint32_t nb = static_cast<uint32_t>(L.blocks - b0 < kGroupBlocks ? L.blocks - b0 : kGroupBlocks);
     SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
     const uint64_t flat0 = static_cast<uint64_t>(t) * L.blocks + b0;
     const uint32_t cnt = tid < nb ? gptr(a.counts)[flat0 + tid] : 0u;
     const uint32_t off = tid < nb ? ((const SZ_GLOBAL uint32_t*)(dst + 64))[b0 + tid] : 0u;
+    uint32_t in_group;
+    group_blocks_scan(cnt, tid, cg.sums, in_group);
+    const SZ_GLOBAL uint8_t* slot0 = gptr(a.staging) + flat0 * kBlockElems;
+    if (in_group <= kLightEscapes * nb) {
+        copy_escapes_light(off, cnt, nb, slot0, dst + L.esc_at, tid);
+        return;
+    }
     plan_copy(cg, off, cnt, nb, tid);
-    copy_escapes(cg, nb, gptr(a.staging) + flat0 * kBlockElems, dst + L.esc_at, tid, split, splits);
+    copy_escapes(cg, nb, slot0, dst + L.esc_at, tid);
 }
 
 // k_offsets and k_scatter in one launch, for tensors of at most
-// kFusedGroups x kGroupBlocks blocks.  The workgroups of group g of tensor
-// t take blocks [256g, 256g + 256): their base offset is the sum of the
-// counts of every earlier block, read directly (fewer than 2^16 reads, from
-// L2), so no workgroup waits for another; an in-group scan gives each block
-// its offset, which split 0 writes to the table, and the group's escapes
-// are copied.  Split 0 of the last group of a tensor writes the header.
+// kFusedGroups x kGroupBlocks blocks.  The workgroup of group g of tensor t
+// takes blocks [256g, 256g + 256): its base offset is the sum of the counts
+// of every earlier block, read directly (fewer than 2^16 reads, from L2), so
+// no workgroup waits for another; an in-group scan gives each block its
+// offset, which goes to the table, and the group's escapes are copied.  The
+// last group of a tensor writes the header.
 constexpr uint64_t kFusedGroups = 256;
 
 template <uint32_t DT>
@@ -992,9 +1021,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_offsets_scatter(EncodeArgs 
     __shared__ CopyGroup cg;
     const Layout L = layout_of(a.n, DT);
     const uint32_t groups = static_cast<uint32_t>((L.blocks + kGroupBlocks - 1) / kGroupBlocks);
-    const uint32_t splits = scatter_splits(a.count, L.blocks);
-    const uint32_t unit = blockIdx.x / splits, split = blockIdx.x - unit * splits;
-    const uint32_t t = unit / groups, g = unit - t * groups, tid = threadIdx.x;
+    const uint32_t t = blockIdx.x / groups, g = blockIdx.x - t * groups, tid = threadIdx.x;
     const uint64_t b0 = static_cast<uint64_t>(g) * kGroupBlocks;
     const uint32_t nb = static_cast<uint32_t>(L.blocks - b0 < kGroupBlocks ? L.blocks - b0 : kGroupBlocks);
     const SZ_GLOBAL uint32_t* counts = gptr(a.counts) + static_cast<uint64_t>(t) * L.blocks;
@@ -1003,15 +1030,17 @@ __global__ __launch_bounds__(kScatterThreads) void k_offsets_scatter(EncodeArgs 
     uint32_t in_group;
     const uint32_t off = base + group_blocks_scan(cnt, tid, cg.sums, in_group);
     SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
-    if (split == 0) {
-        if (tid < nb) ((SZ_GLOBAL uint32_t*)(dst + 64))[b0 + tid] = off;
-        if (g == groups - 1)
-            write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, base + in_group,
-                         a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid, compress_gave_up(a, t));
+    if (tid < nb) ((SZ_GLOBAL uint32_t*)(dst + 64))[b0 + tid] = off;
+    if (g == groups - 1)
+        write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, base + in_group,
+                     a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid, compress_gave_up(a, t));
+    const SZ_GLOBAL uint8_t* slot0 = gptr(a.staging) + (static_cast<uint64_t>(t) * L.blocks + b0) * kBlockElems;
+    if (in_group <= kLightEscapes * nb) {
+        copy_escapes_light(off, cnt, nb, slot0, dst + L.esc_at, tid);
+        return;
     }
     plan_copy(cg, off, cnt, nb, tid);
-    copy_escapes(cg, nb, gptr(a.staging) + (static_cast<uint64_t>(t) * L.blocks + b0) * kBlockElems,
-                 dst + L.esc_at, tid, split, splits);
+    copy_escapes(cg, nb, slot0, dst + L.esc_at, tid);
 }
 
 // n == 0: a header-only stream per tensor
@@ -1391,8 +1420,8 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     // ---- main item: blocks 16 * idx + wave of tensor t.  Block loads and
     // the provisional codebook first (it is normally complete long before);
     // wave 0 checks the codebook and builds the one code table all 16 waves
-    // share, while the LDS histogram is cleared; then every wave encodes its
-    // block and counts its exponents in the same pass, and the item adds
+    // share, while the LDS histogram is cleared; then every wave counts its
+    // block's exponents into the LDS copies and encodes it, and the item adds
     // its counts to the tensor's histogram.
     const Layout L = layout_of(n, DT);
     const uint64_t full_blocks = n / kBlockElems;
@@ -1419,17 +1448,13 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
 #pragma unroll
             for (uint32_t i = 0; i < Geometry<DT>::kInWords; ++i) count_dword<DT>(lds, d[j][i], copy4);
     }
-    uint32_t phantom = 0;
-    if (n % kBlockElems && full_blocks / kPassWaves == it.idx)   // the partial last block is in this item
-        phantom = count_ragged<DT, kPassThreads>(lds, src, full_blocks * kBlockElems, n, tid);
-    __syncthreads();
-    hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * t, phantom);
-    __syncthreads();   // the histogram copies are read: their LDS now stages the waves' escapes
     const uint32_t state = s_word[12];   // 1: encode with P, 2: escape-heavy, count only, 0: gave up
     if (state == 1) {
+        // (the LDS holds the histogram copies until the flush below, so a
+        // dense block stages its escapes without it)
         if (mine_full)
             encode_loaded<DT, true>(a.enc, L, dst_of(a.enc.dst, t), b, flat, lane,
-                                    reinterpret_cast<const uint8_t*>(s_tbl), d, bins + wave * (kBlockElems / 4));
+                                    reinterpret_cast<const uint8_t*>(s_tbl), d, nullptr);
     } else {
         // no escapes for this block yet (so the scatter that follows stays
         // inside the stream if the tensor is never encoded); an escape-heavy
@@ -1437,16 +1462,18 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
         if (mine_full && lane == 0) gptr(a.enc.counts)[flat] = 0;
         if (state == 0) mark_gave_up(a, rec, t, tid);
     }
+    uint32_t phantom = 0;
+    if (n % kBlockElems && full_blocks / kPassWaves == it.idx)   // the partial last block is in this item
+        phantom = count_ragged<DT, kPassThreads>(lds, src, full_blocks * kBlockElems, n, tid);
+    __syncthreads();
+    hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * t, phantom);
 }
 
 // One workgroup per item: the ticket taken at the start fixes the item.
 template <uint32_t DT>
 __global__ __launch_bounds__(kPassThreads, 8) void k_compress(CompressArgs a) {
     static_assert(kPassThreads % 256 == 0 && Geometry<DT>::kDomain % (kPassThreads / 256) == 0, "rank split");
-    // the histogram copies, and after a main item's flush its waves' escape
-    // staging (4 KB each)
-    constexpr uint32_t kStageWords = kPassWaves * (kBlockElems / 4);
-    __shared__ uint32_t bins[HistLds<DT>::kWords > kStageWords ? HistLds<DT>::kWords : kStageWords];
+    __shared__ uint32_t bins[HistLds<DT>::kWords];
     __shared__ uint32_t s_tbl[64];    // the code table of a main item, shared by its waves
     __shared__ uint32_t s_word[20];   // [0], [14], [15] the item
     const uint32_t tid = threadIdx.x, lane = lane_id();
@@ -1745,7 +1772,9 @@ __device__ inline void encode_list(const CompressArgs& a, const SZ_GLOBAL uint32
 // grid so a short list still covers the whole GPU.  With empty lists every
 // workgroup leaves at once.
 template <uint32_t DT>
-__global__ __launch_bounds__(kThreads, 8) void k_transcode(CompressArgs a) {
+// (E5M2 recodes four code words per lane and sub-chunk: bounded to 6 waves
+// per SIMD, 80 VGPRs, where 8 would spill 31 of them)
+__global__ __launch_bounds__(kThreads, DT == kDtypeBF16 ? 8 : 6) void k_transcode(CompressArgs a) {
     __shared__ uint32_t s_tbl[kWavesPerGroup][64];
     __shared__ uint32_t s_esc[kWavesPerGroup][kBlockElems / 4];
     const uint32_t lane = lane_id(), wave = uniform(threadIdx.x / kWaveSize);
@@ -2177,7 +2206,7 @@ template <uint32_t DT>
 void enqueue_encode_finish(const EncodeArgs& a, hipStream_t s) {
     const Layout L = layout_of(a.n, DT);
     const uint64_t groups = (L.blocks + kGroupBlocks - 1) / kGroupBlocks;   // block groups per tensor
-    const dim3 grid(static_cast<uint32_t>(a.count * groups * scatter_splits(a.count, L.blocks)));
+    const dim3 grid(static_cast<uint32_t>(a.count * groups));
     if (groups <= kFusedGroups) {
         hipLaunchKernelGGL(k_offsets_scatter<DT>, grid, dim3(kScatterThreads), 0, s, a);
     } else {
@@ -2227,7 +2256,6 @@ void enqueue_compress(const CompressArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_compress(const CompressArgs& a, uint32_t dtype, hipStream_t s) {
-    if (dtype != kDtypeBF16) return hipErrorInvalidValue;   // E5M2 takes the separate kernels
     const uint64_t words = sync_area_bytes(a.enc.count) / 8;
     const uint64_t most = words > a.enc.count ? words : a.enc.count;
     const uint32_t groups = grid_for(most < 4096ull * 256 ? most : 4096ull * 256, 256);
@@ -2235,7 +2263,10 @@ hipError_t launch_compress(const CompressArgs& a, uint32_t dtype, hipStream_t s)
                        static_cast<uint64_t>(a.enc.count));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    enqueue_compress<kDtypeBF16>(a, s);
+    if (dtype == kDtypeBF16)
+        enqueue_compress<kDtypeBF16>(a, s);
+    else
+        enqueue_compress<kDtypeE5M2>(a, s);
     return hipGetLastError();
 }
 

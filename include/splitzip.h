@@ -183,10 +183,10 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * escape-heavy tensor, where the final codebook nearly always differs and a
  * recode would rewrite most of the stream) is only counted in the first
  * kernel and encoded from its input by the second, with the final codebook.
- * The bytes written are the same as the separate calls'.  E5M2 tensors
- * (measured slower fused) and BF16 tensors below the options'
- * fused_min_elements run the separate calls' kernels, with the same
- * results.
+ * The bytes written are the same as the separate calls'.  Tensors below
+ * the options' fused_min_elements run the separate calls' kernels, with the
+ * same results; by default that is BF16 tensors under 2^21 elements and
+ * every E5M2 tensor (measured faster with the separate kernels).
  *
  * Work inside the kernel waits only for work handed out before it, so a
  * call always makes progress, whatever else shares the GPU.  Waits are
@@ -213,10 +213,11 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * field is SZ_ERR_INVALID_ARGUMENT. ---- */
 
 typedef struct {
-    /* Smallest BF16 tensor (in elements) run through the one-launch kernel;
+    /* Smallest tensor (in elements) run through the one-launch kernel;
      * smaller ones take the separate calls' kernels (same results).  0 means
-     * the default, 2^21 (4 MiB tensors measured 15% faster fused, 2 MiB ones
-     * 10% slower); 1 sends every BF16 tensor through the one-launch kernel. */
+     * the defaults: 2^21 for BF16 (4 MiB tensors measured 15% faster fused,
+     * 2 MiB ones 10% slower) and no E5M2 tensor; 1 sends every tensor of
+     * either type through the one-launch kernel. */
     uint64_t fused_min_elements;
     /* Polls a waiting workgroup makes before it gives up; 0 means the
      * default, 2^20 (about a second).  A small value reaches the give-up

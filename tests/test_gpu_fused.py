@@ -310,71 +310,87 @@ def test_give_up_path_is_reported_and_bounded(sz):
 # histogram ranks differently.  These inputs are built so that the sample
 # and the whole tensor rank differently in a known way (checked with the
 # oracle on the CPU first), which drives the recoding path.
-SAMPLE_CHUNK, SAMPLE_STRIDE = 1 << 16, 16
+SAMPLE_CHUNK, SAMPLE_STRIDE = {BF16: 1 << 16, E5M2: 1 << 17}, 16   # sample chunk: 128 KB of input
 
 
-def _sample_mask(n):
+def _sample_mask(n, dt=BF16):
     m = np.zeros(n, dtype=bool)
-    for c in range(0, -(-n // SAMPLE_CHUNK), SAMPLE_STRIDE):
-        m[c * SAMPLE_CHUNK:(c + 1) * SAMPLE_CHUNK] = True
+    chunk = SAMPLE_CHUNK[dt]
+    for c in range(0, -(-n // chunk), SAMPLE_STRIDE):
+        m[c * chunk:(c + 1) * chunk] = True
     return m
 
 
-def _set_exponent(bits, where, e):
-    bits[where] = (bits[where] & 0x807F) | (e << 7)
+def _exponents(bits, dt):
+    return (bits >> 7) & 0xFF if dt == BF16 else (bits >> 2) & 0x1F
 
 
-def _skewed(n, seed, kind):
-    """single_tensor(n) with its sampled chunks altered: 'order' swaps the
-    sample's two most frequent exponents (same 15 values, other codes),
-    'members' moves the sample's 15th exponent to a value outside the full
-    top 15 (other values: codes and escapes both change)."""
+def _set_exponent(bits, where, e, dt=BF16):
+    if dt == BF16:
+        bits[where] = (bits[where] & 0x807F) | (e << 7)
+    else:
+        bits[where] = (bits[where] & 0x83) | (e << 2)
+
+
+def _skewed(n, seed, kind, dt=BF16):
+    """single_tensor(n) (or its E5M2 quantisation) with its sampled chunks
+    altered: 'order' swaps the sample's two most frequent exponents (same
+    15 values, other codes), 'members' moves the sample's 15th exponent to a
+    value outside the full top 15 (other values: codes and escapes both
+    change)."""
     x = kvsynth.single_tensor(n, seed=seed).copy()
-    s = _sample_mask(n)
-    e = (x >> 7) & 0xFF
-    top = oracle.codebook(oracle.histogram(x, BF16), BF16)[:15]
+    if dt == E5M2:
+        x = kvsynth.e5m2_of(x)
+    s = _sample_mask(n, dt)
+    e = _exponents(x, dt)
+    top = oracle.codebook(oracle.histogram(x, dt), dt)[:15]
     if kind == "order":
         first, second = int(top[0]), int(top[1])
         idx = np.flatnonzero(s & (e == first))
         gap = int((e[s] == first).sum() - (e[s] == second).sum())
-        _set_exponent(x, idx[:gap // 2 + gap // 8 + 1], second)
+        _set_exponent(x, idx[:gap // 2 + gap // 8 + 1], second, dt)
     else:
         out = int(top[14])
-        unused = next(v for v in range(1, 255) if not (e == v).any())
-        _set_exponent(x, s & (e == out), unused)
+        unused = next(v for v in range(1, 31 if dt == E5M2 else 255) if not (e == v).any())
+        _set_exponent(x, s & (e == out), unused, dt)
     return x
 
 
-def _codebooks(x):
-    full = oracle.codebook(oracle.histogram(x, BF16), BF16)[:15]
-    part = oracle.codebook(oracle.histogram(x[_sample_mask(x.size)], BF16), BF16)[:15]
+def _codebooks(x, dt=BF16):
+    full = oracle.codebook(oracle.histogram(x, dt), dt)[:15]
+    part = oracle.codebook(oracle.histogram(x[_sample_mask(x.size, dt)], dt), dt)[:15]
     return full, part
 
 
+@pytest.mark.parametrize("dt", [BF16, E5M2])
 @pytest.mark.parametrize("kind", ["order", "members"])
 @pytest.mark.parametrize("n", [1 << 21, (1 << 21) + 12345])
-def test_fused_recodes_when_the_sample_ranks_differently(sz, kind, n):
+def test_fused_recodes_when_the_sample_ranks_differently(sz, kind, n, dt):
     """Three tensors, the middle one skewed: its provisional codebook is not
     the final one (same values in another order, or other values), so its
     codes -- and for 'members' its escapes -- are recoded after the main
     pass.  Every stream equals the oracle's."""
-    xs = [kvsynth.single_tensor(n, seed=703), _skewed(n, 701, kind), kvsynth.single_tensor(n, seed=702)]
-    full, part = _codebooks(xs[1])
+    plain = [kvsynth.single_tensor(n, seed=s) for s in (703, 702)]
+    if dt == E5M2:
+        plain = [kvsynth.e5m2_of(x) for x in plain]
+    xs = [plain[0], _skewed(n, 701, kind, dt), plain[1]]
+    full, part = _codebooks(xs[1], dt)
     assert not np.array_equal(full, part)
     assert (set(full.tolist()) == set(part.tolist())) == (kind == "order")
-    for x in (xs[0], xs[2]):
-        f, p = _codebooks(x)
-        assert np.array_equal(f, p)   # these two need no recoding
-    say("fused recode", kind, n)
-    bc = sz.codec.BatchCodec(len(xs), n, BF16)
+    if dt == BF16:
+        for x in (xs[0], xs[2]):
+            f, p = _codebooks(x, dt)
+            assert np.array_equal(f, p)   # these two need no recoding (E5M2 ones may: near-ties among rare values)
+    say("fused recode", kind, n, dt)
+    bc = sz.codec.BatchCodec(len(xs), n, dt)
     bc.set_inputs([to_dev(x) for x in xs])
     bc.compress_fused(options=every(sz))
     bc.decompress()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
     for i, x in enumerate(xs):
-        _check_against_oracle(x, BF16, bc.stream(i), bc.hists[i], bc.codebooks[i])
-        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i
+        _check_against_oracle(x, dt, bc.stream(i), bc.hists[i], bc.codebooks[i])
+        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), dt), x), i
 
 
 def _sample_escape_fraction(x):

@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--mode", choices=["bench", "profile", "copy", "transfer", "lc", "ceiling", "configs"],
                    default="bench")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--configs", default="cfg1,cfg3,cfg4,cfg5",
+                   help="the other workloads to run (comma-separated subset of cfg1,cfg3,cfg4,cfg5)")
     p.add_argument("--dtype", choices=["bf16", "e5m2"], default="bf16",
                    help="profile mode only: run the step on the cache as BF16 or quantised to FP8 E5M2")
     return p.parse_args()
@@ -561,9 +563,12 @@ class _One:
         self.sz.check(self.sz.sz_decode(self.dst, nbytes, self.n, self.dt, self.out, self.dstatus), "sz_decode")
 
 
-def _time_one(torch, one, x, reps):
+def _time_one(torch, one, x, reps, back_to_back=2):
     """Median event times of the fused compress, the three calls and decode
-    on tensor x, after checking the round trip and fused == three calls."""
+    on tensor x, after checking the round trip and fused == three calls.
+    Each timed span holds `back_to_back` identical calls queued one after
+    the other (the time is per call), so that the GPU, not the host's launch
+    rate through Python, sets the time of these single-tensor calls."""
     one.three(x)
     torch.cuda.synchronize()
     ref_size = int(one.size.item())
@@ -578,15 +583,18 @@ def _time_one(torch, one, x, reps):
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
     for e in ev:
         e[0].record()
-        one.fused(x)
+        for _ in range(back_to_back):
+            one.fused(x)
         e[1].record()
-        one.three(x)
+        for _ in range(back_to_back):
+            one.three(x)
         e[2].record()
-        one.decode(size)
+        for _ in range(back_to_back):
+            one.decode(size)
         e[3].record()
     torch.cuda.synchronize()
     assert int(one.status.item()) == 0 and int(one.dstatus.item()) == 0 and int(one.size.item()) == size
-    med = [float(np.median([e[k].elapsed_time(e[k + 1]) for e in ev])) for k in range(3)]
+    med = [float(np.median([e[k].elapsed_time(e[k + 1]) for e in ev])) / back_to_back for k in range(3)]
     return med[0], med[1], med[2], size, one.dst[:size]
 
 
@@ -629,7 +637,7 @@ def _oracle_single(x_host, dt, gpu_stream, min_s=1.0):
             "stream_equals_gpu": True}
 
 
-def measure_configs(torch, sz, reps=20, cpu=True):
+def measure_configs(torch, sz, reps=20, cpu=True, which=("cfg1", "cfg3", "cfg4", "cfg5")):
     import kvsynth
     out = {}
     # config 1: one BF16 tensor of 2^20 elements; config 4: its E5M2 quantisation
@@ -637,23 +645,34 @@ def measure_configs(torch, sz, reps=20, cpu=True):
     x4 = kvsynth.e5m2_of(x1)
     for name, host, dt, desc in (("cfg1", x1, 1, "single BF16 tensor, 2^20 elements, N(0,1) + 0.1% forced escapes"),
                                  ("cfg4", x4, 2, "the same tensor quantised to FP8 E5M2 (RNE)")):
+        if name not in which:
+            continue
         x = torch.from_numpy(host.view(np.int16) if dt == 1 else host).to("cuda")
         one = _One(torch, sz, host.size, dt)
-        f, t3, d, size, stream = _time_one(torch, one, x, reps)
+        f, t3, d, size, stream = _time_one(torch, one, x, reps, back_to_back=8)
         orc = _oracle_single(host, dt, stream.cpu().numpy()) if cpu else None
         out[name] = _config_row(desc, host.nbytes, size, f, t3, d, orc, launch_bound=True)
         del x, one
-    # config 5: escape-heavy stress tensor, 2^28 BF16 elements (drawn on the device)
+    if "cfg5" in which:
+        out["cfg5"] = _stress(torch, sz, reps, cpu)
+    if "cfg3" in which:
+        out["cfg3"] = long_context(torch, sz, cpu=cpu)
+    return out
+
+
+def _stress(torch, sz, reps, cpu):
+    """Config 5: escape-heavy stress tensor, 2^28 BF16 elements (drawn on
+    the device)."""
+    import kvsynth
     x = kvsynth.stress_device("cuda")
     one = _One(torch, sz, x.numel(), 1)
     f, t3, d, size, stream = _time_one(torch, one, x, max(3, reps // 2))
     orc = _oracle_single(x.cpu().numpy().view(np.uint16), 1, stream.cpu().numpy(), min_s=0.5) if cpu else None
-    out["cfg5"] = _config_row("escape-heavy stress: 2^28 BF16 (Cauchy x 2^U(-60,60) + 1% special patterns)",
-                              2 * x.numel(), size, f, t3, d, orc)
+    row = _config_row("escape-heavy stress: 2^28 BF16 (Cauchy x 2^U(-60,60) + 1% special patterns)",
+                      2 * x.numel(), size, f, t3, d, orc)
     del x, one, stream
     torch.cuda.empty_cache()
-    out["cfg3"] = long_context(torch, sz, cpu=cpu)
-    return out
+    return row
 
 
 def long_context(torch, sz, cpu=True, reps=2):
@@ -728,7 +747,9 @@ def main():
         return
 
     if args.mode == "configs":
-        print(json.dumps({"mode": "configs", "configs": measure_configs(torch, sz, cpu=not args.no_cpu_baseline)}))
+        which = tuple(c.strip() for c in args.configs.split(",") if c.strip())
+        print(json.dumps({"mode": "configs",
+                          "configs": measure_configs(torch, sz, cpu=not args.no_cpu_baseline, which=which)}))
         return
     xs = make_inputs()
     if args.mode == "transfer":

@@ -803,11 +803,13 @@ constexpr uint32_t kScatterThreads = 1024;
 constexpr uint32_t kCopyUnroll = 4;
 constexpr uint32_t kLightEscapes = 64;   // average escapes per block up to which a group is copied per block
 
+constexpr uint32_t kCoarse = 64;   // whole windows per entry of the coarse block index
 struct CopyGroup {
     uint32_t off[kGroupBlocks];       // escape-region byte offset of each block's first escape
     uint32_t cnt[kGroupBlocks];       // escapes of each block
     uint32_t win[kGroupBlocks + 1];   // first whole window of each block; win[nb] = whole windows of the group
     uint32_t sums[kScatterThreads / kWaveSize];
+    uint32_t coarse[kGroupBlocks * kBlockElems / 16 / kCoarse];   // the block holding whole window 64 m
 };
 
 // Bytes [16 - s, 32 - s) of the 32-byte sequence prev ++ cur (0 < s < 16).
@@ -861,11 +863,19 @@ __device__ inline void copy_escapes(const CopyGroup& cg, uint32_t nb, const SZ_G
     const uint32_t total = cg.win[nb];
     constexpr uint32_t kRound = kScatterThreads * kCopyUnroll;
     for (uint32_t w0 = tid; w0 < total; w0 += kRound) {
+        // the block of each window: the coarse index names the blocks that
+        // hold windows kCoarse*m and kCoarse*(m+1) around it, and a binary
+        // search over win between them (usually zero or one step) finds it
         uint32_t blk[kCopyUnroll];
 #pragma unroll
-        for (uint32_t k = 0; k < kCopyUnroll; ++k) {   // the block of each window (binary search over win)
+        for (uint32_t k = 0; k < kCopyUnroll; ++k) {
             const uint32_t w = w0 + k * kScatterThreads;
-            uint32_t lo = 0, hi = nb;
+            const uint32_t m = w / kCoarse;
+            uint32_t lo = 0, hi = 1;
+            if (w < total) {
+                lo = cg.coarse[m];
+                hi = (m + 1) * kCoarse < total ? cg.coarse[m + 1] + 1 : nb;
+            }
             while (hi - lo > 1) {
                 const uint32_t mid = (lo + hi) / 2;
                 if (cg.win[mid] <= w) lo = mid; else hi = mid;
@@ -954,6 +964,7 @@ __device__ inline void plan_copy(CopyGroup& cg, uint32_t off, uint32_t cnt, uint
         cg.off[tid] = off;
         cg.cnt[tid] = cnt;
         cg.win[tid] = first;
+        for (uint32_t m = (first + kCoarse - 1) / kCoarse; m * kCoarse < first + windows; ++m) cg.coarse[m] = tid;
     }
     if (tid == 0) cg.win[nb] = total;
     __syncthreads();

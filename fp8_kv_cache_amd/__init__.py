@@ -42,6 +42,7 @@ SZ_ERR_HIP = 4
 SZ_ERR_TIMEOUT = 5
 SZ_NOALLOC_MAX_ELEMENTS = 1 << 24                  # include/splitzip.h
 SZ_NOALLOC_SCRATCH_BYTES = (16 << 20) + (32 << 10)
+SZ_ABI_VERSION = 3                                 # include/splitzip.h: the signatures below are for it
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
@@ -72,6 +73,7 @@ _SIGNATURES = {
     "sz_compress_batched": (_i32, [_vp, _u32, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp]),
     "sz_compress_noalloc": (_i32, [_vp, _u64, _i32, _vp, _vp, _vp, _u64, _vp, _vp, _vp, _vp]),
     "sz_status_string": (ctypes.c_char_p, [_i32]),
+    "sz_abi_version": (_u32, []),
     "lc_max_compressed_bytes": (_u64, [_u64]),
     "lc_encode_workspace_bytes": (_u64, [_u64]),
     "lc_encode_workspace_bytes_batched": (_u64, [_u32, _u64]),
@@ -80,6 +82,13 @@ _SIGNATURES = {
     "lc_encode_batched": (_i32, [_vp, _u32, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
     "lc_decode_batched": (_i32, [_vp, _vp, _u32, _u64, _vp, _vp, _vp]),
 }
+if not hasattr(_lib, "sz_abi_version"):
+    raise ImportError(f"{_LIB_PATH} predates the ABI version check; rebuild it")
+_lib.sz_abi_version.restype = _u32
+if _lib.sz_abi_version() != SZ_ABI_VERSION:
+    # a library from another revision: its signatures may not be the ones below
+    raise ImportError(f"{_LIB_PATH} has ABI version {_lib.sz_abi_version()}, this binding wants "
+                      f"{SZ_ABI_VERSION}; rebuild it")
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(_lib, _name)
     _fn.restype = _res

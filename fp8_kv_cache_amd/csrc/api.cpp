@@ -365,6 +365,8 @@ SZ_EXPORT sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t*
                        d_status, stream);
 }
 
+SZ_EXPORT uint32_t sz_abi_version(void) { return SZ_ABI_VERSION; }
+
 SZ_EXPORT const char* sz_status_string(sz_status status) {
     switch (status) {
         case SZ_OK: return "ok";

@@ -263,6 +263,15 @@ sz_status sz_compress_noalloc(const void* d_src, uint64_t n, sz_dtype dtype, uin
 /* Static description of a status code. */
 const char* sz_status_string(sz_status status);
 
+/* ---- ABI version of the library: SZ_ABI_VERSION as it was compiled.  A
+ * binding built against one revision of this header checks it at load and
+ * refuses a library from another revision, whose signatures or size rules
+ * may differ (calling through mismatched signatures passes garbage
+ * pointers).  Bumped whenever a signature, a struct or a size rule here
+ * changes. ---- */
+#define SZ_ABI_VERSION 3u
+uint32_t sz_abi_version(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,16 @@ def test_library_exports_every_declared_symbol(sz):
     assert all(not s.startswith(("sz_", "lc_")) or s in declared_functions() for s in exported)
 
 
+def test_abi_version_matches_header_and_binding(sz):
+    """The library reports the header's SZ_ABI_VERSION and the binding was
+    written for that version (it refuses to load any other)."""
+    text = open(os.path.join(ROOT, "include", "splitzip.h")).read()
+    want = int(re.search(r"#define SZ_ABI_VERSION (\d+)u", text).group(1))
+    lib = ctypes.CDLL(sz.library_path())
+    lib.sz_abi_version.restype = ctypes.c_uint32
+    assert lib.sz_abi_version() == want == sz.SZ_ABI_VERSION
+
+
 def test_library_contains_no_cpu_codec_path(sz):
     """The product library links neither the oracle nor any CPU codec."""
     out = subprocess.run(["nm", "-D", sz.library_path()], capture_output=True, text=True).stdout

@@ -655,8 +655,10 @@ def measure_configs(torch, sz, reps=20, cpu=True, which=("cfg1", "cfg3", "cfg4",
         del x, one
     if "cfg5" in which:
         out["cfg5"] = _stress(torch, sz, reps, cpu)
+        progress("stress tensor done")
     if "cfg3" in which:
         out["cfg3"] = long_context(torch, sz, cpu=cpu)
+        progress("long-context cache done")
     return out
 
 
@@ -722,6 +724,11 @@ def long_context(torch, sz, cpu=True, reps=2):
                "stream_equals_gpu": True}
     return _config_row("Qwen3-32B-shaped long-context KV cache, 128 x [131072, 8, 128] BF16 (34 GB), "
                        "layer by layer", raw, stream, tot[0], tot[1], tot[2], orc)
+
+
+def progress(msg):
+    """One line per finished phase on stderr (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -831,8 +838,10 @@ def main():
         torch.cuda.synchronize()
         return events, time.perf_counter() - t0
 
+    progress("inputs resident, results checked")
     ev3, wall3 = timed(three_call_step, 5)
     evf, wall = timed(fused_step, 3)
+    progress(f"{steps} timed steps done")
     # the timed steps' own results: every fused status, and one round trip
     assert (bc.fused_status.cpu().numpy() == 0).all(), "the fused compress gave up in a timed step"
     for i in range(count):
@@ -940,11 +949,15 @@ def main():
         result["graph"] = graph
         result["three_call"]["graph"] = graph3
     if args.mode == "bench":
+        progress("graph replays done")
         result["single_read_encode"] = single_read_encode(torch, bc, raw_bytes, count)
         result["e5m2"] = e5m2_cache(torch, xs)
+        progress("E5M2 cache done")
         result["lc_comparison"] = lc_comparison(torch, xs)
+        progress("LC-style comparison done")
         result["copy_ceiling"] = copy_ceiling(torch)
         result["hbm_ceilings"] = hbm_ceilings(torch)
+        progress("ceilings done")
         # the same achieved rate against the measured ceiling for the fused
         # compress's mix of reads and writes, beside frac (the published peak)
         if dominant == "sz_compress_batched":
@@ -952,9 +965,12 @@ def main():
                 roofline["achieved"] / result["hbm_ceilings"]["compress_mix_nt_GBps"])
     if args.mode == "bench":
         result["transfer"] = transfer(torch, [x for x in xs])
+        progress("transfer done")
         result["configs"] = measure_configs(torch, sz, cpu=not args.no_cpu_baseline)
+        progress("configs done")
     if args.mode == "bench" and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(xs)
+        progress("cpu baseline done")
     print(json.dumps(result))
 
 

@@ -298,11 +298,31 @@ def test_give_up_path_is_reported_and_bounded(sz):
             # it reports a corrupt stream rather than returning wrong data
             assert bc.stream(i)[:4].cpu().tolist() == [0, 0, 0, 0], i
             assert decoded[i] == sz.SZ_ERR_CORRUPT_STREAM, i
+    # settle() re-encodes a batch with a give-up through the separate calls
+    gave_up = int((status == sz.SZ_ERR_TIMEOUT).sum())
+    assert bc.settle() == gave_up
+    assert (bc.fused_status.cpu().numpy() == 0).all()
+    for i, x in enumerate(xs):
+        assert np.array_equal(bc.stream(i).cpu().numpy(), oracle.encode(x, BF16)), i
     bc.compress_fused(options=every(sz))
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
     for i, x in enumerate(xs):
         assert np.array_equal(bc.stream(i).cpu().numpy(), oracle.encode(x, BF16)), i
+
+
+def test_compress_fused_retries_after_a_give_up(sz):
+    """codec.compress_fused with the poll limit at 1: whether or not the
+    kernel gave up, the call returns SZ_OK and the oracle's stream (a
+    give-up is re-encoded with the separate calls)."""
+    x = kvsynth.stress(64 * 4096, seed=640)
+    expected = oracle.encode(x, BF16)
+    for rep in range(3):
+        say("fused retry", rep)
+        stream, hist, cb, status = sz.codec.compress_fused(to_dev(x), BF16, options=every(sz, spin_limit=1))
+        torch.cuda.synchronize()
+        assert status == 0
+        assert np.array_equal(stream.cpu().numpy(), expected)
 
 
 # The fused kernel ranks a provisional codebook from a sample (every 16th

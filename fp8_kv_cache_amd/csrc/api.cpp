@@ -4,6 +4,7 @@
 // never allocates, frees or synchronises.
 #include "splitzip.h"
 
+#include <cstring>
 #include <mutex>
 
 #include "sz_internal.h"
@@ -22,7 +23,21 @@ using namespace sz;
 
 constexpr uint64_t kMaxElems = uint64_t(1) << 32;   // offsets are u32
 
-bool dtype_ok(sz_dtype dt) { return dt == SZ_DTYPE_BF16 || dt == SZ_DTYPE_FP8_E5M2; }
+// A C caller may pass any int as an enum argument, and a value outside the
+// enumerators' range must not be read as a C++ enum: the enum arguments are
+// checked through their bytes, and forwarded only once they are valid.
+template <typename E>
+int raw_value(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
+bool dtype_ok(const sz_dtype& dt) {
+    const int v = raw_value(dt);
+    return v == SZ_DTYPE_BF16 || v == SZ_DTYPE_FP8_E5M2;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -200,12 +215,15 @@ SZ_EXPORT uint64_t sz_max_compressed_bytes(uint64_t n, sz_dtype dtype) {
     return layout_of(n, dtype).esc_at + n;
 }
 
+// The size queries answer 0 for a batch the calls would reject for its
+// size (so no product here can wrap around 2^64 either).
 SZ_EXPORT uint64_t sz_encode_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype dtype) {
-    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0) return 0;
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n)) return 0;
     return workspace_bytes(count, n);
 }
 
 SZ_EXPORT uint64_t sz_encode_workspace_bytes(uint64_t n, sz_dtype dtype) {
+    if (!dtype_ok(dtype)) return 0;
     return sz_encode_workspace_bytes_batched(1, n, dtype);
 }
 
@@ -249,6 +267,7 @@ SZ_EXPORT sz_status sz_build_codebook_batched(const uint64_t* d_hists, uint32_t 
 
 SZ_EXPORT sz_status sz_build_codebook(const uint64_t* d_hist, sz_dtype dtype, uint8_t* d_codebook,
                                       hipStream_t stream) {
+    if (!dtype_ok(dtype)) return SZ_ERR_INVALID_ARGUMENT;
     return sz_build_codebook_batched(d_hist, 1, dtype, d_codebook, stream);
 }
 
@@ -284,11 +303,14 @@ SZ_EXPORT sz_status sz_encode_batched(const void* const* d_srcs, uint32_t count,
 }
 
 SZ_EXPORT uint64_t sz_compress_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype dtype) {
-    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0) return 0;
+    if (!dtype_ok(dtype) || n >= kMaxElems || count == 0 || !grid_ok(count, n) ||
+        static_cast<uint64_t>(count) * compress_items(n, dtype) >= (uint64_t(1) << 31))
+        return 0;
     return compress_workspace_bytes(count, n);
 }
 
 SZ_EXPORT uint64_t sz_compress_workspace_bytes(uint64_t n, sz_dtype dtype) {
+    if (!dtype_ok(dtype)) return 0;
     return sz_compress_workspace_bytes_batched(1, n, dtype);
 }
 
@@ -368,7 +390,7 @@ SZ_EXPORT sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t*
 SZ_EXPORT uint32_t sz_abi_version(void) { return SZ_ABI_VERSION; }
 
 SZ_EXPORT const char* sz_status_string(sz_status status) {
-    switch (status) {
+    switch (raw_value(status)) {
         case SZ_OK: return "ok";
         case SZ_ERR_INVALID_ARGUMENT: return "invalid argument";
         case SZ_ERR_BUFFER_TOO_SMALL: return "buffer too small";

@@ -51,7 +51,7 @@ sz_status decode_impl(sz::SrcRef src, const uint64_t* d_src_bytes, uint64_t src_
 LC_EXPORT uint64_t lc_max_compressed_bytes(uint64_t n) { return n < lc::kMaxInput ? lc::max_bytes(n) : 0; }
 
 LC_EXPORT uint64_t lc_encode_workspace_bytes_batched(uint32_t count, uint64_t n) {
-    if (count == 0 || n == 0 || n >= lc::kMaxInput) return 0;
+    if (count == 0 || n == 0 || n >= lc::kMaxInput || !grid_ok(count, n)) return 0;
     return lc::workspace_bytes(count, n);
 }
 

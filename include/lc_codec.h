@@ -58,7 +58,8 @@ uint64_t lc_max_compressed_bytes(uint64_t n);
 
 /* Workspace of an encode: one u32 coded size per chunk, rounded up to 256
  * bytes (count tensors for the batched form).  Pure host function; 0 for
- * n = 0, n >= 2^31 or count = 0. */
+ * n = 0, n >= 2^31, count = 0, or a batch of 2^31 chunks or more (which
+ * the batched calls reject). */
 uint64_t lc_encode_workspace_bytes(uint64_t n);
 uint64_t lc_encode_workspace_bytes_batched(uint32_t count, uint64_t n);
 

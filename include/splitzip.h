@@ -133,6 +133,8 @@ sz_status sz_decode(const void* d_src, uint64_t src_bytes, uint64_t n, sz_dtype 
  * single-tensor calls.  T * ceil(n / 4096) must stay below 2^31, else
  * SZ_ERR_INVALID_ARGUMENT. ---- */
 
+/* 0 for count = 0 or a batch the calls reject for its size, as for a bad
+ * dtype or n (the same holds for sz_compress_workspace_bytes_batched). */
 uint64_t sz_encode_workspace_bytes_batched(uint32_t count, uint64_t n, sz_dtype dtype);
 
 /* d_hists: count x 256 u64 */

@@ -85,6 +85,11 @@ def test_workspace_bytes(sz):
     assert sz.sz_encode_workspace_bytes_batched(64, 1 << 23, 1) == 4 * 64 * 2048 + 64 * 2048 * 4096
     assert sz.sz_encode_workspace_bytes_batched(0, 100, 1) == 0
     assert sz.sz_encode_workspace_bytes(1 << 32, 1) == 0
+    # a batch the calls would reject for its size gets 0, not a wrapped size
+    assert sz.sz_encode_workspace_bytes_batched(1 << 31, 4096, 1) == 0
+    assert sz.sz_encode_workspace_bytes_batched(0xFFFFFFFF, (1 << 32) - 1, 1) == 0
+    assert sz.sz_compress_workspace_bytes_batched(0xFFFFFFFF, (1 << 32) - 1, 1) == 0
+    assert sz.lc_encode_workspace_bytes_batched(0xFFFFFFFF, (1 << 31) - 1) == 0
 
 
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced: every call below fails its host check

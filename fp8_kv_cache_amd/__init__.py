@@ -41,8 +41,8 @@ SZ_ERR_CORRUPT_STREAM = 3
 SZ_ERR_HIP = 4
 SZ_ERR_TIMEOUT = 5
 SZ_NOALLOC_MAX_ELEMENTS = 1 << 24                  # include/splitzip.h
-SZ_NOALLOC_SCRATCH_BYTES = (16 << 20) + (32 << 10)
-SZ_ABI_VERSION = 3                                 # include/splitzip.h: the signatures below are for it
+SZ_NOALLOC_SCRATCH_BYTES = (16 << 20) + (64 << 10)
+SZ_ABI_VERSION = 4                                 # include/splitzip.h: the signatures below are for it
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsplitzip.so")

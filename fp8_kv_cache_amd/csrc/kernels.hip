@@ -285,19 +285,20 @@ __device__ inline uint32_t count_range(char* lds, const SZ_GLOBAL uint8_t* src, 
 // Each workgroup counts one contiguous chunk of one tensor.  The grid
 // oversubscribes the GPU, so one workgroup's fold-and-flush tail overlaps
 // other workgroups' streaming.
-template <uint32_t DT>
-__global__ __launch_bounds__(kThreads) void k_histogram(HistArgs a) {
+// (the 1024-thread form is bounded to 8 waves per SIMD: two workgroups per CU)
+template <uint32_t DT, uint32_t NT>
+__global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void k_histogram(HistArgs a) {
     __shared__ uint32_t bins[HistLds<DT>::kWords];
     const uint32_t tid = threadIdx.x;
     const uint32_t t = blockIdx.x / a.groups;
     const uint32_t g = blockIdx.x - t * a.groups;
-    hist_clear<DT>(bins, tid);
+    hist_clear<DT, NT>(bins, tid);
     __syncthreads();
     const uint64_t begin = static_cast<uint64_t>(g) * a.chunk;
     const uint64_t end = begin + a.chunk < a.n ? begin + a.chunk : a.n;
-    const uint32_t phantom = count_range<DT, kThreads>(reinterpret_cast<char*>(bins), src_of(a.src, t), begin, end, tid);
+    const uint32_t phantom = count_range<DT, NT>(reinterpret_cast<char*>(bins), src_of(a.src, t), begin, end, tid);
     __syncthreads();
-    hist_flush<DT>(bins, tid, gptr(a.hists) + 256ull * t, phantom);
+    hist_flush<DT, NT>(bins, tid, gptr(a.hists) + 256ull * t, phantom);
 }
 
 // Histogram of a block sample: only format blocks b with b % stride == 0
@@ -1115,7 +1116,8 @@ __global__ void k_encode_empty(EncodeArgs a) {
 // poll of every waiting workgroup.
 
 struct SyncView {
-    SZ_GLOBAL uint64_t* hist;     // count x 256, whole tensors
+    uint32_t replicas;            // copies of each whole-tensor histogram (hist_replicas)
+    SZ_GLOBAL uint64_t* hist;     // count x replicas x 256, whole tensors
     SZ_GLOBAL uint64_t* sample;   // count x 256, sampled chunks
     SZ_GLOBAL uint32_t* ticket;
     SZ_GLOBAL uint32_t* abort;
@@ -1137,9 +1139,10 @@ constexpr uint32_t kRecGaveUp = 9;       // 1 once any work item of the tensor g
 
 __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     SyncView v;
+    v.replicas = hist_replicas(count);
     v.hist = gptr(reinterpret_cast<uint64_t*>(base));
-    v.sample = v.hist + 256ull * count;
-    SZ_GLOBAL uint32_t* w = gptr(reinterpret_cast<uint32_t*>(base + 4096ull * count));
+    v.sample = v.hist + 256ull * v.replicas * count;
+    SZ_GLOBAL uint32_t* w = gptr(reinterpret_cast<uint32_t*>(base + sync_hist_bytes(count)));
     v.ticket = w;
     v.abort = w + 1;
     v.listed = w + 2;
@@ -1218,17 +1221,20 @@ __device__ inline bool wait_codebook(const SZ_GLOBAL uint32_t* words, uint32_t& 
     }
 }
 
-// Every thread of the workgroup polls a tensor's histogram until its bins
-// sum to `total` (counts only grow, so that reading is final).  Returns 1
-// with c = this thread's bin (0 for threads past the domain), or 2 after
-// giving up.  Uses s_word[8..12].
+// Every thread of the workgroup polls a tensor's histogram (the sum of its
+// `copies` copies of 256 counters) until its bins sum to `total` (counts
+// only grow, so that reading is final).  Returns 1 with c = this thread's
+// bin (0 for threads past the domain), or 2 after giving up.  Uses
+// s_word[8..12].
 template <uint32_t DT>
-__device__ inline uint32_t wait_histogram(const SZ_GLOBAL uint64_t* hist, uint64_t total, const SyncView& sv,
-                                          uint32_t spin_limit, uint32_t* s_word, uint32_t tid, uint32_t lane,
-                                          uint32_t wave, uint64_t& c) {
+__device__ inline uint32_t wait_histogram(const SZ_GLOBAL uint64_t* hist, uint32_t copies, uint64_t total,
+                                          const SyncView& sv, uint32_t spin_limit, uint32_t* s_word, uint32_t tid,
+                                          uint32_t lane, uint32_t wave, uint64_t& c) {
     constexpr uint32_t D = Geometry<DT>::kDomain;
     for (uint32_t polls = 0;; ++polls) {
-        c = tid < D ? load_agent(hist + tid) : 0;
+        c = 0;
+        if (tid < D)
+            for (uint32_t r = 0; r < copies; ++r) c += load_agent(hist + 256ull * r + tid);
         const uint32_t sum = __builtin_amdgcn_readlane(wave_scan_incl(static_cast<uint32_t>(c)), 63);
         if (lane == 0 && wave < 4) s_word[8 + wave] = sum;   // counts are at most n < 2^32
         __syncthreads();
@@ -1312,7 +1318,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     if (it.kind == kItemProvisional) {
         // ---- provisional item: rank the sample, publish the codebook
         uint64_t c = 0;
-        if (wait_histogram<DT>(sv.sample + 256ull * t, a.sample_total, sv, a.spin_limit, s_word, tid, lane, wave,
+        if (wait_histogram<DT>(sv.sample + 256ull * t, 1u, a.sample_total, sv, a.spin_limit, s_word, tid, lane, wave,
                                c) != 1) {
             mark_gave_up(a, rec, t, tid);
             return;
@@ -1343,7 +1349,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     if (it.kind == kItemFinal) {
         // ---- final item: rank the whole histogram, compare with the provisional codebook
         uint64_t c = 0;
-        uint32_t ok = wait_histogram<DT>(sv.hist + 256ull * t, n, sv, a.spin_limit, s_word, tid, lane, wave, c) == 1;
+        uint32_t ok = wait_histogram<DT>(sv.hist + 256ull * sv.replicas * t, sv.replicas, n, sv, a.spin_limit, s_word, tid, lane, wave, c) == 1;
         if (ok) {
             if (wave == 0) {
                 uint32_t word = lane < 4 ? load_agent(rec + kRecProvisional + lane) : 0u, mine;
@@ -1477,7 +1483,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     if (n % kBlockElems && full_blocks / kPassWaves == it.idx)   // the partial last block is in this item
         phantom = count_ragged<DT, kPassThreads>(lds, src, full_blocks * kBlockElems, n, tid);
     __syncthreads();
-    hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * t, phantom);
+    hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * (sv.replicas * t + it.idx % sv.replicas), phantom);
 }
 
 // One workgroup per item: the ticket taken at the start fixes the item.
@@ -2163,22 +2169,36 @@ hipError_t launch_fill_i32(int32_t* p, uint64_t words, int32_t value, hipStream_
     return hipGetLastError();
 }
 
-// Histogram grid: about kHistGroups workgroups in total, each counting a
-// contiguous multiple of one iteration's elements (8 passes x 256 lanes x
-// one 16-byte vector) of one tensor.
-constexpr uint64_t kHistGroups = 2048;
-
-template <uint32_t DT>
-void enqueue_histogram(HistArgs a, hipStream_t s) {
-    constexpr uint64_t kQuantum = 8ull * kThreads * (16 / Geometry<DT>::kElemBytes);
-    uint64_t want = kHistGroups / a.count;
+// Histogram grid: about kGroups workgroups of NT threads in total, each
+// counting a contiguous multiple of one iteration's elements (8 passes x NT
+// lanes x one 16-byte vector) of one tensor.  Every workgroup adds its
+// counts to its tensor's 256 counters with one atomic per non-empty bin, so
+// the workgroups of one tensor queue on the same few addresses.  A call of
+// many tensors spreads them over many counters and takes 2048 workgroups
+// of 256 threads (five per CU, bound by their 32 KB of LDS).  A call of
+// fewer than 16 tensors takes 512 workgroups of 1024 threads (two per CU,
+// 42-45 VGPRs), a quarter as many atomics per counter: on one 2^27-element
+// tensor 45 us against 55 us, which is the rate of the same bytes spread
+// over 64 tensors.
+template <uint32_t DT, uint32_t NT, uint64_t kGroups>
+void enqueue_histogram_grid(HistArgs a, hipStream_t s) {
+    constexpr uint64_t kQuantum = 8ull * NT * (16 / Geometry<DT>::kElemBytes);
+    uint64_t want = kGroups / a.count;
     if (want < 1) want = 1;
     const uint64_t units = (a.n + kQuantum - 1) / kQuantum;
     if (want > units) want = units;
     a.chunk = (units + want - 1) / want * kQuantum;
     if (DT == kDtypeE5M2 && a.chunk > kE5m2MaxChunk) a.chunk = kE5m2MaxChunk;   // 16-bit pair counters
     a.groups = static_cast<uint32_t>((a.n + a.chunk - 1) / a.chunk);
-    hipLaunchKernelGGL(k_histogram<DT>, dim3(a.count * a.groups), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_histogram<DT, NT>), dim3(a.count * a.groups), dim3(NT), 0, s, a);
+}
+
+template <uint32_t DT>
+void enqueue_histogram(const HistArgs& a, hipStream_t s) {
+    if (a.count < 16)
+        enqueue_histogram_grid<DT, 1024, 512>(a, s);
+    else
+        enqueue_histogram_grid<DT, kThreads, 2048>(a, s);
 }
 
 template <uint32_t DT>

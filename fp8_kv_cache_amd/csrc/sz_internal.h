@@ -113,7 +113,8 @@ struct EncodeArgs {
 // One-launch compress (histogram, codebook and encode).  Its workspace is
 // the encode workspace followed by a synchronisation area that a fill
 // kernel zeroes before every launch:
-//   u64 hist[count][256]     exponent counts of the whole tensor
+//   u64 hist[count][R][256]  exponent counts of the whole tensor, in R =
+//                            hist_replicas(count) copies
 //   u64 sample[count][256]   exponent counts of the sampled chunks
 //   u32 ticket, u32 abort, u32 listed[3]   (padded to 256 bytes)
 //   per tensor t a 128-byte record of u32 words: [0..3] the provisional
@@ -152,12 +153,25 @@ __host__ __device__ inline uint64_t sample_chunk_elems(uint32_t dtype) {
     return 8ull * kPassThreads * (dtype == kDtypeBF16 ? 8 : 16);
 }
 
+// Copies of each tensor's whole-tensor histogram in the synchronisation
+// area: main item i of a tensor adds its counts to copy i % R, and the
+// final item sums the copies.  With few tensors in a call every main item
+// would otherwise add to the same 256 counters, and their atomics queue on
+// those few addresses; R x count >= 16 below 16 tensors.
+__host__ __device__ inline uint32_t hist_replicas(uint32_t count) {
+    return count >= 16 ? 1u : count >= 8 ? 2u : count >= 4 ? 4u : count >= 2 ? 8u : 16u;
+}
+
+__host__ __device__ inline uint64_t sync_hist_bytes(uint32_t count) {
+    return 2048ull * count * (hist_replicas(count) + 1);   // the copies, then the sample histograms
+}
+
 __host__ __device__ inline uint64_t sync_area_bytes(uint32_t count) {
-    return 4096ull * count + 256 + 128ull * count + 64ull * kLists * count;
+    return sync_hist_bytes(count) + 256 + 128ull * count + 64ull * kLists * count;
 }
 
 // The per-tensor records inside the synchronisation area (32 u32 words each).
-__host__ __device__ inline uint64_t sync_records_offset(uint32_t count) { return 4096ull * count + 256; }
+__host__ __device__ inline uint64_t sync_records_offset(uint32_t count) { return sync_hist_bytes(count) + 256; }
 
 struct CompressArgs {
     EncodeArgs enc;           // enc.codebooks (count x 16) is written by the compress kernel

@@ -208,7 +208,9 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * SZ_ERR_INVALID_ARGUMENT.
  * d_workspace: >= sz_compress_workspace_bytes[_batched] bytes, contents
  * need not be initialised, clobbered (the encode workspace followed by a
- * synchronisation area: 256 bytes plus 4416 bytes per tensor).  Calls
+ * synchronisation area: 256 bytes plus 2048 x (R + 1) + 320 bytes per
+ * tensor, with R = 16, 8, 4, 2 or 1 copies of each tensor's histogram for
+ * calls of 1, 2-3, 4-7, 8-15 or more tensors).  Calls
  * sharing a workspace must not overlap in time.
  * options: per-call settings (host memory, read when the call is enqueued),
  * or NULL for the defaults; an options struct with a non-zero reserved
@@ -256,7 +258,7 @@ sz_status sz_compress_batched(const void* const* d_srcs, uint32_t count, uint64_
  * overlap in time on one device race: issue them on one stream, or order
  * them.  Other arguments as sz_compress. ---- */
 #define SZ_NOALLOC_MAX_ELEMENTS (1ull << 24)
-#define SZ_NOALLOC_SCRATCH_BYTES ((16ull << 20) + (32ull << 10))
+#define SZ_NOALLOC_SCRATCH_BYTES ((16ull << 20) + (64ull << 10))
 
 sz_status sz_compress_noalloc(const void* d_src, uint64_t n, sz_dtype dtype, uint64_t* d_hist,
                               uint8_t* d_codebook, void* d_dst, uint64_t dst_capacity, uint64_t* d_out_bytes,
@@ -271,7 +273,7 @@ const char* sz_status_string(sz_status status);
  * may differ (calling through mismatched signatures passes garbage
  * pointers).  Bumped whenever a signature, a struct or a size rule here
  * changes. ---- */
-#define SZ_ABI_VERSION 3u
+#define SZ_ABI_VERSION 4u
 uint32_t sz_abi_version(void);
 
 #ifdef __cplusplus

@@ -128,12 +128,15 @@ def test_host_argument_errors_return_before_launch(sz):
 
 
 def test_compress_sizes_and_host_errors(sz):
-    """Single-pass calls: workspace = the encode workspace plus two 2048-byte
-    histograms per tensor (whole tensor and sample), 256 bytes of counters,
-    a 128-byte record per tensor and three 64-byte list entries per tensor;
-    argument errors return before any launch."""
-    for count, n in [(1, 0), (1, 4097), (64, 1 << 23), (3, 100)]:
-        sync = 4096 * count + 256 + 128 * count + 3 * 64 * count
+    """Single-pass calls: workspace = the encode workspace plus, per tensor,
+    R copies of a 2048-byte whole-tensor histogram (R = 16, 8, 4, 2, 1 for
+    1, 2-3, 4-7, 8-15, 16+ tensors) and a 2048-byte sample histogram, then
+    256 bytes of counters, a 128-byte record per tensor and three 64-byte
+    list entries per tensor; argument errors return before any launch."""
+    for count, n in [(1, 0), (1, 4097), (64, 1 << 23), (3, 100), (2, 5000), (7, 5000), (8, 5000), (15, 5000),
+                     (16, 5000)]:
+        copies = 1 if count >= 16 else 2 if count >= 8 else 4 if count >= 4 else 8 if count >= 2 else 16
+        sync = 2048 * count * (copies + 1) + 256 + 128 * count + 3 * 64 * count
         assert sz.sz_compress_workspace_bytes_batched(count, n, 1) == \
             sz.sz_encode_workspace_bytes_batched(count, n, 1) + sync
     assert sz.sz_compress_workspace_bytes(1 << 32, 1) == 0

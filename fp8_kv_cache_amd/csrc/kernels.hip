@@ -349,31 +349,6 @@ __global__ __launch_bounds__(kThreads) void k_histogram_sampled(HistArgs a) {
     hist_flush<DT>(bins, tid, gptr(a.hists) + 256ull * t, DT == kDtypeE5M2 ? unpaired : 0u);
 }
 
-// --------------------------------------------------------------- codebook
-//
-// Rank every exponent value of the type by (count descending, value
-// ascending): value v's rank is the number of values that order before it.
-// The values of rank 0..14 are the codebook.
-
-template <uint32_t DT>
-__global__ __launch_bounds__(256) void k_codebook(CodebookArgs a) {
-    constexpr uint32_t D = Geometry<DT>::kDomain;
-    __shared__ uint64_t counts[256];
-    const uint32_t t = blockIdx.x, v = threadIdx.x;
-    counts[v] = gptr(a.hists)[256ull * t + v];
-    __syncthreads();
-    if (v < D) {
-        const uint64_t mine = counts[v];
-        uint32_t rank = 0;
-        for (uint32_t u = 0; u < D; ++u) {
-            const uint64_t c = counts[u];
-            rank += (c > mine) | ((c == mine) & (u < v));
-        }
-        if (rank < kCodes) gptr(a.codebooks)[16ull * t + rank] = static_cast<uint8_t>(v);
-    }
-    if (v == kEscape) gptr(a.codebooks)[16ull * t + kEscape] = 0;
-}
-
 // ----------------------------------------------------------------- encode
 //
 // Launches of which none waits on another workgroup (so block ids come
@@ -1116,8 +1091,7 @@ __global__ void k_encode_empty(EncodeArgs a) {
 // poll of every waiting workgroup.
 
 struct SyncView {
-    uint32_t replicas;            // copies of each whole-tensor histogram (hist_replicas)
-    SZ_GLOBAL uint64_t* hist;     // count x replicas x 256, whole tensors
+    SZ_GLOBAL uint64_t* hist;     // count x hist_replicas(count) x 256, whole tensors
     SZ_GLOBAL uint64_t* sample;   // count x 256, sampled chunks
     SZ_GLOBAL uint32_t* ticket;
     SZ_GLOBAL uint32_t* abort;
@@ -1139,9 +1113,8 @@ constexpr uint32_t kRecGaveUp = 9;       // 1 once any work item of the tensor g
 
 __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     SyncView v;
-    v.replicas = hist_replicas(count);
     v.hist = gptr(reinterpret_cast<uint64_t*>(base));
-    v.sample = v.hist + 256ull * v.replicas * count;
+    v.sample = v.hist + 256ull * hist_replicas(count) * count;
     SZ_GLOBAL uint32_t* w = gptr(reinterpret_cast<uint32_t*>(base + sync_hist_bytes(count)));
     v.ticket = w;
     v.abort = w + 1;
@@ -1274,7 +1247,9 @@ __device__ inline void rank_codebook(uint64_t c, uint32_t* bins, uint32_t* s_wor
     if (v < D) {
         const uint64_t key = keys[v];
         uint32_t part = 0;
-        for (uint32_t u = q * (D / kParts); u < (q + 1) * (D / kParts); ++u) part += keys[u] > key ? 1u : 0u;
+        const uint64_t* share = keys + q * (D / kParts);
+#pragma unroll
+        for (uint32_t u = 0; u < D / kParts; ++u) part += share[u] > key ? 1u : 0u;
         parts[q * 256 + v] = part;
     }
     __syncthreads();
@@ -1285,6 +1260,25 @@ __device__ inline void rank_codebook(uint64_t c, uint32_t* bins, uint32_t* s_wor
         if (rank < kCodes) reinterpret_cast<uint8_t*>(s_word + 2)[rank] = static_cast<uint8_t>(v);
     }
     __syncthreads();
+}
+
+// --------------------------------------------------------------- codebook
+//
+// The separate codebook call: one workgroup of kPassThreads threads per
+// tensor ranks the values of the domain by (count descending, value
+// ascending) exactly as the one-launch compress does (rank_codebook: four
+// partial ranks per value over packed (count, value) keys), and writes the
+// values of rank 0..14 with cb[15] = 0.
+template <uint32_t DT>
+__global__ __launch_bounds__(kPassThreads) void k_codebook(CodebookArgs a) {
+    constexpr uint32_t D = Geometry<DT>::kDomain;
+    __shared__ uint32_t bins[2 * 256 + (kPassThreads / 256) * 256];   // keys, then the partial ranks
+    __shared__ uint32_t s_word[8];
+    const uint32_t t = blockIdx.x, tid = threadIdx.x;
+    const uint64_t c = tid < D ? gptr(a.hists)[256ull * t + tid] : 0;
+    rank_codebook<DT>(c, bins, s_word, tid);
+    if (tid < 16)
+        gptr(a.codebooks)[16ull * t + tid] = tid < kCodes ? reinterpret_cast<const uint8_t*>(s_word + 2)[tid] : 0;
 }
 
 // One work item; every thread of the workgroup calls it and every return
@@ -1349,7 +1343,8 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     if (it.kind == kItemFinal) {
         // ---- final item: rank the whole histogram, compare with the provisional codebook
         uint64_t c = 0;
-        uint32_t ok = wait_histogram<DT>(sv.hist + 256ull * sv.replicas * t, sv.replicas, n, sv, a.spin_limit, s_word, tid, lane, wave, c) == 1;
+        const uint32_t copies = hist_replicas(a.enc.count);
+        uint32_t ok = wait_histogram<DT>(sv.hist + 256ull * copies * t, copies, n, sv, a.spin_limit, s_word, tid, lane, wave, c) == 1;
         if (ok) {
             if (wave == 0) {
                 uint32_t word = lane < 4 ? load_agent(rec + kRecProvisional + lane) : 0u, mine;
@@ -1483,7 +1478,8 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     if (n % kBlockElems && full_blocks / kPassWaves == it.idx)   // the partial last block is in this item
         phantom = count_ragged<DT, kPassThreads>(lds, src, full_blocks * kBlockElems, n, tid);
     __syncthreads();
-    hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * (sv.replicas * t + it.idx % sv.replicas), phantom);
+    const uint32_t copies = hist_replicas(a.enc.count);   // a power of two
+    hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * (copies * t + (it.idx & (copies - 1))), phantom);
 }
 
 // One workgroup per item: the ticket taken at the start fixes the item.
@@ -2173,13 +2169,13 @@ hipError_t launch_fill_i32(int32_t* p, uint64_t words, int32_t value, hipStream_
 // counting a contiguous multiple of one iteration's elements (8 passes x NT
 // lanes x one 16-byte vector) of one tensor.  Every workgroup adds its
 // counts to its tensor's 256 counters with one atomic per non-empty bin, so
-// the workgroups of one tensor queue on the same few addresses.  A call of
-// many tensors spreads them over many counters and takes 2048 workgroups
-// of 256 threads (five per CU, bound by their 32 KB of LDS).  A call of
-// fewer than 16 tensors takes 512 workgroups of 1024 threads (two per CU,
-// 42-45 VGPRs), a quarter as many atomics per counter: on one 2^27-element
-// tensor 45 us against 55 us, which is the rate of the same bytes spread
-// over 64 tensors.
+// the workgroups of one tensor queue on the same few addresses.  The grid
+// is 2048 workgroups of 256 threads (five per CU, bound by their 32 KB of
+// LDS), unless that would put 512 or more of them on one tensor (a call of
+// a few large tensors): then 512 workgroups of 1024 threads (two per CU,
+// 42-45 VGPRs), a quarter as many atomics per counter.  On one
+// 2^27-element tensor that takes 45 us against 55 us, the rate of the same
+// bytes spread over 64 tensors; a small tensor keeps the finer grid.
 template <uint32_t DT, uint32_t NT, uint64_t kGroups>
 void enqueue_histogram_grid(HistArgs a, hipStream_t s) {
     constexpr uint64_t kQuantum = 8ull * NT * (16 / Geometry<DT>::kElemBytes);
@@ -2195,7 +2191,10 @@ void enqueue_histogram_grid(HistArgs a, hipStream_t s) {
 
 template <uint32_t DT>
 void enqueue_histogram(const HistArgs& a, hipStream_t s) {
-    if (a.count < 16)
+    constexpr uint64_t kQuantum = 8ull * kThreads * (16 / Geometry<DT>::kElemBytes);
+    const uint64_t units = (a.n + kQuantum - 1) / kQuantum;
+    const uint64_t per_tensor = 2048 / a.count < units ? 2048 / a.count : units;   // of the finer grid
+    if (per_tensor >= 512)
         enqueue_histogram_grid<DT, 1024, 512>(a, s);
     else
         enqueue_histogram_grid<DT, kThreads, 2048>(a, s);
@@ -2226,9 +2225,9 @@ hipError_t launch_histogram(const HistArgs& a, uint32_t dtype, hipStream_t s) {
 
 hipError_t launch_codebook(const CodebookArgs& a, uint32_t dtype, hipStream_t s) {
     if (dtype == kDtypeBF16)
-        hipLaunchKernelGGL(k_codebook<kDtypeBF16>, dim3(a.count), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_codebook<kDtypeBF16>, dim3(a.count), dim3(kPassThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(k_codebook<kDtypeE5M2>, dim3(a.count), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_codebook<kDtypeE5M2>, dim3(a.count), dim3(kPassThreads), 0, s, a);
     return hipGetLastError();
 }
 

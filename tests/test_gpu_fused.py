@@ -269,6 +269,30 @@ def test_two_fused_calls_on_two_streams(sz):
             assert np.array_equal(bc.stream(i).cpu().numpy(), oracle.encode(x, BF16)), i
 
 
+@pytest.mark.parametrize("count", [1, 2, 3, 4, 7, 8, 15, 16, 17])
+def test_fused_histogram_copies(sz, count):
+    """The one-launch kernel keeps 16, 8, 4, 2 or 1 copies of each tensor's
+    histogram for calls of 1, 2-3, 4-7, 8-15 or more tensors (its main items
+    add to copy idx mod R, the final item sums them): every batch size that
+    selects each R gives the oracle's histograms, codebooks and streams."""
+    n = 40 * 4096 + 123   # 3 main items per tensor, the last partial
+    xs = [kvsynth.stress(n, seed=800 + i) if i % 3 == 0 else kvsynth.single_tensor(n, seed=800 + i)
+          for i in range(count)]
+    say("fused histogram copies", count)
+    bc = sz.codec.BatchCodec(count, n, BF16)
+    bc.set_inputs([to_dev(x) for x in xs])
+    bc.compress_fused(options=every(sz))
+    torch.cuda.synchronize()
+    assert (bc.fused_status.cpu().numpy() == 0).all()
+    hists = bc.hists.cpu().numpy().view(np.uint64)
+    cbs = bc.codebooks.cpu().numpy()
+    for i, x in enumerate(xs):
+        h = oracle.histogram(x, BF16)
+        assert np.array_equal(hists[i], h), i
+        assert np.array_equal(cbs[i], oracle.codebook(h, BF16)), i
+        assert np.array_equal(bc.stream(i).cpu().numpy(), oracle.encode(x, BF16)), i
+
+
 def test_give_up_path_is_reported_and_bounded(sz):
     """With the poll limit set to 1 from the host, workgroups that find
     their tensor not yet ready give up at once: every tensor ends with

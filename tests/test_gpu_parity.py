@@ -198,6 +198,31 @@ def test_histogram_beyond_2g_elements(sz, dt):
 
 
 @pytest.mark.parametrize("dt", [BF16, E5M2])
+@pytest.mark.parametrize("count,units,extra", [(1, 511, 0), (1, 512, 0), (1, 512, 4097), (3, 512, 77), (4, 512, 0),
+                                               (4, 511, 0), (1, 510, 16383), (5, 520, 1)])
+def test_histogram_grid_choice(sz, dt, count, units, extra):
+    """The histogram takes a coarser grid (1024-thread workgroups) once the
+    finer one would put 512 or more workgroups on one tensor: at most 2048 /
+    count of them, each counting `per` elements (BF16 16384, E5M2 32768).
+    These sizes sit on both sides of that switch for single tensors and
+    batches (five tensors never switch), with ragged ends; every histogram
+    equals the oracle's."""
+    per = 16384 if dt == BF16 else 32768
+    n = units * per + extra
+    xs = [kvsynth.single_tensor(n, seed=700 + i) for i in range(count)]
+    if dt == E5M2:
+        xs = [kvsynth.e5m2_of(x) for x in xs]
+    say("histogram grid", dt, count, n)
+    dev = [to_dev(x) for x in xs]
+    hists = torch.empty(count, 256, dtype=torch.int64, device="cuda")
+    table = sz.pointer_table(dev)
+    sz.check(sz.sz_histogram_batched(table, count, n, dt, hists), "sz_histogram_batched")
+    got = hists.cpu().numpy().view(np.uint64)
+    for i, x in enumerate(xs):
+        assert np.array_equal(got[i], oracle.histogram(x, dt)), i
+
+
+@pytest.mark.parametrize("dt", [BF16, E5M2])
 def test_empty_tensor(sz, dt):
     say("empty", dt)
     x = np.zeros(0, np.uint16 if dt == BF16 else np.uint8)

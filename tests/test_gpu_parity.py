@@ -476,3 +476,47 @@ def test_round_trip_with_escape_offsets_beyond_2_31(sz):
     assert torch.equal(y, x)
     del x, y, stream
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dt", [BF16, E5M2])
+def test_largest_tensor_round_trip(sz, dt):
+    """The largest tensor the format allows, n = 2^32 - 1 (the escape
+    offsets are unsigned 32-bit), of uniformly random bit patterns: with
+    every exponent about equally frequent, 241 of every 256 BF16 elements
+    (17 of 32 E5M2) escape and the offsets climb to about 4.0e9 (BF16).
+    Compressed with the default call and decoded on the GPU.  The oracle
+    would take many minutes here, so the results are checked through what
+    holds at any size: the histogram equals a torch bincount of the
+    exponents, the codebook is the oracle's ranking of that histogram, the
+    header's escape count is n minus the 15 coded values' counts, the stream
+    size is the closed form H + A(S) + A(ceil(n/2)) + E, and the tensor
+    comes back bit for bit."""
+    n = (1 << 32) - 1
+    say("largest tensor", dt, n)
+    if dt == BF16:
+        x = kvsynth.uniform_bits_device("cuda", n, seed=11)
+    else:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(12)
+        x = torch.randint(0, 256, (n,), generator=g, device="cuda", dtype=torch.uint8)
+    stream, hist, cb, status = sz.codec.compress_fused(x, dt)
+    assert status == 0
+    expected = torch.zeros(256, dtype=torch.int64, device="cuda")
+    step = 1 << 28
+    for lo in range(0, n, step):
+        part = x[lo:lo + step].to(torch.int32)
+        e = ((part >> 7) & 0xFF) if dt == BF16 else ((part >> 2) & 0x1F)
+        expected += torch.bincount(e, minlength=256)
+        del part, e
+    got_hist = hist.cpu().numpy().view(np.uint64)
+    assert np.array_equal(got_hist, expected.cpu().numpy().astype(np.uint64))
+    book = oracle.codebook(got_hist, dt)
+    assert np.array_equal(cb.cpu().numpy(), book)
+    escapes = int(stream[16:24].cpu().numpy().view(np.uint64)[0])
+    assert escapes == n - int(sum(int(got_hist[v]) for v in book[:15]))
+    assert stream.numel() == oracle.max_bytes(n, dt) - n + escapes
+    y, st = sz.codec.decompress(stream, n, dt)
+    assert st == 0
+    assert torch.equal(y, x)
+    del x, y, stream, expected
+    torch.cuda.empty_cache()

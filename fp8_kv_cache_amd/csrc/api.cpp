@@ -61,11 +61,15 @@ uint64_t sample_items(uint64_t n, sz_dtype dt) {
 }
 
 // Its work items per tensor: sample items, the provisional codebook item,
-// main items (kPassWaves blocks each, the partial block included), the
+// main items (item_blocks blocks each, the partial block included), the
 // final codebook item.
+uint64_t main_items(uint64_t n, sz_dtype dt) {
+    const uint64_t per = item_blocks(dt == SZ_DTYPE_BF16 ? kDtypeBF16 : kDtypeE5M2);
+    return ((n + kBlockElems - 1) / kBlockElems + per - 1) / per;
+}
+
 uint64_t compress_items(uint64_t n, sz_dtype dt) {
-    const uint64_t blocks = (n + kBlockElems - 1) / kBlockElems;
-    return sample_items(n, dt) + 1 + (blocks + kPassWaves - 1) / kPassWaves + 1;
+    return sample_items(n, dt) + 1 + main_items(n, dt) + 1;
 }
 
 uint64_t compress_workspace_bytes(uint32_t count, uint64_t n) {
@@ -154,7 +158,7 @@ sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uin
         const uint64_t begin = i * kSampleStride * chunk;
         a.sample_total += static_cast<uint32_t>(n - begin < chunk ? n - begin : chunk);
     }
-    a.main_items = static_cast<uint32_t>((layout_of(n, dt).blocks + kPassWaves - 1) / kPassWaves);
+    a.main_items = static_cast<uint32_t>(main_items(n, dt));
     // (compress_items(n, dt) is the item count per tensor; the entry points
     // keep count * that below 2^31, the launch's workgroup count)
     // Main items of a tensor come lag stages after its sample items: long

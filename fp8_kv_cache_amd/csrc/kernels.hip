@@ -126,17 +126,17 @@ __global__ void k_fill_i32(int32_t* p, uint64_t words, int32_t value) {
 //         adds into copy l & 31, so the 32 lanes of a half-wave hit 32
 //         different banks whatever their exponents.  The byte address of
 //         (bin e, copy c) is e*128 + 4c, and e*128 is simply u & 0x7F80.
-//   E5M2: a byte per element makes the LDS atomics, not the reads, the
-//         limit, so the two exponents of each element pair (bytes 0,1 and
-//         2,3 of a dword) are counted together: 1024 pair bins as 16-bit
-//         counters, two to a dword, in 16 lane-striped copies, laid out
-//         [pair/2][copy] (32 KB).  An element without a partner (a ragged
-//         end) is counted as the pair (e, 0), and the fold, which splits each
-//         pair count back onto both of its exponents, takes those partners
-//         off bin 0 again.  A 16-bit counter takes at most
-//         16 * (chunk/512 + 128) increments (16 lanes per copy, one pair per
-//         two elements, fewer than 128 unpaired elements per lane), so E5M2
-//         chunks are capped at 2^20 elements.
+//   E5M2: a byte per element makes the per-element work, not the reads,
+//         the limit, so the exponents of each element pair (bytes 0,1 and
+//         2,3 of a dword) are counted together: 1024 pair bins of 32-bit
+//         counters in 8 copies (32 KB).  The byte address of the counter
+//         of pair (a, b) in copy c is (a << 5) | (b << 10) | (c << 2), three
+//         operations from the input dword; lane l counts into copy l & 7,
+//         so the bank is chosen by the lane, not by the data (the exponents
+//         of a KV cache crowd into a few values).  An element without a
+//         partner (a ragged end) is counted as the pair (e, 0), and the
+//         fold, which adds each pair count to both of its exponents, takes
+//         those partners off bin 0 again.
 template <uint32_t DT>
 struct HistLds;
 template <>
@@ -145,13 +145,18 @@ struct HistLds<kDtypeBF16> {
 };
 template <>
 struct HistLds<kDtypeE5M2> {
-    static constexpr uint32_t kWords = 512 * 16;
+    static constexpr uint32_t kWords = 1024 * 8;
 };
-constexpr uint64_t kE5m2MaxChunk = 1ull << 20;
 
+// the lane's copy: its byte offset inside a bin's 32 (BF16) or 8 (E5M2) copies
 template <uint32_t DT>
 __device__ inline uint32_t hist_lane_bytes(uint32_t tid) {
-    return DT == kDtypeBF16 ? (tid & 31u) << 2 : (tid & 15u) << 2;
+    return DT == kDtypeBF16 ? (tid & 31u) << 2 : (tid & 7u) << 2;
+}
+
+// E5M2: the byte address of the pair of bytes 0 and 1 of x in copy `copy4`
+__device__ inline uint32_t pair_address(uint32_t x, uint32_t copy4) {
+    return ((x << 3) & 0x3E0u) | (x & 0x7C00u) | copy4;
 }
 
 template <uint32_t DT>
@@ -160,11 +165,9 @@ __device__ inline void count_dword(char* lds, uint32_t w, uint32_t lane_bytes) {
         atomicAdd(reinterpret_cast<uint32_t*>(lds + ((w & 0x7F80u) | lane_bytes)), 1u);
         atomicAdd(reinterpret_cast<uint32_t*>(lds + (((w >> 16) & 0x7F80u) | lane_bytes)), 1u);
     } else {
-        // pair index e_first | e_second << 5 of bytes (0,1) in the low half and (2,3) in the high half
-        const uint32_t pk = ((w >> 2) & 0x001F001Fu) | ((w >> 5) & 0x03E003E0u);
-        const uint32_t p0 = pk & 0xFFFFu, p1 = pk >> 16;
-        atomicAdd(reinterpret_cast<uint32_t*>(lds + (((p0 >> 1) << 6) | lane_bytes)), (p0 & 1u) ? 0x10000u : 1u);
-        atomicAdd(reinterpret_cast<uint32_t*>(lds + (((p1 >> 1) << 6) | lane_bytes)), (p1 & 1u) ? 0x10000u : 1u);
+        // the pairs of bytes (0,1) and (2,3)
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + pair_address(w, lane_bytes)), 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + pair_address(w >> 16, lane_bytes)), 1u);
     }
 }
 
@@ -174,8 +177,7 @@ __device__ inline void count_one(char* lds, uint32_t u, uint32_t lane_bytes) {
     if constexpr (DT == kDtypeBF16) {
         atomicAdd(reinterpret_cast<uint32_t*>(lds + ((((u >> 7) & 0xFFu) << 7) | lane_bytes)), 1u);
     } else {
-        const uint32_t p = (u >> 2) & 0x1Fu;
-        atomicAdd(reinterpret_cast<uint32_t*>(lds + (((p >> 1) << 6) | lane_bytes)), (p & 1u) ? 0x10000u : 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + pair_address(u & 0xFFu, lane_bytes)), 1u);
     }
 }
 
@@ -189,14 +191,16 @@ __device__ inline void hist_clear(uint32_t* bins, uint32_t tid) {
 }
 
 // Fold the copies and add the sums to the tensor's u64 histogram.  Every
-// thread of the NT-thread workgroup calls it, after a barrier; the first
-// 256 do the folding.  `unpaired` is the number of phantom zero exponents
+// thread of the NT-thread workgroup calls it, after a barrier; BF16 folds
+// with the first 256.  `unpaired` is the number of phantom zero exponents
 // the workgroup counted (E5M2: elements counted one at a time as the pair
 // (e, 0); both types: zero padding counted past the end of a tensor); they
 // are taken off bin 0.  Rotating the start keeps the lanes of a wave on
-// distinct banks.
+// distinct banks.  E5M2 counters are read through `mask` (the one-launch
+// compress keeps a code byte in their top byte).
 template <uint32_t DT, uint32_t NT = kThreads>
-__device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64_t* hist, uint32_t unpaired) {
+__device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64_t* hist, uint32_t unpaired,
+                                  uint32_t mask = ~0u) {
     static_assert(NT >= 256, "one folding thread per bin");
     const bool folds = NT == 256 || tid < 256;
     if constexpr (DT == kDtypeBF16) {
@@ -207,27 +211,36 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
         if (sum) __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
     } else {
-        // thread t folds pairs 4t..4t+3 (dwords 2t, 2t+1): their first exponents
-        // are (4t + k) & 31, their second exponent is t >> 3
-        uint32_t c[4] = {0, 0, 0, 0};
+        // thread t folds the pairs (a, b) with a = t & 31 and b = t >> 5 (+
+        // NT / 32 per further pair), each pair's 8 copies one 32-byte run;
+        // the 32 lanes of a half-wave share b
+        constexpr uint32_t kPer = 1024 / NT;
+        const uint32_t a = tid & 31u;
+        uint32_t s[kPer];
+        uint32_t sum_a = 0;
 #pragma unroll
-        for (uint32_t k = 0; k < 2; ++k) {
-#pragma unroll 8
-            for (uint32_t j = 0; j < 16; ++j) {
-                const uint32_t w = folds ? bins[(2 * tid + k) * 16 + ((j + tid) & 15u)] : 0u;
-                c[2 * k] += w & 0xFFFFu;
-                c[2 * k + 1] += w >> 16;
-            }
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint4* run = reinterpret_cast<const uint4*>(bins + ((a << 3) | (((tid >> 5) + (NT / 32) * k) << 8)));
+            const uint4 x = run[0], y = run[1];
+            const uint32_t v = (x.x & mask) + (x.y & mask) + (x.z & mask) + (x.w & mask) + (y.x & mask) +
+                               (y.y & mask) + (y.z & mask) + (y.w & mask);
+            s[k] = v;
+            sum_a += v;
         }
         // the first 32 words, read by now, become the 32 exponent bins
         __syncthreads();
         if (tid < 32) bins[tid] = 0;
         __syncthreads();
-        const uint32_t both = c[0] + c[1] + c[2] + c[3];
-        if (both) atomicAdd(bins + (tid >> 3), both);
+        if (sum_a) atomicAdd(bins + a, sum_a);
+        const uint32_t lane = tid & 63u;
 #pragma unroll
-        for (uint32_t k = 0; k < 4; ++k)
-            if (c[k]) atomicAdd(bins + ((4 * tid + k) & 31u), c[k]);   // c[k] = 0 when !folds
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint32_t incl = wave_scan_incl(s[k]);
+            const uint32_t lo = __builtin_amdgcn_readlane(incl, 31), hi = __builtin_amdgcn_readlane(incl, 63) - lo;
+            const uint32_t b = ((tid & ~63u) >> 5) + (NT / 32) * k + (lane >> 5);
+            const uint32_t half = lane == 0 ? lo : lane == 32 ? hi : 0u;
+            if (half) atomicAdd(bins + b, half);
+        }
         __syncthreads();
         const uint32_t sum = tid < 32 ? bins[tid] - (tid == 0 ? unpaired : 0u) : 0u;
         if (sum)
@@ -435,16 +448,33 @@ __device__ inline void encode_lane_bf16(const uint32_t (&d)[4], uint32_t valid, 
     }
 }
 
+// E5M2 sign|mantissa: 32 elements (4 per dword) -> 96 bits of 3-bit
+// fields, element k at bits 3k..3k+2.  Each byte's field (sign << 2 |
+// mantissa) is formed in place, a byte permute splits eight of them into the
+// even and the odd elements, and two masked shifts close the gaps:
+// 6-bit pairs -> 12-bit quads -> 24 bits per eight elements.
+__device__ inline uint32_t sm_bytes_e5m2(uint32_t x) {
+    return (x & 0x03030303u) | ((x >> 5) & 0x04040404u);
+}
+
+__device__ inline void sm_pack_e5m2(const uint32_t (&d)[8], uint32_t (&sm)[3]) {
+    uint32_t u[4];
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        const uint32_t lo = sm_bytes_e5m2(d[2 * q]), hi = sm_bytes_e5m2(d[2 * q + 1]);
+        const uint32_t r = perm(hi, lo, 0x06040200u) | (perm(hi, lo, 0x07050301u) << 3);   // byte j: 2j, 2j+1
+        const uint32_t g = (r & 0x003F003Fu) | ((r >> 2) & ~0x003F003Fu);   // bits 0..11 and 16..27
+        u[q] = (g & 0x00000FFFu) | ((g >> 4) & ~0x00000FFFu);             // bits 0..23
+    }
+    sm[0] = u[0] | (u[1] << 24);
+    sm[1] = (u[1] >> 8) | (u[2] << 16);
+    sm[2] = (u[2] >> 16) | (u[3] << 8);
+}
+
 // E5M2: 32 elements (4 per dword) -> 96 bits of 3-bit sign|mantissa
 // fields (LSB-first) and 32 code nibbles.
 __device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, const uint8_t* tbl,
                                         uint32_t (&sm)[3], uint32_t (&cw)[4], uint32_t (&esc)[4]) {
-    uint32_t f[8];
-#pragma unroll
-    for (uint32_t k = 0; k < 8; ++k) {
-        const uint32_t s = ((d[k] >> 5) & 0x04040404u) | (d[k] & 0x03030303u);
-        f[k] = (s & 0x7u) | ((s >> 5) & 0x38u) | ((s >> 10) & 0x1C0u) | ((s >> 15) & 0xE00u);
-    }
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
         uint32_t w = 0;
@@ -462,9 +492,32 @@ __device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, 
         cw[q] = w;
         esc[q] = escape_nibbles(w);
     }
-    sm[0] = f[0] | (f[1] << 12) | (f[2] << 24);
-    sm[1] = (f[2] >> 8) | (f[3] << 4) | (f[4] << 16) | (f[5] << 28);
-    sm[2] = (f[5] >> 4) | (f[6] << 8) | (f[7] << 20);
+    sm_pack_e5m2(d, sm);
+}
+
+// E5M2, full lanes, counting as it encodes: each pair counter of the
+// histogram copies `hist` holds in its top byte the code byte of its pair
+// (the code of the first element in the low nibble), so one address serves
+// the lookup (a byte load) and the count (an increment of the low 24 bits,
+// which never carries into the code: an item counts 131072 elements).
+__device__ inline void encode_lane_e5m2_pairs(const uint32_t (&d)[8], char* hist, uint32_t copy4,
+                                              uint32_t (&sm)[3], uint32_t (&cw)[4], uint32_t (&esc)[4]) {
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        uint32_t w = 0;
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h) {   // dword 2q + h: pairs 4q + 2h and 4q + 2h + 1
+            const uint32_t x = d[2 * q + h];
+            const uint32_t p0 = pair_address(x, copy4), p1 = pair_address(x >> 16, copy4);
+            w |= (static_cast<uint32_t>(reinterpret_cast<const uint8_t*>(hist)[p0 + 3]) << (16 * h)) |
+                 (static_cast<uint32_t>(reinterpret_cast<const uint8_t*>(hist)[p1 + 3]) << (16 * h + 8));
+            atomicAdd(reinterpret_cast<uint32_t*>(hist + p0), 1u);
+            atomicAdd(reinterpret_cast<uint32_t*>(hist + p1), 1u);
+        }
+        cw[q] = w;
+        esc[q] = escape_nibbles(w);
+    }
+    sm_pack_e5m2(d, sm);
 }
 
 // Escape bytes of a block go to its staging slot at their rank inside the
@@ -612,10 +665,11 @@ __device__ inline const uint8_t* build_code_table(uint32_t* tbl_words, uint32_t 
 // tbl: planes, the block's escape count and its staged escape bytes (flat
 // = the block's index over all tensors).  esc_lds: the wave's 4096 bytes
 // of LDS for gathering a dense block's escapes (16-byte aligned), or null.
-template <uint32_t DT, bool kFull>
+template <uint32_t DT, bool kFull, bool kPairs = false>
 __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b,
                                      uint64_t flat, uint32_t lane, const uint8_t* tbl, const BlockRegs<DT>& d,
-                                     uint32_t* esc_lds) {
+                                     uint32_t* esc_lds, char* hist = nullptr) {
+    static_assert(!kPairs || (DT == kDtypeE5M2 && kFull), "the pair codes serve full E5M2 blocks");
     using G = Geometry<DT>;
     constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
     constexpr uint32_t kSmWords = G::kSmWords;
@@ -634,6 +688,8 @@ __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GL
                                                                  : static_cast<uint32_t>(a.n - elem0));
         if constexpr (DT == kDtypeBF16)
             encode_lane_bf16(d[j], valid, tbl, sm[j], cw[j], esc[j]);
+        else if constexpr (kPairs)
+            encode_lane_e5m2_pairs(d[j], hist, hist_lane_bytes<DT>(lane), sm[j], cw[j], esc[j]);
         else
             encode_lane_e5m2(d[j], valid, tbl, sm[j], cw[j], esc[j]);
         cnt[j] = 0;
@@ -1429,20 +1485,23 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     }
     if (it.kind != kItemMain) return;
 
-    // ---- main item: blocks 16 * idx + wave of tensor t.  Block loads and
-    // the provisional codebook first (it is normally complete long before);
+    // ---- main item: item_blocks(DT) blocks of tensor t from block
+    // idx * item_blocks(DT), wave w taking the next kRounds of them in turn
+    // (BF16 one, E5M2 two: the same bytes per item).  Block loads and the
+    // provisional codebook first (it is normally complete long before);
     // wave 0 checks the codebook and builds the one code table all 16 waves
     // share, while the LDS histogram is cleared; then every wave counts its
-    // block's exponents into the LDS copies and encodes it, and the item adds
-    // its counts to the tensor's histogram.
+    // blocks' exponents into the LDS copies and encodes them, and the item
+    // adds its counts to the tensor's histogram.  E5M2 writes the code of
+    // each element pair into the top byte of the pair's counters (one pair
+    // per thread) and counts inside the encode.
+    constexpr uint32_t kRounds = item_blocks(DT) / kPassWaves;
     const Layout L = layout_of(n, DT);
     const uint64_t full_blocks = n / kBlockElems;
-    const uint64_t b = static_cast<uint64_t>(it.idx) * kPassWaves + wave;
-    const bool mine_full = b < full_blocks;
-    const uint64_t flat = static_cast<uint64_t>(t) * L.blocks + b;
+    const uint64_t b0 = static_cast<uint64_t>(it.idx) * item_blocks(DT) + wave * kRounds;
     uint32_t word = wave == 0 && lane < 4 ? load_agent(rec + kRecProvisional + lane) : 0u;
     BlockRegs<DT> d;
-    if (mine_full) load_block<DT, true>(src, n, b, lane, d);
+    if (b0 < full_blocks) load_block<DT, true>(src, n, b0, lane, d);
     hist_clear<DT, kPassThreads>(bins, tid);
     if (wave == 0) {
         uint32_t mine;
@@ -1453,33 +1512,55 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
         if (lane == 0) s_word[12] = got ? (heavy ? 2u : 1u) : 0u;
     }
     __syncthreads();
-    if (mine_full) {
-        const uint32_t copy4 = hist_lane_bytes<DT>(tid);
-#pragma unroll
-        for (uint32_t j = 0; j < Geometry<DT>::kSubs; ++j)
-#pragma unroll
-            for (uint32_t i = 0; i < Geometry<DT>::kInWords; ++i) count_dword<DT>(lds, d[j][i], copy4);
-    }
     const uint32_t state = s_word[12];   // 1: encode with P, 2: escape-heavy, count only, 0: gave up
-    if (state == 1) {
-        // (the LDS holds the histogram copies until the flush below, so a
-        // dense block stages its escapes without it)
-        if (mine_full)
-            encode_loaded<DT, true>(a.enc, L, dst_of(a.enc.dst, t), b, flat, lane,
-                                    reinterpret_cast<const uint8_t*>(s_tbl), d, nullptr);
-    } else {
-        // no escapes for this block yet (so the scatter that follows stays
-        // inside the stream if the tensor is never encoded); an escape-heavy
-        // tensor is encoded by the recode launch, a give-up is recorded
-        if (mine_full && lane == 0) gptr(a.enc.counts)[flat] = 0;
-        if (state == 0) mark_gave_up(a, rec, t, tid);
+    constexpr bool kPairs = DT == kDtypeE5M2;
+    const bool pairs = kPairs && state == 1;
+    if (pairs) {
+        const uint8_t* tbl = reinterpret_cast<const uint8_t*>(s_tbl);
+        const uint32_t x = tid & 31u, y = tid >> 5;
+        const uint32_t v = (tbl[x] | (static_cast<uint32_t>(tbl[y]) << 4)) << 24;
+        uint4* run = reinterpret_cast<uint4*>(bins + ((x << 3) | (y << 8)));   // the pair's 8 counters
+        run[0] = make_uint4(v, v, v, v);
+        run[1] = make_uint4(v, v, v, v);
+        __syncthreads();
+    }
+    if (state == 0) mark_gave_up(a, rec, t, tid);
+    const auto block = [&](uint64_t b) {   // count and encode full block b (in d)
+        const uint64_t flat = static_cast<uint64_t>(t) * L.blocks + b;
+        if (!pairs) {
+            const uint32_t copy4 = hist_lane_bytes<DT>(tid);
+#pragma unroll
+            for (uint32_t j = 0; j < Geometry<DT>::kSubs; ++j)
+#pragma unroll
+                for (uint32_t i = 0; i < Geometry<DT>::kInWords; ++i) count_dword<DT>(lds, d[j][i], copy4);
+        }
+        if (state == 1) {
+            // (the LDS holds the histogram copies until the flush below, so a
+            // dense block stages its escapes without it)
+            encode_loaded<DT, true, kPairs>(a.enc, L, dst_of(a.enc.dst, t), b, flat, lane,
+                                            reinterpret_cast<const uint8_t*>(s_tbl), d, nullptr, lds);
+        } else if (lane == 0) {
+            // no escapes for this block yet (so the scatter that follows
+            // stays inside the stream if the tensor is never encoded); an
+            // escape-heavy tensor is encoded by the recode launch
+            gptr(a.enc.counts)[flat] = 0;
+        }
+    };
+    static_assert(kRounds == 1 || kRounds == 2, "one or two blocks per wave");
+    if (b0 < full_blocks) block(b0);
+    if constexpr (kRounds == 2) {
+        if (b0 + 1 < full_blocks) {   // wave-uniform
+            load_block<DT, true>(src, n, b0 + 1, lane, d);
+            block(b0 + 1);
+        }
     }
     uint32_t phantom = 0;
-    if (n % kBlockElems && full_blocks / kPassWaves == it.idx)   // the partial last block is in this item
+    if (n % kBlockElems && full_blocks / item_blocks(DT) == it.idx)   // the partial last block is in this item
         phantom = count_ragged<DT, kPassThreads>(lds, src, full_blocks * kBlockElems, n, tid);
     __syncthreads();
     const uint32_t copies = hist_replicas(a.enc.count);   // a power of two
-    hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * (copies * t + (it.idx & (copies - 1))), phantom);
+    hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * (copies * t + (it.idx & (copies - 1))), phantom,
+                                 pairs ? 0x00FFFFFFu : ~0u);
 }
 
 // One workgroup per item: the ticket taken at the start fixes the item.
@@ -2184,7 +2265,6 @@ void enqueue_histogram_grid(HistArgs a, hipStream_t s) {
     const uint64_t units = (a.n + kQuantum - 1) / kQuantum;
     if (want > units) want = units;
     a.chunk = (units + want - 1) / want * kQuantum;
-    if (DT == kDtypeE5M2 && a.chunk > kE5m2MaxChunk) a.chunk = kE5m2MaxChunk;   // 16-bit pair counters
     a.groups = static_cast<uint32_t>((a.n + a.chunk - 1) / a.chunk);
     hipLaunchKernelGGL((k_histogram<DT, NT>), dim3(a.count * a.groups), dim3(NT), 0, s, a);
 }

@@ -127,8 +127,13 @@ struct EncodeArgs {
 //                            codebook was not used as the final one, [0]
 //                            kProvisionalReordered, [1] kProvisionalDiffers,
 //                            [2] kProvisionalCountOnly, in no set order
-constexpr uint32_t kPassWaves = 16;                         // blocks per main item, one per wave
+constexpr uint32_t kPassWaves = 16;                         // waves per workgroup
 constexpr uint32_t kPassThreads = kPassWaves * kWaveSize;   // 1024
+// Blocks per main item: one per wave for BF16, two for E5M2 (a block of
+// half the bytes), so that every item moves the same bytes.
+__host__ __device__ constexpr uint32_t item_blocks(uint32_t dtype) {
+    return dtype == kDtypeBF16 ? kPassWaves : 2 * kPassWaves;
+}
 constexpr uint32_t kSampleStride = 16;                      // one counting chunk in 16 feeds the provisional codebook
 constexpr uint32_t kPassLag = 4;                            // fewest stages between a tensor's sample and its main items
 constexpr uint64_t kPassLagBytes = 128ull << 20;            // input bytes those stages span at least
@@ -179,7 +184,7 @@ struct CompressArgs {
     uint8_t* sync;            // the synchronisation area
     int32_t* status;          // count, may be null
     uint32_t sample_items;    // per tensor: ceil(chunks / kSampleStride), chunks = ceil(n / sample chunk)
-    uint32_t main_items;      // per tensor: ceil(blocks / kPassWaves)
+    uint32_t main_items;      // per tensor: ceil(blocks / item_blocks(dtype))
     uint32_t lag;             // stage of a tensor's main items after its sample items, >= 1
     uint32_t spin_limit;
     uint32_t sample_total;    // elements the sample items of one tensor count (n < 2^32)

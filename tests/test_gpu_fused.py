@@ -63,10 +63,13 @@ def test_fused_parity(sz, name):
 
 
 @pytest.mark.parametrize("dt", [BF16, E5M2])
-@pytest.mark.parametrize("n", [4096, 8 * 4096, 8 * 4096 + 1, 3 * 8 * 4096 + 4097, 25 * 4096 - 3])
+@pytest.mark.parametrize("n", [4096, 8 * 4096, 8 * 4096 + 1, 3 * 8 * 4096 + 4097, 25 * 4096 - 3,
+                               33 * 4096, (2 * 32 + 3) * 4096 + 77])
 def test_fused_batched(sz, dt, n):
-    """Several tensors; whole and partial workgroup items, a partial last
-    block: equal to the oracle and to the three separate calls."""
+    """Several tensors; whole and partial workgroup items (a main item takes
+    16 BF16 or 32 E5M2 blocks, two per wave), an item whose waves run out
+    of blocks after their first, a partial last block: equal to the oracle
+    and to the three separate calls."""
     xs = [kvsynth.stress(n, seed=400 + i) if i % 2 else kvsynth.single_tensor(n, seed=400 + i) for i in range(7)]
     if dt == E5M2:
         xs = [kvsynth.e5m2_of(x) for x in xs]
@@ -269,17 +272,20 @@ def test_two_fused_calls_on_two_streams(sz):
             assert np.array_equal(bc.stream(i).cpu().numpy(), oracle.encode(x, BF16)), i
 
 
-@pytest.mark.parametrize("count", [1, 2, 3, 4, 7, 8, 15, 16, 17])
-def test_fused_histogram_copies(sz, count):
+@pytest.mark.parametrize("count,dt", [(c, BF16) for c in (1, 2, 3, 4, 7, 8, 15, 16, 17)] +
+                         [(c, E5M2) for c in (1, 2, 16, 17)])
+def test_fused_histogram_copies(sz, count, dt):
     """The one-launch kernel keeps 16, 8, 4, 2 or 1 copies of each tensor's
     histogram for calls of 1, 2-3, 4-7, 8-15 or more tensors (its main items
     add to copy idx mod R, the final item sums them): every batch size that
     selects each R gives the oracle's histograms, codebooks and streams."""
-    n = 40 * 4096 + 123   # 3 main items per tensor, the last partial
+    n = 40 * 4096 + 123   # 3 BF16 or 2 E5M2 main items per tensor, the last partial
     xs = [kvsynth.stress(n, seed=800 + i) if i % 3 == 0 else kvsynth.single_tensor(n, seed=800 + i)
           for i in range(count)]
-    say("fused histogram copies", count)
-    bc = sz.codec.BatchCodec(count, n, BF16)
+    if dt == E5M2:
+        xs = [kvsynth.e5m2_of(x) for x in xs]
+    say("fused histogram copies", count, dt)
+    bc = sz.codec.BatchCodec(count, n, dt)
     bc.set_inputs([to_dev(x) for x in xs])
     bc.compress_fused(options=every(sz))
     torch.cuda.synchronize()
@@ -287,10 +293,10 @@ def test_fused_histogram_copies(sz, count):
     hists = bc.hists.cpu().numpy().view(np.uint64)
     cbs = bc.codebooks.cpu().numpy()
     for i, x in enumerate(xs):
-        h = oracle.histogram(x, BF16)
+        h = oracle.histogram(x, dt)
         assert np.array_equal(hists[i], h), i
-        assert np.array_equal(cbs[i], oracle.codebook(h, BF16)), i
-        assert np.array_equal(bc.stream(i).cpu().numpy(), oracle.encode(x, BF16)), i
+        assert np.array_equal(cbs[i], oracle.codebook(h, dt)), i
+        assert np.array_equal(bc.stream(i).cpu().numpy(), oracle.encode(x, dt)), i
 
 
 def test_give_up_path_is_reported_and_bounded(sz):

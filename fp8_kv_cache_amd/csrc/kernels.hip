@@ -741,6 +741,79 @@ __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GL
     stage_escapes<DT>(gptr(a.staging) + flat * kBlockElems, esc_lds, d, esc, cnt, base, uniform(block_total), lane);
 }
 
+// E5M2 one-launch main items, one 2048-element sub-chunk j of full block b
+// at a time, so that a wave can load its next sub-chunk as soon as one is
+// done: codes and counts through the pair counters `hist`, both planes
+// stored, the escapes staged at their rank inside the block.  `below` is
+// the escapes of the block's earlier sub-chunks; returns it plus this
+// sub-chunk's (wave-uniform).
+__device__ inline uint32_t encode_sub_pairs(const EncodeArgs& a, const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b,
+                                            uint32_t j, uint64_t flat, uint32_t lane, const uint32_t (&d)[8],
+                                            char* hist, uint32_t below) {
+    using G = Geometry<kDtypeE5M2>;
+    uint32_t sm[3], cw[4], esc[4];
+    encode_lane_e5m2_pairs(d, hist, hist_lane_bytes<kDtypeE5M2>(lane), sm, cw, esc);
+    const uint64_t elem0 = b * kBlockElems + j * (kWaveSize * G::kLaneElems) + lane * G::kLaneElems;
+    SZ_GLOBAL uint32_t* smp = (SZ_GLOBAL uint32_t*)(dst + L.sm_at + elem0 / 32 * 12);
+#pragma unroll
+    for (uint32_t i = 0; i < 3; ++i) __builtin_nontemporal_store(sm[i], smp + i);
+    __builtin_nontemporal_store(u32x4{cw[0], cw[1], cw[2], cw[3]}, (SZ_GLOBAL u32x4*)(dst + L.code_at + elem0 / 2));
+    const uint32_t cnt = __builtin_popcount(esc[0]) + __builtin_popcount(esc[1]) + __builtin_popcount(esc[2]) +
+                         __builtin_popcount(esc[3]);
+    const uint32_t incl = wave_scan_incl(cnt);
+    const uint32_t total = uniform(__builtin_amdgcn_readlane(incl, 63));
+    SZ_GLOBAL uint8_t* out = gptr(a.staging) + flat * kBlockElems;
+    uint32_t rank = below + incl - cnt;
+    if (total <= kSparseEscapes / 2) {
+        // the four code words' flags as one 128-bit mask, word q at bits
+        // 32q..32q+31: element 8q + k flags bit 32q + 4k, so ascending flag
+        // positions are element order, and the element at position p is byte
+        // (p >> 2) & 3 of input dword p >> 4
+        uint32_t m0 = esc[0], m1 = esc[1], m2 = esc[2], m3 = esc[3];
+        while ((m0 | m1) | (m2 | m3)) {
+            const bool first = (m0 | m1) != 0;   // in words 0, 1
+            const uint32_t x = first ? m0 : m2, y = first ? m1 : m3;
+            const bool even = x != 0;            // in word 0 or 2
+            const uint32_t z = even ? x : y;
+            const uint32_t p = (first ? 0u : 64u) + (even ? 0u : 32u) + __builtin_ctz(z);
+            const uint32_t zc = z & (z - 1);
+            m0 = first && even ? zc : m0;
+            m1 = first && !even ? zc : m1;
+            m2 = !first && even ? zc : m2;
+            m3 = !first && !even ? zc : m3;
+            const uint32_t r0 = first ? d[0] : d[4], r1 = first ? d[1] : d[5];
+            const uint32_t r2 = first ? d[2] : d[6], r3 = first ? d[3] : d[7];
+            const uint32_t s0 = even ? r0 : r2, s1 = even ? r1 : r3;
+            const uint32_t word = (p & 16u) ? s1 : s0;
+            out[rank++] = static_cast<uint8_t>((word >> (((p << 1) & 24u) + 2u)) & 0x1Fu);
+        }
+    } else {
+#pragma unroll
+        for (uint32_t q = 0; q < G::kCodeWords; ++q) {
+            const uint32_t m = esc[q];
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) {
+                const uint32_t bit = 1u << (4 * k);
+                if (m & bit)
+                    out[rank + __builtin_popcount(m & (bit - 1))] =
+                        static_cast<uint8_t>((d[2 * q + (k >> 2)] >> (8 * (k & 3) + 2)) & 0x1Fu);
+            }
+            rank += __builtin_popcount(m);
+        }
+    }
+    return below + total;
+}
+
+// Load sub-chunk j of full block b (E5M2) into d.
+__device__ inline void load_sub_e5m2(const SZ_GLOBAL uint8_t* src, uint64_t b, uint32_t j, uint32_t lane,
+                                     uint32_t (&d)[8]) {
+    const SZ_GLOBAL u32x4* p =
+        (const SZ_GLOBAL u32x4*)(src + b * kBlockElems + j * (kWaveSize * 32) + lane * 32);
+    const u32x4 x = __builtin_nontemporal_load(p), y = __builtin_nontemporal_load(p + 1);
+    d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+    d[4] = y.x; d[5] = y.y; d[6] = y.z; d[7] = y.w;
+}
+
 // One block with the codebook given in memory: the lane's codebook entry
 // first, then the block's input, then the encode.
 template <uint32_t DT, bool kFull>
@@ -1547,12 +1620,35 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
         }
     };
     static_assert(kRounds == 1 || kRounds == 2, "one or two blocks per wave");
-    if (b0 < full_blocks) block(b0);
     if constexpr (kRounds == 2) {
-        if (b0 + 1 < full_blocks) {   // wave-uniform
-            load_block<DT, true>(src, n, b0 + 1, lane, d);
-            block(b0 + 1);
+        const bool two = b0 + 1 < full_blocks;   // wave-uniform, as is b0 < full_blocks
+        if (pairs) {
+            // sub-chunk by sub-chunk: the next one's loads are issued as soon
+            // as a sub-chunk's registers are free
+            SZ_GLOBAL uint8_t* dst = dst_of(a.enc.dst, t);
+            if (b0 < full_blocks) {
+                const uint64_t flat = static_cast<uint64_t>(t) * L.blocks + b0;
+                uint32_t below = encode_sub_pairs(a.enc, L, dst, b0, 0, flat, lane, d[0], lds, 0);
+                if (two) load_sub_e5m2(src, b0 + 1, 0, lane, d[0]);
+                below = encode_sub_pairs(a.enc, L, dst, b0, 1, flat, lane, d[1], lds, below);
+                if (two) load_sub_e5m2(src, b0 + 1, 1, lane, d[1]);
+                if (lane == 0) gptr(a.enc.counts)[flat] = below;
+            }
+            if (two) {
+                const uint64_t flat = static_cast<uint64_t>(t) * L.blocks + b0 + 1;
+                uint32_t below = encode_sub_pairs(a.enc, L, dst, b0 + 1, 0, flat, lane, d[0], lds, 0);
+                below = encode_sub_pairs(a.enc, L, dst, b0 + 1, 1, flat, lane, d[1], lds, below);
+                if (lane == 0) gptr(a.enc.counts)[flat] = below;
+            }
+        } else {
+            if (b0 < full_blocks) block(b0);
+            if (two) {
+                load_block<DT, true>(src, n, b0 + 1, lane, d);
+                block(b0 + 1);
+            }
         }
+    } else {
+        if (b0 < full_blocks) block(b0);
     }
     uint32_t phantom = 0;
     if (n % kBlockElems && full_blocks / item_blocks(DT) == it.idx)   // the partial last block is in this item

@@ -443,12 +443,12 @@ def test_fused_recodes_when_the_sample_ranks_differently(sz, kind, n, dt):
         assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), dt), x), i
 
 
-def _sample_escape_fraction(x):
+def _sample_escape_fraction(x, dt=BF16):
     """Fraction of the sampled elements that escape under the sample's own
     codebook (the fused kernel encodes a tensor from its input, after
     counting it, when this exceeds 1/4)."""
-    h = oracle.histogram(x[_sample_mask(x.size)], BF16)
-    cb = oracle.codebook(h, BF16)[:15]
+    h = oracle.histogram(x[_sample_mask(x.size, dt)], dt)
+    cb = oracle.codebook(h, dt)[:15]
     return 1.0 - h[cb].sum() / h.sum()
 
 
@@ -473,36 +473,39 @@ def test_fused_escape_heavy_tensors_encoded_after_counting(sz):
         assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i
 
 
-def _dense_escapes_outside_sample(n, seed):
+def _dense_escapes_outside_sample(n, seed, dt=BF16):
     """_skewed(..., 'members') with some blocks outside the sample replaced
     by uniformly random bit patterns: the sample escapes rarely (so the
     tensor is encoded with its provisional codebook), the final codebook
     holds other values, and those blocks hold thousands of escapes each, so
-    the recode rewrites dense runs of staged escapes."""
-    x = _skewed(n, seed, "members")
+    they are staged densely and the recode rewrites dense runs of them."""
+    x = _skewed(n, seed, "members", dt)
     rng = np.random.default_rng(seed)
-    outside = np.flatnonzero(~_sample_mask(n)[::4096][:n // 4096]) * 4096
+    outside = np.flatnonzero(~_sample_mask(n, dt)[::4096][:n // 4096]) * 4096
     for b in rng.choice(outside, 24, replace=False):
-        x[b:b + 4096] = rng.integers(0, 1 << 16, 4096, dtype=np.uint32).astype(np.uint16)
+        x[b:b + 4096] = rng.integers(0, 1 << (16 if dt == BF16 else 8), 4096, dtype=np.uint32).astype(x.dtype)
     return x
 
 
-def test_fused_recodes_dense_escape_blocks(sz):
+@pytest.mark.parametrize("dt", [BF16, E5M2])
+def test_fused_recodes_dense_escape_blocks(sz, dt):
     """The 'other values' recode on blocks with thousands of escapes."""
     n = (1 << 21) + 4096 * 3 + 5
-    xs = [_dense_escapes_outside_sample(n, 730), kvsynth.single_tensor(n, seed=731)]
-    full, part = _codebooks(xs[0])
-    assert set(full.tolist()) != set(part.tolist()) and _sample_escape_fraction(xs[0]) < 0.25
-    say("fused recode dense escapes", n)
-    bc = sz.codec.BatchCodec(len(xs), n, BF16)
+    xs = [_dense_escapes_outside_sample(n, 730, dt), kvsynth.single_tensor(n, seed=731)]
+    if dt == E5M2:
+        xs[1] = kvsynth.e5m2_of(xs[1])
+    full, part = _codebooks(xs[0], dt)
+    assert set(full.tolist()) != set(part.tolist()) and _sample_escape_fraction(xs[0], dt) < 0.25
+    say("fused recode dense escapes", n, dt)
+    bc = sz.codec.BatchCodec(len(xs), n, dt)
     bc.set_inputs([to_dev(x) for x in xs])
     bc.compress_fused(options=every(sz))
     bc.decompress()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
     for i, x in enumerate(xs):
-        _check_against_oracle(x, BF16, bc.stream(i), bc.hists[i], bc.codebooks[i])
-        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i
+        _check_against_oracle(x, dt, bc.stream(i), bc.hists[i], bc.codebooks[i])
+        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), dt), x), i
 
 
 def _degenerate(n, kind):

@@ -497,23 +497,22 @@ __device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, 
 
 // E5M2, full lanes, counting as it encodes: each pair counter of the
 // histogram copies `hist` holds in its top byte the code byte of its pair
-// (the code of the first element in the low nibble), so one address serves
-// the lookup (a byte load) and the count (an increment of the low 24 bits,
-// which never carries into the code: an item counts 131072 elements).
+// (the code of the first element in the low nibble), so one returning
+// increment per pair both counts it (in the low 24 bits, which never carry
+// into the code: an item counts 131072 elements) and looks its codes up.
 __device__ inline void encode_lane_e5m2_pairs(const uint32_t (&d)[8], char* hist, uint32_t copy4,
                                               uint32_t (&sm)[3], uint32_t (&cw)[4], uint32_t (&esc)[4]) {
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
-        uint32_t w = 0;
+        uint32_t half[2];
 #pragma unroll
         for (uint32_t h = 0; h < 2; ++h) {   // dword 2q + h: pairs 4q + 2h and 4q + 2h + 1
             const uint32_t x = d[2 * q + h];
-            const uint32_t p0 = pair_address(x, copy4), p1 = pair_address(x >> 16, copy4);
-            w |= (static_cast<uint32_t>(reinterpret_cast<const uint8_t*>(hist)[p0 + 3]) << (16 * h)) |
-                 (static_cast<uint32_t>(reinterpret_cast<const uint8_t*>(hist)[p1 + 3]) << (16 * h + 8));
-            atomicAdd(reinterpret_cast<uint32_t*>(hist + p0), 1u);
-            atomicAdd(reinterpret_cast<uint32_t*>(hist + p1), 1u);
+            const uint32_t c0 = atomicAdd(reinterpret_cast<uint32_t*>(hist + pair_address(x, copy4)), 1u);
+            const uint32_t c1 = atomicAdd(reinterpret_cast<uint32_t*>(hist + pair_address(x >> 16, copy4)), 1u);
+            half[h] = perm(c1, c0, 0x0C0C0703u);   // the two code bytes
         }
+        const uint32_t w = half[0] | (half[1] << 16);
         cw[q] = w;
         esc[q] = escape_nibbles(w);
     }

@@ -77,20 +77,28 @@ uint64_t compress_workspace_bytes(uint32_t count, uint64_t n) {
 }
 
 // Per-call settings of the one-launch compress, defaults filled in.  By
-// default E5M2 tensors take the separate kernels: counting a byte-per-element
-// input in the encode pass (LDS atomics for each pair of elements) measured
-// slower than a second read of it (0.37-0.41 against 0.28-0.34 ms on the
-// E5M2 cache); a caller's fused_min_elements applies to both types.
+// default E5M2 tensors take the one-launch kernel only in large calls: with
+// one byte per element, the second read it saves is small beside its fixed
+// start (sample, provisional codebook) and the recodes, so the default
+// asks for tensors of at least 2^22 elements and at least 2^28 elements in
+// the call (measured: 2^28 and 2^29 elements in the call took 0.80-0.99 of
+// the separate kernels' time, 2^27 about the same time, one 2^27-element
+// tensor 1.04).  A caller's fused_min_elements applies to both types, with
+// no call-size condition.
 struct CompressSettings {
-    uint64_t fused_min_bf16, fused_min_e5m2;
+    uint64_t fused_min_bf16, fused_min_e5m2, call_min_e5m2;
     uint32_t spin_limit;
-    uint64_t fused_min(sz_dtype dt) const { return dt == SZ_DTYPE_BF16 ? fused_min_bf16 : fused_min_e5m2; }
+    bool fuses(sz_dtype dt, uint32_t count, uint64_t n) const {
+        if (dt == SZ_DTYPE_BF16) return n >= fused_min_bf16;
+        return n >= fused_min_e5m2 && static_cast<uint64_t>(count) * n >= call_min_e5m2;
+    }
 };
 
 bool settings_of(const sz_compress_options* o, CompressSettings& c) {
     const bool given = o && o->fused_min_elements;
     c.fused_min_bf16 = given ? o->fused_min_elements : kDefaultFusedMin;
-    c.fused_min_e5m2 = given ? o->fused_min_elements : ~uint64_t(0);
+    c.fused_min_e5m2 = given ? o->fused_min_elements : kDefaultFusedMinE5m2;
+    c.call_min_e5m2 = given ? 0 : kDefaultFusedCallE5m2;
     c.spin_limit = o && o->spin_limit ? o->spin_limit : kDefaultSpinLimit;
     return !o || o->reserved == 0;
 }
@@ -124,13 +132,13 @@ sz_status encode_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, const
 }
 
 // Histogram, codebook and encode in one launch that reads the input once
-// (plus the short transcode, offset and scatter launches) for tensors of at
-// least cs.fused_min elements; smaller tensors take the separate kernels,
-// as does n = 0.  The results are the same either way.
+// (plus the short transcode, offset and scatter launches) for the tensors
+// cs.fuses picks; the others take the separate kernels, as does n = 0.  The
+// results are the same either way.
 sz_status compress_impl(SrcRef src, uint32_t count, uint64_t n, sz_dtype dt, uint64_t* d_hists,
                         uint8_t* d_codebooks, DstRef dst, uint64_t* d_out_bytes, int32_t* d_status,
                         void* d_workspace, const CompressSettings& cs, hipStream_t s) {
-    if (n == 0 || n < cs.fused_min(dt)) {
+    if (n == 0 || !cs.fuses(dt, count, n)) {
         if (d_status && launch_fill_i32(d_status, count, SZ_OK, s) != hipSuccess) return SZ_ERR_HIP;
         sz_status st = histogram_impl(src, count, n, dt, 1, d_hists, s);
         if (st != SZ_OK) return st;

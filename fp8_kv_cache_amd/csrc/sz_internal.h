@@ -139,6 +139,8 @@ constexpr uint32_t kPassLag = 4;                            // fewest stages bet
 constexpr uint64_t kPassLagBytes = 128ull << 20;            // input bytes those stages span at least
 constexpr uint32_t kDefaultSpinLimit = 1u << 20;            // polls before a waiting workgroup gives up
 constexpr uint64_t kDefaultFusedMin = 1ull << 21;           // smallest BF16 tensor (elements) the fused kernel takes
+constexpr uint64_t kDefaultFusedMinE5m2 = 1ull << 22;       // smallest E5M2 tensor it takes,
+constexpr uint64_t kDefaultFusedCallE5m2 = 1ull << 28;      // in calls of at least this many elements
 constexpr uint32_t kProvisionalSame = 1;       // no recoding
 constexpr uint32_t kProvisionalReordered = 2;  // same 15 values, other codes: code nibbles recoded
 constexpr uint32_t kProvisionalDiffers = 3;    // other values: code nibbles and escapes recoded

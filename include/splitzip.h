@@ -187,8 +187,9 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * kernel and encoded from its input by the second, with the final codebook.
  * The bytes written are the same as the separate calls'.  Tensors below
  * the options' fused_min_elements run the separate calls' kernels, with the
- * same results; by default that is BF16 tensors under 2^21 elements and
- * every E5M2 tensor (measured faster with the separate kernels).
+ * same results; by default that is BF16 tensors under 2^21 elements, and
+ * E5M2 tensors under 2^22 elements or in calls of fewer than 2^28 elements
+ * in all (measured faster with the separate kernels).
  *
  * Work inside the kernel waits only for work handed out before it, so a
  * call always makes progress, whatever else shares the GPU.  Waits are
@@ -202,10 +203,10 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * d_hist(s): 256 (count x 256) u64, written.  d_codebook(s): 16 (count x
  * 16) bytes, written.  d_dst(s), dst_capacity, d_out_bytes: as sz_encode.
  * d_status: 1 (count) int32, SZ_OK or SZ_ERR_TIMEOUT, may be NULL.
- * Batched: T x (ceil(ceil(n / K) / 16) + ceil(ceil(n / 4096) / 16) + 2),
- * the kernel's work items (K = 65536 for BF16, 131072 for E5M2: one
- * 128 KB sample chunk), must stay below 2^31 as well, else
- * SZ_ERR_INVALID_ARGUMENT.
+ * Batched: T x (ceil(ceil(n / K) / 16) + ceil(ceil(n / 4096) / M) + 2),
+ * the kernel's work items (K = 65536 and M = 16 for BF16, K = 131072 and
+ * M = 32 for E5M2: one 128 KB sample chunk, one 128 KB main item), must
+ * stay below 2^31 as well, else SZ_ERR_INVALID_ARGUMENT.
  * d_workspace: >= sz_compress_workspace_bytes[_batched] bytes, contents
  * need not be initialised, clobbered (the encode workspace followed by a
  * synchronisation area: 256 bytes plus 2048 x (R + 1) + 320 bytes per
@@ -220,8 +221,9 @@ typedef struct {
     /* Smallest tensor (in elements) run through the one-launch kernel;
      * smaller ones take the separate calls' kernels (same results).  0 means
      * the defaults: 2^21 for BF16 (4 MiB tensors measured 15% faster fused,
-     * 2 MiB ones 10% slower) and no E5M2 tensor; 1 sends every tensor of
-     * either type through the one-launch kernel. */
+     * 2 MiB ones 10% slower), and for E5M2 2^22 in calls of at least 2^28
+     * elements (smaller calls measured as fast or faster separately); 1
+     * sends every tensor of either type through the one-launch kernel. */
     uint64_t fused_min_elements;
     /* Polls a waiting workgroup makes before it gives up; 0 means the
      * default, 2^20 (about a second).  A small value reaches the give-up

@@ -137,6 +137,32 @@ def test_default_size_threshold(sz, n):
     _check_against_oracle(x, BF16, stream, hist, cb)
 
 
+@pytest.mark.parametrize("count", [31, 32])
+def test_e5m2_default_call_size(sz, count):
+    """By default E5M2 tensors of 2^23 elements take the one-launch kernel
+    in a call of 32 of them (2^28 elements) and the separate kernels in a
+    call of 31: either way the streams equal those of the separate kernels
+    (forced with a fused_min_elements above n) and the oracle's."""
+    n = 1 << 23
+    base = kvsynth.e5m2_of(kvsynth.llama_kv(0, 0))
+    xs = [np.roll(base, 7919 * i) for i in range(count)]
+    say("e5m2 default call size", count)
+    dev = [to_dev(x) for x in xs]
+    default = sz.codec.BatchCodec(count, n, E5M2)
+    default.set_inputs(dev)
+    default.compress_fused()
+    separate = sz.codec.BatchCodec(count, n, E5M2)
+    separate.set_inputs(dev)
+    separate.compress_fused(options=sz.compress_options(fused_min_elements=n + 1))
+    torch.cuda.synchronize()
+    assert (default.fused_status.cpu().numpy() == 0).all()
+    assert torch.equal(default.sizes, separate.sizes) and torch.equal(default.hists, separate.hists)
+    for i in range(count):
+        assert torch.equal(default.stream(i), separate.stream(i)), i
+    for i in (0, count - 1):
+        _check_against_oracle(xs[i], E5M2, default.stream(i), default.hists[i], default.codebooks[i])
+
+
 def test_fused_is_deterministic(sz):
     x = to_dev(kvsynth.stress(3 << 20, seed=19))
     say("fused determinism")

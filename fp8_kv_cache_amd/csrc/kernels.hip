@@ -159,6 +159,15 @@ __device__ inline uint32_t pair_address(uint32_t x, uint32_t copy4) {
     return ((x << 3) & 0x3E0u) | (x & 0x7C00u) | copy4;
 }
 
+// The same for both pairs of x at once, the addresses in the two 16-bit
+// halves (a packed 16-bit shift keeps each half's bits in that half);
+// copy4x2 is the copy offset in both halves.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pair_addresses(uint32_t x, uint32_t copy4x2) {
+    const uint32_t t = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, x) << static_cast<uint16_t>(3));
+    return (t & 0x03E003E0u) | (x & 0x7C007C00u) | copy4x2;
+}
+
 template <uint32_t DT>
 __device__ inline void count_dword(char* lds, uint32_t w, uint32_t lane_bytes) {
     if (DT == kDtypeBF16) {
@@ -166,8 +175,9 @@ __device__ inline void count_dword(char* lds, uint32_t w, uint32_t lane_bytes) {
         atomicAdd(reinterpret_cast<uint32_t*>(lds + (((w >> 16) & 0x7F80u) | lane_bytes)), 1u);
     } else {
         // the pairs of bytes (0,1) and (2,3)
-        atomicAdd(reinterpret_cast<uint32_t*>(lds + pair_address(w, lane_bytes)), 1u);
-        atomicAdd(reinterpret_cast<uint32_t*>(lds + pair_address(w >> 16, lane_bytes)), 1u);
+        const uint32_t both = pair_addresses(w, lane_bytes | (lane_bytes << 16));
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + (both & 0xFFFFu)), 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(lds + (both >> 16)), 1u);
     }
 }
 
@@ -507,9 +517,9 @@ __device__ inline void encode_lane_e5m2_pairs(const uint32_t (&d)[8], char* hist
         uint32_t half[2];
 #pragma unroll
         for (uint32_t h = 0; h < 2; ++h) {   // dword 2q + h: pairs 4q + 2h and 4q + 2h + 1
-            const uint32_t x = d[2 * q + h];
-            const uint32_t c0 = atomicAdd(reinterpret_cast<uint32_t*>(hist + pair_address(x, copy4)), 1u);
-            const uint32_t c1 = atomicAdd(reinterpret_cast<uint32_t*>(hist + pair_address(x >> 16, copy4)), 1u);
+            const uint32_t both = pair_addresses(d[2 * q + h], copy4 | (copy4 << 16));
+            const uint32_t c0 = atomicAdd(reinterpret_cast<uint32_t*>(hist + (both & 0xFFFFu)), 1u);
+            const uint32_t c1 = atomicAdd(reinterpret_cast<uint32_t*>(hist + (both >> 16)), 1u);
             half[h] = perm(c1, c0, 0x0C0C0703u);   // the two code bytes
         }
         const uint32_t w = half[0] | (half[1] << 16);

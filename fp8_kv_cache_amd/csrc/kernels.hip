@@ -507,24 +507,30 @@ __device__ inline void encode_lane_e5m2(const uint32_t (&d)[8], uint32_t valid, 
 
 // E5M2, full lanes, counting as it encodes: each pair counter of the
 // histogram copies `hist` holds in its top byte the code byte of its pair
-// (the code of the first element in the low nibble), so one returning
-// increment per pair both counts it (in the low 24 bits, which never carry
-// into the code: an item counts 131072 elements) and looks its codes up.
+// (the code of the first element in the low nibble) and in its byte 2 the
+// pair's escape flags (bit 0: first element, bit 4: second), so one
+// returning increment per pair both counts it (in the low 16 bits, which
+// never carry into the flags: a counter takes at most 8192 increments per
+// item) and looks its codes up.
+__device__ inline uint32_t pair_counter_init(uint32_t c0, uint32_t c1) {
+    return ((c0 | (c1 << 4)) << 24) | ((c0 == kEscape ? 1u : 0u) << 16) | ((c1 == kEscape ? 1u : 0u) << 20);
+}
+
 __device__ inline void encode_lane_e5m2_pairs(const uint32_t (&d)[8], char* hist, uint32_t copy4,
                                               uint32_t (&sm)[3], uint32_t (&cw)[4], uint32_t (&esc)[4]) {
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
-        uint32_t half[2];
+        uint32_t codes[2], flags[2];
 #pragma unroll
         for (uint32_t h = 0; h < 2; ++h) {   // dword 2q + h: pairs 4q + 2h and 4q + 2h + 1
             const uint32_t both = pair_addresses(d[2 * q + h], copy4 | (copy4 << 16));
             const uint32_t c0 = atomicAdd(reinterpret_cast<uint32_t*>(hist + (both & 0xFFFFu)), 1u);
             const uint32_t c1 = atomicAdd(reinterpret_cast<uint32_t*>(hist + (both >> 16)), 1u);
-            half[h] = perm(c1, c0, 0x0C0C0703u);   // the two code bytes
+            codes[h] = perm(c1, c0, 0x0C0C0703u);   // the two code bytes
+            flags[h] = perm(c1, c0, 0x0C0C0602u);   // and their escape flags
         }
-        const uint32_t w = half[0] | (half[1] << 16);
-        cw[q] = w;
-        esc[q] = escape_nibbles(w);
+        cw[q] = codes[0] | (codes[1] << 16);
+        esc[q] = flags[0] | (flags[1] << 16);
     }
     sm_pack_e5m2(d, sm);
 }
@@ -1574,9 +1580,9 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     // wave 0 checks the codebook and builds the one code table all 16 waves
     // share, while the LDS histogram is cleared; then every wave counts its
     // blocks' exponents into the LDS copies and encodes them, and the item
-    // adds its counts to the tensor's histogram.  E5M2 writes the code of
-    // each element pair into the top byte of the pair's counters (one pair
-    // per thread) and counts inside the encode.
+    // adds its counts to the tensor's histogram.  E5M2 writes the codes and
+    // escape flags of each element pair into the top bytes of the pair's
+    // counters (one pair per thread) and counts inside the encode.
     constexpr uint32_t kRounds = item_blocks(DT) / kPassWaves;
     const Layout L = layout_of(n, DT);
     const uint64_t full_blocks = n / kBlockElems;
@@ -1600,7 +1606,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     if (pairs) {
         const uint8_t* tbl = reinterpret_cast<const uint8_t*>(s_tbl);
         const uint32_t x = tid & 31u, y = tid >> 5;
-        const uint32_t v = (tbl[x] | (static_cast<uint32_t>(tbl[y]) << 4)) << 24;
+        const uint32_t v = pair_counter_init(tbl[x], tbl[y]);
         uint4* run = reinterpret_cast<uint4*>(bins + ((x << 3) | (y << 8)));   // the pair's 8 counters
         run[0] = make_uint4(v, v, v, v);
         run[1] = make_uint4(v, v, v, v);
@@ -1665,7 +1671,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
     __syncthreads();
     const uint32_t copies = hist_replicas(a.enc.count);   // a power of two
     hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * (copies * t + (it.idx & (copies - 1))), phantom,
-                                 pairs ? 0x00FFFFFFu : ~0u);
+                                 pairs ? 0x0000FFFFu : ~0u);
 }
 
 // One workgroup per item: the ticket taken at the start fixes the item.

@@ -1950,18 +1950,18 @@ __device__ inline void transcode_list(const CompressArgs& a, const SyncView& sv,
 }
 
 // The full blocks of the escape-heavy tensors (list 2), encoded from the
-// input with their final codebooks exactly as k_encode does, split into
-// equal contiguous runs over the waves of the grid.
+// input with their final codebooks exactly as k_encode does, spread over
+// the waves of the grid.
 template <uint32_t DT>
 __device__ inline void encode_list(const CompressArgs& a, const SZ_GLOBAL uint32_t* list, uint32_t listed, uint64_t w,
                                    uint64_t waves, uint32_t* tbl_words, uint32_t* esc_words, uint32_t lane) {
     const uint64_t full_blocks = a.enc.n / kBlockElems;
     const uint64_t total = static_cast<uint64_t>(listed < a.enc.count ? listed : a.enc.count) * full_blocks;
-    const uint64_t per = (total + waves - 1) / waves;
-    const uint64_t first = w * per;
-    const uint64_t last = first + per < total ? first + per : total;
     const Layout L = layout_of(a.enc.n, DT);
-    for (uint64_t i = first; i < last; ++i) {
+    // grid-stride: the waves in flight at any moment cover consecutive
+    // blocks, as k_encode's do (contiguous runs per wave spread them over the
+    // whole tensor at once and measured slower)
+    for (uint64_t i = w; i < total; i += waves) {
         const uint32_t t = uniform(list[i / full_blocks * kEntryWords]);
         const uint64_t b = i % full_blocks;
         __builtin_amdgcn_wave_barrier();   // the previous block's code table is no longer read

@@ -534,41 +534,49 @@ def test_fused_recodes_dense_escape_blocks(sz, dt):
         assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), dt), x), i
 
 
-def _degenerate(n, kind):
+def _degenerate(n, kind, dt=BF16):
     """'zeros' and 'ones': a single exponent value.  'unsampled': exponents
-    127 and 126 everywhere, and 200 only in chunks the sample skips, so the
-    provisional codebook lacks a value the final one ranks third: its
-    elements are staged as escapes and recoded to code 2."""
+    127 and 126 everywhere (E5M2: 15 and 14), and 200 (E5M2: 25) only in
+    chunks the sample skips, so the provisional codebook lacks a value the
+    final one ranks third: its elements are staged as escapes and recoded to
+    code 2.  (E5M2 'zeros' puts every element pair on one pair counter: the
+    most increments one counter of the one-launch kernel can take.)"""
     if kind == "zeros":
-        return np.zeros(n, np.uint16)
+        return np.zeros(n, np.uint16 if dt == BF16 else np.uint8)
     if kind == "ones":
-        return np.full(n, 0x3F80, np.uint16)
+        return np.full(n, 0x3F80, np.uint16) if dt == BF16 else np.full(n, 0x3C, np.uint8)
     rng = np.random.default_rng(720)
-    e = np.where(rng.random(n) < 0.7, 127, 126)
-    e[~_sample_mask(n) & (rng.random(n) < 0.1)] = 200
+    hi, lo, rare = (127, 126, 200) if dt == BF16 else (15, 14, 25)
+    e = np.where(rng.random(n) < 0.7, hi, lo)
+    e[~_sample_mask(n, dt) & (rng.random(n) < 0.1)] = rare
     sign = rng.integers(0, 2, n)
-    mant = rng.integers(0, 1 << 7, n)
-    return ((sign << 15) | (e << 7) | mant).astype(np.uint16)
+    if dt == BF16:
+        return ((sign << 15) | (e << 7) | rng.integers(0, 1 << 7, n)).astype(np.uint16)
+    return ((sign << 7) | (e << 2) | rng.integers(0, 4, n)).astype(np.uint8)
 
 
+@pytest.mark.parametrize("dt", [BF16, E5M2])
 @pytest.mark.parametrize("kind", ["zeros", "ones", "unsampled"])
-def test_fused_degenerate_alphabets(sz, kind):
+def test_fused_degenerate_alphabets(sz, kind, dt):
     """Tensors with one to three exponent values over several items and a
     ragged end, between two ordinary tensors."""
     n = (1 << 21) + 777
-    xs = [kvsynth.single_tensor(n, seed=721), _degenerate(n, kind), kvsynth.single_tensor(n, seed=722)]
-    full, part = _codebooks(xs[1])
+    xs = [kvsynth.single_tensor(n, seed=721), _degenerate(n, kind, dt), kvsynth.single_tensor(n, seed=722)]
+    if dt == E5M2:
+        xs[0], xs[2] = kvsynth.e5m2_of(xs[0]), kvsynth.e5m2_of(xs[2])
+    full, part = _codebooks(xs[1], dt)
     if kind == "unsampled":
-        assert 200 in full.tolist() and 200 not in part.tolist()
+        rare = 200 if dt == BF16 else 25
+        assert rare in full.tolist() and rare not in part.tolist()
     else:
         assert np.array_equal(full, part)
-    say("fused degenerate", kind, n)
-    bc = sz.codec.BatchCodec(len(xs), n, BF16)
+    say("fused degenerate", kind, n, dt)
+    bc = sz.codec.BatchCodec(len(xs), n, dt)
     bc.set_inputs([to_dev(x) for x in xs])
     bc.compress_fused(options=every(sz))
     bc.decompress()
     torch.cuda.synchronize()
     assert (bc.fused_status.cpu().numpy() == 0).all()
     for i, x in enumerate(xs):
-        _check_against_oracle(x, BF16, bc.stream(i), bc.hists[i], bc.codebooks[i])
-        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i
+        _check_against_oracle(x, dt, bc.stream(i), bc.hists[i], bc.codebooks[i])
+        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), dt), x), i

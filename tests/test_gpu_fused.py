@@ -64,12 +64,12 @@ def test_fused_parity(sz, name):
 
 @pytest.mark.parametrize("dt", [BF16, E5M2])
 @pytest.mark.parametrize("n", [4096, 8 * 4096, 8 * 4096 + 1, 3 * 8 * 4096 + 4097, 25 * 4096 - 3,
-                               33 * 4096, (2 * 32 + 3) * 4096 + 77])
+                               33 * 4096, (2 * 32 + 3) * 4096 + 77, 65 * 4096, (2 * 64 + 7) * 4096 + 77])
 def test_fused_batched(sz, dt, n):
     """Several tensors; whole and partial workgroup items (a main item takes
-    16 BF16 or 32 E5M2 blocks, two per wave), an item whose waves run out
-    of blocks after their first, a partial last block: equal to the oracle
-    and to the three separate calls."""
+    16 BF16 blocks, one per wave, or 32 E5M2 blocks, two per wave), items
+    whose waves run out of blocks part way, a partial last block: equal to
+    the oracle and to the three separate calls."""
     xs = [kvsynth.stress(n, seed=400 + i) if i % 2 else kvsynth.single_tensor(n, seed=400 + i) for i in range(7)]
     if dt == E5M2:
         xs = [kvsynth.e5m2_of(x) for x in xs]
@@ -305,7 +305,7 @@ def test_fused_histogram_copies(sz, count, dt):
     histogram for calls of 1, 2-3, 4-7, 8-15 or more tensors (its main items
     add to copy idx mod R, the final item sums them): every batch size that
     selects each R gives the oracle's histograms, codebooks and streams."""
-    n = 40 * 4096 + 123   # 3 BF16 or 2 E5M2 main items per tensor, the last partial
+    n = 40 * 4096 + 123 if dt == BF16 else 70 * 4096 + 123   # 3 main items per tensor, the last partial
     xs = [kvsynth.stress(n, seed=800 + i) if i % 3 == 0 else kvsynth.single_tensor(n, seed=800 + i)
           for i in range(count)]
     if dt == E5M2:

@@ -1196,11 +1196,14 @@ __global__ void k_encode_empty(EncodeArgs a) {
 //     bins sum to the sampled element count; counts only grow), ranks the
 //     values (count descending, then value ascending) and publishes the
 //     first 15 as the provisional codebook.
-//   main item (16 blocks, one per wave): loads its blocks and the
-//     provisional codebook (waiting for it if it is not complete yet), counts
-//     the blocks into the tensor's full histogram (the item that holds a
-//     partial last block counts that block too) and encodes its full blocks
-//     with the provisional codebook exactly as k_encode does.
+//   main item (128 KB: 16 BF16 blocks, one per wave, or 32 E5M2 blocks,
+//     two per wave): loads its blocks and the provisional codebook (waiting
+//     for it if it is not complete yet), counts the blocks into the tensor's
+//     full histogram (the item that holds a partial last block counts that
+//     block too) and encodes its full blocks with the provisional codebook,
+//     into the same bytes as k_encode (E5M2 counts and looks codes up with
+//     one returning LDS increment per element pair, see
+//     encode_lane_e5m2_pairs).
 //   final item: polls the full histogram until it is complete, writes the
 //     histogram and codebook outputs and records whether the provisional
 //     codebook is the final one.

@@ -65,11 +65,19 @@ def test_source_hash_changes_with_every_kernel_source(tmp_path, monkeypatch):
     base = bench.kernel_source_hash()
     assert base == bench.kernel_source_hash()
     for path in copies:
-        with open(path, "ab") as f:
-            f.write(b"\n")
+        with open(path, "a") as f:   # a comment and blank lines leave the code, and the hash, as they were
+            f.write("\n// a comment\n/* another */\n\n")
+        assert bench.kernel_source_hash() == base
+        with open(path, "a") as f:
+            f.write("int one_more_declaration;\n")
         changed = bench.kernel_source_hash()
         assert changed != base
         base = changed
+
+
+def test_code_only_strips_comments_but_not_literals():
+    src = 'int a = 1; // c\n/* b\n c */ const char* s = "x // y /* z"; char q = \'"\';\n   int   b;'
+    assert bench.code_only(src) == 'int a = 1; const char* s = "x // y /* z"; char q = \'"\'; int b;'
 
 
 def test_committed_traffic_covers_the_roofline_kernels():

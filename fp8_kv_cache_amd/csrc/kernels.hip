@@ -1214,22 +1214,27 @@ __global__ void k_encode_empty(EncodeArgs a) {
 // last block of a tensor is left to k_encode_tail, which runs with the
 // final codebook.
 //
-// Work items are handed out by a ticket counter in the order workgroups
-// start, in stages (pass_plan): stage s holds the sample items of tensor s,
-// the provisional item of tensor s - 1, the main items of tensor s - lag
-// and the final item of tensor s - lag - 1.  Every wait is for items with
-// earlier tickets (a provisional item for sample items, a main item for
-// the provisional item, a final item for main items and the provisional
-// item), and sample items never wait, so every awaited workgroup is already
-// running or done: the launch always makes progress, whatever else shares
-// the GPU.  The waits are still bounded: after spin_limit polls, or once
-// any workgroup has given up, a workgroup sets its tensor's status, zeroes
-// its blocks' escape counts and leaves.
+// Workgroup i runs item i of a fixed schedule, in stages (pass_plan):
+// stage s holds the sample items of tensor s, the provisional item of
+// tensor s - 1, the main items of tensor s - lag and the final item of
+// tensor s - lag - 1.  Every wait is for items of lower workgroup ids (a
+// provisional item for sample items, a main item for the provisional item,
+// a final item for main items and the provisional item), and sample items
+// never wait.  The dispatcher starts each XCD's workgroups in id order, so
+// the lowest unfinished item is either running, or the next to start on
+// its XCD once that XCD's lower ids, all finished, have left; it waits only
+// for lower ids, all finished: the launch makes progress whatever else
+// shares the GPU.  (Items used to come from a ticket counter, which assumes
+// nothing of the dispatch order; under load its one address queued the
+// atomics about 4 us, a fifth of a main item.)  The waits are bounded all
+// the same: after spin_limit polls, or once any workgroup has given up, a
+// workgroup sets its tensor's status, zeroes its blocks' escape counts and
+// leaves.
 //
 // Signalling between workgroups uses no cache-wide maintenance.  Everything
 // one workgroup tells another inside the kernel travels through relaxed
 // agent-scope atomics, which are coherent across the XCDs' L2 caches:
-// read-modify-writes (histogram counts, tickets, the list) or sc1 loads and
+// read-modify-writes (histogram counts, the list) or sc1 loads and
 // stores (the abort word, the provisional codebook).  The provisional
 // codebook needs no separate flag and no store order: a reading of its
 // four words is complete exactly when its 15 bytes differ (see
@@ -1240,7 +1245,6 @@ __global__ void k_encode_empty(EncodeArgs a) {
 struct SyncView {
     SZ_GLOBAL uint64_t* hist;     // count x hist_replicas(count) x 256, whole tensors
     SZ_GLOBAL uint64_t* sample;   // count x 256, sampled chunks
-    SZ_GLOBAL uint32_t* ticket;
     SZ_GLOBAL uint32_t* abort;
     SZ_GLOBAL uint32_t* listed;   // [kLists]: entries in use of the lists
     SZ_GLOBAL uint32_t* records;  // per tensor 32 words, see kRec*
@@ -1263,9 +1267,8 @@ __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     v.hist = gptr(reinterpret_cast<uint64_t*>(base));
     v.sample = v.hist + 256ull * hist_replicas(count) * count;
     SZ_GLOBAL uint32_t* w = gptr(reinterpret_cast<uint32_t*>(base + sync_hist_bytes(count)));
-    v.ticket = w;
-    v.abort = w + 1;
-    v.listed = w + 2;
+    v.abort = w;
+    v.listed = w + 1;
     v.records = w + 64;
     v.list = v.records + 32ull * count;   // kLists x count entries
     return v;
@@ -1677,7 +1680,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
                                  pairs ? 0x0000FFFFu : ~0u);
 }
 
-// One workgroup per item: the ticket taken at the start fixes the item.
+// One workgroup per item: workgroup i runs item i of the schedule.
 template <uint32_t DT>
 __global__ __launch_bounds__(kPassThreads, 8) void k_compress(CompressArgs a) {
     static_assert(kPassThreads % 256 == 0 && Geometry<DT>::kDomain % (kPassThreads / 256) == 0, "rank split");
@@ -1690,8 +1693,7 @@ __global__ __launch_bounds__(kPassThreads, 8) void k_compress(CompressArgs a) {
     if (tid == 0) {
         // one thread locates the item (the schedule arithmetic stays out of
         // the scalar registers the rest of the kernel needs)
-        const uint32_t ticket = __hip_atomic_fetch_add(sv.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const PassItem it = pass_item(ticket, pass_plan(a));
+        const PassItem it = pass_item(blockIdx.x, pass_plan(a));
         s_word[0] = it.kind;
         s_word[14] = it.t;
         s_word[15] = it.idx;

@@ -116,7 +116,7 @@ struct EncodeArgs {
 //   u64 hist[count][R][256]  exponent counts of the whole tensor, in R =
 //                            hist_replicas(count) copies
 //   u64 sample[count][256]   exponent counts of the sampled chunks
-//   u32 ticket, u32 abort, u32 listed[3]   (padded to 256 bytes)
+//   u32 abort, u32 listed[3]   (padded to 256 bytes)
 //   per tensor t a 128-byte record of u32 words: [0..3] the provisional
 //   codebook (published once its bytes 0..14 are distinct; byte 15 is 1
 //   when the tensor is escape-heavy, see kProvisionalCountOnly), [8] the
@@ -192,7 +192,8 @@ struct CompressArgs {
     uint32_t sample_total;    // elements the sample items of one tensor count (n < 2^32)
 };
 
-// Work items of the one-launch compress, in ticket order (see k_compress).
+// Work items of the one-launch compress, in schedule order: workgroup i
+// runs item i (see k_compress).
 enum : uint32_t { kItemSample = 0, kItemProvisional = 1, kItemMain = 2, kItemFinal = 3, kItemNone = 4 };
 constexpr uint32_t kItemKinds = 4;
 
@@ -224,8 +225,8 @@ __host__ __device__ inline PassPlan pass_plan(const CompressArgs& a) {
     return p;
 }
 
-// Ticket k -> item.  Stage sizes are constant between consecutive values
-// of {delay[j], delay[j] + T}, so the ticket is located region by region
+// Item k of the schedule.  Stage sizes are constant between consecutive
+// values of {delay[j], delay[j] + T}, so k is located region by region
 // (fixed-size loops: no dynamically indexed arrays in device code).
 __host__ __device__ inline PassItem pass_item(uint64_t k, const PassPlan& p) {
     constexpr uint32_t kEdges = 2 * kItemKinds;

@@ -191,8 +191,9 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * E5M2 tensors under 2^22 elements or in calls of fewer than 2^28 elements
  * in all (measured faster with the separate kernels).
  *
- * Work inside the kernel waits only for work handed out before it, so a
- * call always makes progress, whatever else shares the GPU.  Waits are
+ * Work inside the kernel waits only for work of lower workgroup ids, which
+ * the dispatcher starts first on each XCD, so a call makes progress
+ * whatever else shares the GPU.  Waits are
  * bounded nonetheless: a workgroup that has polled the options' spin_limit
  * times without progress (about a second) gives up, and so does every
  * workgroup after it; each tensor they belong to gets SZ_ERR_TIMEOUT in

@@ -2,11 +2,11 @@
 // in sz_internal.h, the functions the kernel calls): for every shape in a
 // grid of (tensors, sample items, main items, lag -- up to 5 stages more
 // than the tensor count, since a lone large tensor runs with the minimum
-// lag of 4), every work item appears exactly once among the tickets,
-// nothing lies past the last ticket, and
+// lag of 4), every work item appears exactly once among the item indices (workgroup ids),
+// nothing lies past the last one, and
 // for each tensor its sample items come before its provisional item, which
 // comes before its main items, which come before its final item -- the
-// order the kernel's waits rely on (each waits only for earlier tickets).
+// order the kernel's waits rely on (each waits only for lower workgroup ids).
 // Prints "ok <shapes checked>".
 #include <cstdio>
 #include <map>

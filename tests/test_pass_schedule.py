@@ -1,8 +1,8 @@
-"""The one-launch compress hands out work items through a ticket counter in
-a fixed schedule (pass_item in fp8_kv_cache_amd/csrc/sz_internal.h).  Its
-waits are deadlock-free only if every item appears once and each tensor's
-sample items precede its provisional codebook item, which precedes its main
-items, which precede its final codebook item.
+"""Workgroup i of the one-launch compress runs item i of a fixed schedule
+(pass_item in fp8_kv_cache_amd/csrc/sz_internal.h).  Its waits are
+deadlock-free only if every item appears once and each tensor's sample
+items precede its provisional codebook item, which precedes its main items,
+which precede its final codebook item.
 The same header the kernel is built from is compiled for the host with g++
 and the schedule is enumerated over a grid of shapes (no GPU needed)."""
 import os

@@ -33,8 +33,21 @@ constexpr auto block_scan = sz::block_scan_excl;
 
 constexpr uint32_t kThreads = 256;
 constexpr uint32_t kRowStride = 520;            // LDS stride of a 512-byte input row: 8 spare bytes
-constexpr uint32_t kLds = 32 * kRowStride;      // 16640 bytes: 32 padded rows, or one plane image
 constexpr uint32_t kBitmap = kChunk / 16;       // RZE_2 bitmap bytes of a full chunk (8192 words)
+// A full chunk's RZE_2 words sit in LDS after the bitmap with 4 spare bytes
+// after every 64: thread t's run of non-zero words starts where the counts
+// of the threads before it end, so when every thread holds the same count
+// (a plane of all-zero or all-non-zero words, as 4-bit codes give) the runs
+// are a fixed number of dwords apart, and a 16-dword stride would put 16
+// lanes on one bank; with the spare dword the stride is odd.
+__device__ inline uint32_t word_at(uint32_t w) { return kBitmap + 2 * w + 4 * (w >> 5); }
+constexpr uint32_t kPaddedPayload = kBitmap + (kChunk - kBitmap) / 64 * 68;   // 17344 bytes
+constexpr uint32_t kLds = kPaddedPayload > 32 * kRowStride ? kPaddedPayload : 32 * kRowStride;
+// Payload vector v of a full chunk (16 bytes at 16 v) in LDS: 4 dwords at
+// byte `payload_at(v)` on, contiguous, 4-byte aligned.
+__device__ inline uint32_t payload_at(uint32_t v) {
+    return 16 * v < kBitmap ? 16 * v : word_at((16 * v - kBitmap) / 2);
+}
 
 struct Lds {
     alignas(16) uint8_t buf[kLds];
@@ -203,15 +216,15 @@ __device__ inline uint32_t rze_full(Lds& s, uint32_t tid) {
     if (!kWrite || size >= kChunk) return size < kChunk ? size : kChunk;
     __syncthreads();                                   // every plane word is in registers
     reinterpret_cast<uint32_t*>(s.buf)[tid] = flags;   // bitmap dword t covers words 32t..32t+31
-    uint16_t* words = reinterpret_cast<uint16_t*>(s.buf + kBitmap);
     // word i's slot: the non-zero words before it, counted with a masked popcount
 #pragma unroll
     for (uint32_t i = 0; i < 32; ++i) {
         if (flags & (1u << i))
-            words[base + __builtin_popcount(flags & ((1u << i) - 1u))] = static_cast<uint16_t>(w[i / 2] >> (16 * (i & 1)));
+            *reinterpret_cast<uint16_t*>(s.buf + word_at(base + __builtin_popcount(flags & ((1u << i) - 1u)))) =
+                static_cast<uint16_t>(w[i / 2] >> (16 * (i & 1)));
     }
     const uint32_t padded = static_cast<uint32_t>(align16(size));
-    if (tid < 8 && size + 2 * tid < padded) reinterpret_cast<uint16_t*>(s.buf)[size / 2 + tid] = 0;
+    if (tid < 8 && size + 2 * tid < padded) *reinterpret_cast<uint16_t*>(s.buf + word_at((size - kBitmap) / 2 + tid)) = 0;
     __syncthreads();
     return size;
 }
@@ -384,9 +397,18 @@ __global__ __launch_bounds__(kThreads) void k_lc_write(EncodeArgs a) {
         forward_partial(x, L, s, tid);
         rze_partial<true>(s, L, tid);
     }
-    // the payload and its padding sit in buf[0, A16(size))
-    for (uint32_t v = tid; v < align16(size) / 16; v += kThreads)
-        __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(s.buf)[v], (SZ_GLOBAL u32x4*)(out + 16 * v));
+    // the payload and its padding: buf[0, A16(size)), a full chunk's words
+    // with their spare bytes
+    for (uint32_t v = tid; v < align16(size) / 16; v += kThreads) {
+        u32x4 x;
+        if (L == kChunk) {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(s.buf + payload_at(v));
+            x = u32x4{p[0], p[1], p[2], p[3]};
+        } else {
+            x = reinterpret_cast<const u32x4*>(s.buf)[v];
+        }
+        __builtin_nontemporal_store(x, (SZ_GLOBAL u32x4*)(out + 16 * v));
+    }
 }
 
 // ----------------------------------------------------------------- decode
@@ -424,8 +446,15 @@ __global__ __launch_bounds__(kThreads, 8) void k_lc_decode(DecodeArgs a) {
         }
         return;
     }
-    for (uint32_t v = tid; v < align16(size) / 16; v += kThreads)
-        reinterpret_cast<u32x4*>(s.buf)[v] = __builtin_nontemporal_load((const SZ_GLOBAL u32x4*)(in + 16 * v));
+    for (uint32_t v = tid; v < align16(size) / 16; v += kThreads) {
+        const u32x4 x = __builtin_nontemporal_load((const SZ_GLOBAL u32x4*)(in + 16 * v));
+        if (L == kChunk) {
+            uint32_t* p = reinterpret_cast<uint32_t*>(s.buf + payload_at(v));
+            p[0] = x.x; p[1] = x.y; p[2] = x.z; p[3] = x.w;
+        } else {
+            reinterpret_cast<u32x4*>(s.buf)[v] = x;
+        }
+    }
     __syncthreads();
     const uint32_t V = L / 2, nb = (V + 7) / 8;
     // this thread's 32 words m = 32t + i: flags from the bitmap (bits m >= V cleared)
@@ -443,8 +472,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_lc_decode(DecodeArgs a) {
     // read phase: the thread's words from the payload; word i's slot is the
     // number of non-zero words before it (a masked popcount)
     uint32_t w[16];
-    if (L == kChunk) {                                  // words start 2-byte aligned after the 1024-byte bitmap
-        const uint16_t* words = reinterpret_cast<const uint16_t*>(s.buf + kBitmap);
+    if (L == kChunk) {                                  // words after the 1024-byte bitmap, spare bytes between
 #pragma unroll
         for (uint32_t d = 0; d < 16; ++d) {
             uint32_t v = 0;
@@ -452,7 +480,9 @@ __global__ __launch_bounds__(kThreads, 8) void k_lc_decode(DecodeArgs a) {
             for (uint32_t h = 0; h < 2; ++h) {
                 const uint32_t i = 2 * d + h;
                 if (flags & (1u << i))
-                    v |= static_cast<uint32_t>(words[base + __builtin_popcount(flags & ((1u << i) - 1u))]) << (16 * h);
+                    v |= static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(
+                             s.buf + word_at(base + __builtin_popcount(flags & ((1u << i) - 1u)))))
+                         << (16 * h);
             }
             w[d] = v;
         }

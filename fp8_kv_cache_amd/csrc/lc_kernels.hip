@@ -42,7 +42,16 @@ constexpr uint32_t kBitmap = kChunk / 16;       // RZE_2 bitmap bytes of a full 
 // lanes on one bank; with the spare dword the stride is odd.
 __device__ inline uint32_t word_at(uint32_t w) { return kBitmap + 2 * w + 4 * (w >> 5); }
 constexpr uint32_t kPaddedPayload = kBitmap + (kChunk - kBitmap) / 64 * 68;   // 17344 bytes
-constexpr uint32_t kLds = kPaddedPayload > 32 * kRowStride ? kPaddedPayload : 32 * kRowStride;
+// A full chunk's plane image z sits in LDS with 16 spare bytes after every
+// 256: then neither the transposes (lane (I, c) of a wave takes dword
+// 64(8c + k) + 8(4g + q) + p, the two halves c apart by 8 plane rows) nor a
+// thread's 64-byte read of its own plane words (lanes 64 bytes apart) put
+// two lanes of a wave on one of the 64 banks; without them the first
+// doubles and the second quadruples the cycles of each access.
+__device__ inline uint32_t plane_at(uint32_t z) { return z + 16 * (z >> 8); }
+constexpr uint32_t kPaddedPlane = kChunk / 256 * 272;   // 17408 bytes
+constexpr uint32_t kLds = kPaddedPlane;                  // also holds the padded payload and the 32 input rows
+static_assert(kLds >= kPaddedPayload && kLds >= 32 * kRowStride, "LDS buffer");
 // Payload vector v of a full chunk (16 bytes at 16 v) in LDS: 4 dwords at
 // byte `payload_at(v)` on, contiguous, 4-byte aligned.
 __device__ inline uint32_t payload_at(uint32_t v) {
@@ -136,8 +145,8 @@ __device__ inline void stage_input(const SZ_GLOBAL uint8_t* x, Lds& s, uint32_t 
     }
 }
 
-// Padded input rows in LDS -> plane image z = BIT_8(TUPL8_1(x)) in
-// buf[0, 16384).  Barriers inside; every thread calls it.
+// Padded input rows in LDS -> plane image z = BIT_8(TUPL8_1(x)) in buf
+// (byte z at plane_at(z)).  Barriers inside; every thread calls it.
 __device__ inline void forward_full(Lds& s, uint32_t tid) {
     const uint32_t I = tid & 31, c = tid >> 5, q = I & 3, p = I >> 2;
     uint64_t L[8];
@@ -151,13 +160,14 @@ __device__ inline void forward_full(Lds& s, uint32_t tid) {
 #pragma unroll
         for (uint32_t g = 0; g < 2; ++g) {
             const uint32_t v = quad_transpose(static_cast<uint32_t>(L[k] >> (32 * g)), q);
-            *reinterpret_cast<uint32_t*>(s.buf + (8 * c + k) * 256 + 32 * (4 * g + q) + 4 * p) = v;
+            *reinterpret_cast<uint32_t*>(s.buf + plane_at((8 * c + k) * 256 + 32 * (4 * g + q) + 4 * p)) = v;
         }
     }
     __syncthreads();
 }
 
-// Plane image in buf[0, 16384) -> input bytes, written to out (global).
+// Plane image in buf (byte z at plane_at(z)) -> input bytes, written to
+// out (global).
 __device__ inline void inverse_full(Lds& s, uint32_t tid, SZ_GLOBAL uint8_t* out) {
     const uint32_t I = tid & 31, c = tid >> 5, q = I & 3, p = I >> 2;
     uint64_t L[8];
@@ -166,7 +176,7 @@ __device__ inline void inverse_full(Lds& s, uint32_t tid, SZ_GLOBAL uint8_t* out
         uint64_t w = 0;
 #pragma unroll
         for (uint32_t g = 0; g < 2; ++g) {
-            const uint32_t v = *reinterpret_cast<const uint32_t*>(s.buf + (8 * c + k) * 256 + 32 * (4 * g + q) + 4 * p);
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(s.buf + plane_at((8 * c + k) * 256 + 32 * (4 * g + q) + 4 * p));
             w |= static_cast<uint64_t>(quad_transpose(v, q)) << (32 * g);
         }
         L[k] = w;
@@ -193,7 +203,7 @@ __device__ inline uint32_t read_words(const Lds& s, uint32_t tid, uint32_t (&w)[
     uint32_t flags = 0;
 #pragma unroll
     for (uint32_t v = 0; v < 4; ++v) {
-        const u32x4 x = reinterpret_cast<const u32x4*>(s.buf)[4 * tid + v];
+        const u32x4 x = *reinterpret_cast<const u32x4*>(s.buf + plane_at(16 * (4 * tid + v)));
         w[4 * v] = x.x; w[4 * v + 1] = x.y; w[4 * v + 2] = x.z; w[4 * v + 3] = x.w;
     }
 #pragma unroll
@@ -506,7 +516,8 @@ __global__ __launch_bounds__(kThreads, 8) void k_lc_decode(DecodeArgs a) {
     if (L == kChunk) {
 #pragma unroll
         for (uint32_t v = 0; v < 4; ++v)
-            reinterpret_cast<u32x4*>(s.buf)[4 * tid + v] = u32x4{w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]};
+            *reinterpret_cast<u32x4*>(s.buf + plane_at(16 * (4 * tid + v))) =
+                u32x4{w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]};
         __syncthreads();
         inverse_full(s, tid, out);
         return;

@@ -200,6 +200,20 @@ __device__ inline void hist_clear(uint32_t* bins, uint32_t tid) {
         *reinterpret_cast<uint4*>(bins + i) = make_uint4(0, 0, 0, 0);
 }
 
+// A word another workgroup of the same launch reads once it has seen the
+// counts that follow it complete: stored with a device-scope relaxed atomic
+// store (written through this XCD's L2), which must have completed
+// (vmcnt 0; the "memory" clobber keeps the compiler from moving the store
+// past the wait) before the thread's counting atomics are issued; the
+// reader loads it with a device-scope relaxed atomic load.  An agent-scope
+// release fence would order it as well, but writes back the whole L2 at
+// every fence: one per item of an escape-heavy tensor took its compress
+// from 112 to 800 us.
+__device__ inline void store_before_count(SZ_GLOBAL uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Fold the copies and add the sums to the tensor's u64 histogram.  Every
 // thread of the NT-thread workgroup calls it, after a barrier; BF16 folds
 // with the first 256.  `unpaired` is the number of phantom zero exponents
@@ -207,10 +221,13 @@ __device__ inline void hist_clear(uint32_t* bins, uint32_t tid) {
 // (e, 0); both types: zero padding counted past the end of a tensor); they
 // are taken off bin 0.  Rotating the start keeps the lanes of a wave on
 // distinct banks.  E5M2 counters are read through `mask` (the one-launch
-// compress keeps a code byte in their top byte).
+// compress keeps a code byte in their top byte).  With `row` set, value v's
+// sum is also stored at row[v * stride] before it is added (the one-launch
+// compress's per-item histograms of escape-heavy tensors): see
+// store_before_count.
 template <uint32_t DT, uint32_t NT = kThreads>
 __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64_t* hist, uint32_t unpaired,
-                                  uint32_t mask = ~0u) {
+                                  uint32_t mask = ~0u, SZ_GLOBAL uint32_t* row = nullptr, uint32_t stride = 0) {
     static_assert(NT >= 256, "one folding thread per bin");
     const bool folds = NT == 256 || tid < 256;
     if constexpr (DT == kDtypeBF16) {
@@ -218,6 +235,7 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
         uint32_t sum = tid == 0 ? 0u - unpaired : 0u;
 #pragma unroll 8
         for (uint32_t j = 0; j < 32; ++j) sum += bins[tid * 32 + ((j + tid) & 31u)];
+        if (row) store_before_count(row + static_cast<uint64_t>(tid) * stride, sum);
         if (sum) __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
     } else {
@@ -253,6 +271,7 @@ __device__ inline void hist_flush(uint32_t* bins, uint32_t tid, SZ_GLOBAL uint64
         }
         __syncthreads();
         const uint32_t sum = tid < 32 ? bins[tid] - (tid == 0 ? unpaired : 0u) : 0u;
+        if (row && tid < 32) store_before_count(row + static_cast<uint64_t>(tid) * stride, sum);
         if (sum)
             __hip_atomic_fetch_add(hist + tid, static_cast<uint64_t>(sum), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -398,6 +417,10 @@ __global__ __launch_bounds__(kThreads) void k_histogram_sampled(HistArgs a) {
 // a give-up) gets a zero magic, so that decoding it reports a corrupt
 // stream instead of returning wrong data.
 __device__ inline bool compress_gave_up(const EncodeArgs& a, uint32_t t);
+// An escape-heavy tensor of the one-launch compress, once its final item has
+// run: its escapes are written straight to their place in the stream (not
+// staged), and `escapes` is its escape count.
+__device__ inline bool escapes_in_place(const EncodeArgs& a, uint32_t t, uint32_t& escapes);
 
 __device__ inline void write_header(SZ_GLOBAL uint8_t* dst, const Layout& L, uint32_t dtype,
                                     const SZ_GLOBAL uint8_t* cb, uint64_t escapes, SZ_GLOBAL uint64_t* out_bytes,
@@ -562,6 +585,7 @@ __device__ inline uint32_t exponent_of(const uint32_t (&d)[Geometry<DT>::kInWord
     }
 }
 
+
 template <uint32_t DT>
 __device__ inline void stage_escapes(SZ_GLOBAL uint8_t* esc_out, uint32_t* esc_lds,
                                      const uint32_t (&d)[Geometry<DT>::kSubs][Geometry<DT>::kInWords],
@@ -629,6 +653,7 @@ __device__ inline void stage_escapes(SZ_GLOBAL uint8_t* esc_out, uint32_t* esc_l
     __builtin_amdgcn_wave_barrier();   // the buffer may be reused once every lane has read it
 }
 
+
 // A wave's share of block b: sub-chunk j, lane l holds elements
 // [4096b + j * 64 * kLaneElems + l * kLaneElems, ... + kLaneElems).
 template <uint32_t DT>
@@ -676,6 +701,30 @@ __device__ inline const uint8_t* build_code_table(uint32_t* tbl_words, uint32_t 
     return tbl;
 }
 
+// One lane's share of a sub-chunk, from element elem0 on: its sign/mantissa
+// and code words stored to the planes of stream dst (vectors at or beyond
+// a padded plane's end are not stored).
+template <uint32_t DT, bool kFull>
+__device__ inline void store_lane_planes(const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t elem0,
+                                         const uint32_t (&sm)[Geometry<DT>::kSmWords],
+                                         const uint32_t (&cw)[Geometry<DT>::kCodeWords]) {
+    const uint64_t code_off = elem0 / 2;
+    if constexpr (DT == kDtypeBF16) {
+        if (kFull || elem0 < L.sm_region)
+            __builtin_nontemporal_store(u32x2{sm[0], sm[1]}, (SZ_GLOBAL u32x2*)(dst + L.sm_at + elem0));
+        if (kFull || code_off < L.code_region)
+            __builtin_nontemporal_store(cw[0], (SZ_GLOBAL uint32_t*)(dst + L.code_at + code_off));
+    } else {
+        const uint64_t sm_off = elem0 / 32 * 12;
+        SZ_GLOBAL uint32_t* smp = (SZ_GLOBAL uint32_t*)(dst + L.sm_at + sm_off);
+#pragma unroll
+        for (uint32_t i = 0; i < 3; ++i)
+            if (kFull || sm_off + 4 * i < L.sm_region) __builtin_nontemporal_store(sm[i], smp + i);
+        if (kFull || code_off < L.code_region)
+            __builtin_nontemporal_store(u32x4{cw[0], cw[1], cw[2], cw[3]}, (SZ_GLOBAL u32x4*)(dst + L.code_at + code_off));
+    }
+}
+
 // Encode block b from its registers into stream dst with the code table
 // tbl: planes, the block's escape count and its staged escape bytes (flat
 // = the block's index over all tensors).  esc_lds: the wave's 4096 bytes
@@ -714,25 +763,8 @@ __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GL
 
     // planes; vectors at or beyond the padded plane end are not stored
 #pragma unroll
-    for (uint32_t j = 0; j < G::kSubs; ++j) {
-        const uint64_t elem0 = blk0 + j * kSubElems + lane * G::kLaneElems;
-        const uint64_t code_off = elem0 / 2;
-        if constexpr (DT == kDtypeBF16) {
-            if (kFull || elem0 < L.sm_region)
-                __builtin_nontemporal_store(u32x2{sm[j][0], sm[j][1]}, (SZ_GLOBAL u32x2*)(dst + L.sm_at + elem0));
-            if (kFull || code_off < L.code_region)
-                __builtin_nontemporal_store(cw[j][0], (SZ_GLOBAL uint32_t*)(dst + L.code_at + code_off));
-        } else {
-            const uint64_t sm_off = elem0 / 32 * 12;
-            SZ_GLOBAL uint32_t* smp = (SZ_GLOBAL uint32_t*)(dst + L.sm_at + sm_off);
-#pragma unroll
-            for (uint32_t i = 0; i < 3; ++i)
-                if (kFull || sm_off + 4 * i < L.sm_region) __builtin_nontemporal_store(sm[j][i], smp + i);
-            if (kFull || code_off < L.code_region)
-                __builtin_nontemporal_store(u32x4{cw[j][0], cw[j][1], cw[j][2], cw[j][3]},
-                                            (SZ_GLOBAL u32x4*)(dst + L.code_at + code_off));
-        }
-    }
+    for (uint32_t j = 0; j < G::kSubs; ++j)
+        store_lane_planes<DT, kFull>(L, dst, blk0 + j * kSubElems + lane * G::kLaneElems, sm[j], cw[j]);
 
     // Escape ranks inside the block: element order is (sub-chunk, lane,
     // element), so lane l's first escape in sub-chunk j has rank
@@ -754,6 +786,121 @@ __device__ inline void encode_loaded(const EncodeArgs& a, const Layout& L, SZ_GL
 
     // escape bytes, in element order, staged at their rank inside the block
     stage_escapes<DT>(gptr(a.staging) + flat * kBlockElems, esc_lds, d, esc, cnt, base, uniform(block_total), lane);
+}
+
+// Bytes [16 - s, 32 - s) of the 32-byte sequence prev ++ cur (0 < s < 16).
+__device__ inline u32x4 funnel16(const u32x4& prev, const u32x4& cur, uint32_t s) {
+    const uint32_t q[8] = {prev.x, prev.y, prev.z, prev.w, cur.x, cur.y, cur.z, cur.w};
+    const uint32_t k = 16 - s, j = k >> 2, r = k & 3;   // j in 0..3 (per lane)
+    uint32_t x[5];
+#pragma unroll
+    for (uint32_t i = 0; i < 5; ++i)
+        x[i] = j == 0 ? q[i] : j == 1 ? q[i + 1] : j == 2 ? q[i + 2] : q[i + 3];
+    return u32x4{__builtin_amdgcn_alignbyte(x[1], x[0], r), __builtin_amdgcn_alignbyte(x[2], x[1], r),
+                 __builtin_amdgcn_alignbyte(x[3], x[2], r), __builtin_amdgcn_alignbyte(x[4], x[3], r)};
+}
+
+// Escapes written straight to their place in the stream, in two steps, so
+// that nothing but the count has to be kept in between: encode_gather
+// encodes block b (registers d) sub-chunk by sub-chunk, storing its planes
+// and putting its escape bytes at their rank inside the block into the
+// wave's LDS (esc_lds, kEscLdsWords words), and returns the block's escape
+// count (wave-uniform); place_escapes then stores them to esc_out, which may
+// sit at any byte.  Rank r goes to aligned window (r + s) / 16, s = esc_out &
+// 15.  Windows wholly inside the block's range are stored as 16-byte
+// vectors, each joined from two adjacent LDS vectors by a byte funnel shift.
+// The first and last windows, shared with the neighbouring blocks' escapes,
+// are stored a byte a lane, so each is one coalesced store (with one lane
+// storing a window's bytes in turn, each byte was a write request of its
+// own, and the placement took 65 us of the stress tensor's 0.40 ms compress).
+constexpr uint32_t kEscLdsWords = kBlockElems / 4;
+
+template <uint32_t DT, bool kFull>
+__device__ inline uint32_t encode_gather(const Layout& L, SZ_GLOBAL uint8_t* dst, uint64_t b, uint32_t lane,
+                                         const uint8_t* tbl, const BlockRegs<DT>& d, uint32_t* esc_lds) {
+    using G = Geometry<DT>;
+    constexpr uint32_t kSubElems = kWaveSize * G::kLaneElems;
+    uint8_t* gather = reinterpret_cast<uint8_t*>(esc_lds);
+    uint32_t total = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < G::kSubs; ++j) {
+        const uint64_t elem0 = b * kBlockElems + j * kSubElems + lane * G::kLaneElems;
+        const uint32_t valid = kFull ? G::kLaneElems
+                               : elem0 >= L.n ? 0u
+                               : (L.n - elem0 >= G::kLaneElems ? G::kLaneElems : static_cast<uint32_t>(L.n - elem0));
+        uint32_t sm[G::kSmWords], cw[G::kCodeWords], esc[G::kCodeWords];
+        if constexpr (DT == kDtypeBF16)
+            encode_lane_bf16(d[j], valid, tbl, sm, cw, esc);
+        else
+            encode_lane_e5m2(d[j], valid, tbl, sm, cw, esc);
+        store_lane_planes<DT, kFull>(L, dst, elem0, sm, cw);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (uint32_t q = 0; q < G::kCodeWords; ++q) cnt += __builtin_popcount(esc[q]);
+        const uint32_t incl = wave_scan_incl(cnt);
+        uint32_t rank = total + incl - cnt;
+        const uint32_t sub_total = uniform(__builtin_amdgcn_readlane(incl, 63));
+        total += sub_total;
+        if (sub_total <= kWaveSize) {
+            // sparse: each lane walks its escape flags
+#pragma unroll
+            for (uint32_t q = 0; q < G::kCodeWords; ++q) {
+                uint32_t m = esc[q];
+                while (m) {
+                    gather[rank++] = static_cast<uint8_t>(exponent_of<DT>(d[j], 8 * q + (__builtin_ctz(m) >> 2)));
+                    m &= m - 1;
+                }
+            }
+        } else {
+            // dense: every element slot in turn, its rank a masked popcount
+#pragma unroll
+            for (uint32_t q = 0; q < G::kCodeWords; ++q) {
+                const uint32_t m = esc[q];
+#pragma unroll
+                for (uint32_t k = 0; k < 8; ++k) {
+                    const uint32_t bit = 1u << (4 * k);
+                    if (m & bit)
+                        gather[rank + __builtin_popcount(m & (bit - 1))] =
+                            static_cast<uint8_t>(exponent_of<DT>(d[j], 8 * q + k));
+                }
+                rank += __builtin_popcount(m);
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    return uniform(total);
+}
+
+__device__ inline void place_escapes(SZ_GLOBAL uint8_t* esc_out, const uint32_t* esc_lds, uint32_t block_total,
+                                     uint32_t lane) {
+    if (block_total == 0) return;
+    const uint32_t s = static_cast<uint32_t>(reinterpret_cast<uint64_t>(esc_out) & 15u);
+    SZ_GLOBAL uint8_t* at = esc_out - s;   // 16-byte aligned
+    const uint32_t end = s + block_total;
+    const uint4* vec = reinterpret_cast<const uint4*>(esc_lds);
+    // whole windows [first, last): one 16-byte store each
+    const uint32_t first = s ? 1u : 0u, last = end / 16;
+    for (uint32_t v = first + lane; v < last; v += kWaveSize) {
+        const uint4 c = vec[v];
+        const u32x4 cur{c.x, c.y, c.z, c.w};
+        u32x4 w = cur;
+        if (s) {
+            const uint4 p = vec[v - 1];
+            w = funnel16(u32x4{p.x, p.y, p.z, p.w}, cur, s);
+        }
+        __builtin_nontemporal_store(w, (SZ_GLOBAL u32x4*)(at + 16 * v));
+    }
+    // the first and the last window when the range covers them only in
+    // part: lanes 0..15 and 16..31 store one byte each, one store
+    // instruction for both
+    const uint32_t tail = (end - 1) / 16;
+    const bool head_part = s != 0 || end < 16;
+    const bool tail_part = end % 16 != 0 && tail != 0;
+    const uint32_t v = lane < 16 ? 0u : tail;
+    const uint32_t pos = 16 * v + (lane & 15u);
+    const bool mine = lane < 16 ? head_part : (lane < 32 && tail_part);
+    if (mine && pos >= s && pos < end) at[pos] = reinterpret_cast<const uint8_t*>(esc_lds)[pos - s];
+    __builtin_amdgcn_wave_barrier();   // the buffer may be reused once every lane has read it
 }
 
 // E5M2 one-launch main items, one 2048-element sub-chunk j of full block b
@@ -861,15 +1008,30 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
     encode_block<DT, true>(a, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane_id(), s_tbl[wave], s_esc[wave]);
 }
 
-// The partial last block of every tensor, one wave each.
+// The partial last block of every tensor, one wave each.  An escape-heavy
+// tensor of the one-launch compress places the block's escapes last in its
+// escape region, straight from the encode.
 template <uint32_t DT>
 __global__ __launch_bounds__(kWaveSize) void k_encode_tail(EncodeArgs a) {
     __shared__ uint32_t s_tbl[64];
-    __shared__ uint32_t s_esc[kBlockElems / 4];
+    __shared__ uint32_t s_esc[kEscLdsWords];
     const Layout L = layout_of(a.n, DT);
-    const uint32_t t = blockIdx.x;
-    const uint64_t b = L.blocks - 1;
-    encode_block<DT, false>(a, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane_id(), s_tbl, s_esc);
+    const uint32_t t = blockIdx.x, lane = lane_id();
+    const uint64_t b = L.blocks - 1, flat = static_cast<uint64_t>(t) * L.blocks + b;
+    uint32_t escapes;
+    if (!escapes_in_place(a, t, escapes)) {
+        encode_block<DT, false>(a, L, t, b, flat, lane, s_tbl, s_esc);
+        return;
+    }
+    const SZ_GLOBAL uint8_t* cb = gptr(a.codebooks) + 16ull * t;
+    const uint32_t mine = lane < kCodes ? cb[lane] : 0xFFFFu;
+    SZ_GLOBAL uint8_t* dst = dst_of(a.dst, t);
+    BlockRegs<DT> d;
+    load_block<DT, false>(src_of(a.src, t), a.n, b, lane, d);
+    const uint32_t total = encode_gather<DT, false>(L, dst, b, lane, build_code_table(s_tbl, lane, mine), d, s_esc);
+    if (lane == 0) gptr(a.counts)[flat] = total;
+    if (total <= escapes)   // always, unless the tensor gave up (its stream is then marked corrupt)
+        place_escapes(dst + L.esc_at + (escapes - total), s_esc, total, lane);
 }
 
 // One workgroup per tensor: off[b] = escapes in blocks [0, b), then the
@@ -931,18 +1093,6 @@ struct CopyGroup {
     uint32_t sums[kScatterThreads / kWaveSize];
     uint32_t coarse[kGroupBlocks * kBlockElems / 16 / kCoarse];   // the block holding whole window 64 m
 };
-
-// Bytes [16 - s, 32 - s) of the 32-byte sequence prev ++ cur (0 < s < 16).
-__device__ inline u32x4 funnel16(const u32x4& prev, const u32x4& cur, uint32_t s) {
-    const uint32_t q[8] = {prev.x, prev.y, prev.z, prev.w, cur.x, cur.y, cur.z, cur.w};
-    const uint32_t k = 16 - s, j = k >> 2, r = k & 3;   // j in 0..3 (per lane)
-    uint32_t x[5];
-#pragma unroll
-    for (uint32_t i = 0; i < 5; ++i)
-        x[i] = j == 0 ? q[i] : j == 1 ? q[i + 1] : j == 2 ? q[i + 2] : q[i + 3];
-    return u32x4{__builtin_amdgcn_alignbyte(x[1], x[0], r), __builtin_amdgcn_alignbyte(x[2], x[1], r),
-                 __builtin_amdgcn_alignbyte(x[3], x[2], r), __builtin_amdgcn_alignbyte(x[4], x[3], r)};
-}
 
 // Window lw of a block whose range starts s = off & 15 bytes into its first
 // window: the two staged vectors it draws on (a vector wholly outside
@@ -1130,6 +1280,8 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(EncodeArgs a) {
     uint32_t in_group;
     group_blocks_scan(cnt, tid, cg.sums, in_group);
     const SZ_GLOBAL uint8_t* slot0 = gptr(a.staging) + flat0 * kBlockElems;
+    uint32_t placed;
+    if (escapes_in_place(a, t, placed)) return;   // nothing staged
     if (in_group <= kLightEscapes * nb) {
         copy_escapes_light(off, cnt, nb, slot0, dst + L.esc_at, tid);
         return;
@@ -1166,6 +1318,8 @@ __global__ __launch_bounds__(kScatterThreads) void k_offsets_scatter(EncodeArgs 
         write_header(dst, L, DT, gptr(a.codebooks) + 16ull * t, base + in_group,
                      a.out_bytes ? gptr(a.out_bytes) + t : nullptr, tid, compress_gave_up(a, t));
     const SZ_GLOBAL uint8_t* slot0 = gptr(a.staging) + (static_cast<uint64_t>(t) * L.blocks + b0) * kBlockElems;
+    uint32_t placed;
+    if (escapes_in_place(a, t, placed)) return;   // nothing staged
     if (in_group <= kLightEscapes * nb) {
         copy_escapes_light(off, cnt, nb, slot0, dst + L.esc_at, tid);
         return;
@@ -1261,6 +1415,7 @@ constexpr uint32_t kEntryWords = 16;
 constexpr uint32_t kRecProvisional = 0;  // 4 words: the provisional codebook (complete once 15 bytes differ)
 constexpr uint32_t kRecVerdict = 8;      // kProvisionalSame / Reordered / Differs / CountOnly
 constexpr uint32_t kRecGaveUp = 9;       // 1 once any work item of the tensor gave up
+constexpr uint32_t kRecEscapes = 10;     // an escape-heavy tensor's escape count (its final item)
 
 __device__ inline SyncView sync_view(uint8_t* base, uint32_t count) {
     SyncView v;
@@ -1278,6 +1433,23 @@ __device__ inline bool compress_gave_up(const EncodeArgs& a, uint32_t t) {
     if (!a.records) return false;
     const SZ_GLOBAL uint32_t* rec = gptr(a.records) + 32ull * t;
     return rec[kRecVerdict] == 0 || rec[kRecGaveUp] != 0;
+}
+
+__device__ inline bool escapes_in_place(const EncodeArgs& a, uint32_t t, uint32_t& escapes) {
+    if (!a.records) return false;
+    const SZ_GLOBAL uint32_t* rec = gptr(a.records) + 32ull * t;
+    escapes = rec[kRecEscapes];
+    return rec[kRecVerdict] == kProvisionalCountOnly;
+}
+
+// An escape-heavy tensor's main items only count it, so its staging holds
+// nothing else and carries, as u32 words, each main item's histogram (value
+// v of item i at [v * main_items + i]) and then, from its final item, the
+// escapes of the tensor before each main item's first block ([D *
+// main_items + i]): (D + 1) x main_items words, well inside the tensor's
+// 4096 bytes of staging per block.
+__device__ inline SZ_GLOBAL uint32_t* item_table(const EncodeArgs& a, const Layout& L, uint32_t t) {
+    return gptr(reinterpret_cast<uint32_t*>(a.staging + static_cast<uint64_t>(t) * L.blocks * kBlockElems));
 }
 
 __device__ inline uint32_t load_agent(const SZ_GLOBAL uint32_t* p) {
@@ -1431,6 +1603,69 @@ __global__ __launch_bounds__(kPassThreads) void k_codebook(CodebookArgs a) {
         gptr(a.codebooks)[16ull * t + tid] = tid < kCodes ? reinterpret_cast<const uint8_t*>(s_word + 2)[tid] : 0;
 }
 
+// Final item of an escape-heavy tensor, F (the final codebook) in bytes
+// s_word[2..5], c this thread's bin of the complete histogram: the tensor's
+// escape count (elements whose value F does not hold) goes to the record,
+// and the escapes before each main item, summed from the items' histograms
+// (an item's escapes are its elements less its counts of F's values), to
+// the item table, for the encode launches that place the escapes.
+template <uint32_t DT>
+__device__ inline void heavy_bases(const CompressArgs& a, uint32_t t, uint64_t c, uint32_t* bins,
+                                   const uint32_t* s_word, SZ_GLOBAL uint32_t* rec, uint32_t tid, uint32_t lane,
+                                   uint32_t wave) {
+    constexpr uint32_t D = Geometry<DT>::kDomain;
+    const uint8_t* fb = reinterpret_cast<const uint8_t*>(s_word + 2);
+    uint32_t f[kCodes];
+#pragma unroll
+    for (uint32_t k = 0; k < kCodes; ++k) f[k] = fb[k];
+    bool in_f = false;
+#pragma unroll
+    for (uint32_t k = 0; k < kCodes; ++k) in_f |= f[k] == tid;
+    const uint32_t mine = tid < D && !in_f ? static_cast<uint32_t>(c) : 0u;   // counts are below 2^32
+    const uint32_t wsum = __builtin_amdgcn_readlane(wave_scan_incl(mine), 63);
+    if (lane == 0) bins[wave] = wsum;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t escapes = 0;
+#pragma unroll
+        for (uint32_t w = 0; w < kPassWaves; ++w) escapes += bins[w];
+        rec[kRecEscapes] = escapes;   // read by later launches
+    }
+    __syncthreads();
+    // every main item stored its histogram row before adding its counts,
+    // and the complete histogram has been read (store_before_count)
+    const uint64_t n = a.enc.n;
+    const Layout L = layout_of(n, DT);
+    SZ_GLOBAL uint32_t* tab = item_table(a.enc, L, t);
+    const uint32_t items = a.main_items;
+    constexpr uint64_t kItemElems = static_cast<uint64_t>(item_blocks(DT)) * kBlockElems;
+    uint32_t carry = 0;
+    for (uint32_t i0 = 0; i0 < items; i0 += kPassThreads) {
+        const uint32_t i = i0 + tid;
+        uint32_t e = 0;
+        if (i < items) {
+            uint32_t held = 0;
+#pragma unroll
+            for (uint32_t k = 0; k < kCodes; ++k) held += load_agent(tab + static_cast<uint64_t>(f[k]) * items + i);
+            const uint64_t first = i * kItemElems;
+            e = static_cast<uint32_t>(n - first < kItemElems ? n - first : kItemElems) - held;
+        }
+        const uint32_t incl = wave_scan_incl(e);
+        if (lane == 63) bins[wave] = incl;
+        __syncthreads();
+        uint32_t before = carry, all = 0;
+#pragma unroll
+        for (uint32_t w = 0; w < kPassWaves; ++w) {
+            const uint32_t x = bins[w];
+            before += w < wave ? x : 0u;
+            all += x;
+        }
+        if (i < items) tab[static_cast<uint64_t>(D) * items + i] = before + incl - e;
+        carry += all;
+        __syncthreads();   // every wave has read bins before the next round
+    }
+}
+
 // One work item; every thread of the workgroup calls it and every return
 // is taken by all of them.  LDS: bins (counting and ranking), s_tbl (the
 // code table, 256 bytes), s_word ([2..5] codebook, [6] the final item's
@@ -1575,6 +1810,7 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
                                              : s_word[8 + tid - 12];
             sv.list[static_cast<uint64_t>(slot) * kEntryWords + tid] = word;
         }
+        if (count_only) heavy_bases<DT>(a, t, c, bins, s_word, rec, tid, lane, wave);
         return;
     }
     if (it.kind != kItemMain) return;
@@ -1676,8 +1912,11 @@ __device__ inline void run_item(const CompressArgs& a, const SyncView& sv, const
         phantom = count_ragged<DT, kPassThreads>(lds, src, full_blocks * kBlockElems, n, tid);
     __syncthreads();
     const uint32_t copies = hist_replicas(a.enc.count);   // a power of two
+    // an escape-heavy tensor's items also leave their own histograms, from
+    // which its final item places every item's escapes
+    SZ_GLOBAL uint32_t* row = state == 2 ? item_table(a.enc, L, t) + it.idx : nullptr;
     hist_flush<DT, kPassThreads>(bins, tid, sv.hist + 256ull * (copies * t + (it.idx & (copies - 1))), phantom,
-                                 pairs ? 0x0000FFFFu : ~0u);
+                                 pairs ? 0x0000FFFFu : ~0u, row, a.main_items);
 }
 
 // One workgroup per item: workgroup i runs item i of the schedule.
@@ -1955,22 +2194,72 @@ __device__ inline void transcode_list(const CompressArgs& a, const SyncView& sv,
 }
 
 // The full blocks of the escape-heavy tensors (list 2), encoded from the
-// input with their final codebooks exactly as k_encode does, spread over
-// the waves of the grid.
+// input with their final codebooks exactly as k_encode does, each escape
+// written straight to its place in the stream.  A workgroup takes one main
+// item's blocks at a time (grid-stride over the items of every listed
+// tensor), its waves one block each per round in block order; the item's
+// first escape goes where the final item's sum over the earlier items put
+// it, and a round's blocks follow their predecessors' counts, shared
+// through s_cnt (two slots per wave, alternating by round).  The
+// workgroup's waves all call it.
 template <uint32_t DT>
-__device__ inline void encode_list(const CompressArgs& a, const SZ_GLOBAL uint32_t* list, uint32_t listed, uint64_t w,
-                                   uint64_t waves, uint32_t* tbl_words, uint32_t* esc_words, uint32_t lane) {
-    const uint64_t full_blocks = a.enc.n / kBlockElems;
-    const uint64_t total = static_cast<uint64_t>(listed < a.enc.count ? listed : a.enc.count) * full_blocks;
-    const Layout L = layout_of(a.enc.n, DT);
-    // grid-stride: the waves in flight at any moment cover consecutive
-    // blocks, as k_encode's do (contiguous runs per wave spread them over the
-    // whole tensor at once and measured slower)
-    for (uint64_t i = w; i < total; i += waves) {
-        const uint32_t t = uniform(list[i / full_blocks * kEntryWords]);
-        const uint64_t b = i % full_blocks;
-        __builtin_amdgcn_wave_barrier();   // the previous block's code table is no longer read
-        encode_block<DT, true>(a.enc, L, t, b, static_cast<uint64_t>(t) * L.blocks + b, lane, tbl_words, esc_words);
+__device__ inline void encode_heavy(const CompressArgs& a, const SZ_GLOBAL uint32_t* list, uint32_t listed,
+                                    uint32_t* tbl_words, uint32_t* esc_words, uint32_t* s_cnt, uint32_t lane,
+                                    uint32_t wave) {
+    constexpr uint32_t kIB = item_blocks(DT);
+    constexpr uint32_t kRounds = kIB / kWavesPerGroup;
+    const uint64_t n = a.enc.n;
+    const uint64_t full_blocks = n / kBlockElems;
+    const uint64_t items = (full_blocks + kIB - 1) / kIB;   // the items holding full blocks
+    const uint64_t total = static_cast<uint64_t>(listed < a.enc.count ? listed : a.enc.count) * items;
+    const Layout L = layout_of(n, DT);
+    uint32_t round = 0;
+    for (uint64_t j = blockIdx.x; j < total; j += gridDim.x) {
+        const uint32_t t = uniform(list[j / items * kEntryWords]);
+        const uint64_t item = j % items;
+        const SZ_GLOBAL uint32_t* tab = item_table(a.enc, L, t);
+        uint32_t escapes = 0;
+        escapes_in_place(a.enc, t, escapes);
+        uint64_t run = uniform(tab[static_cast<uint64_t>(Geometry<DT>::kDomain) * a.main_items + item]);
+        const SZ_GLOBAL uint8_t* cb = gptr(a.enc.codebooks) + 16ull * t;
+        const uint32_t mine = lane < kCodes ? cb[lane] : 0xFFFFu;
+        const SZ_GLOBAL uint8_t* src = src_of(a.enc.src, t);
+        SZ_GLOBAL uint8_t* dst = dst_of(a.enc.dst, t);
+        __builtin_amdgcn_wave_barrier();   // the previous item's code table is no longer read
+        const uint8_t* tbl = build_code_table(tbl_words, lane, mine);
+        BlockRegs<DT> d;
+        uint64_t b = item * kIB + wave;
+        bool live = b < full_blocks;   // wave-uniform
+        if (live) load_block<DT, true>(src, n, b, lane, d);
+        for (uint32_t r = 0; r < kRounds; ++r, ++round) {
+            uint32_t count = 0;
+            if (live) {
+                count = encode_gather<DT, true>(L, dst, b, lane, tbl, d, esc_words);
+                if (lane == 0) gptr(a.enc.counts)[static_cast<uint64_t>(t) * L.blocks + b] = count;
+            }
+            // the next round's block is read while this one's escapes are placed
+            const uint64_t b_next = b + kWavesPerGroup;
+            const bool live_next = r + 1 < kRounds && b_next < full_blocks;
+            if (live_next) load_block<DT, true>(src, n, b_next, lane, d);
+            uint32_t* slot = s_cnt + (round & 1u) * kWavesPerGroup;
+            if (lane == 0) slot[wave] = count;
+            __syncthreads();
+            uint32_t before = 0, all = 0;
+#pragma unroll
+            for (uint32_t w = 0; w < kWavesPerGroup; ++w) {
+                const uint32_t x = slot[w];
+                before += w < wave ? x : 0u;
+                all += x;
+            }
+            // (the places stay inside the escape region even if the tensor
+            // gave up and the sums are not its own: its stream is then
+            // marked corrupt)
+            if (live && run + before + count <= escapes)
+                place_escapes(dst + L.esc_at + run + before, esc_words, count, lane);
+            run += all;
+            b = b_next;
+            live = live_next;
+        }
     }
 }
 
@@ -1986,7 +2275,8 @@ template <uint32_t DT>
 // per SIMD, 80 VGPRs, where 8 would spill 31 of them)
 __global__ __launch_bounds__(kThreads, DT == kDtypeBF16 ? 8 : 6) void k_transcode(CompressArgs a) {
     __shared__ uint32_t s_tbl[kWavesPerGroup][64];
-    __shared__ uint32_t s_esc[kWavesPerGroup][kBlockElems / 4];
+    __shared__ uint32_t s_esc[kWavesPerGroup][kEscLdsWords];
+    __shared__ uint32_t s_cnt[2 * kWavesPerGroup];
     const uint32_t lane = lane_id(), wave = uniform(threadIdx.x / kWaveSize);
     const SyncView sv = sync_view(a.sync, a.enc.count);
     const uint64_t waves = static_cast<uint64_t>(gridDim.x) * kWavesPerGroup;
@@ -1995,7 +2285,7 @@ __global__ __launch_bounds__(kThreads, DT == kDtypeBF16 ? 8 : 6) void k_transcod
     transcode_list<DT, true>(a, sv, sv.list, uniform(sv.listed[0]), w, waves, s_tbl[wave], s_esc[wave], lane);
     transcode_list<DT, false>(a, sv, sv.list + entries, uniform(sv.listed[1]), w, waves, s_tbl[wave], s_esc[wave],
                               lane);
-    encode_list<DT>(a, sv.list + 2 * entries, uniform(sv.listed[2]), w, waves, s_tbl[wave], s_esc[wave], lane);
+    encode_heavy<DT>(a, sv.list + 2 * entries, uniform(sv.listed[2]), s_tbl[wave], s_esc[wave], s_cnt, lane, wave);
 }
 
 // ----------------------------------------------------------------- decode

@@ -499,6 +499,41 @@ def test_fused_escape_heavy_tensors_encoded_after_counting(sz):
         assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), BF16), x), i
 
 
+def _heavy(n, seed, dt):
+    """An escape-heavy tensor: the stress tensor for BF16; for E5M2
+    uniformly random bytes (the 15 commonest of 32 exponents cover about
+    half the elements)."""
+    if dt == BF16:
+        return kvsynth.stress(n, seed=seed)
+    return np.random.default_rng(seed).integers(0, 256, n, dtype=np.uint16).astype(np.uint8)
+
+
+@pytest.mark.parametrize("dt,n", [(BF16, 3000), (BF16, 5 * 4096), (BF16, (1 << 26) + 65536 + 5),
+                                  (E5M2, 3000), (E5M2, (1 << 21) + 4096 + 9), (E5M2, (1 << 27) + 3 * 4096 + 7)])
+def test_fused_escape_heavy_escapes_in_place(sz, dt, n):
+    """Escape-heavy tensors have their escapes written straight to their
+    place: each main item's histogram and the final item's sum over the
+    earlier items give every item's first escape, and the partial last
+    block's escapes go last.  A tensor with only a partial block, one
+    without one, and more than 1024 main items (two rounds of the final
+    item's sum); beside an ordinary tensor."""
+    plain = kvsynth.single_tensor(n, seed=751)
+    if dt == E5M2:
+        plain = kvsynth.e5m2_of(plain)
+    xs = [_heavy(n, 750, dt), plain, _heavy(n, 752, dt)]
+    assert [_sample_escape_fraction(x, dt) > 0.25 for x in xs] == [True, False, True]
+    say("fused escapes in place", dt, n)
+    bc = sz.codec.BatchCodec(len(xs), n, dt)
+    bc.set_inputs([to_dev(x) for x in xs])
+    bc.compress_fused(options=every(sz))
+    bc.decompress()
+    torch.cuda.synchronize()
+    assert (bc.fused_status.cpu().numpy() == 0).all()
+    for i, x in enumerate(xs):
+        _check_against_oracle(x, dt, bc.stream(i), bc.hists[i], bc.codebooks[i])
+        assert int(bc.status[i]) == 0 and np.array_equal(to_host(bc.output(i), dt), x), i
+
+
 def _dense_escapes_outside_sample(n, seed, dt=BF16):
     """_skewed(..., 'members') with some blocks outside the sample replaced
     by uniformly random bit patterns: the sample escapes rarely (so the

@@ -878,7 +878,13 @@ __device__ inline void place_escapes(SZ_GLOBAL uint8_t* esc_out, const uint32_t*
     SZ_GLOBAL uint8_t* at = esc_out - s;   // 16-byte aligned
     const uint32_t end = s + block_total;
     const uint4* vec = reinterpret_cast<const uint4*>(esc_lds);
-    // whole windows [first, last): one 16-byte store each
+    // whole windows [first, last): one 16-byte store each.  Plain stores:
+    // a block's first and last lines are shared with its neighbours' escapes,
+    // written by other waves at other times, and the L2 merges them, where
+    // non-temporal stores of them made partial-line writes (the stress
+    // tensor's compress 0.355 ms against 0.397 ms; the separate calls'
+    // escape copy, which stores whole windows of one group at a time, is
+    // faster non-temporal: 0.365 against 0.426 ms)
     const uint32_t first = s ? 1u : 0u, last = end / 16;
     for (uint32_t v = first + lane; v < last; v += kWaveSize) {
         const uint4 c = vec[v];
@@ -888,7 +894,7 @@ __device__ inline void place_escapes(SZ_GLOBAL uint8_t* esc_out, const uint32_t*
             const uint4 p = vec[v - 1];
             w = funnel16(u32x4{p.x, p.y, p.z, p.w}, cur, s);
         }
-        __builtin_nontemporal_store(w, (SZ_GLOBAL u32x4*)(at + 16 * v));
+        *(SZ_GLOBAL u32x4*)(at + 16 * v) = w;
     }
     // the first and the last window when the range covers them only in
     // part: lanes 0..15 and 16..31 store one byte each, one store

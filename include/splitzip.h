@@ -184,8 +184,10 @@ sz_status sz_decode_batched(const void* const* d_srcs, const uint64_t* d_src_byt
  * a quarter of the sample escapes under its own provisional codebook (an
  * escape-heavy tensor, where the final codebook nearly always differs and a
  * recode would rewrite most of the stream) is only counted in the first
- * kernel and encoded from its input by the second, with the final codebook.
- * The bytes written are the same as the separate calls'.  Tensors below
+ * kernel and encoded from its input by the second, with the final codebook,
+ * its escapes written straight to their place (from per-item histograms the
+ * first kernel keeps in the workspace).  The bytes written are the same as
+ * the separate calls'.  Tensors below
  * the options' fused_min_elements run the separate calls' kernels, with the
  * same results; by default that is BF16 tensors under 2^21 elements, and
  * E5M2 tensors under 2^22 elements or in calls of fewer than 2^28 elements
